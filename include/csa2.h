@@ -1,0 +1,186 @@
+/*
+ * csa2.h — C ABI of the CSA2 (Compressed Sparse Attention 2) decode hot path
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are those of the CSA2 attention step as described in section
+ * 一 of the teardown "DeepSeek V4.1 Flash 拆解：KV Cache 压掉 3/4 的工程胜利，
+ * 与它没解决的三个问题" (austincafe.tech) and in the arXiv abstract of
+ * "DeepSeek-V4.1-Flash: Pushing the Limits of KV Cache Compression":
+ *   - the main KV cache is stored as FP4 (E2M1 codes plus one E4M3 scale per
+ *     16 channels, "MXFP4" in the page's words); the sliding-window (SWA) KV
+ *     stays in FP8;
+ *   - a Full-mode layer runs its own indexer over every cached entry, keeps a
+ *     Top-K and builds a candidate pool of whole 8-position blocks;
+ *   - a Reindex-mode layer rescores only the pool with its own indexer query
+ *     and keeps its own Top-K;
+ *   - a Reuse-mode layer attends sparsely with an earlier layer's indices.
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument except `stream` is a DEVICE pointer owned by the
+ *     caller.  The library never allocates, frees or synchronises, keeps no
+ *     pointer after returning, and holds no global state other than a
+ *     thread-local copy of the last error message.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work is enqueued asynchronously on it.
+ *   - The main cache is packed: sequence b occupies cache rows
+ *     [seq_start[b], seq_start[b] + n) and entry ids inside a sequence are
+ *     sequence-local (0 .. n-1).  A query row r belongs to sequence
+ *     row_seq[r] and sees its first row_len[r] entries.
+ *   - Index lists are int32, ascending, padded at the end with -1.
+ *   - Arguments are validated on the host before any HIP call; on failure
+ *     the call returns a non-zero status, enqueues nothing and leaves every
+ *     output untouched.  Values stored in device memory (row lengths, index
+ *     lists) cannot be validated on the host: kernels skip any index outside
+ *     its valid range instead of reading or writing out of bounds.
+ *   - Calls that share a workspace must not overlap on different streams.
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CSA2_OK = 0,
+    CSA2_ERR_NULL = 1,         /* a required pointer is NULL */
+    CSA2_ERR_SHAPE = 2,        /* a size argument is negative or inconsistent */
+    CSA2_ERR_UNSUPPORTED = 3,  /* well-defined, but outside this library's limits */
+    CSA2_ERR_WORKSPACE = 4,    /* workspace missing, too small or not 256-byte aligned */
+    CSA2_ERR_LAUNCH = 5        /* a HIP launch failed (detail in csa2_last_error) */
+} csa2_status_t;
+
+typedef enum {
+    CSA2_F32 = 0,   /* IEEE binary32 */
+    CSA2_BF16 = 1   /* bfloat16 */
+} csa2_dtype_t;
+
+/* Name of a status code (static storage). */
+const char* csa2_status_string(int status);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char* csa2_last_error(void);
+
+/* ABI version of this header; bumped on any incompatible change. */
+#define CSA2_ABI_VERSION 1
+int csa2_abi_version(void);
+
+/* ---------------------------------------------------------------------- */
+/* Quantize + append.  FP4 KV cache paragraph: E2M1 codes with one E4M3      */
+/* scale per 16 channels.                                                    */
+/* ---------------------------------------------------------------------- */
+/*
+ * Quantize T rows of D channels and store row t at cache row dst_row[t].
+ *   x        [T, D] in `x_dtype` (CSA2_F32 or CSA2_BF16), row-major.
+ *   dst_row  [T] int64 destination cache rows; rows outside [0, cache_rows)
+ *            are skipped.
+ *   codes    [cache_rows, D/2] uint8: channel 2i in the low nibble, 2i+1 in
+ *            the high nibble; bit 3 of a code is the sign, bits 0..2 the
+ *            E2M1 magnitude.
+ *   scales   [cache_rows, D/16] uint8: OCP E4M3 bits, one per 16 channels.
+ * Rule per group of 16 channels: scale = E4M3(amax/6) rounded to nearest
+ * even, saturating at 448; each code is the E2M1 value nearest to x/scale
+ * (ties to even, clipped at +-6); a scale of zero gives zero magnitudes;
+ * the code's sign bit copies the sign of x.  Inputs must be finite.
+ * Limits: T >= 0, 16 <= D <= 8192, D % 16 == 0.
+ */
+csa2_status_t csa2_quantize_append(const void* x, int32_t x_dtype, int32_t T, int32_t D,
+                                   const int64_t* dst_row, uint8_t* codes, uint8_t* scales,
+                                   int64_t cache_rows, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Full mode: own indexer over every entry, Top-K, block pool.               */
+/* CSA2 modes and Hierarchical Sparse Indexer paragraphs.                    */
+/* ---------------------------------------------------------------------- */
+/*
+ * Score of entry j for query row r (the pages give none; the reading used):
+ *   s_j = sum_h w[r,h] * max(0, sum_d qI[r,h,d] * ikeys[seq_start + j, d])
+ * with qI and ikeys decoded from OCP E4M3, computed in fp32 (exact whenever
+ * the inputs are small integers, as in every shipped workload).
+ *   qI        [R, Hi, Di] uint8 E4M3     w  [R, Hi] float32
+ *   ikeys     [rows, Di] uint8 E4M3 (one key per cache row)
+ *   seq_start [S] int64   row_seq [R] int32   row_len [R] int32 (<= max_len)
+ *   topk_idx  [R, K] int32 out: the min(K, n) entries first in the order
+ *             (score descending, entry id ascending), written ascending and
+ *             padded with -1.  Scores compare as reals (-0 == +0).
+ *   pool_blocks [R, P] int32 out (may be NULL): the min(P, ceil(n/8)) blocks
+ *             [8b, 8b+8) first in the order (block max descending, block id
+ *             ascending), where a block's max is over its visible entries;
+ *             ascending, -1 padded.
+ *   workspace: csa2_index_full_workspace_bytes(R, max_len, K, P, block)
+ *             bytes of device memory, 256-byte aligned, contents ignored.
+ * Limits: block == 8; 1 <= K <= 2048; 0 <= P <= 2048 (P == 0 iff
+ * pool_blocks == NULL); 1 <= Hi <= 64; 32 <= Di <= 256, Di % 32 == 0;
+ * 0 <= max_len < 2^31 - 64.
+ */
+size_t csa2_index_full_workspace_bytes(int32_t R, int32_t max_len, int32_t K, int32_t P,
+                                       int32_t block);
+csa2_status_t csa2_index_full(const uint8_t* qI, const float* w, const uint8_t* ikeys,
+                              const int64_t* seq_start, const int32_t* row_seq,
+                              const int32_t* row_len, int32_t R, int32_t Hi, int32_t Di,
+                              int32_t max_len, int32_t K, int32_t P, int32_t block,
+                              int32_t* topk_idx, int32_t* pool_blocks,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Reindex mode: rescore only the pool with this layer's own indexer query.  */
+/* CSA2 modes and Hierarchical Sparse Indexer paragraphs.                    */
+/* ---------------------------------------------------------------------- */
+/*
+ * Candidates of row r are positions 8b + t (t < 8, 8b + t < row_len[r]) of
+ * every pool block b = pool_blocks[r, p] that is in [0, ceil(n/8)); -1 and
+ * out-of-range ids are skipped; ids must be distinct.  Scores use this call's
+ * qI / w with the shared ikeys (same formula as csa2_index_full); the output
+ * is the Top-K of the candidates in the same order, ascending, -1 padded.
+ * Limits: block == 8; 1 <= K <= 2048; 1 <= P <= 2048; Hi, Di as above.
+ */
+size_t csa2_index_reindex_workspace_bytes(int32_t R, int32_t K, int32_t P, int32_t block);
+csa2_status_t csa2_index_reindex(const uint8_t* qI, const float* w, const uint8_t* ikeys,
+                                 const int64_t* seq_start, const int32_t* row_seq,
+                                 const int32_t* row_len, const int32_t* pool_blocks,
+                                 int32_t R, int32_t Hi, int32_t Di, int32_t K, int32_t P,
+                                 int32_t block, int32_t* topk_idx,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------- */
+/* Sparse attention (Reuse mode = this call with inherited indices).        */
+/* CSA2 modes paragraph; FP4 main KV and FP8 SWA KV.                         */
+/* ---------------------------------------------------------------------- */
+/*
+ * For query row r and head h, one softmax over the key set
+ *   { deq(main entry j) : j in topk_idx[r, :], 0 <= j < row_len[r] }
+ *   followed by { SWA rows swa_row_start[r] .. + min(swa_len[r], W) - 1 },
+ * where one cached latent per entry is both key and value (all H heads share
+ * it): out[r,h] = sum_k softmax(scale * q[r,h] . key_k) * key_k, and
+ * lse[r,h] = log-sum-exp of the logits.  An empty key set gives out = 0 and
+ * lse = -inf.
+ *   q        [R, H, D] bfloat16 bits.  Used in the matrix cores as fp16, which
+ *            holds every bf16 value of magnitude in [2^-14, 65504] exactly;
+ *            |q| must stay below 65504.
+ *   codes / scales: the main cache as written by csa2_quantize_append.
+ *   topk_idx [R, K] int32, -1 = no entry.
+ *   swa      [swa_rows, D] uint8 E4M3 (unscaled FP8 SWA rows).
+ *   out      [R, H, D] float32;  lse [R, H] float32 (may be NULL).
+ *   workspace: csa2_sparse_attn_workspace_bytes(R, H, D, K, W) bytes,
+ *            256-byte aligned (may be 0 bytes and NULL when that is 0).
+ * Arithmetic: dequantised keys are exact in fp16; logits accumulate in fp32;
+ * softmax in fp32; probabilities enter the PV product rounded to fp16;
+ * outputs accumulate in fp32.
+ * Limits: H >= 1; D in {64, 128, 256, 512}; 0 <= K <= 4096; 0 <= W <= 4096.
+ */
+size_t csa2_sparse_attn_workspace_bytes(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W);
+csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                               const int64_t* seq_start, const int32_t* row_seq,
+                               const int32_t* row_len, const int32_t* topk_idx, int32_t K,
+                               const uint8_t* swa, const int64_t* swa_row_start,
+                               const int32_t* swa_len, int32_t R, int32_t H, int32_t D,
+                               int32_t W, float softmax_scale, float* out, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

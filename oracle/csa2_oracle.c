@@ -284,34 +284,32 @@ int ora_index_full(const uint8_t* qI, const float* w, const uint8_t* ikeys,
     build_tables();
     if (R < 0 || K <= 0 || P < 0 || block <= 0 || Hi <= 0 || Di <= 0) return -1;
     for (int32_t r = 0; r < R; ++r) if (row_len[r] < 0 || row_len[r] > max_len) return -2;
-    int err = 0;
-#pragma omp parallel for schedule(dynamic, 1) reduction(|:err)
+    /* rows one after another; the independent entry scores of a row in parallel */
     for (int32_t r = 0; r < R; ++r) {
         int32_t n = row_len[r];
         int64_t nb = ((int64_t)n + block - 1) / block;
         const uint8_t* kb = ikeys + seq_start[row_seq[r]] * Di;
         item_t* it = (item_t*)malloc(sizeof(item_t) * (size_t)(n > 0 ? n : 1));
-        double* sc = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
         item_t* bl = (item_t*)malloc(sizeof(item_t) * (size_t)(nb > 0 ? nb : 1));
-        if (!it || !sc || !bl) { err = 1; free(it); free(sc); free(bl); continue; }
+        if (!it || !bl) { free(it); free(bl); return -3; }
+#pragma omp parallel for schedule(static)
         for (int32_t j = 0; j < n; ++j) {
             /* scores are the float results, as the library returns them */
-            sc[j] = (double)(float)index_score(qI + (int64_t)r * Hi * Di, w + (int64_t)r * Hi,
-                                               kb + (int64_t)j * Di, Hi, Di);
-            it[j].v = sc[j];
+            it[j].v = (double)(float)index_score(qI + (int64_t)r * Hi * Di, w + (int64_t)r * Hi,
+                                                 kb + (int64_t)j * Di, Hi, Di);
             it[j].id = j;
         }
         for (int64_t b = 0; b < nb; ++b) {
             double m = -INFINITY;
-            for (int64_t j = b * block; j < (b + 1) * block && j < n; ++j) if (sc[j] > m) m = sc[j];
+            for (int64_t j = b * block; j < (b + 1) * block && j < n; ++j) if (it[j].v > m) m = it[j].v;
             bl[b].v = m;
             bl[b].id = b;
         }
         take_first_k(it, n, K, topk_idx + (int64_t)r * K);
         if (pool_blocks) take_first_k(bl, nb, P, pool_blocks + (int64_t)r * P);
-        free(it); free(sc); free(bl);
+        free(it); free(bl);
     }
-    return err ? -3 : 0;
+    return 0;
 }
 
 /* Reindex mode (CSA2 modes and Hierarchical Sparse Indexer paragraphs): reuse

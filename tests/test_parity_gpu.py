@@ -1,0 +1,297 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on seeded
+synthetic inputs.  Codes, scales and index lists must match bit for bit;
+attention outputs must meet the tolerance in tests/helpers.py.
+
+Sizes: small cases that span several tiles/workgroups with ragged tails and
+the degenerate cases (empty rows, fewer entries than K or P*8, all-equal
+scores, -1 and out-of-range indices, empty key sets), plus the tiny workload
+in full.  The full-size workloads are in test_parity_full_gpu.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import oracle.step
+import sparse_attention_fp4_amd as csa2
+from sparse_attention_fp4_amd.step import CSA2Step
+import workloads
+from helpers import (bits16, check_attn, log, np_, oracle_attn_rows, oracle_index_rows, oracle_quantize,
+                     oracle_reindex_rows)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    csa2.lib()
+
+
+def gen(seed):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return g
+
+
+# ----------------------------------------------------------------- quantize
+
+def run_quantize(x, dst=None, rows=None):
+    T, D = x.shape
+    rows = T if rows is None else rows
+    dst = torch.arange(T, dtype=torch.int64, device=DEV) if dst is None else dst
+    codes = torch.full((rows, D // 2), 0xAB, dtype=torch.uint8, device=DEV)
+    scales = torch.full((rows, D // 16), 0xCD, dtype=torch.uint8, device=DEV)
+    csa2.csa2_quantize_append(x, dst, codes, scales)
+    torch.cuda.synchronize()
+    return np_(codes), np_(scales)
+
+
+@pytest.mark.parametrize("case", ["f32_normal_d128", "bf16_normal_d512", "bf16_student_outliers_d512"])
+def test_quantize_matches_oracle(case):
+    log(f"quantize parity: {case}")
+    g = gen(11)
+    if case == "f32_normal_d128":
+        x = torch.randn(4099, 128, generator=g, device=DEV)
+    elif case == "bf16_normal_d512":
+        x = torch.randn(3001, 512, generator=g, device=DEV).to(torch.bfloat16)
+    else:
+        cfg = workloads.scaled(workloads.CONFIGS[5], B=2)
+        wl = workloads.make(cfg, DEV, layers=[0], lengths=np.array([1500, 1501]))
+        x = wl.kv_raw
+    c, s = run_quantize(x)
+    rc, rs = oracle_quantize(x)
+    assert np.array_equal(s, rs), "scales differ"
+    assert np.array_equal(c, rc), "codes differ"
+
+
+def test_quantize_edge_values_and_midpoints():
+    """Zeros, -0, tiny and huge values (saturation), and elements exactly on and
+    one ulp around every E2M1 midpoint for every scale code."""
+    rows = []
+    for S in range(1, 0x7F):
+        s = oracle.e4m3_value(S)
+        for mid in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0):
+            m32 = np.float32(mid * s)
+            g = np.zeros(16, np.float32)
+            g[0] = np.float32(6.0 * s)
+            g[1] = np.nextafter(m32, np.float32(0))
+            g[2] = m32
+            g[3] = np.nextafter(m32, np.float32(1e30))
+            g[4] = -m32
+            g[5] = -0.0
+            rows.append(g)
+        # amax exactly on a scale midpoint (tie between two scale codes) and around it
+        if S < 0x7E:
+            mid = 0.5 * (s + oracle.e4m3_value(S + 1))
+            for v in (np.nextafter(np.float32(6 * mid), np.float32(0)), np.float32(6 * mid),
+                      np.nextafter(np.float32(6 * mid), np.float32(1e30))):
+                g = np.zeros(16, np.float32)
+                g[7] = v
+                g[8] = -np.float32(v) * np.float32(0.3)
+                rows.append(g)
+    special = np.zeros((6, 16), np.float32)
+    special[1, :] = -0.0
+    special[2, 3] = 1e-30
+    special[3, 0] = 3e38
+    special[3, 1] = -1.0
+    special[4, :] = np.float32(6.0 * 448.0)
+    special[5, 2] = np.float32(6.0 * 2.0 ** -10)
+    x = np.concatenate([np.stack(rows), special])          # [groups, 16]: one group per row
+    xt = torch.tensor(x, device=DEV)
+    c, s = run_quantize(xt)
+    rc, rs = oracle_quantize(xt)
+    assert np.array_equal(s, rs) and np.array_equal(c, rc)
+
+
+def test_quantize_scatter_and_skips_out_of_range_rows():
+    g = gen(12)
+    x = torch.randn(40, 32, generator=g, device=DEV).to(torch.bfloat16)
+    dst = torch.tensor([(7 * i) % 50 for i in range(38)] + [-1, 50], dtype=torch.int64, device=DEV)
+    c, s = run_quantize(x, dst, rows=50)
+    rc, rs = oracle_quantize(x)
+    d = np_(dst)
+    for i in range(38):
+        assert np.array_equal(c[d[i]], rc[i]) and np.array_equal(s[d[i]], rs[i])
+    untouched = sorted(set(range(50)) - set(int(v) for v in d[:38]))
+    assert (c[untouched] == 0xAB).all() and (s[untouched] == 0xCD).all()
+
+
+# ----------------------------------------------------------------- indexer
+
+def small_workload(lengths, Hi=64, Di=128, idx_dist="int3", w_dist="u01_16", layers="FRU", seed=3, D=128, H=16,
+                   W=16):
+    cfg = workloads.Config(90 + seed, "small", B=len(lengths), N=None, D=D, W=W, H=H, Hi=Hi, Di=Di, K=0, P=0,
+                           idx_dist=idx_dist, w_dist=w_dist, layers=layers)
+    return workloads.make(cfg, DEV, lengths=np.array(lengths))
+
+
+def gpu_index_full(wl, layer, K, P):
+    topk, pool = csa2.csa2_index_full(wl.qI[layer], wl.w[layer], wl.ikeys, wl.seq_start, wl.row_seq,
+                                      wl.row_len, int(max(wl.lengths.max(), 1)), K, P, want_pool=P > 0)
+    torch.cuda.synchronize()
+    return np_(topk), (np_(pool) if pool is not None else None)
+
+
+@pytest.mark.parametrize("name,lengths,Hi,Di,K,P,idx", [
+    ("ragged_int3", [1, 7, 100, 1000, 4097, 20001], 64, 128, 512, 2048, "int3"),
+    ("ties_alphabet", [30000, 17, 8191, 25000], 64, 128, 512, 2048, "ties"),
+    ("p_below_k", [5000, 3333], 64, 128, 100, 10, "int3"),
+    ("small_k_p", [3000, 64, 9], 8, 64, 64, 256, "int3"),
+    ("hi40_di256", [6000, 2500], 40, 256, 300, 500, "int3"),
+    ("hi1_di64", [4096], 1, 64, 64, 256, "int3"),
+    ("empty_row", [0, 900], 16, 64, 32, 40, "int3"),
+])
+def test_index_full_matches_oracle(name, lengths, Hi, Di, K, P, idx):
+    log(f"index_full parity: {name}")
+    wl = small_workload(lengths, Hi=Hi, Di=Di, idx_dist=idx)
+    rows = list(range(len(lengths)))
+    topk, pool = gpu_index_full(wl, 0, K, P)
+    rt, rp, _ = oracle_index_rows(wl, 0, rows, K, P)
+    assert np.array_equal(topk, rt), f"{name}: top-k differs"
+    assert np.array_equal(pool, rp), f"{name}: pool differs"
+
+
+def test_index_full_all_equal_scores_and_no_pool():
+    wl = small_workload([5000, 123], Hi=16, Di=64)
+    wl.w[0].zero_()                      # every score is 0: ties everywhere
+    topk, pool = gpu_index_full(wl, 0, 200, 30)
+    rt, rp, _ = oracle_index_rows(wl, 0, [0, 1], 200, 30)
+    assert np.array_equal(topk, rt) and np.array_equal(pool, rp)
+    assert topk[0].tolist() == list(range(200))
+    topk2, none = gpu_index_full(wl, 0, 200, 0)
+    assert none is None and np.array_equal(topk2, rt)
+
+
+@pytest.mark.parametrize("name,lengths,Hi,Di,K,P,idx", [
+    ("ragged_int3", [1, 7, 100, 1000, 4097, 20001], 64, 128, 512, 2048, "int3"),
+    ("ties_alphabet", [30000, 17, 8191], 64, 128, 512, 2048, "ties"),
+    ("small", [3000, 64, 9], 8, 64, 64, 256, "int3"),
+])
+def test_index_reindex_matches_oracle(name, lengths, Hi, Di, K, P, idx):
+    log(f"index_reindex parity: {name}")
+    wl = small_workload(lengths, Hi=Hi, Di=Di, idx_dist=idx)
+    rows = list(range(len(lengths)))
+    _, rpool, packed = oracle_index_rows(wl, 0, rows, K, P)
+    want = oracle_reindex_rows(wl, 1, rows, packed, rpool, K)
+    pool_t = torch.tensor(rpool, device=DEV)
+    got = csa2.csa2_index_reindex(wl.qI[1], wl.w[1], wl.ikeys, wl.seq_start, wl.row_seq, wl.row_len, pool_t, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(got), want)
+
+
+def test_index_reindex_unsorted_pool_with_invalid_ids():
+    wl = small_workload([2000, 500], Hi=16, Di=64)
+    rng = np.random.default_rng(5)
+    K, P = 50, 40
+    pool = np.full((2, P), -1, np.int32)
+    for r, n in enumerate([2000, 500]):
+        nb = (n + 7) // 8
+        ids = rng.choice(nb, 30, replace=False)
+        ids[3] = nb + 5                              # out of range: skipped
+        pool[r, :30] = ids
+        pool[r, 30:35] = -1
+        pool[r, 35:] = rng.choice(np.setdiff1d(np.arange(nb), ids), 5, replace=False)
+    packed = oracle_index_rows(wl, 0, [0, 1], K, P)[2]
+    want = oracle_reindex_rows(wl, 1, [0, 1], packed, pool, K)
+    got = csa2.csa2_index_reindex(wl.qI[1], wl.w[1], wl.ikeys, wl.seq_start, wl.row_seq, wl.row_len,
+                                  torch.tensor(pool, device=DEV), K)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(got), want)
+
+
+# ----------------------------------------------------------------- attention
+
+def run_attn(wl, layer, topk, W, scale):
+    out, lse = csa2.csa2_sparse_attn(wl.q[layer], wl.codes_dev, wl.scales_dev, wl.seq_start, wl.row_seq,
+                                     wl.row_len, topk, wl.swa[layer], wl.swa_row_start, wl.swa_len, W, scale)
+    torch.cuda.synchronize()
+    return np_(out), np_(lse)
+
+
+def with_cache(wl):
+    rows, D = wl.kv_raw.shape
+    wl.codes_dev = torch.empty(rows, D // 2, dtype=torch.uint8, device=DEV)
+    wl.scales_dev = torch.empty(rows, D // 16, dtype=torch.uint8, device=DEV)
+    csa2.csa2_quantize_append(wl.kv_raw, torch.arange(rows, dtype=torch.int64, device=DEV), wl.codes_dev,
+                              wl.scales_dev)
+    return wl
+
+
+@pytest.mark.parametrize("name,lengths,D,H,K,W", [
+    ("d128_h8_k64_w32_single_row_split", [4096], 128, 8, 64, 32),
+    ("d512_h64_k512_w128_split", [9000, 700, 30000], 512, 64, 512, 128),
+    ("d512_h64_many_rows_nosplit", [300 + 37 * i for i in range(130)], 512, 64, 512, 128),
+    ("d256_h24_k100_w7", [1000, 77, 5000, 2222], 256, 24, 100, 7),
+    ("d64_h3_k33_w0", [500, 40], 64, 3, 33, 0),
+    ("d512_h16_k0_swa_only", [100, 100], 512, 16, 0, 128),
+])
+def test_sparse_attn_matches_oracle(name, lengths, D, H, K, W):
+    log(f"sparse_attn parity: {name}")
+    wl = with_cache(small_workload(lengths, Hi=8, Di=64, D=D, H=H, W=W, layers="F"))
+    R = len(lengths)
+    rng = np.random.default_rng(len(name))
+    topk = np.full((R, K), -1, np.int32)
+    for r, n in enumerate(lengths):
+        k = min(K, n)
+        sel = np.sort(rng.choice(n, k, replace=False)) if k else np.array([], np.int64)
+        topk[r, :k] = sel
+        if K >= 4 and k >= 4:                      # holes and out-of-range ids are skipped
+            topk[r, 1] = -1
+            topk[r, 2] = n + 3
+    if W > 0:
+        sl = np_(wl.swa_len)
+        sl[0] = W // 2                              # partial window
+        if R > 1:
+            sl[1] = 0                               # no window
+        wl.swa_len = torch.tensor(sl, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    out, lse = run_attn(wl, 0, torch.tensor(topk, device=DEV), W, scale)
+    ref = oracle_attn_rows(wl, {r: topk[r] for r in range(R)}, 0, list(range(R)), W, scale)
+    check_attn(out, np.stack([ref[r][0] for r in range(R)]), lse, np.stack([ref[r][1] for r in range(R)]),
+               what=name)
+
+
+def test_sparse_attn_empty_key_set():
+    wl = with_cache(small_workload([50, 60], Hi=8, Di=64, D=128, H=8, W=0, layers="F"))
+    topk = torch.full((2, 16), -1, dtype=torch.int32, device=DEV)
+    out, lse = run_attn(wl, 0, topk, 0, 0.1)
+    assert (out == 0).all() and np.isneginf(lse).all()
+
+
+# ----------------------------------------------------------------- whole tiny workload
+
+def test_tiny_workload_step_matches_oracle():
+    """Config 1 (N=4096, D=128, 8 heads, 1x64 indexer, Top-64, 256x8 pool,
+    Full + Reindex + Reuse) through the same launch sequence as the benchmark."""
+    cfg = workloads.CONFIGS[1]
+    wl = workloads.make(cfg, DEV)
+    rows, D = wl.kv_raw.shape
+    codes = torch.empty(rows, D // 2, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(rows, D // 16, dtype=torch.uint8, device=DEV)
+    csa2.csa2_quantize_append(wl.kv_raw, torch.arange(rows, dtype=torch.int64, device=DEV), codes, scales)
+    new_kv = wl.kv_raw[wl.new_rows].contiguous()
+    scale = 1.0 / math.sqrt(D)
+    step = CSA2Step(list(cfg.layers), codes=codes, scales=scales, ikeys=wl.ikeys, seq_start=wl.seq_start,
+                    row_seq=wl.row_seq, row_len=wl.row_len, max_len=int(wl.lengths.max()), new_kv=new_kv,
+                    new_rows=wl.new_rows, qI=wl.qI, w=wl.w, q=wl.q, swa=wl.swa, swa_row_start=wl.swa_row_start,
+                    swa_len=wl.swa_len, W=cfg.W, K=cfg.K, P=cfg.P, softmax_scale=scale)
+    step.run()
+    torch.cuda.synchronize()
+    rc, rs = oracle_quantize(wl.kv_raw)
+    assert np.array_equal(np_(codes), rc) and np.array_equal(np_(scales), rs)
+    inp = dict(qI={l: np_(t) for l, t in wl.qI.items()}, w={l: np_(t) for l, t in wl.w.items()},
+               q_bits={l: bits16(t) for l, t in wl.q.items()}, swa={l: np_(t) for l, t in wl.swa.items()},
+               codes=rc, scales=rs, ikeys=np_(wl.ikeys), seq_start=np_(wl.seq_start), row_seq=np_(wl.row_seq),
+               row_len=np_(wl.row_len), max_len=int(wl.lengths.max()), swa_row_start=np_(wl.swa_row_start),
+               swa_len=np_(wl.swa_len))
+    topk, pool, outs = oracle.step.decode_step(list(cfg.layers), inp, cfg.K, cfg.P, cfg.W, scale)
+    assert np.array_equal(np_(step.pool), pool)
+    for l in topk:
+        assert np.array_equal(np_(step.topk[l]), topk[l]), f"layer {l} top-k"
+    for l in outs:
+        check_attn(np_(step.out[l]), outs[l][0], np_(step.lse[l]), outs[l][1], what=f"tiny layer {l}")

@@ -154,7 +154,8 @@ class Workload:
         return int(self.row_seq.shape[0])
 
 
-def make(cfg: Config, device="cpu", layers: Optional[List[int]] = None) -> Workload:
+def make(cfg: Config, device="cpu", layers: Optional[List[int]] = None,
+         lengths: Optional[np.ndarray] = None) -> Workload:
     """Draw every input of one step of `cfg` on `device` with the config's seed.
 
     Decode configs: one query row per sequence seeing all its entries; the last
@@ -164,7 +165,7 @@ def make(cfg: Config, device="cpu", layers: Optional[List[int]] = None) -> Workl
     [i, i + W) of one [W - 1 + rows, D] buffer.
     """
     g = _gen(cfg.seed, device)
-    lengths = seq_lengths(cfg)
+    lengths = seq_lengths(cfg) if lengths is None else np.asarray(lengths, np.int64)
     starts = np.concatenate([[0], np.cumsum(lengths)[:-1]]).astype(np.int64)
     rows_total = int(lengths.sum())
     modes = layer_modes(cfg)
@@ -204,7 +205,7 @@ def make(cfg: Config, device="cpu", layers: Optional[List[int]] = None) -> Workl
         swa_row_start = torch.arange(0, R, dtype=torch.int64, device=device)
         swa_rows = cfg.W - 1 + R
     else:
-        R = cfg.B
+        R = len(lengths)
         row_seq = torch.arange(R, dtype=torch.int32, device=device)
         row_len = torch.tensor(lengths, dtype=torch.int32, device=device)
         new_rows = torch.tensor(starts + lengths - 1, dtype=torch.int64, device=device)
