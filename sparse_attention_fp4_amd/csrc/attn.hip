@@ -35,6 +35,7 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kTile = 64;
+constexpr float kLazy = 8.0f;   // log2-domain slack before a running max is raised
 
 template <int NB>
 __device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src)
@@ -57,6 +58,158 @@ __device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src)
     }
 }
 
+
+// Scale words / fp16 scale pairs held per lane (one scale per 16 channels).
+template <int DW> constexpr int kScaleWords = (DW / 16 + 3) / 4;
+template <int DW> constexpr int kScalePairs = (DW / 32) > 0 ? (DW / 32) : 1;
+
+// Raw bytes of one lane's quarter-key for one tile: FP4 codes and E4M3 scales
+// of a selected main entry, or FP8 bytes of an SWA row; zeros when the slot
+// holds no valid key (which dequantise to zeros on either path).
+template <int DW>
+struct TileRaw {
+    uint32_t raw[DW / 4];
+    uint32_t sraw[kScaleWords<DW>];
+    bool valid, is_main;
+
+    // j: the Top-K entry of a main slot (ignored for SWA slots); slot: the
+    // lane's key slot (main slots first, then SWA rows).
+    __device__ __forceinline__ void load(int j, int slot, int K, int n, int64_t base, int nsw, int64_t swa0,
+                                         const uint8_t* codes, const uint8_t* scales, const uint8_t* swa, int D,
+                                         int grp)
+    {
+        int64_t row;
+        if (slot < K) {
+            valid = j >= 0 && j < n;
+            is_main = true;
+            row = base + (valid ? j : 0);
+        } else {
+            const int i = slot - K;
+            valid = i < nsw;
+            is_main = false;
+            row = swa0 + (valid ? i : 0);
+        }
+#pragma unroll
+        for (int i = 0; i < DW / 4; ++i) raw[i] = 0u;
+#pragma unroll
+        for (int i = 0; i < kScaleWords<DW>; ++i) sraw[i] = 0u;
+        if (valid) {
+            if (is_main) {
+                load_bytes<DW / 2>(raw, codes + row * (D / 2) + grp * (DW / 2));
+                load_bytes<DW / 16>(sraw, scales + row * (D / 16) + grp * (DW / 16));
+            } else {
+                load_bytes<DW>(raw, swa + row * D + grp * DW);
+            }
+        }
+    }
+};
+
+// Dequantise k-step t (8 channels) of this lane's key to fp16.
+//   MODE 0: FP4 codes (one 32-bit word per step) times the group's E4M3 scale;
+//   MODE 1: FP8 E4M3 bytes (two words per step), unscaled;
+//   MODE 2: either, chosen per lane by is_main.
+template <int MODE>
+__device__ __forceinline__ f16x8 dequant_step(const uint32_t* raw, const f16x2* sc, bool is_main, int t)
+{
+    f16x8 a, b;
+    if (MODE != 1) {
+        const uint32_t c = raw[t];
+        const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0);
+        const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1);
+        const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2);
+        const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3);
+        const _Float16 s = sc[t >> 2][(t >> 1) & 1];
+        a = (f16x8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]} * s;
+    }
+    if (MODE != 0) {
+        const uint32_t c0 = raw[2 * t], c1 = raw[2 * t + 1];
+        const f16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, false);
+        const f16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, true);
+        const f16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1, 1.0f, false);
+        const f16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1, 1.0f, true);
+        b = (f16x8){b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+    }
+    if (MODE == 0) return a;
+    if (MODE == 1) return b;
+    return is_main ? a : b;
+}
+
+// S^T for this wave's 16 keys: dequantise each k-step, store it to the V tile
+// and accumulate K Q^T (plain fp32 accumulation, or fresh partials folded by
+// TwoSum when PRECISE).
+template <int MODE, bool PRECISE, int HT, int KST>
+__device__ __forceinline__ void s_tile(const uint32_t* raw, const f16x2* sc, bool is_main,
+                                       const f16x8 (&qf)[HT][KST], _Float16* vrow, f32x4 (&sacc)[HT],
+                                       f32x4 (&slo)[HT])
+{
+#pragma unroll
+    for (int t = 0; t < KST; ++t) {
+        const f16x8 kf = dequant_step<MODE>(raw, sc, is_main, t);
+        *reinterpret_cast<f16x8*>(vrow + 8 * t) = kf;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            if (PRECISE) {
+                const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ht][t],
+                                                                          (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {   // TwoSum: hi + part == s + err exactly
+                    const float a = sacc[ht][i], b = part[i];
+                    const float s2 = a + b;
+                    const float bb = s2 - a;
+                    const float err = (a - (s2 - bb)) + (b - bb);
+                    sacc[ht][i] = s2;
+                    slo[ht][i] += err;
+                }
+            } else {
+                sacc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ht][t], sacc[ht], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// O[heads x this wave's channels] += P V for one 64-key tile.  The B operand
+// is read with ds_read_b64_tr_b16: within each 16-lane group, lane l receives
+// element l%4 of the 8-byte rows addressed by lanes 4i + l/4, so addressing
+// row (key 4g + l/4, channels c0 + 4(l%4)) hands lane l the 4 keys 4g + 0..3
+// of channel c0 + l, matching the probability fragment's key order.
+template <bool SPLIT, int HT, int NDT, int VST, int PST>
+__device__ __forceinline__ void pv_tile(const _Float16* Pt, const _Float16* Plo, const _Float16* V, int col,
+                                        int grp, int c0, f32x4 (&o)[HT][NDT])
+{
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        f16x8 pa[HT], pl[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const int off = (ht * 16 + col) * PST + 32 * kk + 4 * grp;
+            const f16x4 a0 = *reinterpret_cast<const f16x4*>(&Pt[off]);
+            const f16x4 a1 = *reinterpret_cast<const f16x4*>(&Pt[off + 16]);
+            pa[ht] = (f16x8){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+            if (SPLIT) {
+                const f16x4 b0 = *reinterpret_cast<const f16x4*>(&Plo[off]);
+                const f16x4 b1 = *reinterpret_cast<const f16x4*>(&Plo[off + 16]);
+                pl[ht] = (f16x8){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            }
+        }
+        const _Float16* v1 = V + (32 * kk + 4 * grp + (col >> 2)) * VST + c0 + 4 * (col & 3);
+        const _Float16* v2 = v1 + 16 * VST;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const lds_f16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                (lds_f16x4 __attribute__((address_space(3)))*)(v1 + 16 * dt));
+            const lds_f16x4 b2 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                (lds_f16x4 __attribute__((address_space(3)))*)(v2 + 16 * dt));
+            const f16x8 vb8 = {(_Float16)b1[0], (_Float16)b1[1], (_Float16)b1[2], (_Float16)b1[3],
+                               (_Float16)b2[0], (_Float16)b2[1], (_Float16)b2[2], (_Float16)b2[3]};
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[ht], vb8, o[ht][dt], 0, 0, 0);
+                if (SPLIT) o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[ht], vb8, o[ht][dt], 0, 0, 0);
+            }
+        }
+    }
+}
+
 template <int HT, int D>
 __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
@@ -76,7 +229,9 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
 
     __shared__ __attribute__((aligned(16))) _Float16 Vt[2][kTile * VST];
     __shared__ __attribute__((aligned(16))) _Float16 Pt[NH * PST];
+    __shared__ __attribute__((aligned(16))) _Float16 Plo[NH * PST];
     __shared__ float wmax[4][NH];
+    __shared__ uint32_t wvmax[4];   // per wave: its keys may exceed |v| = 8
     __shared__ float wl[4][NH];
 
     const int lane = lane_id(), wave = threadIdx.x >> 6;
@@ -113,6 +268,9 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
         }
     }
 
+    // Online softmax state (log2 domain).  The reference max of a head is
+    // raised only when a tile's max exceeds it by more than kLazy, so the
+    // accumulated output is rarely rescaled; probabilities stay <= 2^kLazy.
     float m_p[HT], l_p[HT], m_o[HT][4];
     f32x4 o[HT][NDT];
 #pragma unroll
@@ -125,70 +283,78 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
         for (int dt = 0; dt < NDT; ++dt) o[ht][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     }
 
+    // Software pipeline over tiles: while tile t is processed, the raw bytes
+    // of tile t+1 and the index of tile t+2 are already in flight, so the
+    // dependent index -> row loads never stall the matrix work.
+    auto slot_index = [&](int tile) -> int {     // Top-K entry of this lane's slot (or -2)
+        const int slot = tile * kTile + wave * 16 + col;
+        return (tile < t_end && slot < K) ? topk[(int64_t)r * K + slot] : -2;
+    };
+    TileRaw<DW> cur, nxt;
+    int idx_next = slot_index(t_begin + 1);
+    cur.load(slot_index(t_begin), t_begin * kTile + wave * 16 + col, K, n, base, nsw, swa0, codes, scales, swa, D,
+             grp);
+
     for (int tile = t_begin; tile < t_end; ++tile) {
         const int buf = (tile - t_begin) & 1;
         _Float16* V = Vt[buf];
-        const int slot = tile * kTile + wave * 16 + col;
-        bool valid, is_main;
-        int64_t row;
-        if (slot < K) {
-            const int j = topk[(int64_t)r * K + slot];
-            valid = j >= 0 && j < n;
-            is_main = true;
-            row = base + (valid ? j : 0);
-        } else {
-            const int i = slot - K;
-            valid = i < nsw;
-            is_main = false;
-            row = swa0 + (valid ? i : 0);
+        if (tile + 1 < t_end) {
+            const int idx_after = slot_index(tile + 2);
+            nxt.load(idx_next, (tile + 1) * kTile + wave * 16 + col, K, n, base, nsw, swa0, codes, scales, swa, D,
+                     grp);
+            idx_next = idx_after;
         }
-        uint32_t raw[DW / 4];
-        uint32_t sraw[(DW / 16 + 3) / 4 + 1];
-        if (valid) {
-            if (is_main) {
-                load_bytes<DW / 2>(raw, codes + row * (D / 2) + grp * (DW / 2));
-                load_bytes<DW / 16>(sraw, scales + row * (D / 16) + grp * (DW / 16));
-            } else {
-                load_bytes<DW>(raw, swa + row * D + grp * DW);
-            }
+        const bool valid = cur.valid, is_main = cur.is_main;
+        const uint32_t* raw = cur.raw;
+        const uint32_t* sraw = cur.sraw;
+
+        // Large values (|v| > 8) make the output sensitive to logit rounding:
+        // a logit error e moves the output by about e * |v - out|.  A wave whose
+        // keys may hold such values accumulates S^T with one fresh MFMA result
+        // per k-step folded into an fp32 (hi, lo) pair by an exact TwoSum, and
+        // the tile uses two-part probabilities in PV.  The test is on the
+        // stored bytes: an FP4 group holds |v| <= 6 * scale, so a scale byte of
+        // 0x3B (1.375) or more; an FP8 SWA byte of magnitude 0x50 (8.0) or more.
+        // Adding 0x45 (resp. 0x30) to a 7-bit magnitude sets bit 7 exactly
+        // when the magnitude reaches 0x3B (resp. 0x50), with no carry between
+        // bytes (missing bytes are zero).
+        uint32_t bigbits = 0u;
+        if (is_main) {
+#pragma unroll
+            for (int i = 0; i < kScaleWords<DW>; ++i) bigbits |= ((sraw[i] & 0x7F7F7F7Fu) + 0x45454545u) & 0x80808080u;
+            // bytes past the lane's DW/16 scales are zero and read as 0x45 < 0x80
+        } else {
+#pragma unroll
+            for (int i = 0; i < DW / 4; ++i) bigbits |= ((raw[i] & 0x7F7F7F7Fu) + 0x30303030u) & 0x80808080u;
+        }
+        const bool precise = __ballot(bigbits != 0u) != 0ull;
+        const uint64_t bmain = __ballot(valid && is_main), bswa = __ballot(valid && !is_main);
+
+        f16x2 sc[kScalePairs<DW>];
+#pragma unroll
+        for (int i = 0; i < kScalePairs<DW>; i += 2) {
+            sc[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sraw[i >> 1], 1.0f, false);
+            if (i + 1 < kScalePairs<DW>) sc[i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sraw[i >> 1], 1.0f, true);
         }
 
-        f32x4 sacc[HT];
+        f32x4 sacc[HT], slo[HT];
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) sacc[ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-        _Float16* vrow = V + (wave * 16 + col) * VST + grp * DW;
-#pragma unroll
-        for (int t = 0; t < KST; ++t) {
-            f16x8 kf;
-            if (!valid) {
-                kf = (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
-            } else if (is_main) {
-                const uint32_t c = raw[t];
-                const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0);
-                const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1);
-                const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2);
-                const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3);
-                const uint32_t sb = (sraw[t >> 3] >> (8 * ((t >> 1) & 3))) & 0xFFu;
-                const _Float16 sc = (_Float16)e4m3_to_f32(sb);
-                kf = (f16x8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-                kf = kf * sc;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const uint32_t c = raw[2 * t + e];
-                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(c, false);
-                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(c, true);
-                    kf[4 * e] = (_Float16)lo[0];
-                    kf[4 * e + 1] = (_Float16)lo[1];
-                    kf[4 * e + 2] = (_Float16)hi[0];
-                    kf[4 * e + 3] = (_Float16)hi[1];
-                }
-            }
-            *reinterpret_cast<f16x8*>(vrow + 8 * t) = kf;
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
-                sacc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ht][t], sacc[ht], 0, 0, 0);
+        for (int ht = 0; ht < HT; ++ht) {
+            sacc[ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+            slo[ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
         }
+        _Float16* vrow = V + (wave * 16 + col) * VST + grp * DW;
+        if (bswa == 0ull) {
+            if (precise) s_tile<0, true, HT, KST>(raw, sc, is_main, qf, vrow, sacc, slo);
+            else s_tile<0, false, HT, KST>(raw, sc, is_main, qf, vrow, sacc, slo);
+        } else if (bmain == 0ull) {
+            if (precise) s_tile<1, true, HT, KST>(raw, sc, is_main, qf, vrow, sacc, slo);
+            else s_tile<1, false, HT, KST>(raw, sc, is_main, qf, vrow, sacc, slo);
+        } else {
+            if (precise) s_tile<2, true, HT, KST>(raw, sc, is_main, qf, vrow, sacc, slo);
+            else s_tile<2, false, HT, KST>(raw, sc, is_main, qf, vrow, sacc, slo);
+        }
+        if (lane == 0) wvmax[wave] = precise ? 1u : 0u;
 
         // S^T lane layout: head (h0 + 16 ht + col), keys wave*16 + 4 grp + i
         const uint64_t vb = __ballot(valid);
@@ -199,7 +365,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool kv = (vb >> (4 * grp + i)) & 1ull;
-                x[ht][i] = kv ? sacc[ht][i] * scale_log2e : -INFINITY;
+                x[ht][i] = kv ? (sacc[ht][i] + slo[ht][i]) * scale_log2e : -INFINITY;
                 mx = fmaxf(mx, x[ht][i]);
             }
             mx = fmaxf(mx, shfl_xor_f(mx, 16));
@@ -208,68 +374,61 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
         }
         __syncthreads();
 
+        // Probabilities enter PV as fp16, whose rounding (relative 2^-12) moves
+        // the output by up to 2^-12 * |v - out|.  For tiles whose keys may hold
+        // |v| > 8 the probability is split into fp16 hi + lo parts and PV runs
+        // twice, which brings the rounding to ~2^-23.
+        const bool split = (wvmax[0] | wvmax[1] | wvmax[2] | wvmax[3]) != 0u;
         float alpha[HT][4];
+        bool rescale = false;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
             const int hh = ht * 16 + col;
             const float mt = fmaxf(fmaxf(wmax[0][hh], wmax[1][hh]), fmaxf(wmax[2][hh], wmax[3][hh]));
-            const float mn = fmaxf(m_p[ht], mt);
+            const float mn = (mt > m_p[ht] + kLazy) ? mt : m_p[ht];
             const bool live = mn != -INFINITY;
             const float ap = live ? exp2f(m_p[ht] - mn) : 1.0f;
             float ps = 0.0f;
-            f16x4 p4;
+            f16x4 p4, q4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const _Float16 p = (_Float16)(live ? exp2f(x[ht][i] - mn) : 0.0f);
+                // the exponent's argument is formed with one rounding at its own
+                // (small) magnitude; the reference itself only has to be consistent
+                const float d = fmaf(sacc[ht][i], scale_log2e, -mn) + slo[ht][i] * scale_log2e;
+                const float pf = (live && x[ht][i] != -INFINITY) ? exp2f(d) : 0.0f;
+                const _Float16 p = (_Float16)pf;
                 p4[i] = p;
-                ps += (float)p;
+                q4[i] = (_Float16)(pf - (float)p);
+                ps += split ? pf : (float)p;   // normalise by what PV actually weights
             }
             l_p[ht] = l_p[ht] * ap + ps;
             m_p[ht] = mn;
             *reinterpret_cast<f16x4*>(&Pt[hh * PST + wave * 16 + 4 * grp]) = p4;
+            if (split) *reinterpret_cast<f16x4*>(&Plo[hh * PST + wave * 16 + 4 * grp]) = q4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ho = ht * 16 + 4 * grp + i;
                 const float mto = fmaxf(fmaxf(wmax[0][ho], wmax[1][ho]), fmaxf(wmax[2][ho], wmax[3][ho]));
-                const float mno = fmaxf(m_o[ht][i], mto);
-                alpha[ht][i] = (mno != -INFINITY) ? exp2f(m_o[ht][i] - mno) : 1.0f;
+                const float mno = (mto > m_o[ht][i] + kLazy) ? mto : m_o[ht][i];
+                alpha[ht][i] = (m_o[ht][i] != -INFINITY) ? exp2f(m_o[ht][i] - mno) : 1.0f;
+                rescale |= mno != m_o[ht][i] && m_o[ht][i] != -INFINITY;
                 m_o[ht][i] = mno;
             }
         }
         __syncthreads();
 
+        if (__ballot(rescale) != 0ull) {
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
+            for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
+                for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[ht][dt][i] *= alpha[ht][i];
-
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            f16x8 pa[HT];
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                const _Float16* pr = &Pt[(ht * 16 + col) * PST + 32 * kk + 4 * grp];
-                const f16x4 lo = *reinterpret_cast<const f16x4*>(pr);
-                const f16x4 hi = *reinterpret_cast<const f16x4*>(pr + 16);
-                pa[ht] = (f16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            }
-            const _Float16* v1 = V + (32 * kk + 4 * grp + (col >> 2)) * VST + wave * DW + 4 * (col & 3);
-            const _Float16* v2 = v1 + 16 * VST;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const lds_f16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-                    (lds_f16x4 __attribute__((address_space(3)))*)(v1 + 16 * dt));
-                const lds_f16x4 b2 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-                    (lds_f16x4 __attribute__((address_space(3)))*)(v2 + 16 * dt));
-                const f16x8 vb8 = {(_Float16)b1[0], (_Float16)b1[1], (_Float16)b1[2], (_Float16)b1[3],
-                                   (_Float16)b2[0], (_Float16)b2[1], (_Float16)b2[2], (_Float16)b2[3]};
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht)
-                    o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[ht], vb8, o[ht][dt], 0, 0, 0);
-            }
+                    for (int i = 0; i < 4; ++i) o[ht][dt][i] *= alpha[ht][i];
         }
+
+        if (split) pv_tile<true, HT, NDT, VST, PST>(Pt, Plo, V, col, grp, wave * DW, o);
+        else pv_tile<false, HT, NDT, VST, PST>(Pt, Plo, V, col, grp, wave * DW, o);
+        cur = nxt;
     }
 
     // Row sums over the four waves' keys.
@@ -312,6 +471,8 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
 }
 
 // Merge of split partials: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// One workgroup per (row, head); each thread owns four consecutive channels.
+constexpr int kMaxSplits = 64;
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, int32_t H,
                                                       int32_t D, int32_t S, float* __restrict__ out,
@@ -319,26 +480,36 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
 {
     const int rh = blockIdx.x;          // r * H + h
     const int r = rh / H, h = rh % H;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) {
-        const float* ml = part_ml + (((int64_t)r * S + s) * H + h) * 2;
-        if (ml[1] > 0.0f) M = fmaxf(M, ml[0]);
-    }
-    float L = 0.0f;
-    for (int s = 0; s < S; ++s) {
-        const float* ml = part_ml + (((int64_t)r * S + s) * H + h) * 2;
-        if (ml[1] > 0.0f) L += ml[1] * exp2f(ml[0] - M);
-    }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    for (int d = threadIdx.x; d < D; d += blockDim.x) {
-        float acc = 0.0f;
+    __shared__ float wgt[kMaxSplits];
+    __shared__ float Ls;
+    if (threadIdx.x == 0) {
+        float M = -INFINITY;
         for (int s = 0; s < S; ++s) {
             const float* ml = part_ml + (((int64_t)r * S + s) * H + h) * 2;
-            if (ml[1] > 0.0f) acc += part_o[(((int64_t)r * S + s) * H + h) * D + d] * exp2f(ml[0] - M);
+            if (ml[1] > 0.0f) M = fmaxf(M, ml[0]);
         }
-        out[(int64_t)rh * D + d] = acc * inv;
+        float L = 0.0f;
+        for (int s = 0; s < S; ++s) {
+            const float* ml = part_ml + (((int64_t)r * S + s) * H + h) * 2;
+            const float w = ml[1] > 0.0f ? exp2f(ml[0] - M) : 0.0f;
+            wgt[s] = w;
+            L += ml[1] * w;
+        }
+        Ls = L;
+        if (lse) lse[rh] = L > 0.0f ? M * kLn2 + logf(L) : -INFINITY;
     }
-    if (lse && threadIdx.x == 0) lse[rh] = L > 0.0f ? M * kLn2 + logf(L) : -INFINITY;
+    __syncthreads();
+    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    for (int d = 4 * threadIdx.x; d < D; d += 4 * blockDim.x) {
+        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        for (int s = 0; s < S; ++s) {
+            const float w = wgt[s];
+            const float4 v = *reinterpret_cast<const float4*>(part_o + (((int64_t)r * S + s) * H + h) * D + d);
+            acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+        }
+        *reinterpret_cast<float4*>(out + (int64_t)rh * D + d) =
+            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    }
 }
 
 struct AttnPlan {
@@ -356,6 +527,7 @@ AttnPlan plan_attn(int32_t R, int32_t H, int32_t K, int32_t W)
     const int64_t base = (int64_t)R * p.HG;
     int64_t S = base >= 256 ? 1 : (256 + base - 1) / base;
     if (S > p.ntiles) S = p.ntiles;
+    if (S > kMaxSplits) S = kMaxSplits;
     p.S = (int)S;
     return p;
 }

@@ -30,11 +30,12 @@
 
 namespace {
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / CSA2_WAVE;
 constexpr int kMaxK = 2048;
 constexpr int kMaxP = 2048;
 constexpr int kBins = 2048;
+constexpr int kLoadBatch = 16;      // global loads kept in flight per select thread
 constexpr int kFullChunk = 1024;     // entries per Full-score workgroup
 constexpr int kReChunk = 512;        // pool slots per Reindex-score workgroup
 
@@ -163,33 +164,7 @@ struct SelShared {
     int digit, above, nvalid;
 };
 
-// Exclusive block-wide counts of two predicates in thread order, plus totals.
-__device__ __forceinline__ void block_count2(SelShared& sh, bool a, bool b, int& ea, int& eb, int& ta,
-                                             int& tb)
-{
-    const int lane = lane_id(), wave = threadIdx.x / CSA2_WAVE;
-    const uint64_t ba = __ballot(a), bb = __ballot(b);
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int la = __popcll(ba & lt), lb = __popcll(bb & lt);
-    __syncthreads();
-    if (lane == 0) {
-        sh.wave_a[wave] = __popcll(ba);
-        sh.wave_b[wave] = __popcll(bb);
-    }
-    __syncthreads();
-    int oa = 0, ob = 0;
-    ta = 0;
-    tb = 0;
-#pragma unroll
-    for (int i = 0; i < kSelWaves; ++i) {
-        const int xa = sh.wave_a[i], xb = sh.wave_b[i];
-        if (i < wave) { oa += xa; ob += xb; }
-        ta += xa;
-        tb += xb;
-    }
-    ea = oa + la;
-    eb = ob + lb;
-}
+__device__ __forceinline__ uint64_t lanes_below() { const int l = lane_id(); return l ? (~0ull >> (64 - l)) : 0ull; }
 
 // Exclusive block-wide prefix sum of an int in thread order; returns the total.
 __device__ __forceinline__ int block_excl_sum(SelShared& sh, int v, int& excl)
@@ -215,75 +190,185 @@ __device__ __forceinline__ int block_excl_sum(SelShared& sh, int v, int& excl)
     return total;
 }
 
+// Items are processed in rounds of kRound; within a round thread t holds the
+// kE consecutive items t*kE .. t*kE+kE-1 in registers.  Key 0 marks an
+// invalid item (order_key never maps a finite float to 0).  Keys live in LDS
+// at padded positions (one spare word per 32) so that the 64 lanes reading
+// word t*kE + e of their own run hit 64 different banks.
+constexpr int kE = 32;
+constexpr int kRound = kSelThreads * kE;
+constexpr int kPadded = kRound + kRound / 32;
+__device__ __forceinline__ int padded(int i) { return i + (i >> 5); }
+
+// Where the keys come from: an LDS array holding all of them (cnt <= kRound),
+// or global floats staged into the LDS array one round at a time.
+struct KeySource {
+    uint32_t* lds;
+    const float* gsrc;   // null when the keys are already in lds
+    int cnt;
+
+    __device__ __forceinline__ int rounds() const { return (cnt + kRound - 1) / kRound; }
+
+    __device__ __forceinline__ void stage(int rd) const
+    {
+        if (!gsrc) return;
+        __syncthreads();
+        const int base = rd * kRound;
+        for (int c0 = 0; c0 < kRound; c0 += kSelThreads * kLoadBatch) {
+            float v[kLoadBatch];
+#pragma unroll
+            for (int u = 0; u < kLoadBatch; ++u) {
+                const int c = base + c0 + u * kSelThreads + threadIdx.x;
+                v[u] = c < cnt ? gsrc[c] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < kLoadBatch; ++u) {
+                const int li = c0 + u * kSelThreads + threadIdx.x;
+                lds[padded(li)] = base + li < cnt ? order_key(v[u]) : 0u;
+            }
+        }
+        __syncthreads();
+    }
+
+    __device__ __forceinline__ void load(int rd, uint32_t (&key)[kE]) const
+    {
+        if (rounds() > 1) stage(rd);
+        const int l0 = threadIdx.x * kE;
+        const int i0 = rd * kRound + l0;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) key[e] = (i0 + e < cnt) ? lds[padded(l0 + e)] : 0u;
+    }
+};
+
 // Finds the threshold of the k largest keys among the valid items 0..cnt-1.
-// get(i, key) returns whether item i is valid and its key.
-template <class Get>
-__device__ SelState radix_select(SelShared& sh, int cnt, int k, Get get)
+// The bits shared by every valid key are skipped first (an AND/OR reduction
+// finds the highest bit that differs), then radix passes over 11-bit digits
+// below it (LDS histograms) narrow to the digit holding the k-th largest key,
+// stopping early once a whole digit bin is taken.  get(i) returns the key of
+// item i, or 0 when the item is invalid.
+__device__ __forceinline__ SelState radix_select(SelShared& sh, const KeySource& src, int k)
 {
-    SelState st{0u, 0u, 0};
-    const int shifts[3] = {21, 10, 0};
-    const uint32_t digit_masks[3] = {0x7FFu, 0x7FFu, 0x3FFu};
+    constexpr int BPT = kBins / kSelThreads;      // bins per thread in the digit search
+    const int lane = lane_id(), wave = threadIdx.x / CSA2_WAVE;
+    const int rounds = src.rounds();
+    uint32_t key[kE];
+    if (rounds == 1) src.load(0, key);
+    // population and common prefix of the valid keys
+    uint32_t kand = 0xFFFFFFFFu, kor = 0u;
+    int nv = 0;
+    for (int rd = 0; rd < rounds; ++rd) {
+        if (rounds > 1) src.load(rd, key);
+#pragma unroll
+        for (int e = 0; e < kE; ++e)
+            if (key[e]) { kand &= key[e]; kor |= key[e]; ++nv; }
+    }
+#pragma unroll
+    for (int off = 1; off < CSA2_WAVE; off <<= 1) {
+        kand &= (uint32_t)__shfl_xor((int)kand, off, CSA2_WAVE);
+        kor |= (uint32_t)__shfl_xor((int)kor, off, CSA2_WAVE);
+        nv += __shfl_xor(nv, off, CSA2_WAVE);
+    }
+    __syncthreads();
+    if (lane == 0) { sh.hist[wave] = (int)kand; sh.hist[kSelWaves + wave] = (int)kor; sh.wave_b[wave] = nv; }
+    __syncthreads();
+    kand = 0xFFFFFFFFu; kor = 0u; nv = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+        kand &= (uint32_t)sh.hist[w];
+        kor |= (uint32_t)sh.hist[kSelWaves + w];
+        nv += sh.wave_b[w];
+    }
+    __syncthreads();
+    SelState st{0u, 0u, nv};
+    if (nv <= k) return st;                       // everything valid is selected (mask 0)
+    const uint32_t diff = kand ^ kor;             // bits that vary among valid keys
+    st.mask = diff ? ~((2u << (31 - __builtin_clz(diff))) - 1u) : 0xFFFFFFFFu;
+    st.prefix = kand & st.mask;
+    st.need = k;
+    if (diff == 0u) return st;                    // all valid keys equal: ties only
+    int top = 31 - __builtin_clz(diff);           // highest varying bit
     int krem = k;
-    for (int pass = 0; pass < 3; ++pass) {
+    while (top >= 0) {
+        const int width = top + 1 < 11 ? top + 1 : 11;
+        const int shift = top + 1 - width;
+        const uint32_t dmask = (1u << width) - 1u;
         for (int i = threadIdx.x; i < kBins; i += kSelThreads) sh.hist[i] = 0;
         __syncthreads();
-        for (int i = threadIdx.x; i < cnt; i += kSelThreads) {
-            uint32_t key;
-            if (get(i, key) && (key & st.mask) == st.prefix)
-                atomicAdd(&sh.hist[(key >> shifts[pass]) & digit_masks[pass]], 1);
+        for (int rd = 0; rd < rounds; ++rd) {
+            if (rounds > 1) src.load(rd, key);
+#pragma unroll
+            for (int e = 0; e < kE; ++e)
+                if (key[e] && (key[e] & st.mask) == st.prefix) atomicAdd(&sh.hist[(key[e] >> shift) & dmask], 1);
         }
         __syncthreads();
-        // digits in descending order: thread t owns bins 2047-2t and 2046-2t
-        const int b0 = kBins - 1 - 2 * threadIdx.x, b1 = b0 - 1;
-        const int h0 = sh.hist[b0], h1 = sh.hist[b1];
+        int h[BPT], sum = 0;
+#pragma unroll
+        for (int b = 0; b < BPT; ++b) { h[b] = sh.hist[kBins - 1 - BPT * threadIdx.x - b]; sum += h[b]; }
         int before;
-        const int total = block_excl_sum(sh, h0 + h1, before);
-        if (pass == 0 && threadIdx.x == 0) sh.nvalid = total;
-        if (before < krem && krem <= before + h0) { sh.digit = b0; sh.above = before; }
-        else if (before + h0 < krem && krem <= before + h0 + h1) { sh.digit = b1; sh.above = before + h0; }
-        __syncthreads();
-        if (pass == 0 && sh.nvalid <= k) {      // everything valid is selected
-            st.prefix = 0u; st.mask = 0u; st.need = sh.nvalid;
-            __syncthreads();
-            return st;
+        block_excl_sum(sh, sum, before);
+        int acc = before;
+#pragma unroll
+        for (int b = 0; b < BPT; ++b) {
+            if (acc < krem && krem <= acc + h[b]) { sh.digit = kBins - 1 - BPT * threadIdx.x - b; sh.above = acc; }
+            acc += h[b];
         }
+        __syncthreads();
         const int d = sh.digit;
         krem -= sh.above;
         const int in_bin = sh.hist[d];
-        st.prefix |= (uint32_t)d << shifts[pass];
-        st.mask |= digit_masks[pass] << shifts[pass];
+        st.prefix |= (uint32_t)d << shift;
+        st.mask |= dmask << shift;
         st.need = krem;
         __syncthreads();
         if (in_bin == krem) break;   // the whole bin is taken: no tie to resolve
+        top = shift - 1;
     }
     return st;
 }
 
-// Ordered compaction: writes the ids of selected items in item order.
-template <class Get, class Emit>
-__device__ int select_compact(SelShared& sh, int cnt, SelState st, Get get, Emit emit)
+// Ordered compaction: emit(pos, i) for the selected items in item order.  A
+// thread counts the keys above the threshold and those equal to it among its
+// items; one block scan of the packed counts gives every thread the number of
+// selected items before its own (all keys above, plus the first `need` equal
+// keys: ties go to the lowest index), and the thread then writes its items in
+// order.  Returns the number selected.
+template <class Emit>
+__device__ __forceinline__ int select_compact(SelShared& sh, const KeySource& src, SelState st, Emit emit)
 {
-    int eq_seen = 0, out = 0;
-    for (int base = 0; base < cnt; base += kSelThreads) {
-        const int i = base + threadIdx.x;
-        uint32_t key = 0;
-        const bool valid = i < cnt && get(i, key);
-        const uint32_t mk = key & st.mask;
-        const bool gt = valid && mk > st.prefix;
-        const bool eq = valid && mk == st.prefix;
-        int e_eq, e_x, t_eq, t_x;
-        block_count2(sh, eq, false, e_eq, e_x, t_eq, t_x);
-        const bool sel = gt || (eq && eq_seen + e_eq < st.need);
-        int e_sel, e_y, t_sel, t_y;
-        block_count2(sh, sel, false, e_sel, e_y, t_sel, t_y);
-        if (sel) emit(out + e_sel, i);
-        eq_seen += t_eq;
-        out += t_sel;
+    const int rounds = src.rounds();
+    int gt_run = 0, eq_run = 0;
+    uint32_t key[kE];
+    for (int rd = 0; rd < rounds; ++rd) {
+        src.load(rd, key);
+        int gt = 0, eq = 0;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            const uint32_t mk = key[e] & st.mask;
+            gt += (key[e] && mk > st.prefix) ? 1 : 0;
+            eq += (key[e] && mk == st.prefix) ? 1 : 0;
+        }
+        int before;
+        const int total = block_excl_sum(sh, (gt << 16) | eq, before);   // counts < 2^15 per round
+        const int gt_before = gt_run + (before >> 16), eq_before = eq_run + (before & 0xFFFF);
+        int out = gt_before + (eq_before < st.need ? eq_before : st.need);
+        int eq_seen = eq_before;
+        const int i0 = rd * kRound + threadIdx.x * kE;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            const uint32_t mk = key[e] & st.mask;
+            const bool is_gt = key[e] && mk > st.prefix, is_eq = key[e] && mk == st.prefix;
+            const bool sel = is_gt || (is_eq && eq_seen < st.need);
+            if (sel) emit(out++, i0 + e);
+            eq_seen += is_eq ? 1 : 0;
+        }
+        gt_run += total >> 16;
+        eq_run += total & 0xFFFF;
     }
-    return out;
+    __syncthreads();
+    return gt_run + (eq_run < st.need ? eq_run : st.need);
 }
 
-// Bitonic sort (ascending) of n <= 2*kSelThreads ints in LDS, padded with INT_MAX.
+// Bitonic sort (ascending) of n_pow2 ints in LDS.
 __device__ void bitonic_sort(int* a, int n_pow2)
 {
     for (int k = 2; k <= n_pow2; k <<= 1) {
@@ -303,7 +388,7 @@ __device__ void bitonic_sort(int* a, int n_pow2)
 
 struct SelectLds {
     SelShared sh;
-    uint32_t cand_key[kMaxP * 8];
+    uint32_t keys[kPadded];     // block-max keys (Full), then candidate keys; padded positions
     int blocks[kMaxP];
     int outbuf[kMaxK];
     int flag;
@@ -320,36 +405,38 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     const int n = row_len[r];
     const int nb = (n + 7) >> 3;
     const float* sc = scores + (int64_t)r * ld_scores;
-    int ncand_blocks;   // candidate blocks listed in L.blocks (ascending unless reindex input is not)
+    int ncand_blocks;   // candidate blocks listed in L.blocks
 
     if (FULL) {
         const float* bm = bmax + (int64_t)r * ld_bmax;
-        auto get_b = [&](int i, uint32_t& key) -> bool {
-            if (i >= nb) return false;
-            key = order_key(bm[i]);
-            return true;
-        };
+        // Block maxima: staged into LDS once when they fit in one round, else
+        // round by round inside each pass.
+        KeySource bsrc{L.keys, bm, nb};
+        if (nb <= kRound) {
+            bsrc.stage(0);
+            bsrc.gsrc = nullptr;
+        }
         const int pint = K > P ? K : P;   // blocks that must hold the Top-K (and the pool)
+        if (pool_out && P < K && nb > P) {   // pool smaller than the Top-K block set: select it first
+            int32_t* po = pool_out + (int64_t)r * P;
+            SelState st = radix_select(L.sh, bsrc, P);
+            int np = select_compact(L.sh, bsrc, st, [&](int pos, int i) { if (pos < P) po[pos] = i; });
+            np = np < P ? np : P;
+            for (int i = np + threadIdx.x; i < P; i += kSelThreads) po[i] = -1;
+        }
         if (nb <= pint) {
             for (int i = threadIdx.x; i < nb; i += kSelThreads) L.blocks[i] = i;
             ncand_blocks = nb;
         } else {
-            SelState st = radix_select(L.sh, nb, pint, get_b);
-            ncand_blocks = select_compact(L.sh, nb, st, get_b, [&](int pos, int i) { if (pos < pint) L.blocks[pos] = i; });
+            SelState st = radix_select(L.sh, bsrc, pint);
+            ncand_blocks = select_compact(L.sh, bsrc, st, [&](int pos, int i) { if (pos < pint) L.blocks[pos] = i; });
             ncand_blocks = ncand_blocks < pint ? ncand_blocks : pint;
         }
         __syncthreads();
-        if (pool_out) {
+        if (pool_out && (P >= K || nb <= P)) {
             int32_t* po = pool_out + (int64_t)r * P;
-            if (P >= K || nb <= P) {
-                const int np = ncand_blocks < P ? ncand_blocks : P;
-                for (int i = threadIdx.x; i < P; i += kSelThreads) po[i] = i < np ? L.blocks[i] : -1;
-            } else {
-                SelState st = radix_select(L.sh, nb, P, get_b);
-                int np = select_compact(L.sh, nb, st, get_b, [&](int pos, int i) { if (pos < P) po[pos] = i; });
-                np = np < P ? np : P;
-                for (int i = np + threadIdx.x; i < P; i += kSelThreads) po[i] = -1;
-            }
+            const int np = ncand_blocks < P ? ncand_blocks : P;
+            for (int i = threadIdx.x; i < P; i += kSelThreads) po[i] = i < np ? L.blocks[i] : -1;
         }
     } else {
         const int32_t* pl = pool_in + (int64_t)r * P;
@@ -368,30 +455,36 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
 
     // Candidate entries: slot c -> block L.blocks[c/8], position 8*block + c%8
     const int ncand = ncand_blocks * 8;
-    for (int c = threadIdx.x; c < ncand; c += kSelThreads) {
-        const int b = L.blocks[c >> 3];
-        const int64_t j = (int64_t)b * 8 + (c & 7);
-        const bool valid = b >= 0 && b < nb && j < n;
-        const float s = valid ? (FULL ? sc[j] : sc[c]) : 0.0f;
-        L.cand_key[c] = order_key(s);
+    // Key 0 marks a slot without a visible entry (every finite score maps above
+    // it).  Loads are batched so that many are in flight per thread.
+    for (int c0 = 0; c0 < ncand; c0 += kSelThreads * kLoadBatch) {
+        float v[kLoadBatch];
+        bool ok[kLoadBatch];
+#pragma unroll
+        for (int u = 0; u < kLoadBatch; ++u) {
+            const int c = c0 + u * kSelThreads + threadIdx.x;
+            const int b = c < ncand ? L.blocks[c >> 3] : -1;
+            const int64_t j = (int64_t)b * 8 + (c & 7);
+            ok[u] = b >= 0 && b < nb && j < n;
+            v[u] = ok[u] ? (FULL ? sc[j] : sc[c]) : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kLoadBatch; ++u) {
+            const int c = c0 + u * kSelThreads + threadIdx.x;
+            if (c < ncand) L.keys[padded(c)] = ok[u] ? order_key(v[u]) : 0u;
+        }
     }
     __syncthreads();
-    auto get_c = [&](int c, uint32_t& key) -> bool {
-        const int b = L.blocks[c >> 3];
-        const int64_t j = (int64_t)b * 8 + (c & 7);
-        if (!(b >= 0 && b < nb && j < n)) return false;
-        key = L.cand_key[c];
-        return true;
-    };
+    const KeySource csrc{L.keys, nullptr, ncand};
     int32_t* to = topk + (int64_t)r * K;
-    SelState st = radix_select(L.sh, ncand, K, get_c);
+    SelState st = radix_select(L.sh, csrc, K);
     if (FULL) {
-        int nk = select_compact(L.sh, ncand, st, get_c,
+        int nk = select_compact(L.sh, csrc, st,
                                 [&](int pos, int c) { if (pos < K) to[pos] = L.blocks[c >> 3] * 8 + (c & 7); });
         nk = nk < K ? nk : K;
         for (int i = nk + threadIdx.x; i < K; i += kSelThreads) to[i] = -1;
     } else {
-        int nk = select_compact(L.sh, ncand, st, get_c,
+        int nk = select_compact(L.sh, csrc, st,
                                 [&](int pos, int c) { if (pos < K) L.outbuf[pos] = L.blocks[c >> 3] * 8 + (c & 7); });
         nk = nk < K ? nk : K;
         __syncthreads();

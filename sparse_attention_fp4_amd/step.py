@@ -77,21 +77,36 @@ class CSA2Step:
                      csa2_sparse_attn_workspace_bytes(R, H, D, self.K, self.W), 256)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
 
-    def run(self, stream=None, layers=None) -> None:
+    def run(self, stream=None, layers=None, mark=None) -> None:
+        """Enqueue the step.  `mark(label, phase)` (optional) is called right
+        before ("begin") and after ("end") each library call, on the host, so a
+        caller can record HIP events around individual calls."""
+        def _mark(label, phase):
+            if mark is not None:
+                mark(label, phase)
+
         if self.new_kv is not None and self.new_kv.shape[0] > 0:
+            _mark("quantize_append", "begin")
             csa2_quantize_append(self.new_kv, self.new_rows, self.codes, self.scales, stream=stream)
+            _mark("quantize_append", "end")
         for l, m in enumerate(self.modes):
             if m == "F":
+                _mark("index_full", "begin")
                 csa2_index_full(self.qI[l], self.w[l], self.ikeys, self.seq_start, self.row_seq, self.row_len,
                                 self.max_len, self.K, self.P, self.block, topk_idx=self.topk[l],
                                 pool_blocks=self.pool, workspace=self.workspace, stream=stream)
+                _mark("index_full", "end")
             elif m == "R":
+                _mark("index_reindex", "begin")
                 csa2_index_reindex(self.qI[l], self.w[l], self.ikeys, self.seq_start, self.row_seq,
                                    self.row_len, self.pool, self.K, self.block, topk_idx=self.topk[l],
                                    workspace=self.workspace, stream=stream)
+                _mark("index_reindex", "end")
             if layers is not None and l not in layers:
                 continue
+            _mark("sparse_attn", "begin")
             csa2_sparse_attn(self.q[l], self.codes, self.scales, self.seq_start, self.row_seq, self.row_len,
                              self.topk[self.parents[l]], self.swa[l], self.swa_row_start, self.swa_len, self.W,
                              self.scale, out=self.out[l], lse=self.lse[l], workspace=self.workspace,
                              stream=stream)
+            _mark("sparse_attn", "end")

@@ -124,9 +124,9 @@ def test_quantize_scatter_and_skips_out_of_range_rows():
 # ----------------------------------------------------------------- indexer
 
 def small_workload(lengths, Hi=64, Di=128, idx_dist="int3", w_dist="u01_16", layers="FRU", seed=3, D=128, H=16,
-                   W=16):
+                   W=16, kv_dist="normal"):
     cfg = workloads.Config(90 + seed, "small", B=len(lengths), N=None, D=D, W=W, H=H, Hi=Hi, Di=Di, K=0, P=0,
-                           idx_dist=idx_dist, w_dist=w_dist, layers=layers)
+                           idx_dist=idx_dist, w_dist=w_dist, layers=layers, kv_dist=kv_dist)
     return workloads.make(cfg, DEV, lengths=np.array(lengths))
 
 
@@ -224,6 +224,8 @@ def with_cache(wl):
 
 @pytest.mark.parametrize("name,lengths,D,H,K,W", [
     ("d128_h8_k64_w32_single_row_split", [4096], 128, 8, 64, 32),
+    ("d512_h64_student_outliers", [9000, 3000, 20000], 512, 64, 512, 128),
+    ("d128_h8_student_outliers_nosplit_rows", [500 + 11 * i for i in range(140)], 128, 8, 64, 32),
     ("d512_h64_k512_w128_split", [9000, 700, 30000], 512, 64, 512, 128),
     ("d512_h64_many_rows_nosplit", [300 + 37 * i for i in range(130)], 512, 64, 512, 128),
     ("d256_h24_k100_w7", [1000, 77, 5000, 2222], 256, 24, 100, 7),
@@ -232,7 +234,8 @@ def with_cache(wl):
 ])
 def test_sparse_attn_matches_oracle(name, lengths, D, H, K, W):
     log(f"sparse_attn parity: {name}")
-    wl = with_cache(small_workload(lengths, Hi=8, Di=64, D=D, H=H, W=W, layers="F"))
+    wl = with_cache(small_workload(lengths, Hi=8, Di=64, D=D, H=H, W=W, layers="F",
+                                   kv_dist="student_t_outliers" if "outliers" in name else "normal"))
     R = len(lengths)
     rng = np.random.default_rng(len(name))
     topk = np.full((R, K), -1, np.int32)
