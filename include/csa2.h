@@ -169,7 +169,7 @@ csa2_status_t csa2_index_reindex(const uint8_t* qI, const float* w, const uint8_
  * Arithmetic: dequantised keys are exact in fp16; logits accumulate in fp32;
  * softmax in fp32; probabilities enter the PV product rounded to fp16;
  * outputs accumulate in fp32.
- * Limits: H >= 1; D in {64, 128, 256, 512}; 0 <= K <= 4096; 0 <= W <= 4096.
+ * Limits: H >= 1; D in {128, 256, 512}; 0 <= K <= 4096; 0 <= W <= 4096.
  */
 size_t csa2_sparse_attn_workspace_bytes(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W);
 csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,

@@ -8,34 +8,49 @@
 // is shared by all query heads; the selected entries and the SWA rows form one
 // key set under one softmax.
 //
-// Work decomposition (one workgroup = 4 waves = one query row x NH heads x a
-// contiguous range of 64-key tiles):
-//   * Each wave owns 16 keys of a tile.  A lane loads the raw bytes of one
-//     key's quarter of the channels straight from the cache, dequantises them
-//     to fp16 in registers (E2M1 -> fp16 by the hardware converter, times the
-//     E4M3 scale; the product is exact in fp16) and feeds them as the A operand
-//     of S^T = K Q^T on v_mfma_f32_16x16x32_f16, with the NH query heads held
-//     in registers as the B operand.  Because the contraction order is the
-//     same for both operands, each lane can hold a contiguous quarter of the
-//     channels.
-//   * The same fp16 values are stored once into an LDS tile [64 keys][D].
-//   * Softmax statistics are exchanged through LDS (online softmax across
-//     tiles, log2 domain); probabilities are written to LDS as fp16.
-//   * PV: each wave produces D/4 output channels for all NH heads.  The B
-//     operand (keys x channels) is read transposed with ds_read_b64_tr_b16,
-//     whose 16-lane 4x4 block transpose delivers 4 keys of one channel per
-//     lane per instruction.
-//   * When a row's tiles are split across several workgroups, each writes its
-//     unnormalised partial output and (max, sum) and k_attn_combine merges
-//     them with the usual log-sum-exp weights.
+// Work decomposition.  One workgroup (4 waves) = one query row x NH = 16*HT
+// heads x a contiguous range of 64-key tiles.  Wave w owns the channel slice
+// [w*D/4, (w+1)*D/4) in both products, so every key is dequantised once per
+// workgroup and the query registers hold only a quarter of the channels:
+//   * S^T = K Q^T: each lane dequantises D/16 channels of 4 keys (one per
+//     16-key fragment) straight from the cache to fp16 in registers (E2M1 ->
+//     fp16 by the hardware converter, times the E4M3 scale; the product is
+//     exact in fp16) and feeds them as the A operand of
+//     v_mfma_f32_16x16x32_f16 against the NH query heads (B operand).  The
+//     contraction order only has to agree between the two operands; it is
+//     chosen so that in every MFMA lanes 0-31 carry the two halves of one
+//     16-channel scale group and lanes 32-63 those of another (see below).
+//     The same fp16 values go once into an LDS tile [64 keys][D].
+//   * The four channel-slice partials of S^T are summed through LDS; wave w
+//     keeps the 16 keys of fragment w.
+//   * Online softmax across tiles (log2 domain, lazily raised reference max);
+//     probabilities go to LDS as fp16.
+//   * PV: wave w produces its D/4 output channels for all NH heads; the B
+//     operand (keys x channels) is read with ds_read_b64_tr_b16.
+//   * Rows whose tiles are split across workgroups write unnormalised partial
+//     outputs plus (max, sum); k_attn_combine merges them.
+//
+// Exact scores for keys with large values.  The matrix cores sum products
+// with errors of a few units in the last place of the largest addend, and
+// with |v| in the hundreds a near tie between two keys turns such a score
+// error into an output error far above the tolerance.  Where a wave's keys
+// may hold |v| > 8 it computes S exactly instead: each query head is split as
+// q = a + b, a being q rounded to a multiple of 2^(E-11) with 2^E > max|q| of
+// the head (11 bits, exact in fp16), b the small remainder.  Within one scale
+// group every a*k product is then an integer multiple of one quantum and the
+// 16 products sum to less than 2^24 quanta, so an MFMA restricted to one group
+// (the other lane half masked to zero) returns the group sum exactly; the
+// group sums are accumulated in fp64, and K b^T (small, nonzero only for
+// channels with |q| < max|q|/16) is added from an ordinary MFMA chain.
 #include "csa2_device.h"
 #include "csa2_host.h"
 
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kTile = 64;
-constexpr float kLazy = 8.0f;   // log2-domain slack before a running max is raised
+constexpr int kTile = 64;           // keys per tile: 4 fragments of 16
+constexpr float kLazy = 8.0f;       // log2-domain slack before a running max is raised
+constexpr int kMaxSplits = 64;
 
 template <int NB>
 __device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src)
@@ -58,71 +73,121 @@ __device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src)
     }
 }
 
+// Channel layout of a lane (col, grp) in wave w, with p = grp / 2 and
+// h = grp % 2: k-step t (t < KT = D/128) covers the 8 channels
+//   w*D/4 + 16*(p*KT + t) + 8*h .. + 8,
+// i.e. half h of scale group p*KT + t of the wave's slice.  In each MFMA the
+// lanes with p = 0 thus hold one whole scale group and those with p = 1 another.
+template <int D>
+__device__ __forceinline__ int lane_ch0(int wave, int grp)
+{
+    constexpr int KT = D / 128;
+    return wave * (D / 4) + 16 * ((grp >> 1) * KT) + 8 * (grp & 1);
+}
 
-// Scale words / fp16 scale pairs held per lane (one scale per 16 channels).
-template <int DW> constexpr int kScaleWords = (DW / 16 + 3) / 4;
-template <int DW> constexpr int kScalePairs = (DW / 32) > 0 ? (DW / 32) : 1;
-
-// Raw bytes of one lane's quarter-key for one tile: FP4 codes and E4M3 scales
-// of a selected main entry, or FP8 bytes of an SWA row; zeros when the slot
-// holds no valid key (which dequantise to zeros on either path).
-template <int DW>
+// Raw bytes of one tile held by one lane: for each of the 4 key fragments, the
+// lane's key (16 f + col) restricted to its channels: FP4 codes (one word per
+// k-step) and its KT E4M3 scale bytes of a selected main entry, or FP8 bytes
+// (two words per k-step) of an SWA row.  A slot without a valid key gets a
+// zero scale (main; its code bytes are left as they are, any E2M1 code times
+// zero is zero) or zero bytes (SWA), so it dequantises to zeros.
+template <int D>
 struct TileRaw {
-    uint32_t raw[DW / 4];
-    uint32_t sraw[kScaleWords<DW>];
-    bool valid, is_main;
+    static constexpr int KT = D / 128;
+    uint32_t raw[4][2 * KT];
+    uint32_t sc[4];
+    bool valid[4], is_main[4];
 
-    // j: the Top-K entry of a main slot (ignored for SWA slots); slot: the
-    // lane's key slot (main slots first, then SWA rows).
-    __device__ __forceinline__ void load(int j, int slot, int K, int n, int64_t base, int nsw, int64_t swa0,
-                                         const uint8_t* codes, const uint8_t* scales, const uint8_t* swa, int D,
-                                         int grp)
+    __device__ __forceinline__ void load(const int32_t* topk_row, int tile, int col, int K, int n, int64_t base,
+                                         int nsw, int64_t swa0, const uint8_t* codes, const uint8_t* scales,
+                                         const uint8_t* swa, int ch0, int t_end)
     {
-        int64_t row;
-        if (slot < K) {
-            valid = j >= 0 && j < n;
-            is_main = true;
-            row = base + (valid ? j : 0);
-        } else {
-            const int i = slot - K;
-            valid = i < nsw;
-            is_main = false;
-            row = swa0 + (valid ? i : 0);
-        }
 #pragma unroll
-        for (int i = 0; i < DW / 4; ++i) raw[i] = 0u;
-#pragma unroll
-        for (int i = 0; i < kScaleWords<DW>; ++i) sraw[i] = 0u;
-        if (valid) {
-            if (is_main) {
-                load_bytes<DW / 2>(raw, codes + row * (D / 2) + grp * (DW / 2));
-                load_bytes<DW / 16>(sraw, scales + row * (D / 16) + grp * (DW / 16));
+        for (int f = 0; f < 4; ++f) {
+            const int slot = tile * kTile + 16 * f + col;
+            int64_t row;
+            if (tile >= t_end) {
+                valid[f] = false;
+                is_main[f] = true;
+                row = 0;
+            } else if (slot < K) {
+                const int j = topk_row[slot];
+                valid[f] = j >= 0 && j < n;
+                is_main[f] = true;
+                row = base + (valid[f] ? j : 0);
             } else {
-                load_bytes<DW>(raw, swa + row * D + grp * DW);
+                const int i = slot - K;
+                valid[f] = i < nsw;
+                is_main[f] = false;
+                row = swa0 + (valid[f] ? i : 0);
+            }
+            sc[f] = 0u;
+            if (valid[f]) {
+                if (is_main[f]) {
+                    const uint8_t* cr = codes + row * (D / 2) + ch0 / 2;
+#pragma unroll
+                    for (int t = 0; t < KT; ++t) raw[f][t] = *reinterpret_cast<const uint32_t*>(cr + 8 * t);
+                    load_bytes<KT>(&sc[f], scales + row * (D / 16) + ch0 / 16);
+                } else {
+                    const uint8_t* sr = swa + row * D + ch0;
+#pragma unroll
+                    for (int t = 0; t < KT; ++t) {
+                        const uint2 v = *reinterpret_cast<const uint2*>(sr + 16 * t);
+                        raw[f][2 * t] = v.x;
+                        raw[f][2 * t + 1] = v.y;
+                    }
+                }
+            } else if (!is_main[f]) {
+#pragma unroll
+                for (int i = 0; i < 2 * KT; ++i) raw[f][i] = 0u;
             }
         }
     }
+
+    // Whether this lane's keys may hold |v| > 8: an FP4 group holds
+    // |v| <= 6 * scale, so a scale byte of 0x3B (1.375) or more; an FP8 byte
+    // of magnitude 0x50 (8.0) or more.  Adding 0x45 (resp. 0x30) to a 7-bit
+    // magnitude sets bit 7 exactly at that threshold, with no carry between
+    // bytes; the unused high bytes of sc are zero and stay below bit 7.
+    __device__ __forceinline__ bool big() const
+    {
+        uint32_t bits = 0u;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            if (!valid[f]) continue;
+            if (is_main[f]) {
+                bits |= ((sc[f] & 0x7F7F7F7Fu) + 0x45454545u) & 0x80808080u;
+            } else {
+#pragma unroll
+                for (int i = 0; i < 2 * KT; ++i) bits |= ((raw[f][i] & 0x7F7F7F7Fu) + 0x30303030u) & 0x80808080u;
+            }
+        }
+        return bits != 0u;
+    }
 };
 
-// Dequantise k-step t (8 channels) of this lane's key to fp16.
-//   MODE 0: FP4 codes (one 32-bit word per step) times the group's E4M3 scale;
+// Dequantise k-step t (8 channels) of fragment f to fp16.
+//   MODE 0: FP4 codes (one word per step) times the group's E4M3 scale
+//           (scale byte t of the lane's KT scale bytes);
 //   MODE 1: FP8 E4M3 bytes (two words per step), unscaled;
-//   MODE 2: either, chosen per lane by is_main.
-template <int MODE>
-__device__ __forceinline__ f16x8 dequant_step(const uint32_t* raw, const f16x2* sc, bool is_main, int t)
+//   MODE 2: either, chosen per lane.
+template <int MODE, int D>
+__device__ __forceinline__ f16x8 dequant_step(const TileRaw<D>& tr, int f, int t)
 {
     f16x8 a, b;
     if (MODE != 1) {
-        const uint32_t c = raw[t];
+        const uint32_t c = tr.raw[f][t];
         const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0);
         const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1);
         const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2);
         const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3);
-        const _Float16 s = sc[t >> 2][(t >> 1) & 1];
+        const f16x2 sp = (t & 2) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(tr.sc[f], 1.0f, true)
+                                 : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(tr.sc[f], 1.0f, false);
+        const _Float16 s = sp[t & 1];
         a = (f16x8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]} * s;
     }
     if (MODE != 0) {
-        const uint32_t c0 = raw[2 * t], c1 = raw[2 * t + 1];
+        const uint32_t c0 = tr.raw[f][2 * t], c1 = tr.raw[f][2 * t + 1];
         const f16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, false);
         const f16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, true);
         const f16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1, 1.0f, false);
@@ -131,38 +196,98 @@ __device__ __forceinline__ f16x8 dequant_step(const uint32_t* raw, const f16x2* 
     }
     if (MODE == 0) return a;
     if (MODE == 1) return b;
-    return is_main ? a : b;
+    return tr.is_main[f] ? a : b;
 }
 
-// S^T for this wave's 16 keys: dequantise each k-step, store it to the V tile
-// and accumulate K Q^T (plain fp32 accumulation, or fresh partials folded by
-// TwoSum when PRECISE).
-template <int MODE, bool PRECISE, int HT, int KST>
-__device__ __forceinline__ void s_tile(const uint32_t* raw, const f16x2* sc, bool is_main,
-                                       const f16x8 (&qf)[HT][KST], _Float16* vrow, f32x4 (&sacc)[HT],
-                                       f32x4 (&slo)[HT])
+// TwoSum, elementwise: (hi, lo) += b, where hi + b == new hi + its rounding
+// error exactly and the error is added to lo.
+__device__ __forceinline__ void two_sum_into(f32x4& hi, f32x4& lo, f32x4 b)
+{
+    const f32x4 s = hi + b;
+    const f32x4 bb = s - hi;
+    lo += (hi - (s - bb)) + (b - bb);
+    hi = s;
+}
+
+// One fragment of S^T over this lane's channels, fp32 MFMA chain; the
+// dequantised keys also go to the V tile (piece t at channel offset 16 t).
+template <int MODE, int HT, int KT, int D>
+__device__ __forceinline__ void s_frag(const TileRaw<D>& tr, int f, const f16x8 (&qf)[HT][KT], _Float16* vrow,
+                                       f32x4 (&acc)[HT])
 {
 #pragma unroll
-    for (int t = 0; t < KST; ++t) {
-        const f16x8 kf = dequant_step<MODE>(raw, sc, is_main, t);
-        *reinterpret_cast<f16x8*>(vrow + 8 * t) = kf;
+    for (int t = 0; t < KT; ++t) {
+        const f16x8 kf = dequant_step<MODE, D>(tr, f, t);
+        *reinterpret_cast<f16x8*>(vrow + 16 * t) = kf;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ht][t], acc[ht], 0, 0, 0);
+    }
+}
+
+// The same fragment with S computed exactly as (hi, lo) = K a^T + K b^T
+// (split of q described at the top of the file).  qa: this lane's a-part
+// pieces in LDS, [HT * KT][256 lanes]; upper: lane >= 32.
+template <int MODE, int HT, int KT, int D>
+__device__ __forceinline__ void s_frag_exact(const TileRaw<D>& tr, int f, const f16x8 (&qf)[HT][KT],
+                                             const f16x8* qa, bool upper, _Float16* vrow, f32x4 (&acc)[HT],
+                                             f32x4 (&lo)[HT])
+{
+    double ex[HT][4];
+    f32x4 sb[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        sb[ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ex[ht][i] = 0.0;
+    }
+    const f16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+        const f16x8 kf = dequant_step<MODE, D>(tr, f, t);
+        *reinterpret_cast<f16x8*>(vrow + 16 * t) = kf;
+        const f16x8 k_lo = upper ? zero : kf;     // scale group p*KT + t with p = 0
+        const f16x8 k_hi = upper ? kf : zero;     // and with p = 1
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-            if (PRECISE) {
-                const f32x4 part = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ht][t],
-                                                                          (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            const f16x8 a = qa[(ht * KT + t) * 256];
+            const f16x8 b = qf[ht][t] - a;        // exact: the low bits of q
+            sb[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, b, sb[ht], 0, 0, 0);
+            const f32x4 g0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_lo, a, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            const f32x4 g1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_hi, a, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {   // TwoSum: hi + part == s + err exactly
-                    const float a = sacc[ht][i], b = part[i];
-                    const float s2 = a + b;
-                    const float bb = s2 - a;
-                    const float err = (a - (s2 - bb)) + (b - bb);
-                    sacc[ht][i] = s2;
-                    slo[ht][i] += err;
-                }
-            } else {
-                sacc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ht][t], sacc[ht], 0, 0, 0);
-            }
+            for (int i = 0; i < 4; ++i) ex[ht][i] += (double)g0[i] + (double)g1[i];
+        }
+    }
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const double v = ex[ht][i] + (double)sb[ht][i];
+            const float h = (float)v;
+            acc[ht][i] = h;
+            lo[ht][i] = (float)(v - (double)h);
+        }
+}
+
+// S^T partials of all 4 fragments over this lane's channels.  vbase: V tile
+// at (key col of fragment 0, this lane's first channel).
+template <bool EXACT, int HT, int KT, int D, int VST>
+__device__ __forceinline__ void s_tile(const TileRaw<D>& tr, const f16x8 (&qf)[HT][KT], const f16x8* qa,
+                                       bool upper, _Float16* vbase, f32x4 (&acc)[4][HT], f32x4 (&lo)[4][HT])
+{
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+        const uint64_t bm = __ballot(tr.valid[f] && tr.is_main[f]);
+        const uint64_t bs = __ballot(tr.valid[f] && !tr.is_main[f]);
+        _Float16* vrow = vbase + 16 * f * VST;
+        if (EXACT) {
+            if (bs == 0ull) s_frag_exact<0, HT, KT, D>(tr, f, qf, qa, upper, vrow, acc[f], lo[f]);
+            else if (bm == 0ull) s_frag_exact<1, HT, KT, D>(tr, f, qf, qa, upper, vrow, acc[f], lo[f]);
+            else s_frag_exact<2, HT, KT, D>(tr, f, qf, qa, upper, vrow, acc[f], lo[f]);
+        } else {
+            if (bs == 0ull) s_frag<0, HT, KT, D>(tr, f, qf, vrow, acc[f]);
+            else if (bm == 0ull) s_frag<1, HT, KT, D>(tr, f, qf, vrow, acc[f]);
+            else s_frag<2, HT, KT, D>(tr, f, qf, vrow, acc[f]);
         }
     }
 }
@@ -210,6 +335,20 @@ __device__ __forceinline__ void pv_tile(const _Float16* Pt, const _Float16* Plo,
     }
 }
 
+// LDS slot of the partial S^T that wave `src` computed for fragment f != src.
+__device__ __forceinline__ int red_slot(int f, int src) { return f * 3 + (src < f ? src : src - 1); }
+
+template <int HT>
+__device__ __forceinline__ void pick_own(const f32x4 (&a)[4][HT], int wave, f32x4 (&dst)[HT])
+{
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const f32x4 x01 = wave == 0 ? a[0][ht] : a[1][ht];
+        const f32x4 x23 = wave == 2 ? a[2][ht] : a[3][ht];
+        dst[ht] = wave < 2 ? x01 : x23;
+    }
+}
+
 template <int HT, int D>
 __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
@@ -220,19 +359,23 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     int32_t ntiles, float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml)
 {
-    constexpr int DW = D / 4;        // channels per lane (S^T) and per wave (PV)
-    constexpr int KST = D / 32;      // k-steps of 8 channels per lane
+    constexpr int DW = D / 4;        // channels per wave
+    constexpr int KT = D / 128;      // k-steps per fragment
     constexpr int NDT = DW / 16;     // 16-channel output tiles per wave
     constexpr int VST = D + 16;      // V tile row stride in halves (bank spread)
     constexpr int PST = kTile + 8;   // P row stride in halves
     constexpr int NH = HT * 16;
 
-    __shared__ __attribute__((aligned(16))) _Float16 Vt[2][kTile * VST];
+    __shared__ __attribute__((aligned(16))) _Float16 Vt[kTile * VST];
+    __shared__ __attribute__((aligned(16))) f32x4 red[12][HT][CSA2_WAVE];
     __shared__ __attribute__((aligned(16))) _Float16 Pt[NH * PST];
     __shared__ __attribute__((aligned(16))) _Float16 Plo[NH * PST];
+    __shared__ __attribute__((aligned(16))) f16x8 qa_s[HT * KT][256];
     __shared__ float wmax[4][NH];
-    __shared__ uint32_t wvmax[4];   // per wave: its keys may exceed |v| = 8
+    __shared__ __attribute__((aligned(16))) float alpha_s[NH];
     __shared__ float wl[4][NH];
+    __shared__ float mfin[NH];
+    __shared__ uint32_t wbig[4];
 
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
@@ -244,120 +387,144 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     nsw = nsw < 0 ? 0 : (nsw > W ? W : nsw);
     const int64_t swa0 = W > 0 ? swa_row_start[r] : 0;
     const int t_begin = (int)((int64_t)ntiles * s / S), t_end = (int)((int64_t)ntiles * (s + 1) / S);
+    const int32_t* topk_row = topk + (int64_t)r * K;
+    const int ch0 = lane_ch0<D>(wave, grp);     // channel of this lane's k-step 0
+    const bool upper = lane >= 32;
 
-    // Query heads as fp16 B-operand fragments: lane (head col, grp) holds
-    // channels grp*DW + 8t .. +8 of its head for k-step t.
-    f16x8 qf[HT][KST];
+    // Query heads (B operand): lane (head col, grp) holds channels ch0 + 16 t
+    // .. +8 for k-step t.  bf16 -> fp16 is exact for |q| in [2^-14, 65504].
+    f16x8 qf[HT][KT];
+    float q32[HT][KT][8];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const int h = h0 + ht * 16 + col;
-        uint32_t raw[DW / 2];
-        if (h < H) load_bytes<DW * 2>(raw, reinterpret_cast<const uint8_t*>(q + ((int64_t)r * H + h) * D + grp * DW));
-        else {
+        float m = 0.0f;
 #pragma unroll
-            for (int i = 0; i < DW / 2; ++i) raw[i] = 0;
-        }
-#pragma unroll
-        for (int t = 0; t < KST; ++t) {
+        for (int t = 0; t < KT; ++t) {
+            uint4 w = {0u, 0u, 0u, 0u};
+            if (h < H) w = *reinterpret_cast<const uint4*>(q + ((int64_t)r * H + h) * D + ch0 + 16 * t);
+            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const uint32_t w = raw[4 * t + e];
-                qf[ht][t][2 * e] = (_Float16)__uint_as_float(w << 16);
-                qf[ht][t][2 * e + 1] = (_Float16)__uint_as_float(w & 0xFFFF0000u);
+                q32[ht][t][2 * e] = __uint_as_float(ws[e] << 16);
+                q32[ht][t][2 * e + 1] = __uint_as_float(ws[e] & 0xFFFF0000u);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                qf[ht][t][e] = (_Float16)q32[ht][t][e];
+                m = fmaxf(m, fabsf(q32[ht][t][e]));
             }
         }
+        m = fmaxf(m, shfl_xor_f(m, 16));
+        m = fmaxf(m, shfl_xor_f(m, 32));
+        if (grp == 0) wmax[wave][ht * 16 + col] = m;
     }
+    __syncthreads();
+    // a-part of each head: q rounded to a multiple of 2^(E-11), 2^E > max|q|
+    // (E >= -13 keeps the quantum within fp16's subnormal grid).  Adding and
+    // subtracting 1.5 * 2^(E+12) rounds to that multiple in fp32.
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const int hh = ht * 16 + col;
+        const float m = fmaxf(fmaxf(wmax[0][hh], wmax[1][hh]), fmaxf(wmax[2][hh], wmax[3][hh]));
+        int E = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 0xFF) - 126 : -13;
+        E = E < -13 ? -13 : E;
+        const float C = __uint_as_float((uint32_t)(E + 12 + 127) << 23 | 0x400000u);
+#pragma unroll
+        for (int t = 0; t < KT; ++t) {
+            f16x8 av;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) av[e] = (_Float16)((q32[ht][t][e] + C) - C);
+            qa_s[ht * KT + t][threadIdx.x] = av;
+        }
+    }
+    // (qa_s and wmax are next touched after the first barrier of the tile loop)
 
     // Online softmax state (log2 domain).  The reference max of a head is
     // raised only when a tile's max exceeds it by more than kLazy, so the
     // accumulated output is rarely rescaled; probabilities stay <= 2^kLazy.
-    float m_p[HT], l_p[HT], m_o[HT][4];
+    // Every wave tracks the same reference (from the workgroup-wide tile max)
+    // and its own keys' part of the row sum.
+    float m_p[HT], l_p[HT];
     f32x4 o[HT][NDT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         m_p[ht] = -INFINITY;
         l_p[ht] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m_o[ht][i] = -INFINITY;
-#pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[ht][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     }
+    _Float16* const vbase = Vt + col * VST + ch0;
+    const f16x8* const qa_lane = &qa_s[0][threadIdx.x];
 
-    // Software pipeline over tiles: while tile t is processed, the raw bytes
-    // of tile t+1 and the index of tile t+2 are already in flight, so the
-    // dependent index -> row loads never stall the matrix work.
-    auto slot_index = [&](int tile) -> int {     // Top-K entry of this lane's slot (or -2)
-        const int slot = tile * kTile + wave * 16 + col;
-        return (tile < t_end && slot < K) ? topk[(int64_t)r * K + slot] : -2;
-    };
-    TileRaw<DW> cur, nxt;
-    int idx_next = slot_index(t_begin + 1);
-    cur.load(slot_index(t_begin), t_begin * kTile + wave * 16 + col, K, n, base, nsw, swa0, codes, scales, swa, D,
-             grp);
-
-    for (int tile = t_begin; tile < t_end; ++tile) {
-        const int buf = (tile - t_begin) & 1;
-        _Float16* V = Vt[buf];
-        if (tile + 1 < t_end) {
-            const int idx_after = slot_index(tile + 2);
-            nxt.load(idx_next, (tile + 1) * kTile + wave * 16 + col, K, n, base, nsw, swa0, codes, scales, swa, D,
-                     grp);
-            idx_next = idx_after;
-        }
-        const bool valid = cur.valid, is_main = cur.is_main;
-        const uint32_t* raw = cur.raw;
-        const uint32_t* sraw = cur.sraw;
-
+    auto body = [&](int tile, const TileRaw<D>& cur, TileRaw<D>& nxt) {
+        __syncthreads();   // (A) LDS buffers of the previous tile are free
         // Large values (|v| > 8) make the output sensitive to logit rounding:
         // a logit error e moves the output by about e * |v - out|.  A wave whose
-        // keys may hold such values accumulates S^T with one fresh MFMA result
-        // per k-step folded into an fp32 (hi, lo) pair by an exact TwoSum, and
-        // the tile uses two-part probabilities in PV.  The test is on the
-        // stored bytes: an FP4 group holds |v| <= 6 * scale, so a scale byte of
-        // 0x3B (1.375) or more; an FP8 SWA byte of magnitude 0x50 (8.0) or more.
-        // Adding 0x45 (resp. 0x30) to a 7-bit magnitude sets bit 7 exactly
-        // when the magnitude reaches 0x3B (resp. 0x50), with no carry between
-        // bytes (missing bytes are zero).
-        uint32_t bigbits = 0u;
-        if (is_main) {
+        // keys may hold such values computes its score slice exactly as a
+        // (hi, lo) pair; the whole tile then sums the slices with TwoSum and
+        // uses two-part probabilities in PV.
+        const bool my_big = __ballot(cur.big()) != 0ull;
+        nxt.load(topk_row, tile + 1, col, K, n, base, nsw, swa0, codes, scales, swa, ch0, t_end);
+
+        f32x4 acc[4][HT], lo[4][HT];
 #pragma unroll
-            for (int i = 0; i < kScaleWords<DW>; ++i) bigbits |= ((sraw[i] & 0x7F7F7F7Fu) + 0x45454545u) & 0x80808080u;
-            // bytes past the lane's DW/16 scales are zero and read as 0x45 < 0x80
+        for (int f = 0; f < 4; ++f)
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                acc[f][ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+                lo[f][ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+            }
+        if (my_big) s_tile<true, HT, KT, D, VST>(cur, qf, qa_lane, upper, vbase, acc, lo);
+        else s_tile<false, HT, KT, D, VST>(cur, qf, qa_lane, upper, vbase, acc, lo);
+
+        // ---- sum the four channel slices: wave w keeps fragment w
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+            if (f != wave)
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) red[red_slot(f, wave)][ht][lane] = acc[f][ht];
+        if (lane == 0) wbig[wave] = my_big ? 1u : 0u;
+        __syncthreads();   // (B)
+        const bool precise = (wbig[0] | wbig[1] | wbig[2] | wbig[3]) != 0u;
+        f32x4 sh[HT], sl[HT];
+        pick_own<HT>(acc, wave, sh);
+        pick_own<HT>(lo, wave, sl);
+        if (precise) {
+#pragma unroll
+            for (int k = 1; k < 4; ++k) {
+                const int src = (wave + k) & 3;
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) {
+                    two_sum_into(sh[ht], sl[ht], red[red_slot(wave, src)][ht][lane]);
+                }
+            }
+            __syncthreads();   // all high parts read; the buffer takes the low parts
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+                if (f != wave)
+#pragma unroll
+                    for (int ht = 0; ht < HT; ++ht) red[red_slot(f, wave)][ht][lane] = lo[f][ht];
+            __syncthreads();
+#pragma unroll
+            for (int k = 1; k < 4; ++k) {
+                const int src = (wave + k) & 3;
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht) sl[ht] += red[red_slot(wave, src)][ht][lane];
+            }
         } else {
 #pragma unroll
-            for (int i = 0; i < DW / 4; ++i) bigbits |= ((raw[i] & 0x7F7F7F7Fu) + 0x30303030u) & 0x80808080u;
-        }
-        const bool precise = __ballot(bigbits != 0u) != 0ull;
-        const uint64_t bmain = __ballot(valid && is_main), bswa = __ballot(valid && !is_main);
-
-        f16x2 sc[kScalePairs<DW>];
+            for (int k = 1; k < 4; ++k) {
+                const int src = (wave + k) & 3;
 #pragma unroll
-        for (int i = 0; i < kScalePairs<DW>; i += 2) {
-            sc[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sraw[i >> 1], 1.0f, false);
-            if (i + 1 < kScalePairs<DW>) sc[i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sraw[i >> 1], 1.0f, true);
+                for (int ht = 0; ht < HT; ++ht) sh[ht] += red[red_slot(wave, src)][ht][lane];
+            }
         }
 
-        f32x4 sacc[HT], slo[HT];
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            sacc[ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-            slo[ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-        }
-        _Float16* vrow = V + (wave * 16 + col) * VST + grp * DW;
-        if (bswa == 0ull) {
-            if (precise) s_tile<0, true, HT, KST>(raw, sc, is_main, qf, vrow, sacc, slo);
-            else s_tile<0, false, HT, KST>(raw, sc, is_main, qf, vrow, sacc, slo);
-        } else if (bmain == 0ull) {
-            if (precise) s_tile<1, true, HT, KST>(raw, sc, is_main, qf, vrow, sacc, slo);
-            else s_tile<1, false, HT, KST>(raw, sc, is_main, qf, vrow, sacc, slo);
-        } else {
-            if (precise) s_tile<2, true, HT, KST>(raw, sc, is_main, qf, vrow, sacc, slo);
-            else s_tile<2, false, HT, KST>(raw, sc, is_main, qf, vrow, sacc, slo);
-        }
-        if (lane == 0) wvmax[wave] = precise ? 1u : 0u;
-
-        // S^T lane layout: head (h0 + 16 ht + col), keys wave*16 + 4 grp + i
-        const uint64_t vb = __ballot(valid);
+        // S^T lane layout: head h0 + 16 ht + col, keys 16 wave + 4 grp + i
+        const bool v0 = wave == 0 ? cur.valid[0] : cur.valid[1];
+        const bool v1 = wave == 2 ? cur.valid[2] : cur.valid[3];
+        const uint64_t vb = __ballot(wave < 2 ? v0 : v1);
         float x[HT][4];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
@@ -365,22 +532,18 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool kv = (vb >> (4 * grp + i)) & 1ull;
-                x[ht][i] = kv ? (sacc[ht][i] + slo[ht][i]) * scale_log2e : -INFINITY;
+                x[ht][i] = kv ? (sh[ht][i] + sl[ht][i]) * scale_log2e : -INFINITY;
                 mx = fmaxf(mx, x[ht][i]);
             }
             mx = fmaxf(mx, shfl_xor_f(mx, 16));
             mx = fmaxf(mx, shfl_xor_f(mx, 32));
             if (grp == 0) wmax[wave][ht * 16 + col] = mx;
         }
-        __syncthreads();
+        __syncthreads();   // (C)
 
         // Probabilities enter PV as fp16, whose rounding (relative 2^-12) moves
-        // the output by up to 2^-12 * |v - out|.  For tiles whose keys may hold
-        // |v| > 8 the probability is split into fp16 hi + lo parts and PV runs
-        // twice, which brings the rounding to ~2^-23.
-        const bool split = (wvmax[0] | wvmax[1] | wvmax[2] | wvmax[3]) != 0u;
-        float alpha[HT][4];
-        bool rescale = false;
+        // the output by up to 2^-12 * |v - out|; in a precise tile they are
+        // split into fp16 hi + lo parts and PV runs twice (rounding ~2^-23).
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
             const int hh = ht * 16 + col;
@@ -394,50 +557,58 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
             for (int i = 0; i < 4; ++i) {
                 // the exponent's argument is formed with one rounding at its own
                 // (small) magnitude; the reference itself only has to be consistent
-                const float d = fmaf(sacc[ht][i], scale_log2e, -mn) + slo[ht][i] * scale_log2e;
+                const float d = fmaf(sh[ht][i], scale_log2e, -mn) + sl[ht][i] * scale_log2e;
                 const float pf = (live && x[ht][i] != -INFINITY) ? exp2f(d) : 0.0f;
                 const _Float16 p = (_Float16)pf;
                 p4[i] = p;
                 q4[i] = (_Float16)(pf - (float)p);
-                ps += split ? pf : (float)p;   // normalise by what PV actually weights
+                ps += precise ? pf : (float)p;   // normalise by what PV actually weights
             }
             l_p[ht] = l_p[ht] * ap + ps;
+            if (wave == 0 && grp == 0) alpha_s[hh] = (m_p[ht] != -INFINITY && mn != m_p[ht]) ? ap : 1.0f;
             m_p[ht] = mn;
             *reinterpret_cast<f16x4*>(&Pt[hh * PST + wave * 16 + 4 * grp]) = p4;
-            if (split) *reinterpret_cast<f16x4*>(&Plo[hh * PST + wave * 16 + 4 * grp]) = q4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ho = ht * 16 + 4 * grp + i;
-                const float mto = fmaxf(fmaxf(wmax[0][ho], wmax[1][ho]), fmaxf(wmax[2][ho], wmax[3][ho]));
-                const float mno = (mto > m_o[ht][i] + kLazy) ? mto : m_o[ht][i];
-                alpha[ht][i] = (m_o[ht][i] != -INFINITY) ? exp2f(m_o[ht][i] - mno) : 1.0f;
-                rescale |= mno != m_o[ht][i] && m_o[ht][i] != -INFINITY;
-                m_o[ht][i] = mno;
-            }
+            if (precise) *reinterpret_cast<f16x4*>(&Plo[hh * PST + wave * 16 + 4 * grp]) = q4;
         }
-        __syncthreads();
+        __syncthreads();   // (D)
 
+        // O lane layout: channel c0 + 16 dt + col, heads 16 ht + 4 grp + i
+        bool rescale = false;
+        f32x4 al[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            al[ht] = *reinterpret_cast<const f32x4*>(&alpha_s[ht * 16 + 4 * grp]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rescale |= al[ht][i] != 1.0f;
+        }
         if (__ballot(rescale) != 0ull) {
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) o[ht][dt][i] *= alpha[ht][i];
+                for (int dt = 0; dt < NDT; ++dt) o[ht][dt] *= al[ht];
         }
+        if (precise) pv_tile<true, HT, NDT, VST, PST>(Pt, Plo, Vt, col, grp, wave * DW, o);
+        else pv_tile<false, HT, NDT, VST, PST>(Pt, Plo, Vt, col, grp, wave * DW, o);
+    };
 
-        if (split) pv_tile<true, HT, NDT, VST, PST>(Pt, Plo, V, col, grp, wave * DW, o);
-        else pv_tile<false, HT, NDT, VST, PST>(Pt, Plo, V, col, grp, wave * DW, o);
-        cur = nxt;
+    // Software pipeline: tile t+1's raw bytes load while tile t runs; the two
+    // register sets swap roles every tile.
+    TileRaw<D> ra, rb;
+    ra.load(topk_row, t_begin, col, K, n, base, nsw, swa0, codes, scales, swa, ch0, t_end);
+    for (int tile = t_begin; tile < t_end; tile += 2) {
+        body(tile, ra, rb);
+        if (tile + 1 < t_end) body(tile + 1, rb, ra);
     }
 
-    // Row sums over the four waves' keys.
+    // Row sums over the four waves' keys; the reference max is the same in
+    // every wave.
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         float lt = l_p[ht];
         lt += shfl_xor_f(lt, 16);
         lt += shfl_xor_f(lt, 32);
         if (grp == 0) wl[wave][ht * 16 + col] = lt;
+        if (wave == 0 && grp == 0) mfin[ht * 16 + col] = m_p[ht];
     }
     __syncthreads();
 #pragma unroll
@@ -448,7 +619,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
             const int h = h0 + hh;
             if (h >= H) continue;
             const float L = wl[0][hh] + wl[1][hh] + wl[2][hh] + wl[3][hh];
-            const float M = m_o[ht][i];
+            const float M = mfin[hh];
             if (S == 1) {
                 const float inv = L > 0.0f ? 1.0f / L : 0.0f;
                 float* op = out + ((int64_t)r * H + h) * D + wave * DW + col;
@@ -472,7 +643,6 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
 
 // Merge of split partials: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
 // One workgroup per (row, head); each thread owns four consecutive channels.
-constexpr int kMaxSplits = 64;
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, int32_t H,
                                                       int32_t D, int32_t S, float* __restrict__ out,
@@ -516,13 +686,17 @@ struct AttnPlan {
     int HT, HG, S, ntiles;
 };
 
-AttnPlan plan_attn(int32_t R, int32_t H, int32_t K, int32_t W)
+// Heads per workgroup (16 HT) and key splits per row.  All heads of a group
+// share one dequantisation of each key, so HT is as large as the head count
+// allows; a row's tiles are split over workgroups only as far as needed to
+// occupy the compute units, since every split adds a partial output.
+AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
 {
     AttnPlan p;
     p.ntiles = (K + W + kTile - 1) / kTile;
     if (p.ntiles < 1) p.ntiles = 1;
-    const int hg2 = (H + 31) / 32;
-    p.HT = (H > 16 && (int64_t)R * hg2 * p.ntiles >= 256) ? 2 : 1;
+    // 64 heads per group only where the registers allow it (D = 128)
+    p.HT = (H > 32 && D <= 128) ? 4 : (H > 16 ? 2 : 1);
     p.HG = (H + 16 * p.HT - 1) / (16 * p.HT);
     const int64_t base = (int64_t)R * p.HG;
     int64_t S = base >= 256 ? 1 : (256 + base - 1) / base;
@@ -548,7 +722,7 @@ void launch_attn(dim3 grid, hipStream_t st, const uint16_t* q, const uint8_t* co
 extern "C" size_t csa2_sparse_attn_workspace_bytes(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
 {
     if (R <= 0 || H <= 0 || D <= 0 || K < 0 || W < 0) return 0;
-    const AttnPlan p = plan_attn(R, H, K, W);
+    const AttnPlan p = plan_attn(R, H, D, K, W);
     if (p.S <= 1) return 0;
     return csa2::align_up((size_t)R * p.S * H * D * 4, 256) + csa2::align_up((size_t)R * p.S * H * 2 * 4, 256);
 }
@@ -564,8 +738,8 @@ extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* code
     CSA2_REQUIRE(R >= 0, CSA2_ERR_SHAPE, "sparse_attn: R=%d < 0", R);
     CSA2_REQUIRE(H >= 1, CSA2_ERR_SHAPE, "sparse_attn: H=%d < 1", H);
     CSA2_REQUIRE(D >= 16 && D % 16 == 0, CSA2_ERR_SHAPE, "sparse_attn: D=%d must be a positive multiple of 16", D);
-    CSA2_REQUIRE(D == 64 || D == 128 || D == 256 || D == 512, CSA2_ERR_UNSUPPORTED,
-                 "sparse_attn: D=%d (supported: 64, 128, 256, 512)", D);
+    CSA2_REQUIRE(D == 128 || D == 256 || D == 512, CSA2_ERR_UNSUPPORTED,
+                 "sparse_attn: D=%d (supported: 128, 256, 512)", D);
     CSA2_REQUIRE(K >= 0 && W >= 0, CSA2_ERR_SHAPE, "sparse_attn: K=%d, W=%d must be >= 0", K, W);
     CSA2_REQUIRE(K <= 4096 && W <= 4096, CSA2_ERR_UNSUPPORTED, "sparse_attn: K=%d or W=%d > 4096", K, W);
     if (R == 0) return CSA2_OK;
@@ -574,7 +748,7 @@ extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* code
     CSA2_REQUIRE(K == 0 || topk_idx, CSA2_ERR_NULL, "sparse_attn: topk_idx is NULL with K > 0");
     CSA2_REQUIRE(W == 0 || (swa && swa_row_start && swa_len), CSA2_ERR_NULL,
                  "sparse_attn: SWA pointers are NULL with W > 0");
-    const AttnPlan p = plan_attn(R, H, K, W);
+    const AttnPlan p = plan_attn(R, H, D, K, W);
     CSA2_REQUIRE((int64_t)R * p.HG <= 0x7FFFFFFF, CSA2_ERR_UNSUPPORTED, "sparse_attn: grid too large");
     const size_t need = csa2_sparse_attn_workspace_bytes(R, H, D, K, W);
     CSA2_REQUIRE(need == 0 || (workspace && workspace_bytes >= need && ((uintptr_t)workspace & 255) == 0),
@@ -596,8 +770,9 @@ extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* code
         launch_attn<ht, d>(grid, st, q, codes, scales, seq_start, row_seq, row_len, topk_idx, K, swa,   \
                            swa_row_start, swa_len, H, W, sl2e, p.HG, p.S, p.ntiles, out, lse, po, pml); \
     }
-    CSA2_ATTN(1, 64) CSA2_ATTN(1, 128) CSA2_ATTN(1, 256) CSA2_ATTN(1, 512)
-    CSA2_ATTN(2, 64) CSA2_ATTN(2, 128) CSA2_ATTN(2, 256) CSA2_ATTN(2, 512)
+    CSA2_ATTN(1, 128) CSA2_ATTN(1, 256) CSA2_ATTN(1, 512)
+    CSA2_ATTN(2, 128) CSA2_ATTN(2, 256) CSA2_ATTN(2, 512)
+    CSA2_ATTN(4, 128)
 #undef CSA2_ATTN
     if (p.S > 1)
         hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(R * H)), dim3(128), 0, st, po, pml, H, D, p.S, out, lse);

@@ -130,6 +130,7 @@ def attn_args(**kw):
 def test_sparse_attn_validation():
     f = csa2.lib().csa2_sparse_attn
     assert f(*attn_args(D=96)) == 3
+    assert f(*attn_args(D=64)) == 3
     assert f(*attn_args(D=40)) == 2
     assert f(*attn_args(H=0)) == 2
     assert f(*attn_args(K=-1)) == 2

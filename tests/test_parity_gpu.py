@@ -229,7 +229,9 @@ def with_cache(wl):
     ("d512_h64_k512_w128_split", [9000, 700, 30000], 512, 64, 512, 128),
     ("d512_h64_many_rows_nosplit", [300 + 37 * i for i in range(130)], 512, 64, 512, 128),
     ("d256_h24_k100_w7", [1000, 77, 5000, 2222], 256, 24, 100, 7),
-    ("d64_h3_k33_w0", [500, 40], 64, 3, 33, 0),
+    ("d128_h3_k33_w0", [500, 40], 128, 3, 33, 0),
+    ("d128_h40_k200_w16", [3000, 250, 900], 128, 40, 200, 16),
+    ("d256_h64_k300_w64", [5000, 301, 64], 256, 64, 300, 64),
     ("d512_h16_k0_swa_only", [100, 100], 512, 16, 0, 128),
 ])
 def test_sparse_attn_matches_oracle(name, lengths, D, H, K, W):
