@@ -166,9 +166,12 @@ csa2_status_t csa2_index_reindex(const uint8_t* qI, const float* w, const uint8_
  *   out      [R, H, D] float32;  lse [R, H] float32 (may be NULL).
  *   workspace: csa2_sparse_attn_workspace_bytes(R, H, D, K, W) bytes,
  *            256-byte aligned (may be 0 bytes and NULL when that is 0).
- * Arithmetic: dequantised keys are exact in fp16; logits accumulate in fp32;
- * softmax in fp32; probabilities enter the PV product rounded to fp16;
- * outputs accumulate in fp32.
+ * Arithmetic: dequantised keys are exact in fp16; logits accumulate in fp32,
+ * and are exact (then rounded once) for key tiles whose scales or FP8 bytes
+ * allow |value| > 8; softmax in fp32; probabilities enter the PV product
+ * rounded to fp16 (split into two fp16 parts in those tiles) and the output is
+ * normalised by the sum of the weights PV used; outputs accumulate in fp32;
+ * lse uses the unrounded fp32 probabilities.
  * Limits: H >= 1; D in {128, 256, 512}; 0 <= K <= 4096; 0 <= W <= 4096.
  */
 size_t csa2_sparse_attn_workspace_bytes(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W);

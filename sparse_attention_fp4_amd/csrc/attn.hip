@@ -85,6 +85,14 @@ __device__ __forceinline__ int lane_ch0(int wave, int grp)
     return wave * (D / 4) + 16 * ((grp >> 1) * KT) + 8 * (grp & 1);
 }
 
+// Local unit holding piece t after TileRaw::unpair(): {0, 2, 1, 3} for four
+// pieces, identity otherwise.
+template <int D>
+__device__ __forceinline__ constexpr int kperm(int t)
+{
+    return D / 128 == 4 ? ((t & 1) << 1 | (t >> 1)) : t;
+}
+
 // Raw bytes of one tile held by one lane: for each of the 4 key fragments, the
 // lane's key (16 f + col) restricted to its channels: FP4 codes (one word per
 // k-step) and its KT E4M3 scale bytes of a selected main entry, or FP8 bytes
@@ -98,48 +106,104 @@ struct TileRaw {
     uint32_t sc[4];
     bool valid[4], is_main[4];
 
-    __device__ __forceinline__ void load(const int32_t* topk_row, int tile, int col, int K, int n, int64_t base,
-                                         int nsw, int64_t swa0, const uint8_t* codes, const uint8_t* scales,
-                                         const uint8_t* swa, int ch0, int t_end)
+    // idx: the Top-K entries of the lane's 4 slots (fetched a tile earlier;
+    // only read for Top-K slots).  crow / srow / wrow: code, scale and SWA
+    // pointers of the row's first entry, already offset to the lane's
+    // channels.  One straight-line path for every kind of slot: each load is
+    // predicated and writes its registers in place, so the loads stay in
+    // flight until the bytes are used a tile later.  FP4 piece t lands in word
+    // 2t, FP8 piece t in words 2t and 2t+1.
+    __device__ __forceinline__ void load(int tile, const int (&idx)[4], int col, int h, int K, int n, int nsw,
+                                         const uint8_t* crow, const uint8_t* srow, const uint8_t* wrow)
     {
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
             const int slot = tile * kTile + 16 * f + col;
-            int64_t row;
-            if (tile >= t_end) {
-                valid[f] = false;
-                is_main[f] = true;
-                row = 0;
-            } else if (slot < K) {
-                const int j = topk_row[slot];
-                valid[f] = j >= 0 && j < n;
-                is_main[f] = true;
-                row = base + (valid[f] ? j : 0);
-            } else {
-                const int i = slot - K;
-                valid[f] = i < nsw;
-                is_main[f] = false;
-                row = swa0 + (valid[f] ? i : 0);
-            }
+            const bool m = slot < K;
+            const int j = idx[f], i = slot - K;
+            const bool vm = m && j >= 0 && j < n;
+            const bool vs = !m && i < nsw;
+            valid[f] = vm || vs;
+            is_main[f] = m;
             sc[f] = 0u;
-            if (valid[f]) {
-                if (is_main[f]) {
-                    const uint8_t* cr = codes + row * (D / 2) + ch0 / 2;
+            // The lane pair (p, 0), (p, 1) of a key needs one contiguous block
+            // (codes: 4*KT bytes, SWA: 16*KT bytes); each lane loads its half,
+            // into consecutive words, and unpair() exchanges the halves a tile
+            // later.  The first access serves both kinds (its address is chosen
+            // per lane), so no two loads in flight write the same registers.
+            const uint8_t* ca = crow + (size_t)j * (D / 2) + (KT == 4 ? 12 : (KT == 2 ? 4 : 0)) * h;
+            const uint8_t* sa = wrow + (size_t)i * D + (KT == 4 ? 24 : (KT == 2 ? 8 : 0)) * h;
+            const uint8_t* a1 = vm ? ca : sa;
 #pragma unroll
-                    for (int t = 0; t < KT; ++t) raw[f][t] = *reinterpret_cast<const uint32_t*>(cr + 8 * t);
-                    load_bytes<KT>(&sc[f], scales + row * (D / 16) + ch0 / 16);
+            for (int w = 0; w < 2 * KT; ++w) raw[f][w] = 0u;
+            if (vm || vs) {
+                if constexpr (KT == 4) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(a1);
+                    raw[f][0] = v.x; raw[f][1] = v.y; raw[f][2] = v.z; raw[f][3] = v.w;
+                } else if constexpr (KT == 2) {
+                    const uint2 v = *reinterpret_cast<const uint2*>(a1);
+                    raw[f][0] = v.x; raw[f][1] = v.y;
                 } else {
-                    const uint8_t* sr = swa + row * D + ch0;
+                    raw[f][0] = *reinterpret_cast<const uint32_t*>(a1);
+                }
+            }
+            if (vs) {                 // the second half of an SWA lane's bytes
+                if constexpr (KT == 4) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(sa + 16);
+                    raw[f][4] = v.x; raw[f][5] = v.y; raw[f][6] = v.z; raw[f][7] = v.w;
+                } else if constexpr (KT == 2) {
+                    const uint2 v = *reinterpret_cast<const uint2*>(sa + 8);
+                    raw[f][2] = v.x; raw[f][3] = v.y;
+                } else {
+                    raw[f][1] = *reinterpret_cast<const uint32_t*>(sa + 4);
+                }
+            }
+            if (vm) load_bytes<KT>(&sc[f], srow + (size_t)j * (D / 16));
+        }
+    }
+
+    // Unit u of a pair's block (a code word, or 8 FP8 bytes) is piece u/2 of
+    // half u%2; after load() lane h holds units 2h, 2h+1 (KT = 2) or 4h .. 4h+3
+    // (KT = 4) in consecutive words.  v_permlane16_swap(x, y) exchanges row 1
+    // of x with row 0 of y (rows are the 16-lane groups: rows 0/1 are the
+    // halves h = 0/1 of p = 0, rows 2/3 those of p = 1).  Swapping local units
+    // (0, 1) and, for KT = 4, (2, 3) leaves the lane's own half of piece t in
+    // local unit kPerm[t]: code word kPerm[t], or FP8 words 2 kPerm[t] and
+    // 2 kPerm[t] + 1.  KIND as for the tile (main, SWA, or both per lane).
+    template <int KIND>
+    __device__ __forceinline__ void unpair()
+    {
+        if constexpr (KT >= 2) {
 #pragma unroll
-                    for (int t = 0; t < KT; ++t) {
-                        const uint2 v = *reinterpret_cast<const uint2*>(sr + 16 * t);
-                        raw[f][2 * t] = v.x;
-                        raw[f][2 * t + 1] = v.y;
+            for (int f = 0; f < 4; ++f) {
+                uint32_t c[KT], w[2 * KT];
+#pragma unroll
+                for (int u = 0; u < KT / 2; ++u) {
+                    if (KIND != 1) {      // code words 2u <-> 2u+1
+                        const auto r = __builtin_amdgcn_permlane16_swap(raw[f][2 * u], raw[f][2 * u + 1], false, false);
+                        c[2 * u] = r[0];
+                        c[2 * u + 1] = r[1];
+                    }
+                    if (KIND != 0) {      // FP8 units 2u <-> 2u+1, both words
+                        const auto ra = __builtin_amdgcn_permlane16_swap(raw[f][4 * u], raw[f][4 * u + 2], false, false);
+                        const auto rb = __builtin_amdgcn_permlane16_swap(raw[f][4 * u + 1], raw[f][4 * u + 3], false, false);
+                        w[4 * u] = ra[0];
+                        w[4 * u + 2] = ra[1];
+                        w[4 * u + 1] = rb[0];
+                        w[4 * u + 3] = rb[1];
                     }
                 }
-            } else if (!is_main[f]) {
+                if (KIND == 0) {
 #pragma unroll
-                for (int i = 0; i < 2 * KT; ++i) raw[f][i] = 0u;
+                    for (int k = 0; k < KT; ++k) raw[f][k] = c[k];
+                } else if (KIND == 1) {
+#pragma unroll
+                    for (int k = 0; k < 2 * KT; ++k) raw[f][k] = w[k];
+                } else {
+                    const bool mm = is_main[f];
+#pragma unroll
+                    for (int k = 0; k < 2 * KT; ++k) raw[f][k] = mm ? (k < KT ? c[k] : 0u) : w[k];
+                }
             }
         }
     }
@@ -167,16 +231,16 @@ struct TileRaw {
 };
 
 // Dequantise k-step t (8 channels) of fragment f to fp16.
-//   MODE 0: FP4 codes (one word per step) times the group's E4M3 scale
+//   MODE 0: FP4 codes (word kperm(t)) times the group's E4M3 scale
 //           (scale byte t of the lane's KT scale bytes);
-//   MODE 1: FP8 E4M3 bytes (two words per step), unscaled;
+//   MODE 1: FP8 E4M3 bytes (words 2 kperm(t), +1), unscaled;
 //   MODE 2: either, chosen per lane.
 template <int MODE, int D>
 __device__ __forceinline__ f16x8 dequant_step(const TileRaw<D>& tr, int f, int t)
 {
     f16x8 a, b;
     if (MODE != 1) {
-        const uint32_t c = tr.raw[f][t];
+        const uint32_t c = tr.raw[f][kperm<D>(t)];
         const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0);
         const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1);
         const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2);
@@ -187,7 +251,7 @@ __device__ __forceinline__ f16x8 dequant_step(const TileRaw<D>& tr, int f, int t
         a = (f16x8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]} * s;
     }
     if (MODE != 0) {
-        const uint32_t c0 = tr.raw[f][2 * t], c1 = tr.raw[f][2 * t + 1];
+        const uint32_t c0 = tr.raw[f][2 * kperm<D>(t)], c1 = tr.raw[f][2 * kperm<D>(t) + 1];
         const f16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, false);
         const f16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, true);
         const f16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1, 1.0f, false);
@@ -270,25 +334,17 @@ __device__ __forceinline__ void s_frag_exact(const TileRaw<D>& tr, int f, const 
 }
 
 // S^T partials of all 4 fragments over this lane's channels.  vbase: V tile
-// at (key col of fragment 0, this lane's first channel).
-template <bool EXACT, int HT, int KT, int D, int VST>
+// at (key col of fragment 0, this lane's first channel).  KIND as in
+// TileRaw::load; the exact path uses one general dequantisation for all kinds.
+template <bool EXACT, int KIND, int HT, int KT, int D, int VST>
 __device__ __forceinline__ void s_tile(const TileRaw<D>& tr, const f16x8 (&qf)[HT][KT], const f16x8* qa,
                                        bool upper, _Float16* vbase, f32x4 (&acc)[4][HT], f32x4 (&lo)[4][HT])
 {
 #pragma unroll
     for (int f = 0; f < 4; ++f) {
-        const uint64_t bm = __ballot(tr.valid[f] && tr.is_main[f]);
-        const uint64_t bs = __ballot(tr.valid[f] && !tr.is_main[f]);
         _Float16* vrow = vbase + 16 * f * VST;
-        if (EXACT) {
-            if (bs == 0ull) s_frag_exact<0, HT, KT, D>(tr, f, qf, qa, upper, vrow, acc[f], lo[f]);
-            else if (bm == 0ull) s_frag_exact<1, HT, KT, D>(tr, f, qf, qa, upper, vrow, acc[f], lo[f]);
-            else s_frag_exact<2, HT, KT, D>(tr, f, qf, qa, upper, vrow, acc[f], lo[f]);
-        } else {
-            if (bs == 0ull) s_frag<0, HT, KT, D>(tr, f, qf, vrow, acc[f]);
-            else if (bm == 0ull) s_frag<1, HT, KT, D>(tr, f, qf, vrow, acc[f]);
-            else s_frag<2, HT, KT, D>(tr, f, qf, vrow, acc[f]);
-        }
+        if (EXACT) s_frag_exact<2, HT, KT, D>(tr, f, qf, qa, upper, vrow, acc[f], lo[f]);
+        else s_frag<KIND, HT, KT, D>(tr, f, qf, vrow, acc[f]);
     }
 }
 
@@ -335,6 +391,12 @@ __device__ __forceinline__ void pv_tile(const _Float16* Pt, const _Float16* Plo,
     }
 }
 
+// Kind of a 64-key tile (uniform): 0 all Top-K slots, 1 all SWA rows, 2 both.
+__device__ __forceinline__ int tile_kind(int tile, int K)
+{
+    return (tile + 1) * kTile <= K ? 0 : (tile * kTile >= K ? 1 : 2);
+}
+
 // LDS slot of the partial S^T that wave `src` computed for fragment f != src.
 __device__ __forceinline__ int red_slot(int f, int src) { return f * 3 + (src < f ? src : src - 1); }
 
@@ -374,6 +436,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     __shared__ float wmax[4][NH];
     __shared__ __attribute__((aligned(16))) float alpha_s[NH];
     __shared__ float wl[4][NH];
+    __shared__ float wle[4][NH];
     __shared__ float mfin[NH];
     __shared__ uint32_t wbig[4];
 
@@ -390,6 +453,29 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     const int32_t* topk_row = topk + (int64_t)r * K;
     const int ch0 = lane_ch0<D>(wave, grp);     // channel of this lane's k-step 0
     const bool upper = lane >= 32;
+    const uint8_t* const crow = codes + base * (D / 2) + ch0 / 2;
+    const uint8_t* const srow = scales + base * (D / 16) + ch0 / 16;
+    const uint8_t* const wrow = swa + swa0 * D + ch0;   // not dereferenced when W == 0
+
+    // Top-K entries of the lane's 4 slots of a tile.  SWA slots are left as
+    // they are (TileRaw::load never reads them); no select on the loaded
+    // value, so nothing waits for the load here.
+    auto load_idx = [&](int tile, int (&idx)[4]) {
+#pragma unroll
+        for (int f = 0; f < 4; ++f) {
+            const int slot = tile * kTile + 16 * f + col;
+            if (slot < K) idx[f] = topk_row[slot];
+        }
+    };
+    // The first tile's bytes are requested before the query set-up below.
+    TileRaw<D> cur, nxt;   // cur is unpaired in place at the start of its tile
+    int idx_n[4] = {0, 0, 0, 0};
+    {
+        int idx0[4] = {0, 0, 0, 0};
+        load_idx(t_begin, idx0);
+        cur.load(t_begin, idx0, col, grp & 1, K, n, nsw, crow, srow, wrow);
+        if (t_begin + 1 < t_end) load_idx(t_begin + 1, idx_n);
+    }
 
     // Query heads (B operand): lane (head col, grp) holds channels ch0 + 16 t
     // .. +8 for k-step t.  bf16 -> fp16 is exact for |q| in [2^-14, 65504].
@@ -445,19 +531,22 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     // accumulated output is rarely rescaled; probabilities stay <= 2^kLazy.
     // Every wave tracks the same reference (from the workgroup-wide tile max)
     // and its own keys' part of the row sum.
-    float m_p[HT], l_p[HT];
+    // l_p: sum of the probabilities as PV weights them (normalises the
+    // output); l_e: sum of the unrounded probabilities (for lse).
+    float m_p[HT], l_p[HT], l_e[HT];
     f32x4 o[HT][NDT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         m_p[ht] = -INFINITY;
         l_p[ht] = 0.0f;
+        l_e[ht] = 0.0f;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[ht][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     }
     _Float16* const vbase = Vt + col * VST + ch0;
     const f16x8* const qa_lane = &qa_s[0][threadIdx.x];
 
-    auto body = [&](int tile, const TileRaw<D>& cur, TileRaw<D>& nxt) {
+    for (int tile = t_begin; tile < t_end; ++tile) {
         __syncthreads();   // (A) LDS buffers of the previous tile are free
         // Large values (|v| > 8) make the output sensitive to logit rounding:
         // a logit error e moves the output by about e * |v - out|.  A wave whose
@@ -465,7 +554,15 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
         // (hi, lo) pair; the whole tile then sums the slices with TwoSum and
         // uses two-part probabilities in PV.
         const bool my_big = __ballot(cur.big()) != 0ull;
-        nxt.load(topk_row, tile + 1, col, K, n, base, nsw, swa0, codes, scales, swa, ch0, t_end);
+        const int kind = tile_kind(tile, K);
+        if (kind == 0) cur.template unpair<0>();
+        else if (kind == 1) cur.template unpair<1>();
+        else cur.template unpair<2>();
+        // prefetch: raw bytes of the next tile, Top-K entries of the one after
+        if (tile + 1 < t_end) {
+            nxt.load(tile + 1, idx_n, col, grp & 1, K, n, nsw, crow, srow, wrow);
+            if (tile + 2 < t_end) load_idx(tile + 2, idx_n);
+        }
 
         f32x4 acc[4][HT], lo[4][HT];
 #pragma unroll
@@ -475,8 +572,10 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
                 acc[f][ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
                 lo[f][ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
             }
-        if (my_big) s_tile<true, HT, KT, D, VST>(cur, qf, qa_lane, upper, vbase, acc, lo);
-        else s_tile<false, HT, KT, D, VST>(cur, qf, qa_lane, upper, vbase, acc, lo);
+        if (my_big) s_tile<true, 2, HT, KT, D, VST>(cur, qf, qa_lane, upper, vbase, acc, lo);
+        else if (kind == 0) s_tile<false, 0, HT, KT, D, VST>(cur, qf, qa_lane, upper, vbase, acc, lo);
+        else if (kind == 1) s_tile<false, 1, HT, KT, D, VST>(cur, qf, qa_lane, upper, vbase, acc, lo);
+        else s_tile<false, 2, HT, KT, D, VST>(cur, qf, qa_lane, upper, vbase, acc, lo);
 
         // ---- sum the four channel slices: wave w keeps fragment w
 #pragma unroll
@@ -551,7 +650,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
             const float mn = (mt > m_p[ht] + kLazy) ? mt : m_p[ht];
             const bool live = mn != -INFINITY;
             const float ap = live ? exp2f(m_p[ht] - mn) : 1.0f;
-            float ps = 0.0f;
+            float ps = 0.0f, pe = 0.0f;
             f16x4 p4, q4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -563,8 +662,10 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
                 p4[i] = p;
                 q4[i] = (_Float16)(pf - (float)p);
                 ps += precise ? pf : (float)p;   // normalise by what PV actually weights
+                pe += pf;
             }
             l_p[ht] = l_p[ht] * ap + ps;
+            l_e[ht] = l_e[ht] * ap + pe;
             if (wave == 0 && grp == 0) alpha_s[hh] = (m_p[ht] != -INFINITY && mn != m_p[ht]) ? ap : 1.0f;
             m_p[ht] = mn;
             *reinterpret_cast<f16x4*>(&Pt[hh * PST + wave * 16 + 4 * grp]) = p4;
@@ -589,25 +690,22 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
         }
         if (precise) pv_tile<true, HT, NDT, VST, PST>(Pt, Plo, Vt, col, grp, wave * DW, o);
         else pv_tile<false, HT, NDT, VST, PST>(Pt, Plo, Vt, col, grp, wave * DW, o);
-    };
-
-    // Software pipeline: tile t+1's raw bytes load while tile t runs; the two
-    // register sets swap roles every tile.
-    TileRaw<D> ra, rb;
-    ra.load(topk_row, t_begin, col, K, n, base, nsw, swa0, codes, scales, swa, ch0, t_end);
-    for (int tile = t_begin; tile < t_end; tile += 2) {
-        body(tile, ra, rb);
-        if (tile + 1 < t_end) body(tile + 1, rb, ra);
+        cur = nxt;
     }
 
     // Row sums over the four waves' keys; the reference max is the same in
     // every wave.
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        float lt = l_p[ht];
+        float lt = l_p[ht], le = l_e[ht];
         lt += shfl_xor_f(lt, 16);
         lt += shfl_xor_f(lt, 32);
-        if (grp == 0) wl[wave][ht * 16 + col] = lt;
+        le += shfl_xor_f(le, 16);
+        le += shfl_xor_f(le, 32);
+        if (grp == 0) {
+            wl[wave][ht * 16 + col] = lt;
+            wle[wave][ht * 16 + col] = le;
+        }
         if (wave == 0 && grp == 0) mfin[ht * 16 + col] = m_p[ht];
     }
     __syncthreads();
@@ -619,6 +717,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
             const int h = h0 + hh;
             if (h >= H) continue;
             const float L = wl[0][hh] + wl[1][hh] + wl[2][hh] + wl[3][hh];
+            const float Le = wle[0][hh] + wle[1][hh] + wle[2][hh] + wle[3][hh];
             const float M = mfin[hh];
             if (S == 1) {
                 const float inv = L > 0.0f ? 1.0f / L : 0.0f;
@@ -626,23 +725,24 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) op[16 * dt] = o[ht][dt][i] * inv;
                 if (lse && wave == 0 && col == 0)
-                    lse[(int64_t)r * H + h] = L > 0.0f ? M * kLn2 + logf(L) : -INFINITY;
+                    lse[(int64_t)r * H + h] = L > 0.0f ? M * kLn2 + logf(Le) : -INFINITY;
             } else {
                 float* op = part_o + (((int64_t)r * S + s) * H + h) * D + wave * DW + col;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) op[16 * dt] = o[ht][dt][i];
                 if (wave == 0 && col == 0) {
-                    float* ml = part_ml + (((int64_t)r * S + s) * H + h) * 2;
-                    ml[0] = M;
-                    ml[1] = L;
+                    *reinterpret_cast<float4*>(part_ml + (((int64_t)r * S + s) * H + h) * 4) =
+                        make_float4(M, L, Le, 0.0f);
                 }
             }
         }
     }
 }
 
-// Merge of split partials: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
-// One workgroup per (row, head); each thread owns four consecutive channels.
+// Merge of split partials: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),
+// lse from the unrounded sums.  Partial statistics per (row, split, head):
+// (m, l, l_exact, 0).  One workgroup per (row, head); each thread owns four
+// consecutive channels.
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, int32_t H,
                                                       int32_t D, int32_t S, float* __restrict__ out,
@@ -655,18 +755,19 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
     if (threadIdx.x == 0) {
         float M = -INFINITY;
         for (int s = 0; s < S; ++s) {
-            const float* ml = part_ml + (((int64_t)r * S + s) * H + h) * 2;
-            if (ml[1] > 0.0f) M = fmaxf(M, ml[0]);
+            const float4 ml = *reinterpret_cast<const float4*>(part_ml + (((int64_t)r * S + s) * H + h) * 4);
+            if (ml.y > 0.0f) M = fmaxf(M, ml.x);
         }
-        float L = 0.0f;
+        float L = 0.0f, Le = 0.0f;
         for (int s = 0; s < S; ++s) {
-            const float* ml = part_ml + (((int64_t)r * S + s) * H + h) * 2;
-            const float w = ml[1] > 0.0f ? exp2f(ml[0] - M) : 0.0f;
+            const float4 ml = *reinterpret_cast<const float4*>(part_ml + (((int64_t)r * S + s) * H + h) * 4);
+            const float w = ml.y > 0.0f ? exp2f(ml.x - M) : 0.0f;
             wgt[s] = w;
-            L += ml[1] * w;
+            L += ml.y * w;
+            Le += ml.z * w;
         }
         Ls = L;
-        if (lse) lse[rh] = L > 0.0f ? M * kLn2 + logf(L) : -INFINITY;
+        if (lse) lse[rh] = L > 0.0f ? M * kLn2 + logf(Le) : -INFINITY;
     }
     __syncthreads();
     const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
@@ -686,22 +787,32 @@ struct AttnPlan {
     int HT, HG, S, ntiles;
 };
 
-// Heads per workgroup (16 HT) and key splits per row.  All heads of a group
-// share one dequantisation of each key, so HT is as large as the head count
-// allows; a row's tiles are split over workgroups only as far as needed to
-// occupy the compute units, since every split adds a partial output.
+// Heads per workgroup (16 HT) and key splits per row.  A workgroup's cost is
+// dominated by per-tile latency (loads, four barriers) rather than by its
+// MFMA work, so the head count per group only grows (sharing each key's
+// dequantisation among more heads) once the rows alone give every compute
+// unit a workgroup; otherwise rows are spread over head groups and, as far as
+// needed to reach about one workgroup per compute unit, over key splits
+// (each split adds a partial output for the merge kernel).  Measured on
+// MI355X at 64 heads, D = 512, 640 keys per row: 32 rows -> 16 heads x 2
+// splits; 256 rows -> 32 heads, no split; 4 rows -> 16 heads x 8 splits.
 AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
 {
+    constexpr int64_t kTargetGroups = 256;
+    constexpr int kMaxPlanSplits = 8;
     AttnPlan p;
     p.ntiles = (K + W + kTile - 1) / kTile;
     if (p.ntiles < 1) p.ntiles = 1;
-    // 64 heads per group only where the registers allow it (D = 128)
-    p.HT = (H > 32 && D <= 128) ? 4 : (H > 16 ? 2 : 1);
+    const int64_t rows_x_32 = (int64_t)R * ((H + 31) / 32);
+    const int64_t rows_x_64 = (int64_t)R * ((H + 63) / 64);
+    if (D <= 128 && H > 32 && rows_x_64 >= kTargetGroups) p.HT = 4;
+    else if (H > 16 && rows_x_32 >= kTargetGroups) p.HT = 2;
+    else p.HT = 1;
     p.HG = (H + 16 * p.HT - 1) / (16 * p.HT);
     const int64_t base = (int64_t)R * p.HG;
-    int64_t S = base >= 256 ? 1 : (256 + base - 1) / base;
+    int64_t S = base >= kTargetGroups ? 1 : (kTargetGroups + base - 1) / base;
+    if (S > kMaxPlanSplits) S = kMaxPlanSplits;
     if (S > p.ntiles) S = p.ntiles;
-    if (S > kMaxSplits) S = kMaxSplits;
     p.S = (int)S;
     return p;
 }
@@ -724,7 +835,7 @@ extern "C" size_t csa2_sparse_attn_workspace_bytes(int32_t R, int32_t H, int32_t
     if (R <= 0 || H <= 0 || D <= 0 || K < 0 || W < 0) return 0;
     const AttnPlan p = plan_attn(R, H, D, K, W);
     if (p.S <= 1) return 0;
-    return csa2::align_up((size_t)R * p.S * H * D * 4, 256) + csa2::align_up((size_t)R * p.S * H * 2 * 4, 256);
+    return csa2::align_up((size_t)R * p.S * H * D * 4, 256) + csa2::align_up((size_t)R * p.S * H * 4 * 4, 256);
 }
 
 extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,

@@ -228,10 +228,13 @@ def with_cache(wl):
     ("d128_h8_student_outliers_nosplit_rows", [500 + 11 * i for i in range(140)], 128, 8, 64, 32),
     ("d512_h64_k512_w128_split", [9000, 700, 30000], 512, 64, 512, 128),
     ("d512_h64_many_rows_nosplit", [300 + 37 * i for i in range(130)], 512, 64, 512, 128),
+    ("d512_h64_many_rows_student_outliers", [700 + 31 * i for i in range(130)], 512, 64, 512, 128),
     ("d256_h24_k100_w7", [1000, 77, 5000, 2222], 256, 24, 100, 7),
     ("d128_h3_k33_w0", [500, 40], 128, 3, 33, 0),
     ("d128_h40_k200_w16", [3000, 250, 900], 128, 40, 200, 16),
     ("d256_h64_k300_w64", [5000, 301, 64], 256, 64, 300, 64),
+    ("d128_h48_many_rows_64heads_per_group", [150 + 7 * i for i in range(260)], 128, 48, 64, 16),
+    ("d256_h40_many_rows_32heads_per_group", [90 + 5 * i for i in range(300)], 256, 40, 40, 24),
     ("d512_h16_k0_swa_only", [100, 100], 512, 16, 0, 128),
 ])
 def test_sparse_attn_matches_oracle(name, lengths, D, H, K, W):
