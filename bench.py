@@ -11,9 +11,11 @@ replayed; `value` is whole-job decode throughput (query rows per second).
 
 Also reported: the algorithmic HBM bytes moved per step and the achieved
 fraction of the 8 TB/s peak, a per-call breakdown, a cold-cache step time
-(L2 and Infinity Cache flushed before every step), the roofline of the
-dominant call (Full-mode indexing), and the CPU oracle timed on a bounded
-sample of the same workload on this host.
+(L2 and Infinity Cache flushed before every step), the roofline of the call
+that takes most of the step (by measured time x calls per step; sparse
+attention, which every layer runs, on the decode workloads) and of the
+Full-mode index call, and the CPU oracle timed on a bounded sample of the
+same workload on this host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|5|4]
 """
@@ -38,11 +40,17 @@ import workloads  # noqa: E402
 METRIC = "CSA2 decode tokens/s + achieved HBM GB/s (% of peak) at 64K and 1M KV entries"
 HBM_PEAK_GBPS = 8000.0
 
-# HBM traffic of the Full-mode index call measured with rocprofv3 --pmc
-# (FETCH_SIZE and WRITE_SIZE per dispatch, scaled by the same counters on a
-# plain 1 GiB device copy), keyed by the hash of the kernel source it was
-# taken on.  Reported as null whenever index.hip has changed since.
+# HBM traffic per call measured with rocprofv3 --pmc (FETCH_SIZE and
+# WRITE_SIZE per dispatch, scaled by the same counters on a plain 1 GiB device
+# copy), keyed by (workload id, call, hash of the kernel source the counters
+# were taken on).  Reported as null whenever that source has changed since.
 TRAFFIC = {}
+CALL_SOURCE = {"sparse_attn": "attn.hip", "index_full": "index.hip", "index_reindex": "index.hip",
+               "quantize_append": "quantize.hip"}
+CALL_KERNELS = {"sparse_attn": "k_sparse_attn (+ k_attn_combine when key tiles are split)",
+                "index_full": "k_index_score + k_select (Full)",
+                "index_reindex": "k_index_score + k_select (Reindex)",
+                "quantize_append": "k_quantize_append"}
 
 
 def log(msg):
@@ -289,18 +297,29 @@ def main():
     tokens_per_s = R / (ms / 1000.0) if not cfg.prefill_rows else cfg.prefill_rows / (ms / 1000.0)
     step_gbps = alg["total"] / (ms / 1000.0) / 1e9
 
-    breakdown, roofline = {}, None
+    breakdown, roofline, index_roofline, shares = {}, None, None, {}
     if not args.no_breakdown:
         log("bench: per-call timing")
         breakdown = per_call_times(step)
-        us = breakdown["index_full"]
-        achieved = alg["a2"] / (us / 1e6) / 1e9
-        h = source_hash("index.hip")
-        tr = TRAFFIC.get((cfg.cid, h))
-        roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+        modes = list(cfg.layers)
+        calls_per_step = {"quantize_append": 1, "index_full": modes.count("F"),
+                          "index_reindex": modes.count("R"), "sparse_attn": len(modes)}
+        call_bytes = {"quantize_append": alg["a1"], "index_full": alg["a2"],
+                      "index_reindex": alg["a4_per_layer"], "sparse_attn": alg["a5_per_layer"]}
+        shares = {k: breakdown[k] * calls_per_step[k] / 1000.0 / ms for k in breakdown}
+
+        def roof(call):
+            us = breakdown[call]
+            achieved = call_bytes[call] / (us / 1e6) / 1e9
+            tr = TRAFFIC.get((cfg.cid, call, source_hash(CALL_SOURCE[call])))
+            return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                         frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=tr,
-                        kernel="csa2_index_full (k_index_score + k_select)", us_per_launch=round(us, 2),
-                        algorithmic_bytes_per_launch=alg["a2"])
+                        kernel=f"csa2_{call}: {CALL_KERNELS[call]}", us_per_launch=round(us, 2),
+                        launches_per_step=calls_per_step[call], share_of_step=round(shares[call], 3),
+                        algorithmic_bytes_per_launch=int(call_bytes[call]))
+        dominant = max(shares, key=shares.get)
+        roofline = roof(dominant)
+        index_roofline = roof("index_full")
     log("bench: cold-cache steps")
     cold_ms = cold_step_ms(g, min(args.steps, 10))
     extra = {}
@@ -339,6 +358,7 @@ def main():
         "ms_per_step_eager": round(eager_ms, 3),
         "per_call_us": {k: round(v, 2) for k, v in breakdown.items()},
         "roofline": roofline,
+        "roofline_index_full": index_roofline,
         "cpu_baseline": cpu,
     }
     result.update(extra)

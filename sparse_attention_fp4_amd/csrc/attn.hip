@@ -391,6 +391,21 @@ __device__ __forceinline__ void pv_tile(const _Float16* Pt, const _Float16* Plo,
     }
 }
 
+// Workgroups are handed to the 8 XCDs of the chip round-robin by linear id,
+// and each XCD has its own L2.  All G workgroups of a row are placed on one
+// XCD (row r on XCD r % 8, at consecutive slots there), so the head groups and
+// key splits of a row share its key bytes in one L2 and the merge kernel finds
+// the row's partial outputs there.
+constexpr int kXcds = 8;
+__host__ __device__ inline int64_t xcd_grid(int64_t R, int64_t G) { return (R + kXcds - 1) / kXcds * kXcds * G; }
+// workgroup id -> (row, index g < G within the row)
+__device__ __forceinline__ int xcd_slot(unsigned id, int G, int& r)
+{
+    const int xcd = (int)(id % kXcds), slot = (int)(id / kXcds);
+    r = slot / G * kXcds + xcd;
+    return slot % G;
+}
+
 // Kind of a 64-key tile (uniform): 0 all Top-K slots, 1 all SWA rows, 2 both.
 __device__ __forceinline__ int tile_kind(int tile, int K)
 {
@@ -417,8 +432,8 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     const int64_t* __restrict__ seq_start, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ topk, int32_t K,
     const uint8_t* __restrict__ swa, const int64_t* __restrict__ swa_row_start,
-    const int32_t* __restrict__ swa_len, int32_t H, int32_t W, float scale_log2e, int32_t HG, int32_t S,
-    int32_t ntiles, float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    const int32_t* __restrict__ swa_len, int32_t R, int32_t H, int32_t W, float scale_log2e, int32_t HG,
+    int32_t S, int32_t ntiles, float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml)
 {
     constexpr int DW = D / 4;        // channels per wave
@@ -442,7 +457,13 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
 
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int r = blockIdx.x / HG, hg = blockIdx.x % HG, s = blockIdx.y;
+    int r, hg, s;
+    {
+        const int g = xcd_slot(blockIdx.x, HG * S, r);
+        hg = g % HG;
+        s = g / HG;
+    }
+    if (r >= R) return;   // padding of the XCD mapping (whole workgroup, before any barrier)
     const int h0 = hg * NH;
     const int n = row_len[r];
     const int64_t base = seq_start[row_seq[r]];
@@ -744,12 +765,14 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
 // (m, l, l_exact, 0).  One workgroup per (row, head); each thread owns four
 // consecutive channels.
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_o,
-                                                      const float* __restrict__ part_ml, int32_t H,
+                                                      const float* __restrict__ part_ml, int32_t R, int32_t H,
                                                       int32_t D, int32_t S, float* __restrict__ out,
                                                       float* __restrict__ lse)
 {
-    const int rh = blockIdx.x;          // r * H + h
-    const int r = rh / H, h = rh % H;
+    int r;
+    const int h = xcd_slot(blockIdx.x, H, r);
+    if (r >= R) return;
+    const int rh = r * H + h;
     __shared__ float wgt[kMaxSplits];
     __shared__ float Ls;
     if (threadIdx.x == 0) {
@@ -821,10 +844,11 @@ template <int HT, int D>
 void launch_attn(dim3 grid, hipStream_t st, const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
                  const int64_t* seq_start, const int32_t* row_seq, const int32_t* row_len, const int32_t* topk,
                  int32_t K, const uint8_t* swa, const int64_t* swa_row_start, const int32_t* swa_len, int32_t H,
-                 int32_t W, float sl2e, int HG, int S, int ntiles, float* out, float* lse, float* po, float* pml)
+                 int32_t R, int32_t W, float sl2e, int HG, int S, int ntiles, float* out, float* lse, float* po,
+                 float* pml)
 {
     hipLaunchKernelGGL((k_sparse_attn<HT, D>), grid, dim3(256), 0, st, q, codes, scales, seq_start, row_seq,
-                       row_len, topk, K, swa, swa_row_start, swa_len, H, W, sl2e, HG, S, ntiles, out, lse, po,
+                       row_len, topk, K, swa, swa_row_start, swa_len, R, H, W, sl2e, HG, S, ntiles, out, lse, po,
                        pml);
 }
 
@@ -860,7 +884,8 @@ extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* code
     CSA2_REQUIRE(W == 0 || (swa && swa_row_start && swa_len), CSA2_ERR_NULL,
                  "sparse_attn: SWA pointers are NULL with W > 0");
     const AttnPlan p = plan_attn(R, H, D, K, W);
-    CSA2_REQUIRE((int64_t)R * p.HG <= 0x7FFFFFFF, CSA2_ERR_UNSUPPORTED, "sparse_attn: grid too large");
+    CSA2_REQUIRE(xcd_grid(R, (int64_t)p.HG * p.S) <= 0x7FFFFFFF && xcd_grid(R, H) <= 0x7FFFFFFF,
+                 CSA2_ERR_UNSUPPORTED, "sparse_attn: grid too large");
     const size_t need = csa2_sparse_attn_workspace_bytes(R, H, D, K, W);
     CSA2_REQUIRE(need == 0 || (workspace && workspace_bytes >= need && ((uintptr_t)workspace & 255) == 0),
                  CSA2_ERR_WORKSPACE, "sparse_attn: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
@@ -875,17 +900,18 @@ extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* code
     // With W == 0 or K == 0 the kernels never dereference the unused pointers.
     hipStream_t st = csa2::as_stream(stream);
     const float sl2e = softmax_scale * 1.44269504088896340736f;
-    dim3 grid((unsigned)(R * p.HG), (unsigned)p.S);
+    const dim3 grid((unsigned)xcd_grid(R, p.HG * p.S));
 #define CSA2_ATTN(ht, d)                                                                               \
     if (p.HT == ht && D == d) {                                                                         \
         launch_attn<ht, d>(grid, st, q, codes, scales, seq_start, row_seq, row_len, topk_idx, K, swa,   \
-                           swa_row_start, swa_len, H, W, sl2e, p.HG, p.S, p.ntiles, out, lse, po, pml); \
+                           swa_row_start, swa_len, H, R, W, sl2e, p.HG, p.S, p.ntiles, out, lse, po, pml); \
     }
     CSA2_ATTN(1, 128) CSA2_ATTN(1, 256) CSA2_ATTN(1, 512)
     CSA2_ATTN(2, 128) CSA2_ATTN(2, 256) CSA2_ATTN(2, 512)
     CSA2_ATTN(4, 128)
 #undef CSA2_ATTN
     if (p.S > 1)
-        hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)(R * H)), dim3(128), 0, st, po, pml, H, D, p.S, out, lse);
+        hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)xcd_grid(R, H)), dim3(128), 0, st, po, pml, R, H, D, p.S,
+                           out, lse);
     return csa2::check_launch("sparse_attn");
 }
