@@ -44,7 +44,12 @@ HBM_PEAK_GBPS = 8000.0
 # WRITE_SIZE per dispatch, scaled by the same counters on a plain 1 GiB device
 # copy), keyed by (workload id, call, hash of the kernel source the counters
 # were taken on).  Reported as null whenever that source has changed since.
-TRAFFIC = {}
+TRAFFIC = {
+    # profiles/sparse_attn_decode_64k.md: k_sparse_attn + k_attn_combine per call
+    (2, "sparse_attn", "cb3b5b84310a4749"): 32055878,
+    # profiles/index_full_decode_64k.md: k_index_score (Full) + k_select (Full) per call
+    (2, "index_full", "ebafcfd255f8f1e5"): 288803402,
+}
 CALL_SOURCE = {"sparse_attn": "attn.hip", "index_full": "index.hip", "index_reindex": "index.hip",
                "quantize_append": "quantize.hip"}
 CALL_KERNELS = {"sparse_attn": "k_sparse_attn (+ k_attn_combine when key tiles are split)",
@@ -187,7 +192,7 @@ def copy_check():
     return dict(bytes_read=n * 4, bytes_written=n * 4, ms=ms, gbps=2 * n * 4 / ms / 1e6)
 
 
-def cpu_baseline(cfg, wl, budget_s=12.0):
+def cpu_baseline(cfg, wl, budget_s=15.0):
     """The oracle (as it stands) on this host: whole decode steps for a sample of
     query rows, one row at a time, until about budget_s of CPU work is done."""
     import oracle
@@ -198,8 +203,8 @@ def cpu_baseline(cfg, wl, budget_s=12.0):
     rows_done, t_total = 0, 0.0
     rng = np.random.default_rng(cfg.seed)
     order = rng.permutation(wl.R)
-    for r in order:
-        r = int(r)
+    visits = [int(order[k % wl.R]) for k in range(64 * wl.R)]   # rows repeat until the budget is spent
+    for r in visits:
         b = int(wl.row_seq[r].item())
         a = int(wl.seq_start[b].item())
         n = int(wl.row_len[r].item())
@@ -231,7 +236,7 @@ def cpu_baseline(cfg, wl, budget_s=12.0):
         if t_total >= budget_s:
             break
     return dict(value=rows_done / t_total, unit="tokens/s", cores=nthreads, kind="oracle",
-                sample=f"{rows_done} of {wl.R} query rows of the same workload, each a whole step "
+                sample=f"{rows_done} query-row steps over the {wl.R} rows of the same workload, each a whole step "
                        f"(append + Full + {modes.count('R')} Reindex + {len(modes)} attention layers), "
                        f"{t_total:.1f} s of CPU time with {nthreads} OpenMP threads")
 
