@@ -28,7 +28,7 @@
 //   * PV: wave w produces its D/4 output channels for all NH heads; the B
 //     operand (keys x channels) is read with ds_read_b64_tr_b16.
 //   * Rows whose tiles are split across workgroups write unnormalised partial
-//     outputs plus (max, sum); k_attn_combine merges them.
+//     outputs plus (max, sums); k_attn_combine merges them.
 //
 // Exact scores for keys with large values.  The matrix cores sum products
 // with errors of a few units in the last place of the largest addend, and
@@ -50,7 +50,7 @@ namespace {
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kTile = 64;           // keys per tile: 4 fragments of 16
 constexpr float kLazy = 8.0f;       // log2-domain slack before a running max is raised
-constexpr int kMaxSplits = 64;
+constexpr int kMaxPlanSplits = 8;     // key splits per row, at most
 
 template <int NB>
 __device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src)
@@ -762,8 +762,8 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
 
 // Merge of split partials: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),
 // lse from the unrounded sums.  Partial statistics per (row, split, head):
-// (m, l, l_exact, 0).  One workgroup per (row, head); each thread owns four
-// consecutive channels.
+// (m, l, l_exact, 0).  One workgroup per (row, head), placed on the row's XCD;
+// each thread owns four consecutive channels and requests all splits at once.
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, int32_t R, int32_t H,
                                                       int32_t D, int32_t S, float* __restrict__ out,
@@ -772,37 +772,36 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
     int r;
     const int h = xcd_slot(blockIdx.x, H, r);
     if (r >= R) return;
-    const int rh = r * H + h;
-    __shared__ float wgt[kMaxSplits];
-    __shared__ float Ls;
-    if (threadIdx.x == 0) {
-        float M = -INFINITY;
-        for (int s = 0; s < S; ++s) {
-            const float4 ml = *reinterpret_cast<const float4*>(part_ml + (((int64_t)r * S + s) * H + h) * 4);
-            if (ml.y > 0.0f) M = fmaxf(M, ml.x);
-        }
-        float L = 0.0f, Le = 0.0f;
-        for (int s = 0; s < S; ++s) {
-            const float4 ml = *reinterpret_cast<const float4*>(part_ml + (((int64_t)r * S + s) * H + h) * 4);
-            const float w = ml.y > 0.0f ? exp2f(ml.x - M) : 0.0f;
-            wgt[s] = w;
-            L += ml.y * w;
-            Le += ml.z * w;
-        }
-        Ls = L;
-        if (lse) lse[rh] = L > 0.0f ? M * kLn2 + logf(Le) : -INFINITY;
+    const int64_t rh = (int64_t)r * H + h;
+    float4 st[kMaxPlanSplits];
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMaxPlanSplits; ++k) {
+        st[k] = k < S ? *reinterpret_cast<const float4*>(part_ml + (((int64_t)r * S + k) * H + h) * 4)
+                      : make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
+        if (st[k].y > 0.0f) M = fmaxf(M, st[k].x);
     }
-    __syncthreads();
-    const float inv = Ls > 0.0f ? 1.0f / Ls : 0.0f;
+    float L = 0.0f, Le = 0.0f, w[kMaxPlanSplits];
+#pragma unroll
+    for (int k = 0; k < kMaxPlanSplits; ++k) {
+        w[k] = st[k].y > 0.0f ? exp2f(st[k].x - M) : 0.0f;
+        L += st[k].y * w[k];
+        Le += st[k].z * w[k];
+    }
+    if (lse && threadIdx.x == 0) lse[rh] = L > 0.0f ? M * kLn2 + logf(Le) : -INFINITY;
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     for (int d = 4 * threadIdx.x; d < D; d += 4 * blockDim.x) {
+        float4 v[kMaxPlanSplits];
+#pragma unroll
+        for (int k = 0; k < kMaxPlanSplits; ++k)
+            v[k] = k < S ? *reinterpret_cast<const float4*>(part_o + (((int64_t)r * S + k) * H + h) * D + d)
+                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        for (int s = 0; s < S; ++s) {
-            const float w = wgt[s];
-            const float4 v = *reinterpret_cast<const float4*>(part_o + (((int64_t)r * S + s) * H + h) * D + d);
-            acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+#pragma unroll
+        for (int k = 0; k < kMaxPlanSplits; ++k) {
+            acc.x += w[k] * v[k].x; acc.y += w[k] * v[k].y; acc.z += w[k] * v[k].z; acc.w += w[k] * v[k].w;
         }
-        *reinterpret_cast<float4*>(out + (int64_t)rh * D + d) =
-            make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        *reinterpret_cast<float4*>(out + rh * D + d) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
     }
 }
 
@@ -822,7 +821,6 @@ struct AttnPlan {
 AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
 {
     constexpr int64_t kTargetGroups = 256;
-    constexpr int kMaxPlanSplits = 8;
     AttnPlan p;
     p.ntiles = (K + W + kTile - 1) / kTile;
     if (p.ntiles < 1) p.ntiles = 1;
@@ -884,8 +882,8 @@ extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* code
     CSA2_REQUIRE(W == 0 || (swa && swa_row_start && swa_len), CSA2_ERR_NULL,
                  "sparse_attn: SWA pointers are NULL with W > 0");
     const AttnPlan p = plan_attn(R, H, D, K, W);
-    CSA2_REQUIRE(xcd_grid(R, (int64_t)p.HG * p.S) <= 0x7FFFFFFF && xcd_grid(R, H) <= 0x7FFFFFFF,
-                 CSA2_ERR_UNSUPPORTED, "sparse_attn: grid too large");
+    CSA2_REQUIRE(xcd_grid(R, (int64_t)p.HG * p.S) <= 0x7FFFFFFF, CSA2_ERR_UNSUPPORTED, "sparse_attn: grid too large");
+    CSA2_REQUIRE(xcd_grid(R, H) <= 0x7FFFFFFF, CSA2_ERR_UNSUPPORTED, "sparse_attn: grid too large");
     const size_t need = csa2_sparse_attn_workspace_bytes(R, H, D, K, W);
     CSA2_REQUIRE(need == 0 || (workspace && workspace_bytes >= need && ((uintptr_t)workspace & 255) == 0),
                  CSA2_ERR_WORKSPACE, "sparse_attn: workspace needs %zu bytes, 256-byte aligned (got %zu)", need,
