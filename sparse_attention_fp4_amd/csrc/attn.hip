@@ -116,6 +116,10 @@ struct TileRaw {
     __device__ __forceinline__ void load(int tile, const int (&idx)[4], int col, int h, int K, int n, int nsw,
                                          const uint8_t* crow, const uint8_t* srow, const uint8_t* wrow)
     {
+        // SWA slots without a row must read as zero bytes (a main slot without
+        // an entry gets a zero scale instead); only tiles that reach past the
+        // Top-K slots can have them.
+        const bool any_swa = (tile + 1) * kTile > K;
 #pragma unroll
         for (int f = 0; f < 4; ++f) {
             const int slot = tile * kTile + 16 * f + col;
@@ -134,8 +138,10 @@ struct TileRaw {
             const uint8_t* ca = crow + (size_t)j * (D / 2) + (KT == 4 ? 12 : (KT == 2 ? 4 : 0)) * h;
             const uint8_t* sa = wrow + (size_t)i * D + (KT == 4 ? 24 : (KT == 2 ? 8 : 0)) * h;
             const uint8_t* a1 = vm ? ca : sa;
+            if (any_swa) {
 #pragma unroll
-            for (int w = 0; w < 2 * KT; ++w) raw[f][w] = 0u;
+                for (int w = 0; w < 2 * KT; ++w) raw[f][w] = 0u;
+            }
             if (vm || vs) {
                 if constexpr (KT == 4) {
                     const uint4 v = *reinterpret_cast<const uint4*>(a1);
@@ -454,6 +460,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     __shared__ float wle[4][NH];
     __shared__ float mfin[NH];
     __shared__ uint32_t wbig[4];
+    __shared__ uint32_t wraise[4];
 
     const int lane = lane_id(), wave = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
@@ -465,19 +472,25 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     }
     if (r >= R) return;   // padding of the XCD mapping (whole workgroup, before any barrier)
     const int h0 = hg * NH;
-    const int n = row_len[r];
-    const int64_t base = seq_start[row_seq[r]];
-    int nsw = W > 0 ? swa_len[r] : 0;
-    nsw = nsw < 0 ? 0 : (nsw > W ? W : nsw);
-    const int64_t swa0 = W > 0 ? swa_row_start[r] : 0;
-    const int t_begin = (int)((int64_t)ntiles * s / S), t_end = (int)((int64_t)ntiles * (s + 1) / S);
-    const int32_t* topk_row = topk + (int64_t)r * K;
     const int ch0 = lane_ch0<D>(wave, grp);     // channel of this lane's k-step 0
     const bool upper = lane >= 32;
-    const uint8_t* const crow = codes + base * (D / 2) + ch0 / 2;
-    const uint8_t* const srow = scales + base * (D / 16) + ch0 / 16;
-    const uint8_t* const wrow = swa + swa0 * D + ch0;   // not dereferenced when W == 0
+    const int t_begin = (int)((int64_t)ntiles * s / S), t_end = (int)((int64_t)ntiles * (s + 1) / S);
+    const int32_t* topk_row = topk + (int64_t)r * K;
 
+    // Loads are issued in dependency order so that waiting for one never waits
+    // for a later chain: the query first, then the row's metadata and the
+    // first two tiles' Top-K entries, then (after the sequence's first row is
+    // known) the first tile's key bytes.  The query is converted while those
+    // are in flight.
+    uint4 qraw[HT][KT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        const int h = h0 + ht * 16 + col;
+#pragma unroll
+        for (int t = 0; t < KT; ++t)
+            qraw[ht][t] = h < H ? *reinterpret_cast<const uint4*>(q + ((int64_t)r * H + h) * D + ch0 + 16 * t)
+                                : make_uint4(0u, 0u, 0u, 0u);
+    }
     // Top-K entries of the lane's 4 slots of a tile.  SWA slots are left as
     // they are (TileRaw::load never reads them); no select on the loaded
     // value, so nothing waits for the load here.
@@ -488,15 +501,20 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
             if (slot < K) idx[f] = topk_row[slot];
         }
     };
-    // The first tile's bytes are requested before the query set-up below.
+    int idx0[4] = {0, 0, 0, 0}, idx_n[4] = {0, 0, 0, 0};
+    const int n = row_len[r];
+    const int seq = row_seq[r];
+    int nsw = W > 0 ? swa_len[r] : 0;
+    const int64_t swa0 = W > 0 ? swa_row_start[r] : 0;
+    load_idx(t_begin, idx0);
+    if (t_begin + 1 < t_end) load_idx(t_begin + 1, idx_n);
+    nsw = nsw < 0 ? 0 : (nsw > W ? W : nsw);
+    const int64_t base = seq_start[seq];
+    const uint8_t* const crow = codes + base * (D / 2) + ch0 / 2;
+    const uint8_t* const srow = scales + base * (D / 16) + ch0 / 16;
+    const uint8_t* const wrow = swa + swa0 * D + ch0;   // not dereferenced when W == 0
     TileRaw<D> cur, nxt;   // cur is unpaired in place at the start of its tile
-    int idx_n[4] = {0, 0, 0, 0};
-    {
-        int idx0[4] = {0, 0, 0, 0};
-        load_idx(t_begin, idx0);
-        cur.load(t_begin, idx0, col, grp & 1, K, n, nsw, crow, srow, wrow);
-        if (t_begin + 1 < t_end) load_idx(t_begin + 1, idx_n);
-    }
+    cur.load(t_begin, idx0, col, grp & 1, K, n, nsw, crow, srow, wrow);
 
     // Query heads (B operand): lane (head col, grp) holds channels ch0 + 16 t
     // .. +8 for k-step t.  bf16 -> fp16 is exact for |q| in [2^-14, 65504].
@@ -504,13 +522,10 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     float q32[HT][KT][8];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        const int h = h0 + ht * 16 + col;
         float m = 0.0f;
 #pragma unroll
         for (int t = 0; t < KT; ++t) {
-            uint4 w = {0u, 0u, 0u, 0u};
-            if (h < H) w = *reinterpret_cast<const uint4*>(q + ((int64_t)r * H + h) * D + ch0 + 16 * t);
-            const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+            const uint32_t ws[4] = {qraw[ht][t].x, qraw[ht][t].y, qraw[ht][t].z, qraw[ht][t].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 q32[ht][t][2 * e] = __uint_as_float(ws[e] << 16);
@@ -659,19 +674,20 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
             mx = fmaxf(mx, shfl_xor_f(mx, 32));
             if (grp == 0) wmax[wave][ht * 16 + col] = mx;
         }
-        __syncthreads();   // (C)
 
         // Probabilities enter PV as fp16, whose rounding (relative 2^-12) moves
         // the output by up to 2^-12 * |v - out|; in a precise tile they are
         // split into fp16 hi + lo parts and PV runs twice (rounding ~2^-23).
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
+        // They are first formed against the current reference m_p, which is
+        // right unless some key of the tile exceeds it by more than kLazy; a
+        // wave that sees such a key flags it, and after the barrier all waves
+        // redo the tile's probabilities against the raised reference (the
+        // first tile of a workgroup, and rarely later ones).
+        auto probs = [&](int ht, float mn, float& ps, float& pe) {
             const int hh = ht * 16 + col;
-            const float mt = fmaxf(fmaxf(wmax[0][hh], wmax[1][hh]), fmaxf(wmax[2][hh], wmax[3][hh]));
-            const float mn = (mt > m_p[ht] + kLazy) ? mt : m_p[ht];
             const bool live = mn != -INFINITY;
-            const float ap = live ? exp2f(m_p[ht] - mn) : 1.0f;
-            float ps = 0.0f, pe = 0.0f;
+            ps = 0.0f;
+            pe = 0.0f;
             f16x4 p4, q4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -685,29 +701,59 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
                 ps += precise ? pf : (float)p;   // normalise by what PV actually weights
                 pe += pf;
             }
-            l_p[ht] = l_p[ht] * ap + ps;
-            l_e[ht] = l_e[ht] * ap + pe;
-            if (wave == 0 && grp == 0) alpha_s[hh] = (m_p[ht] != -INFINITY && mn != m_p[ht]) ? ap : 1.0f;
-            m_p[ht] = mn;
             *reinterpret_cast<f16x4*>(&Pt[hh * PST + wave * 16 + 4 * grp]) = p4;
             if (precise) *reinterpret_cast<f16x4*>(&Plo[hh * PST + wave * 16 + 4 * grp]) = q4;
+        };
+        bool raise = false;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) raise |= x[ht][i] > m_p[ht] + kLazy;
+        const bool wave_raise = __ballot(raise) != 0ull;
+        float ps[HT], pe[HT];
+        if (!wave_raise) {
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) probs(ht, m_p[ht], ps[ht], pe[ht]);
         }
-        __syncthreads();   // (D)
+        if (lane == 0) wraise[wave] = wave_raise ? 1u : 0u;
+        __syncthreads();   // (C) P against the old reference, raise flags
 
-        // O lane layout: channel c0 + 16 dt + col, heads 16 ht + 4 grp + i
-        bool rescale = false;
-        f32x4 al[HT];
+        if ((wraise[0] | wraise[1] | wraise[2] | wraise[3]) != 0u) {
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            al[ht] = *reinterpret_cast<const f32x4*>(&alpha_s[ht * 16 + 4 * grp]);
+            for (int ht = 0; ht < HT; ++ht) {
+                const int hh = ht * 16 + col;
+                const float mt = fmaxf(fmaxf(wmax[0][hh], wmax[1][hh]), fmaxf(wmax[2][hh], wmax[3][hh]));
+                const float mn = (mt > m_p[ht] + kLazy) ? mt : m_p[ht];
+                const float ap = mn != -INFINITY ? exp2f(m_p[ht] - mn) : 1.0f;
+                probs(ht, mn, ps[ht], pe[ht]);
+                l_p[ht] = l_p[ht] * ap + ps[ht];
+                l_e[ht] = l_e[ht] * ap + pe[ht];
+                if (wave == 0 && grp == 0) alpha_s[hh] = (m_p[ht] != -INFINITY && mn != m_p[ht]) ? ap : 1.0f;
+                m_p[ht] = mn;
+            }
+            __syncthreads();   // (D) rewritten P, rescale factors
+
+            // O lane layout: channel c0 + 16 dt + col, heads 16 ht + 4 grp + i
+            bool rescale = false;
+            f32x4 al[HT];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rescale |= al[ht][i] != 1.0f;
-        }
-        if (__ballot(rescale) != 0ull) {
+            for (int ht = 0; ht < HT; ++ht) {
+                al[ht] = *reinterpret_cast<const f32x4*>(&alpha_s[ht * 16 + 4 * grp]);
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht)
+                for (int i = 0; i < 4; ++i) rescale |= al[ht][i] != 1.0f;
+            }
+            if (__ballot(rescale) != 0ull) {
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) o[ht][dt] *= al[ht];
+                for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) o[ht][dt] *= al[ht];
+            }
+        } else {
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                l_p[ht] += ps[ht];
+                l_e[ht] += pe[ht];
+            }
         }
         if (precise) pv_tile<true, HT, NDT, VST, PST>(Pt, Plo, Vt, col, grp, wave * DW, o);
         else pv_tile<false, HT, NDT, VST, PST>(Pt, Plo, Vt, col, grp, wave * DW, o);
