@@ -9,255 +9,226 @@
 // key set under one softmax.
 //
 // Work decomposition.  One workgroup (4 waves) = one query row x NH = 16*HT
-// heads x a contiguous range of 64-key tiles.  Wave w owns the channel slice
-// [w*D/4, (w+1)*D/4) in both products, so every key is dequantised once per
-// workgroup and the query registers hold only a quarter of the channels:
-//   * S^T = K Q^T: each lane dequantises D/16 channels of 4 keys (one per
-//     16-key fragment) straight from the cache to fp16 in registers (E2M1 ->
-//     fp16 by the hardware converter, times the E4M3 scale; the product is
-//     exact in fp16) and feeds them as the A operand of
-//     v_mfma_f32_16x16x32_f16 against the NH query heads (B operand).  The
+// heads x a contiguous range of 16-key fragments.  The waves take the range's
+// fragments in turn and each runs a complete online softmax over its own
+// fragments, so no wave waits for another before the final merge:
+//   * S^T = K Q^T: lane (key col, grp) dequantises D/4 channels of key col
+//     straight from the cache to fp16 in registers (E2M1 -> fp16 by the
+//     hardware converter, times the E4M3 scale; the product is exact in fp16)
+//     and feeds them as the A operand of v_mfma_f32_16x16x32_f16 against the
+//     NH query heads (B operand, all D channels held in registers).  The
 //     contraction order only has to agree between the two operands; it is
 //     chosen so that in every MFMA lanes 0-31 carry the two halves of one
 //     16-channel scale group and lanes 32-63 those of another (see below).
-//     The same fp16 values go once into an LDS tile [64 keys][D].
-//   * The four channel-slice partials of S^T are summed through LDS; wave w
-//     keeps the 16 keys of fragment w.
-//   * Online softmax across tiles (log2 domain, lazily raised reference max);
-//     probabilities go to LDS as fp16.
-//   * PV: wave w produces its D/4 output channels for all NH heads; the B
-//     operand (keys x channels) is read with ds_read_b64_tr_b16.
-//   * Rows whose tiles are split across workgroups write unnormalised partial
-//     outputs plus (max, sums); k_attn_combine merges them.
+//   * The same fp16 values go to the wave's own LDS tile [16 keys][D] and come
+//     back transposed (ds_read_b64_tr_b16) as the B operand of PV.
+//   * The S^T accumulator (lane = head, 4 keys) is already the A operand
+//     layout of v_mfma_f32_16x16x16_f16, so probabilities never leave the
+//     registers.  Online softmax in the log2 domain with a lazily raised
+//     reference max.
+//   * At the end the four waves' (max, sums, O) are merged through LDS; wave w
+//     writes output channels [w*D/4, (w+1)*D/4).  Rows whose fragments are
+//     split across workgroups write unnormalised partial outputs plus (max,
+//     sums); k_attn_combine merges them.
 //
 // Exact scores for keys with large values.  The matrix cores sum products
 // with errors of a few units in the last place of the largest addend, and
 // with |v| in the hundreds a near tie between two keys turns such a score
-// error into an output error far above the tolerance.  Where a wave's keys
-// may hold |v| > 8 it computes S exactly instead: each query head is split as
-// q = a + b, a being q rounded to a multiple of 2^(E-11) with 2^E > max|q| of
-// the head (11 bits, exact in fp16), b the small remainder.  Within one scale
-// group every a*k product is then an integer multiple of one quantum and the
-// 16 products sum to less than 2^24 quanta, so an MFMA restricted to one group
-// (the other lane half masked to zero) returns the group sum exactly; the
-// group sums are accumulated in fp64, and K b^T (small, nonzero only for
-// channels with |q| < max|q|/16) is added from an ordinary MFMA chain.
+// error into an output error far above the tolerance.  Where a fragment's
+// keys may hold |v| > 8 its scores are computed exactly instead: each query
+// head is split as q = a + b, a being q rounded to a multiple of 2^(E-11) with
+// 2^E > max|q| of the head (11 bits, exact in fp16), b the small remainder.
+// Within one scale group every a*k product is then an integer multiple of one
+// quantum and the 16 products sum to less than 2^24 quanta, so an MFMA
+// restricted to one group (the other lane half masked to zero) returns the
+// group sum exactly; the group sums are accumulated in fp64, and K b^T (small,
+// nonzero only for channels with |q| < max|q|/16) is added from an ordinary
+// MFMA chain.
 #include "csa2_device.h"
 #include "csa2_host.h"
 
 namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr int kTile = 64;           // keys per tile: 4 fragments of 16
+constexpr int kFrag = 16;           // keys per fragment (one MFMA row block)
+constexpr int kWaves = 4;           // waves per workgroup
 constexpr float kLazy = 8.0f;       // log2-domain slack before a running max is raised
-constexpr int kMaxPlanSplits = 8;     // key splits per row, at most
+constexpr int kMaxPlanSplits = 8;   // key splits per row, at most
 
-template <int NB>
-__device__ __forceinline__ void load_bytes(uint32_t* dst, const uint8_t* src)
-{
-    if constexpr (NB >= 16) {
-#pragma unroll
-        for (int i = 0; i < NB / 16; ++i) {
-            uint4 v = reinterpret_cast<const uint4*>(src)[i];
-            dst[4 * i] = v.x; dst[4 * i + 1] = v.y; dst[4 * i + 2] = v.z; dst[4 * i + 3] = v.w;
-        }
-    } else if constexpr (NB == 8) {
-        uint2 v = *reinterpret_cast<const uint2*>(src);
-        dst[0] = v.x; dst[1] = v.y;
-    } else if constexpr (NB == 4) {
-        dst[0] = *reinterpret_cast<const uint32_t*>(src);
-    } else if constexpr (NB == 2) {
-        dst[0] = *reinterpret_cast<const uint16_t*>(src);
-    } else {
-        dst[0] = *src;
-    }
-}
-
-// Channel layout of a lane (col, grp) in wave w, with p = grp / 2 and
-// h = grp % 2: k-step t (t < KT = D/128) covers the 8 channels
-//   w*D/4 + 16*(p*KT + t) + 8*h .. + 8,
-// i.e. half h of scale group p*KT + t of the wave's slice.  In each MFMA the
-// lanes with p = 0 thus hold one whole scale group and those with p = 1 another.
+// Channel layout of a lane (col, grp), p = grp / 2, hf = grp % 2: k-step t
+// (t < KS = D/32) covers the 8 channels
+//   D/2*p + 16*t + 8*hf .. +8,
+// i.e. half hf of scale group KS*p + t.  In each MFMA the lanes with p = 0
+// thus hold one whole scale group and those with p = 1 another.
 template <int D>
-__device__ __forceinline__ int lane_ch0(int wave, int grp)
+__device__ __forceinline__ int step_ch(int grp, int t)
 {
-    constexpr int KT = D / 128;
-    return wave * (D / 4) + 16 * ((grp >> 1) * KT) + 8 * (grp & 1);
+    return (D / 2) * (grp >> 1) + 16 * t + 8 * (grp & 1);
 }
 
-// Local unit holding piece t after TileRaw::unpair(): {0, 2, 1, 3} for four
-// pieces, identity otherwise.
+// Local unit holding piece t after FragRaw::unpair(): pieces 0 .. KS/2-1 sit
+// at even units, the rest at odd ones.
 template <int D>
 __device__ __forceinline__ constexpr int kperm(int t)
 {
-    return D / 128 == 4 ? ((t & 1) << 1 | (t >> 1)) : t;
+    constexpr int KS = D / 32;
+    return t < KS / 2 ? 2 * t : 2 * t - KS + 1;
 }
 
-// Raw bytes of one tile held by one lane: for each of the 4 key fragments, the
-// lane's key (16 f + col) restricted to its channels: FP4 codes (one word per
-// k-step) and its KT E4M3 scale bytes of a selected main entry, or FP8 bytes
-// (two words per k-step) of an SWA row.  A slot without a valid key gets a
-// zero scale (main; its code bytes are left as they are, any E2M1 code times
-// zero is zero) or zero bytes (SWA), so it dequantises to zeros.
-template <int D>
-struct TileRaw {
-    static constexpr int KT = D / 128;
-    uint32_t raw[4][2 * KT];
-    uint32_t sc[4];
-    bool valid[4], is_main[4];
+// Zero bytes that slots without a key read instead of the cache, so that every
+// load is unconditional (a predicated load leaves part of its destination
+// registers as they were, and the compiler then copies and waits on them).
+// One SWA lane block at most: D/4 bytes for D <= 512.
+// (Not const: a const device array is placed outside the global address
+// space, and the selected pointers would turn into generic loads.)
+__device__ __attribute__((aligned(64))) uint8_t kZeroRow[128];
 
-    // idx: the Top-K entries of the lane's 4 slots (fetched a tile earlier;
-    // only read for Top-K slots).  crow / srow / wrow: code, scale and SWA
-    // pointers of the row's first entry, already offset to the lane's
-    // channels.  One straight-line path for every kind of slot: each load is
-    // predicated and writes its registers in place, so the loads stay in
-    // flight until the bytes are used a tile later.  FP4 piece t lands in word
-    // 2t, FP8 piece t in words 2t and 2t+1.
-    __device__ __forceinline__ void load(int tile, const int (&idx)[4], int col, int h, int K, int n, int nsw,
-                                         const uint8_t* crow, const uint8_t* srow, const uint8_t* wrow)
+// Raw bytes of one fragment held by one lane: the lane's channels of its key
+// (col): FP4 codes (one word per k-step) and the KS E4M3 scale bytes of a
+// selected main entry, or FP8 bytes (two words per k-step) of an SWA row.  A
+// slot without a valid key reads zero bytes, so it dequantises to zeros.
+template <int D>
+struct FragRaw {
+    static constexpr int KS = D / 32;
+    static constexpr int NSC = KS / 4;
+    uint32_t raw[2 * KS];
+    uint32_t sc[NSC];
+    f16x2 sp[KS / 2];   // scales of pieces 2u, 2u+1 as fp16 (set by unpair())
+    bool valid, is_main;
+
+    // j: the slot's Top-K entry (only read for Top-K slots); crow / srow /
+    // wrow: code, scale and SWA pointers of the row's first entry, already
+    // offset to the lane's pair block.  The lane pair (p, 0), (p, 1) of a key
+    // needs one contiguous block (codes: D/4 bytes, SWA: D/2 bytes); each lane
+    // loads its half into consecutive words and unpair() exchanges the halves.
+    // The same straight-line loads serve every kind of slot (each address is
+    // chosen per lane), so every register is written by exactly one load and
+    // nothing waits for a load before its bytes are used.
+    __device__ __forceinline__ void load(int slot, int j, int hf, int K, int n, int nsw, const uint8_t* crow,
+                                         const uint8_t* srow, const uint8_t* wrow)
     {
-        // SWA slots without a row must read as zero bytes (a main slot without
-        // an entry gets a zero scale instead); only tiles that reach past the
-        // Top-K slots can have them.
-        const bool any_swa = (tile + 1) * kTile > K;
+        const bool m = slot < K;
+        const int i = slot - K;
+        const bool vm = m && j >= 0 && j < n;
+        const bool vs = !m && i < nsw;
+        valid = vm || vs;
+        is_main = m;
+        const uint8_t* ca = crow + (int64_t)(vm ? j : 0) * (D / 2) + (D / 8) * hf;
+        const uint8_t* sa = wrow + (int64_t)(vs ? i : 0) * D + (D / 4) * hf;
+        const uint8_t* a1 = vm ? ca : (vs ? sa : kZeroRow);
+        const uint8_t* a2 = vs ? sa + D / 8 : kZeroRow;      // second half of an SWA lane's bytes
+        const uint8_t* sp = vm ? srow + (int64_t)j * (D / 16) : kZeroRow;
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            const int slot = tile * kTile + 16 * f + col;
-            const bool m = slot < K;
-            const int j = idx[f], i = slot - K;
-            const bool vm = m && j >= 0 && j < n;
-            const bool vs = !m && i < nsw;
-            valid[f] = vm || vs;
-            is_main[f] = m;
-            sc[f] = 0u;
-            // The lane pair (p, 0), (p, 1) of a key needs one contiguous block
-            // (codes: 4*KT bytes, SWA: 16*KT bytes); each lane loads its half,
-            // into consecutive words, and unpair() exchanges the halves a tile
-            // later.  The first access serves both kinds (its address is chosen
-            // per lane), so no two loads in flight write the same registers.
-            const uint8_t* ca = crow + (size_t)j * (D / 2) + (KT == 4 ? 12 : (KT == 2 ? 4 : 0)) * h;
-            const uint8_t* sa = wrow + (size_t)i * D + (KT == 4 ? 24 : (KT == 2 ? 8 : 0)) * h;
-            const uint8_t* a1 = vm ? ca : sa;
-            if (any_swa) {
+        for (int u = 0; u < KS / 4; ++u) {
+            const uint4 v = reinterpret_cast<const uint4*>(a1)[u];
+            raw[4 * u] = v.x; raw[4 * u + 1] = v.y; raw[4 * u + 2] = v.z; raw[4 * u + 3] = v.w;
+        }
 #pragma unroll
-                for (int w = 0; w < 2 * KT; ++w) raw[f][w] = 0u;
-            }
-            if (vm || vs) {
-                if constexpr (KT == 4) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(a1);
-                    raw[f][0] = v.x; raw[f][1] = v.y; raw[f][2] = v.z; raw[f][3] = v.w;
-                } else if constexpr (KT == 2) {
-                    const uint2 v = *reinterpret_cast<const uint2*>(a1);
-                    raw[f][0] = v.x; raw[f][1] = v.y;
-                } else {
-                    raw[f][0] = *reinterpret_cast<const uint32_t*>(a1);
-                }
-            }
-            if (vs) {                 // the second half of an SWA lane's bytes
-                if constexpr (KT == 4) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(sa + 16);
-                    raw[f][4] = v.x; raw[f][5] = v.y; raw[f][6] = v.z; raw[f][7] = v.w;
-                } else if constexpr (KT == 2) {
-                    const uint2 v = *reinterpret_cast<const uint2*>(sa + 8);
-                    raw[f][2] = v.x; raw[f][3] = v.y;
-                } else {
-                    raw[f][1] = *reinterpret_cast<const uint32_t*>(sa + 4);
-                }
-            }
-            if (vm) load_bytes<KT>(&sc[f], srow + (size_t)j * (D / 16));
+        for (int u = 0; u < KS / 4; ++u) {
+            const uint4 v = reinterpret_cast<const uint4*>(a2)[u];
+            raw[KS + 4 * u] = v.x; raw[KS + 4 * u + 1] = v.y; raw[KS + 4 * u + 2] = v.z; raw[KS + 4 * u + 3] = v.w;
+        }
+        if constexpr (NSC == 4) {
+            const uint4 v = *reinterpret_cast<const uint4*>(sp);
+            sc[0] = v.x; sc[1] = v.y; sc[2] = v.z; sc[3] = v.w;
+        } else if constexpr (NSC == 2) {
+            const uint2 v = *reinterpret_cast<const uint2*>(sp);
+            sc[0] = v.x; sc[1] = v.y;
+        } else {
+            sc[0] = *reinterpret_cast<const uint32_t*>(sp);
         }
     }
 
     // Unit u of a pair's block (a code word, or 8 FP8 bytes) is piece u/2 of
-    // half u%2; after load() lane h holds units 2h, 2h+1 (KT = 2) or 4h .. 4h+3
-    // (KT = 4) in consecutive words.  v_permlane16_swap(x, y) exchanges row 1
-    // of x with row 0 of y (rows are the 16-lane groups: rows 0/1 are the
-    // halves h = 0/1 of p = 0, rows 2/3 those of p = 1).  Swapping local units
-    // (0, 1) and, for KT = 4, (2, 3) leaves the lane's own half of piece t in
-    // local unit kPerm[t]: code word kPerm[t], or FP8 words 2 kPerm[t] and
-    // 2 kPerm[t] + 1.  KIND as for the tile (main, SWA, or both per lane).
+    // half u%2; after load() lane hf holds units KS*hf .. KS*hf + KS-1 in
+    // consecutive words.  v_permlane16_swap(x, y) exchanges row 1 of x with
+    // row 0 of y (rows are the 16-lane groups: rows 0/1 are the halves hf =
+    // 0/1 of p = 0, rows 2/3 those of p = 1).  Swapping local units 2v and
+    // 2v+1 leaves the lane's own half of piece t in local unit kperm(t): code
+    // word kperm(t), or FP8 words 2 kperm(t) and 2 kperm(t) + 1.  KIND: 0
+    // Top-K slots only, 1 SWA rows only, 2 either (chosen per lane).
     template <int KIND>
     __device__ __forceinline__ void unpair()
     {
-        if constexpr (KT >= 2) {
+        // The scales are converted here, before the next fragment's loads are
+        // issued, so that nothing after those loads reads the raw scale words.
+        if (KIND != 1) {
 #pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                uint32_t c[KT], w[2 * KT];
+            for (int u = 0; u < KS / 2; ++u)
+                sp[u] = (u & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[u >> 1], 1.0f, true)
+                                : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[u >> 1], 1.0f, false);
+        }
+        uint32_t c[KS], w[2 * KS];
 #pragma unroll
-                for (int u = 0; u < KT / 2; ++u) {
-                    if (KIND != 1) {      // code words 2u <-> 2u+1
-                        const auto r = __builtin_amdgcn_permlane16_swap(raw[f][2 * u], raw[f][2 * u + 1], false, false);
-                        c[2 * u] = r[0];
-                        c[2 * u + 1] = r[1];
-                    }
-                    if (KIND != 0) {      // FP8 units 2u <-> 2u+1, both words
-                        const auto ra = __builtin_amdgcn_permlane16_swap(raw[f][4 * u], raw[f][4 * u + 2], false, false);
-                        const auto rb = __builtin_amdgcn_permlane16_swap(raw[f][4 * u + 1], raw[f][4 * u + 3], false, false);
-                        w[4 * u] = ra[0];
-                        w[4 * u + 2] = ra[1];
-                        w[4 * u + 1] = rb[0];
-                        w[4 * u + 3] = rb[1];
-                    }
-                }
-                if (KIND == 0) {
-#pragma unroll
-                    for (int k = 0; k < KT; ++k) raw[f][k] = c[k];
-                } else if (KIND == 1) {
-#pragma unroll
-                    for (int k = 0; k < 2 * KT; ++k) raw[f][k] = w[k];
-                } else {
-                    const bool mm = is_main[f];
-#pragma unroll
-                    for (int k = 0; k < 2 * KT; ++k) raw[f][k] = mm ? (k < KT ? c[k] : 0u) : w[k];
-                }
+        for (int v = 0; v < KS / 2; ++v) {
+            if (KIND != 1) {
+                const auto r = __builtin_amdgcn_permlane16_swap(raw[2 * v], raw[2 * v + 1], false, false);
+                c[2 * v] = r[0];
+                c[2 * v + 1] = r[1];
             }
+            if (KIND != 0) {
+                const auto ra = __builtin_amdgcn_permlane16_swap(raw[4 * v], raw[4 * v + 2], false, false);
+                const auto rb = __builtin_amdgcn_permlane16_swap(raw[4 * v + 1], raw[4 * v + 3], false, false);
+                w[4 * v] = ra[0];
+                w[4 * v + 2] = ra[1];
+                w[4 * v + 1] = rb[0];
+                w[4 * v + 3] = rb[1];
+            }
+        }
+        if (KIND == 0) {
+#pragma unroll
+            for (int k = 0; k < KS; ++k) raw[k] = c[k];
+        } else if (KIND == 1) {
+#pragma unroll
+            for (int k = 0; k < 2 * KS; ++k) raw[k] = w[k];
+        } else {
+#pragma unroll
+            for (int k = 0; k < 2 * KS; ++k) raw[k] = is_main ? (k < KS ? c[k] : 0u) : w[k];
         }
     }
 
-    // Whether this lane's keys may hold |v| > 8: an FP4 group holds
+    // Whether this lane's key may hold |v| > 8: an FP4 group holds
     // |v| <= 6 * scale, so a scale byte of 0x3B (1.375) or more; an FP8 byte
     // of magnitude 0x50 (8.0) or more.  Adding 0x45 (resp. 0x30) to a 7-bit
     // magnitude sets bit 7 exactly at that threshold, with no carry between
-    // bytes; the unused high bytes of sc are zero and stay below bit 7.
+    // bytes.
+    template <int KIND>
     __device__ __forceinline__ bool big() const
     {
-        uint32_t bits = 0u;
+        uint32_t bm = 0u, bs = 0u;   // both reductions in full, then one select
+        if (KIND != 1) {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            if (!valid[f]) continue;
-            if (is_main[f]) {
-                bits |= ((sc[f] & 0x7F7F7F7Fu) + 0x45454545u) & 0x80808080u;
-            } else {
-#pragma unroll
-                for (int i = 0; i < 2 * KT; ++i) bits |= ((raw[f][i] & 0x7F7F7F7Fu) + 0x30303030u) & 0x80808080u;
-            }
+            for (int w = 0; w < NSC; ++w) bm |= ((sc[w] & 0x7F7F7F7Fu) + 0x45454545u) & 0x80808080u;
         }
-        return bits != 0u;
+        if (KIND != 0) {
+#pragma unroll
+            for (int w = 0; w < 2 * KS; ++w) bs |= ((raw[w] & 0x7F7F7F7Fu) + 0x30303030u) & 0x80808080u;
+        }
+        const uint32_t bits = KIND == 0 ? bm : (KIND == 1 ? bs : (is_main ? bm : bs));
+        return valid && bits != 0u;
     }
 };
 
-// Dequantise k-step t (8 channels) of fragment f to fp16.
-//   MODE 0: FP4 codes (word kperm(t)) times the group's E4M3 scale
-//           (scale byte t of the lane's KT scale bytes);
+// Dequantise k-step t (8 channels) of the lane's key to fp16.
+//   MODE 0: FP4 codes (word kperm(t)) times the group's E4M3 scale (scale
+//           byte t of the lane's KS scale bytes);
 //   MODE 1: FP8 E4M3 bytes (words 2 kperm(t), +1), unscaled;
 //   MODE 2: either, chosen per lane.
 template <int MODE, int D>
-__device__ __forceinline__ f16x8 dequant_step(const TileRaw<D>& tr, int f, int t)
+__device__ __forceinline__ f16x8 dequant_step(const FragRaw<D>& fr, int t)
 {
     f16x8 a, b;
     if (MODE != 1) {
-        const uint32_t c = tr.raw[f][kperm<D>(t)];
+        const uint32_t c = fr.raw[kperm<D>(t)];
         const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0);
         const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1);
         const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2);
         const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3);
-        const f16x2 sp = (t & 2) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(tr.sc[f], 1.0f, true)
-                                 : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(tr.sc[f], 1.0f, false);
-        const _Float16 s = sp[t & 1];
+        const _Float16 s = fr.sp[t >> 1][t & 1];
         a = (f16x8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]} * s;
     }
     if (MODE != 0) {
-        const uint32_t c0 = tr.raw[f][2 * kperm<D>(t)], c1 = tr.raw[f][2 * kperm<D>(t) + 1];
+        const uint32_t c0 = fr.raw[2 * kperm<D>(t)], c1 = fr.raw[2 * kperm<D>(t) + 1];
         const f16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, false);
         const f16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, true);
         const f16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1, 1.0f, false);
@@ -266,42 +237,49 @@ __device__ __forceinline__ f16x8 dequant_step(const TileRaw<D>& tr, int f, int t
     }
     if (MODE == 0) return a;
     if (MODE == 1) return b;
-    return tr.is_main[f] ? a : b;
+    return fr.is_main ? a : b;
 }
 
-// TwoSum, elementwise: (hi, lo) += b, where hi + b == new hi + its rounding
-// error exactly and the error is added to lo.
-__device__ __forceinline__ void two_sum_into(f32x4& hi, f32x4& lo, f32x4 b)
+// The workgroup's output channels are part c of CS equal parts of D; its V
+// tile holds only those.  k-step t of lane group grp falls in part
+// (D/2 * p + 16 t) / (D/CS), p = grp / 2.
+template <int D, int CS>
+__device__ __forceinline__ bool in_part(int grp, int t, int c)
 {
-    const f32x4 s = hi + b;
-    const f32x4 bb = s - hi;
-    lo += (hi - (s - bb)) + (b - bb);
-    hi = s;
+    return step_ch<D>(grp, t) / (D / CS) == c;
 }
 
-// One fragment of S^T over this lane's channels, fp32 MFMA chain; the
-// dequantised keys also go to the V tile (piece t at channel offset 16 t).
-template <int MODE, int HT, int KT, int D>
-__device__ __forceinline__ void s_frag(const TileRaw<D>& tr, int f, const f16x8 (&qf)[HT][KT], _Float16* vrow,
-                                       f32x4 (&acc)[HT])
+// Store k-step t of the lane's key to the V tile (vrow: the lane's key row of
+// the tile, already offset by -c D/CS) if it belongs to the part.
+template <int D, int CS>
+__device__ __forceinline__ void v_store(_Float16* vrow, int grp, int t, int c, f16x8 kf)
+{
+    if (in_part<D, CS>(grp, t, c)) *reinterpret_cast<f16x8*>(vrow + step_ch<D>(grp, t)) = kf;
+}
+
+// S^T of one fragment, fp32 MFMA chain; the dequantised keys of the
+// workgroup's channel part also go to the wave's V tile.
+template <int MODE, int HT, int D, int CS>
+__device__ __forceinline__ void s_frag(const FragRaw<D>& fr, const f16x8 (&qf)[HT][D / 32], _Float16* vrow, int grp,
+                                       int c, f32x4 (&acc)[HT])
 {
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-        const f16x8 kf = dequant_step<MODE, D>(tr, f, t);
-        *reinterpret_cast<f16x8*>(vrow + 16 * t) = kf;
+    for (int t = 0; t < D / 32; ++t) {
+        const f16x8 kf = dequant_step<MODE, D>(fr, t);
+        v_store<D, CS>(vrow, grp, t, c, kf);
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ht][t], acc[ht], 0, 0, 0);
     }
 }
 
 // The same fragment with S computed exactly as (hi, lo) = K a^T + K b^T
-// (split of q described at the top of the file).  qa: this lane's a-part
-// pieces in LDS, [HT * KT][256 lanes]; upper: lane >= 32.
-template <int MODE, int HT, int KT, int D>
-__device__ __forceinline__ void s_frag_exact(const TileRaw<D>& tr, int f, const f16x8 (&qf)[HT][KT],
-                                             const f16x8* qa, bool upper, _Float16* vrow, f32x4 (&acc)[HT],
-                                             f32x4 (&lo)[HT])
+// (split of q described at the top of the file).  qab: this lane's a- and
+// b-part pieces in LDS, [2][HT * KS][64 lanes]; upper: lane >= 32.
+template <int HT, int D, int CS>
+__device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const f16x8* qab, bool upper, _Float16* vrow,
+                                             int grp, int c, f32x4 (&acc)[HT], f32x4 (&lo)[HT])
 {
+    constexpr int KS = D / 32;
     double ex[HT][4];
     f32x4 sb[HT];
 #pragma unroll
@@ -312,15 +290,15 @@ __device__ __forceinline__ void s_frag_exact(const TileRaw<D>& tr, int f, const 
     }
     const f16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-        const f16x8 kf = dequant_step<MODE, D>(tr, f, t);
-        *reinterpret_cast<f16x8*>(vrow + 16 * t) = kf;
-        const f16x8 k_lo = upper ? zero : kf;     // scale group p*KT + t with p = 0
-        const f16x8 k_hi = upper ? kf : zero;     // and with p = 1
+    for (int t = 0; t < KS; ++t) {
+        const f16x8 kf = dequant_step<2, D>(fr, t);
+        v_store<D, CS>(vrow, grp, t, c, kf);
+        const f16x8 k_lo = upper ? zero : kf;     // scale group t (p = 0)
+        const f16x8 k_hi = upper ? kf : zero;     // and scale group KS + t (p = 1)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-            const f16x8 a = qa[(ht * KT + t) * 256];
-            const f16x8 b = qf[ht][t] - a;        // exact: the low bits of q
+            const f16x8 a = qab[(ht * KS + t) * CSA2_WAVE];
+            const f16x8 b = qab[((HT + ht) * KS + t) * CSA2_WAVE];
             sb[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, b, sb[ht], 0, 0, 0);
             const f32x4 g0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_lo, a, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
             const f32x4 g1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_hi, a, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
@@ -339,61 +317,23 @@ __device__ __forceinline__ void s_frag_exact(const TileRaw<D>& tr, int f, const 
         }
 }
 
-// S^T partials of all 4 fragments over this lane's channels.  vbase: V tile
-// at (key col of fragment 0, this lane's first channel).  KIND as in
-// TileRaw::load; the exact path uses one general dequantisation for all kinds.
-template <bool EXACT, int KIND, int HT, int KT, int D, int VST>
-__device__ __forceinline__ void s_tile(const TileRaw<D>& tr, const f16x8 (&qf)[HT][KT], const f16x8* qa,
-                                       bool upper, _Float16* vbase, f32x4 (&acc)[4][HT], f32x4 (&lo)[4][HT])
+// O[heads x the part's channels] += P V for one fragment.  The B operand is read with
+// ds_read_b64_tr_b16: within each 16-lane group, lane l receives element l%4
+// of the 8-byte rows addressed by lanes 4i + l/4, so addressing row (key
+// 4g + l/4, channels c0 + 4(l%4)) hands lane l the 4 keys 4g + 0..3 of channel
+// c0 + l, the key order of the probability operand.
+template <int HT, int NDT, int VS>
+__device__ __forceinline__ void pv_frag(const f16x4 (&pa)[HT], const _Float16* vt, int col, int grp,
+                                        f32x4 (&o)[HT][NDT])
 {
+    const _Float16* vr = vt + (4 * grp + (col >> 2)) * VS + 4 * (col & 3);
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-        _Float16* vrow = vbase + 16 * f * VST;
-        if (EXACT) s_frag_exact<2, HT, KT, D>(tr, f, qf, qa, upper, vrow, acc[f], lo[f]);
-        else s_frag<KIND, HT, KT, D>(tr, f, qf, vrow, acc[f]);
-    }
-}
-
-// O[heads x this wave's channels] += P V for one 64-key tile.  The B operand
-// is read with ds_read_b64_tr_b16: within each 16-lane group, lane l receives
-// element l%4 of the 8-byte rows addressed by lanes 4i + l/4, so addressing
-// row (key 4g + l/4, channels c0 + 4(l%4)) hands lane l the 4 keys 4g + 0..3
-// of channel c0 + l, matching the probability fragment's key order.
-template <bool SPLIT, int HT, int NDT, int VST, int PST>
-__device__ __forceinline__ void pv_tile(const _Float16* Pt, const _Float16* Plo, const _Float16* V, int col,
-                                        int grp, int c0, f32x4 (&o)[HT][NDT])
-{
+    for (int dt = 0; dt < NDT; ++dt) {
+        const lds_f16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+            (lds_f16x4 __attribute__((address_space(3)))*)(vr + 16 * dt));
+        const f16x4 vb = {(_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        f16x8 pa[HT], pl[HT];
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            const int off = (ht * 16 + col) * PST + 32 * kk + 4 * grp;
-            const f16x4 a0 = *reinterpret_cast<const f16x4*>(&Pt[off]);
-            const f16x4 a1 = *reinterpret_cast<const f16x4*>(&Pt[off + 16]);
-            pa[ht] = (f16x8){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-            if (SPLIT) {
-                const f16x4 b0 = *reinterpret_cast<const f16x4*>(&Plo[off]);
-                const f16x4 b1 = *reinterpret_cast<const f16x4*>(&Plo[off + 16]);
-                pl[ht] = (f16x8){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-            }
-        }
-        const _Float16* v1 = V + (32 * kk + 4 * grp + (col >> 2)) * VST + c0 + 4 * (col & 3);
-        const _Float16* v2 = v1 + 16 * VST;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const lds_f16x4 b1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-                (lds_f16x4 __attribute__((address_space(3)))*)(v1 + 16 * dt));
-            const lds_f16x4 b2 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-                (lds_f16x4 __attribute__((address_space(3)))*)(v2 + 16 * dt));
-            const f16x8 vb8 = {(_Float16)b1[0], (_Float16)b1[1], (_Float16)b1[2], (_Float16)b1[3],
-                               (_Float16)b2[0], (_Float16)b2[1], (_Float16)b2[2], (_Float16)b2[3]};
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[ht], vb8, o[ht][dt], 0, 0, 0);
-                if (SPLIT) o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[ht], vb8, o[ht][dt], 0, 0, 0);
-            }
-        }
+        for (int ht = 0; ht < HT; ++ht) o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa[ht], vb, o[ht][dt], 0, 0, 0);
     }
 }
 
@@ -412,163 +352,170 @@ __device__ __forceinline__ int xcd_slot(unsigned id, int G, int& r)
     return slot % G;
 }
 
-// Kind of a 64-key tile (uniform): 0 all Top-K slots, 1 all SWA rows, 2 both.
-__device__ __forceinline__ int tile_kind(int tile, int K)
+// Kind of a fragment (uniform): 0 all Top-K slots, 1 all SWA rows, 2 both.
+__device__ __forceinline__ int frag_kind(int fr, int K)
 {
-    return (tile + 1) * kTile <= K ? 0 : (tile * kTile >= K ? 1 : 2);
+    return (fr + 1) * kFrag <= K ? 0 : (fr * kFrag >= K ? 1 : 2);
 }
 
-// LDS slot of the partial S^T that wave `src` computed for fragment f != src.
-__device__ __forceinline__ int red_slot(int f, int src) { return f * 3 + (src < f ? src : src - 1); }
+// LDS of one workgroup: the waves' V tiles and the a-parts of the query during
+// the key loop, then the merge buffers.
+template <int HT, int D, int CS>
+struct AttnSmem {
+    static constexpr int KS = D / 32;
+    static constexpr int DP = D / CS;              // channels of the workgroup's part
+    static constexpr int NDT = DP / 16;            // output tiles per head tile
+    static constexpr int VS = DP + 8;              // V row stride in halves (conflict-free rows and transposes)
+    static constexpr int kVBytes = kWaves * kFrag * VS * 2;
+    static constexpr int kQaBytes = 2 * HT * KS * CSA2_WAVE * 16;   // a and b parts
+    static constexpr int kLoop = kVBytes + kQaBytes;
+    // Merge: rounds over RT output tiles at a time (a multiple of the wave
+    // count); per round every wave stores its RT tiles per head tile,
+    // [wave][HT][RT][64] f32x4.
+    static constexpr int RT = NDT < 16 / HT ? NDT : 16 / HT;
+    static_assert(RT % kWaves == 0 && NDT % RT == 0, "merge rounds");
+    static constexpr int kMerge = kWaves * HT * RT * CSA2_WAVE * 16;
+    static constexpr int kBytes = kLoop > kMerge ? kLoop : kMerge;
+};
 
-template <int HT>
-__device__ __forceinline__ void pick_own(const f32x4 (&a)[4][HT], int wave, f32x4 (&dst)[HT])
-{
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const f32x4 x01 = wave == 0 ? a[0][ht] : a[1][ht];
-        const f32x4 x23 = wave == 2 ? a[2][ht] : a[3][ht];
-        dst[ht] = wave < 2 ? x01 : x23;
-    }
-}
-
-template <int HT, int D>
+template <int HT, int D, int CS>
 __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const int64_t* __restrict__ seq_start, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ topk, int32_t K,
     const uint8_t* __restrict__ swa, const int64_t* __restrict__ swa_row_start,
     const int32_t* __restrict__ swa_len, int32_t R, int32_t H, int32_t W, float scale_log2e, int32_t HG,
-    int32_t S, int32_t ntiles, float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    int32_t S, int32_t nfrag, float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml)
 {
-    constexpr int DW = D / 4;        // channels per wave
-    constexpr int KT = D / 128;      // k-steps per fragment
-    constexpr int NDT = DW / 16;     // 16-channel output tiles per wave
-    constexpr int VST = D + 16;      // V tile row stride in halves (bank spread)
-    constexpr int PST = kTile + 8;   // P row stride in halves
+    using SM = AttnSmem<HT, D, CS>;
+    constexpr int KS = SM::KS;
+    constexpr int NDT = SM::NDT;
+    constexpr int VS = SM::VS;
     constexpr int NH = HT * 16;
 
-    __shared__ __attribute__((aligned(16))) _Float16 Vt[kTile * VST];
-    __shared__ __attribute__((aligned(16))) f32x4 red[12][HT][CSA2_WAVE];
-    __shared__ __attribute__((aligned(16))) _Float16 Pt[NH * PST];
-    __shared__ __attribute__((aligned(16))) _Float16 Plo[NH * PST];
-    __shared__ __attribute__((aligned(16))) f16x8 qa_s[HT * KT][256];
-    __shared__ float wmax[4][NH];
-    __shared__ __attribute__((aligned(16))) float alpha_s[NH];
-    __shared__ float wl[4][NH];
-    __shared__ float wle[4][NH];
-    __shared__ float mfin[NH];
-    __shared__ uint32_t wbig[4];
-    __shared__ uint32_t wraise[4];
+    __shared__ __attribute__((aligned(16))) char smem[SM::kBytes];
+    __shared__ float wm[kWaves][NH];
+    __shared__ float wl[kWaves][NH];
+    __shared__ float wle[kWaves][NH];
+    _Float16* const vt = reinterpret_cast<_Float16*>(smem) + (threadIdx.x >> 6) * (kFrag * VS);
+    f16x8* const qa_s = reinterpret_cast<f16x8*>(smem + SM::kVBytes);   // [2][HT * KS][64]: a, b
+    f32x4* const xo = reinterpret_cast<f32x4*>(smem);                    // merge buffers (after the loop)
 
-    const int lane = lane_id(), wave = threadIdx.x >> 6;
-    const int col = lane & 15, grp = lane >> 4;
-    int r, hg, s;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: branches on it are scalar
+    const int col = lane & 15, grp = lane >> 4, hf = grp & 1;
+    int r, hg, c, s;   // row, head group, channel part, key split
     {
-        const int g = xcd_slot(blockIdx.x, HG * S, r);
+        const int g = xcd_slot(blockIdx.x, HG * CS * S, r);
         hg = g % HG;
-        s = g / HG;
+        c = g / HG % CS;
+        s = g / (HG * CS);
     }
     if (r >= R) return;   // padding of the XCD mapping (whole workgroup, before any barrier)
     const int h0 = hg * NH;
-    const int ch0 = lane_ch0<D>(wave, grp);     // channel of this lane's k-step 0
     const bool upper = lane >= 32;
-    const int t_begin = (int)((int64_t)ntiles * s / S), t_end = (int)((int64_t)ntiles * (s + 1) / S);
+    const int f_begin = (int)((int64_t)nfrag * s / S), f_end = (int)((int64_t)nfrag * (s + 1) / S);
     const int32_t* topk_row = topk + (int64_t)r * K;
 
     // Loads are issued in dependency order so that waiting for one never waits
     // for a later chain: the query first, then the row's metadata and the
-    // first two tiles' Top-K entries, then (after the sequence's first row is
-    // known) the first tile's key bytes.  The query is converted while those
-    // are in flight.
-    uint4 qraw[HT][KT];
+    // wave's first two fragments' Top-K entries, then (once the sequence's
+    // first cache row is known) the first fragment's key bytes.  The query is
+    // converted while the sequence's first row is fetched.
+    uint4 qraw[HT][KS];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const int h = h0 + ht * 16 + col;
 #pragma unroll
-        for (int t = 0; t < KT; ++t)
-            qraw[ht][t] = h < H ? *reinterpret_cast<const uint4*>(q + ((int64_t)r * H + h) * D + ch0 + 16 * t)
+        for (int t = 0; t < KS; ++t)
+            qraw[ht][t] = h < H ? *reinterpret_cast<const uint4*>(q + ((int64_t)r * H + h) * D + step_ch<D>(grp, t))
                                 : make_uint4(0u, 0u, 0u, 0u);
     }
-    // Top-K entries of the lane's 4 slots of a tile.  SWA slots are left as
-    // they are (TileRaw::load never reads them); no select on the loaded
-    // value, so nothing waits for the load here.
-    auto load_idx = [&](int tile, int (&idx)[4]) {
-#pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            const int slot = tile * kTile + 16 * f + col;
-            if (slot < K) idx[f] = topk_row[slot];
-        }
+    // Top-K entry of the lane's key in a fragment; SWA slots are left as they
+    // are (FragRaw::load never reads them), and no select on the loaded value
+    // so nothing waits for the load here.
+    auto load_idx = [&](int fr, int& idx) {
+        const int slot = fr * kFrag + col;
+        if (slot < K) idx = topk_row[slot];
     };
-    int idx0[4] = {0, 0, 0, 0}, idx_n[4] = {0, 0, 0, 0};
+    int fr = f_begin + wave;
+    int idx_c = 0, idx_n = 0;
     const int n = row_len[r];
     const int seq = row_seq[r];
     int nsw = W > 0 ? swa_len[r] : 0;
     const int64_t swa0 = W > 0 ? swa_row_start[r] : 0;
-    load_idx(t_begin, idx0);
-    if (t_begin + 1 < t_end) load_idx(t_begin + 1, idx_n);
+    if (fr < f_end) load_idx(fr, idx_c);
+    if (fr + kWaves < f_end) load_idx(fr + kWaves, idx_n);
     nsw = nsw < 0 ? 0 : (nsw > W ? W : nsw);
     const int64_t base = seq_start[seq];
-    const uint8_t* const crow = codes + base * (D / 2) + ch0 / 2;
-    const uint8_t* const srow = scales + base * (D / 16) + ch0 / 16;
-    const uint8_t* const wrow = swa + swa0 * D + ch0;   // not dereferenced when W == 0
-    TileRaw<D> cur, nxt;   // cur is unpaired in place at the start of its tile
-    cur.load(t_begin, idx0, col, grp & 1, K, n, nsw, crow, srow, wrow);
-
-    // Query heads (B operand): lane (head col, grp) holds channels ch0 + 16 t
-    // .. +8 for k-step t.  bf16 -> fp16 is exact for |q| in [2^-14, 65504].
-    f16x8 qf[HT][KT];
-    float q32[HT][KT][8];
+    // Query heads (B operand): lane (head col, grp) holds channels
+    // step_ch(grp, t) .. +8 for k-step t.  bf16 -> fp16 is exact for |q| in
+    // [2^-14, 65504].
+    f16x8 qf[HT][KS];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
+        float q32[KS][8];
         float m = 0.0f;
 #pragma unroll
-        for (int t = 0; t < KT; ++t) {
+        for (int t = 0; t < KS; ++t) {
             const uint32_t ws[4] = {qraw[ht][t].x, qraw[ht][t].y, qraw[ht][t].z, qraw[ht][t].w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                q32[ht][t][2 * e] = __uint_as_float(ws[e] << 16);
-                q32[ht][t][2 * e + 1] = __uint_as_float(ws[e] & 0xFFFF0000u);
+                q32[t][2 * e] = __uint_as_float(ws[e] << 16);
+                q32[t][2 * e + 1] = __uint_as_float(ws[e] & 0xFFFF0000u);
             }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                qf[ht][t][e] = (_Float16)q32[ht][t][e];
-                m = fmaxf(m, fabsf(q32[ht][t][e]));
+                qf[ht][t][e] = (_Float16)q32[t][e];
+                m = fmaxf(m, fabsf(q32[t][e]));
             }
         }
         m = fmaxf(m, shfl_xor_f(m, 16));
         m = fmaxf(m, shfl_xor_f(m, 32));
-        if (grp == 0) wmax[wave][ht * 16 + col] = m;
-    }
-    __syncthreads();
-    // a-part of each head: q rounded to a multiple of 2^(E-11), 2^E > max|q|
-    // (E >= -13 keeps the quantum within fp16's subnormal grid).  Adding and
-    // subtracting 1.5 * 2^(E+12) rounds to that multiple in fp32.
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const int hh = ht * 16 + col;
-        const float m = fmaxf(fmaxf(wmax[0][hh], wmax[1][hh]), fmaxf(wmax[2][hh], wmax[3][hh]));
+        // a-part of the head: q rounded to a multiple of 2^(E-11), 2^E > max|q|
+        // (E >= -13 keeps the quantum within fp16's subnormal grid).  Adding
+        // and subtracting 1.5 * 2^(E+12) rounds to that multiple in fp32.
+        // Every wave holds the same query; wave w stores the pieces
+        // (ht * KS + t) % 4 == w.
         int E = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 0xFF) - 126 : -13;
         E = E < -13 ? -13 : E;
         const float C = __uint_as_float((uint32_t)(E + 12 + 127) << 23 | 0x400000u);
 #pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            f16x8 av;
+        for (int t = 0; t < KS; ++t) {
+            if ((ht * KS + t) % kWaves != wave) continue;
+            f16x8 av, bv;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) av[e] = (_Float16)((q32[ht][t][e] + C) - C);
-            qa_s[ht * KT + t][threadIdx.x] = av;
+            for (int e = 0; e < 8; ++e) {
+                const float a = (q32[t][e] + C) - C;
+                av[e] = (_Float16)a;
+                bv[e] = (_Float16)(q32[t][e] - a);   // exact: the low bits of q
+            }
+            qa_s[(ht * KS + t) * CSA2_WAVE + lane] = av;
+            qa_s[((HT + ht) * KS + t) * CSA2_WAVE + lane] = bv;
         }
+#pragma unroll
+        for (int t = 0; t < KS; ++t) asm volatile("" : "+a"(qf[ht][t]));
     }
-    // (qa_s and wmax are next touched after the first barrier of the tile loop)
+    const int p = grp >> 1;
+    const uint8_t* const crow = codes + base * (D / 2) + (D / 4) * p;
+    const uint8_t* const srow = scales + base * (D / 16) + KS * p;
+    const uint8_t* const wrow = swa + swa0 * D + (D / 2) * p;   // not dereferenced when W == 0
+    auto load_frag = [&](FragRaw<D>& f, int fr_, int idx) {
+        f.load(fr_ * kFrag + col, idx, hf, K, n, nsw, crow, srow, wrow);
+    };
+    FragRaw<D> cur, nxt;   // cur is unpaired in place at the start of its fragment
+    if (fr < f_end) load_frag(cur, fr, idx_c);
 
-    // Online softmax state (log2 domain).  The reference max of a head is
-    // raised only when a tile's max exceeds it by more than kLazy, so the
-    // accumulated output is rarely rescaled; probabilities stay <= 2^kLazy.
-    // Every wave tracks the same reference (from the workgroup-wide tile max)
-    // and its own keys' part of the row sum.
+    __syncthreads();
+
+    // Online softmax state (log2 domain), per head in the S^T layout (lane
+    // col = head).  The reference max of a head is raised only when a
+    // fragment's max exceeds it by more than kLazy, so the accumulated output
+    // is rarely rescaled; probabilities stay <= 2^kLazy.
     // l_p: sum of the probabilities as PV weights them (normalises the
-    // output); l_e: sum of the unrounded probabilities (for lse).
+    // output); l_e: sum of the unrounded probabilities (for lse).  Both are
+    // per-lane partial sums over the lane's keys.
     float m_p[HT], l_p[HT], l_e[HT];
     f32x4 o[HT][NDT];
 #pragma unroll
@@ -579,189 +526,120 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[ht][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     }
-    _Float16* const vbase = Vt + col * VST + ch0;
-    const f16x8* const qa_lane = &qa_s[0][threadIdx.x];
+    _Float16* const vrow = vt + col * VS - c * SM::DP;   // indexed by the key's channel
+    const f16x8* const qa_lane = qa_s + lane;
 
-    for (int tile = t_begin; tile < t_end; ++tile) {
-        __syncthreads();   // (A) LDS buffers of the previous tile are free
+    // Register classes: the query pieces (MFMA B operands) and the output
+    // accumulators stay in the matrix-core registers (AGPRs) for the whole
+    // loop, leaving the VGPRs to the raw bytes and the dequantisation.  The
+    // empty asm statements only name that class for the compiler.
+    for (; fr < f_end; fr += kWaves) {
         // Large values (|v| > 8) make the output sensitive to logit rounding:
-        // a logit error e moves the output by about e * |v - out|.  A wave whose
-        // keys may hold such values computes its score slice exactly as a
-        // (hi, lo) pair; the whole tile then sums the slices with TwoSum and
-        // uses two-part probabilities in PV.
-        const bool my_big = __ballot(cur.big()) != 0ull;
-        const int kind = tile_kind(tile, K);
+        // a logit error e moves the output by about e * |v - out|.  Such a
+        // fragment gets exact scores and two-part probabilities.
+        const int kind = frag_kind(fr, K);
+        const bool precise = __ballot(kind == 0 ? cur.template big<0>() : (kind == 1 ? cur.template big<1>()
+                                                                                     : cur.template big<2>())) != 0ull;
         if (kind == 0) cur.template unpair<0>();
         else if (kind == 1) cur.template unpair<1>();
         else cur.template unpair<2>();
-        // prefetch: raw bytes of the next tile, Top-K entries of the one after
-        if (tile + 1 < t_end) {
-            nxt.load(tile + 1, idx_n, col, grp & 1, K, n, nsw, crow, srow, wrow);
-            if (tile + 2 < t_end) load_idx(tile + 2, idx_n);
+        const uint64_t vb = __ballot(cur.valid);   // bit k: key k of the fragment (lanes 0..15)
+        // prefetch: raw bytes of the wave's next fragment, Top-K entry of the one after
+        {
+            const int f1 = fr + kWaves;
+            if (f1 < f_end) {
+                load_frag(nxt, f1, idx_n);
+                if (f1 + kWaves < f_end) load_idx(f1 + kWaves, idx_n);
+            }
         }
 
-        f32x4 acc[4][HT], lo[4][HT];
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                acc[f][ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-                lo[f][ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-            }
-        if (my_big) s_tile<true, 2, HT, KT, D, VST>(cur, qf, qa_lane, upper, vbase, acc, lo);
-        else if (kind == 0) s_tile<false, 0, HT, KT, D, VST>(cur, qf, qa_lane, upper, vbase, acc, lo);
-        else if (kind == 1) s_tile<false, 1, HT, KT, D, VST>(cur, qf, qa_lane, upper, vbase, acc, lo);
-        else s_tile<false, 2, HT, KT, D, VST>(cur, qf, qa_lane, upper, vbase, acc, lo);
-
-        // ---- sum the four channel slices: wave w keeps fragment w
-#pragma unroll
-        for (int f = 0; f < 4; ++f)
-            if (f != wave)
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht) red[red_slot(f, wave)][ht][lane] = acc[f][ht];
-        if (lane == 0) wbig[wave] = my_big ? 1u : 0u;
-        __syncthreads();   // (B)
-        const bool precise = (wbig[0] | wbig[1] | wbig[2] | wbig[3]) != 0u;
         f32x4 sh[HT], sl[HT];
-        pick_own<HT>(acc, wave, sh);
-        pick_own<HT>(lo, wave, sl);
-        if (precise) {
-#pragma unroll
-            for (int k = 1; k < 4; ++k) {
-                const int src = (wave + k) & 3;
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht) {
-                    two_sum_into(sh[ht], sl[ht], red[red_slot(wave, src)][ht][lane]);
-                }
-            }
-            __syncthreads();   // all high parts read; the buffer takes the low parts
-#pragma unroll
-            for (int f = 0; f < 4; ++f)
-                if (f != wave)
-#pragma unroll
-                    for (int ht = 0; ht < HT; ++ht) red[red_slot(f, wave)][ht][lane] = lo[f][ht];
-            __syncthreads();
-#pragma unroll
-            for (int k = 1; k < 4; ++k) {
-                const int src = (wave + k) & 3;
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht) sl[ht] += red[red_slot(wave, src)][ht][lane];
-            }
-        } else {
-#pragma unroll
-            for (int k = 1; k < 4; ++k) {
-                const int src = (wave + k) & 3;
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht) sh[ht] += red[red_slot(wave, src)][ht][lane];
-            }
-        }
-
-        // S^T lane layout: head h0 + 16 ht + col, keys 16 wave + 4 grp + i
-        const bool v0 = wave == 0 ? cur.valid[0] : cur.valid[1];
-        const bool v1 = wave == 2 ? cur.valid[2] : cur.valid[3];
-        const uint64_t vb = __ballot(wave < 2 ? v0 : v1);
-        float x[HT][4];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
+            sh[ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+            sl[ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+        }
+        if (precise) s_frag_exact<HT, D, CS>(cur, qa_lane, upper, vrow, grp, c, sh, sl);
+        else if (kind == 0) s_frag<0, HT, D, CS>(cur, qf, vrow, grp, c, sh);
+        else if (kind == 1) s_frag<1, HT, D, CS>(cur, qf, vrow, grp, c, sh);
+        else s_frag<2, HT, D, CS>(cur, qf, vrow, grp, c, sh);
+
+        // S^T lane layout: head h0 + 16 ht + col, keys 4 grp + i.
+        // Probabilities enter PV as fp16, whose rounding (relative 2^-12)
+        // moves the output by up to 2^-12 * |v - out|; in a precise fragment
+        // they are split into fp16 hi + lo parts and PV runs twice (rounding
+        // ~2^-23).
+        f16x4 pa[HT], pl[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            float x[4];
             float mx = -INFINITY;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const bool kv = (vb >> (4 * grp + i)) & 1ull;
-                x[ht][i] = kv ? (sh[ht][i] + sl[ht][i]) * scale_log2e : -INFINITY;
-                mx = fmaxf(mx, x[ht][i]);
+                x[i] = kv ? (sh[ht][i] + sl[ht][i]) * scale_log2e : -INFINITY;
+                mx = fmaxf(mx, x[i]);
             }
             mx = fmaxf(mx, shfl_xor_f(mx, 16));
             mx = fmaxf(mx, shfl_xor_f(mx, 32));
-            if (grp == 0) wmax[wave][ht * 16 + col] = mx;
-        }
-
-        // Probabilities enter PV as fp16, whose rounding (relative 2^-12) moves
-        // the output by up to 2^-12 * |v - out|; in a precise tile they are
-        // split into fp16 hi + lo parts and PV runs twice (rounding ~2^-23).
-        // They are first formed against the current reference m_p, which is
-        // right unless some key of the tile exceeds it by more than kLazy; a
-        // wave that sees such a key flags it, and after the barrier all waves
-        // redo the tile's probabilities against the raised reference (the
-        // first tile of a workgroup, and rarely later ones).
-        auto probs = [&](int ht, float mn, float& ps, float& pe) {
-            const int hh = ht * 16 + col;
-            const bool live = mn != -INFINITY;
-            ps = 0.0f;
-            pe = 0.0f;
-            f16x4 p4, q4;
+            // Raise the head's reference when the fragment's max exceeds it by
+            // more than kLazy (a head without any key so far has l = 0 and
+            // o = 0: nothing to rescale).
+            const bool raise = mx > m_p[ht] + kLazy;
+            if (__ballot(raise) != 0ull) {
+                const float al = (raise && m_p[ht] != -INFINITY) ? __builtin_amdgcn_exp2f(m_p[ht] - mx) : 1.0f;
+                l_p[ht] *= al;
+                l_e[ht] *= al;
+                if (raise) m_p[ht] = mx;
+                // O lane layout: channel 16 dt + col, heads 4 grp + i; the
+                // factor of head 4 grp + i sits in lane 4 grp + i.
+                float ai[4];
+                bool rescale = false;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ai[i] = __shfl(al, 4 * grp + i, CSA2_WAVE);
+                    rescale |= ai[i] != 1.0f;
+                }
+                if (__ballot(rescale) != 0ull) {
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        asm volatile("" : "+a"(o[ht][dt]));   // copies out of the AGPRs happen only here
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) o[ht][dt][i] *= ai[i];
+                        asm volatile("" : "+a"(o[ht][dt]));
+                    }
+                }
+            }
+            const float mn = m_p[ht];
+            float ps = 0.0f, pe = 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // the exponent's argument is formed with one rounding at its own
                 // (small) magnitude; the reference itself only has to be consistent
                 const float d = fmaf(sh[ht][i], scale_log2e, -mn) + sl[ht][i] * scale_log2e;
-                const float pf = (live && x[ht][i] != -INFINITY) ? exp2f(d) : 0.0f;
-                const _Float16 p = (_Float16)pf;
-                p4[i] = p;
-                q4[i] = (_Float16)(pf - (float)p);
-                ps += precise ? pf : (float)p;   // normalise by what PV actually weights
+                const float pf = x[i] != -INFINITY ? __builtin_amdgcn_exp2f(d) : 0.0f;
+                const _Float16 ph = (_Float16)pf;
+                pa[ht][i] = ph;
+                pl[ht][i] = (_Float16)(pf - (float)ph);
+                ps += precise ? pf : (float)ph;   // normalise by what PV actually weights
                 pe += pf;
             }
-            *reinterpret_cast<f16x4*>(&Pt[hh * PST + wave * 16 + 4 * grp]) = p4;
-            if (precise) *reinterpret_cast<f16x4*>(&Plo[hh * PST + wave * 16 + 4 * grp]) = q4;
-        };
-        bool raise = false;
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) raise |= x[ht][i] > m_p[ht] + kLazy;
-        const bool wave_raise = __ballot(raise) != 0ull;
-        float ps[HT], pe[HT];
-        if (!wave_raise) {
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) probs(ht, m_p[ht], ps[ht], pe[ht]);
+            l_p[ht] += ps;
+            l_e[ht] += pe;
         }
-        if (lane == 0) wraise[wave] = wave_raise ? 1u : 0u;
-        __syncthreads();   // (C) P against the old reference, raise flags
-
-        if ((wraise[0] | wraise[1] | wraise[2] | wraise[3]) != 0u) {
+        pv_frag<HT, NDT, VS>(pa, vt, col, grp, o);
+        if (precise) pv_frag<HT, NDT, VS>(pl, vt, col, grp, o);
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                const int hh = ht * 16 + col;
-                const float mt = fmaxf(fmaxf(wmax[0][hh], wmax[1][hh]), fmaxf(wmax[2][hh], wmax[3][hh]));
-                const float mn = (mt > m_p[ht] + kLazy) ? mt : m_p[ht];
-                const float ap = mn != -INFINITY ? exp2f(m_p[ht] - mn) : 1.0f;
-                probs(ht, mn, ps[ht], pe[ht]);
-                l_p[ht] = l_p[ht] * ap + ps[ht];
-                l_e[ht] = l_e[ht] * ap + pe[ht];
-                if (wave == 0 && grp == 0) alpha_s[hh] = (m_p[ht] != -INFINITY && mn != m_p[ht]) ? ap : 1.0f;
-                m_p[ht] = mn;
-            }
-            __syncthreads();   // (D) rewritten P, rescale factors
-
-            // O lane layout: channel c0 + 16 dt + col, heads 16 ht + 4 grp + i
-            bool rescale = false;
-            f32x4 al[HT];
+        for (int ht = 0; ht < HT; ++ht) {
 #pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                al[ht] = *reinterpret_cast<const f32x4*>(&alpha_s[ht * 16 + 4 * grp]);
+            for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(o[ht][dt]));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) rescale |= al[ht][i] != 1.0f;
-            }
-            if (__ballot(rescale) != 0ull) {
-#pragma unroll
-                for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) o[ht][dt] *= al[ht];
-            }
-        } else {
-#pragma unroll
-            for (int ht = 0; ht < HT; ++ht) {
-                l_p[ht] += ps[ht];
-                l_e[ht] += pe[ht];
-            }
+            for (int t = 0; t < KS; ++t) asm volatile("" : "+a"(qf[ht][t]));
         }
-        if (precise) pv_tile<true, HT, NDT, VST, PST>(Pt, Plo, Vt, col, grp, wave * DW, o);
-        else pv_tile<false, HT, NDT, VST, PST>(Pt, Plo, Vt, col, grp, wave * DW, o);
         cur = nxt;
     }
 
-    // Row sums over the four waves' keys; the reference max is the same in
-    // every wave.
+    // ---- merge the four waves.  Per-head statistics first.
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         float lt = l_p[ht], le = l_e[ht];
@@ -770,39 +648,89 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
         le += shfl_xor_f(le, 16);
         le += shfl_xor_f(le, 32);
         if (grp == 0) {
+            wm[wave][ht * 16 + col] = m_p[ht];
             wl[wave][ht * 16 + col] = lt;
             wle[wave][ht * 16 + col] = le;
         }
-        if (wave == 0 && grp == 0) mfin[ht * 16 + col] = m_p[ht];
     }
-    __syncthreads();
+    __syncthreads();   // statistics visible; every wave is done with its V tile and qa
+    // Per head (S^T layout, lane col = head): the merged max M, the sums and
+    // this wave's weight 2^(m_w - M).  The O layout (lane (col, grp) holds
+    // heads 4 grp + i) takes the weight and 1 / L of head 4 grp + i from lane
+    // 4 grp + i.
+    float own_o[HT][4], inv_o[HT][4];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
+        const int hh = ht * 16 + col;
+        float m4[kWaves], l4[kWaves], e4[kWaves];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hh = ht * 16 + 4 * grp + i;
-            const int h = h0 + hh;
-            if (h >= H) continue;
-            const float L = wl[0][hh] + wl[1][hh] + wl[2][hh] + wl[3][hh];
-            const float Le = wle[0][hh] + wle[1][hh] + wle[2][hh] + wle[3][hh];
-            const float M = mfin[hh];
+        for (int w = 0; w < kWaves; ++w) {
+            m4[w] = wm[w][hh];
+            l4[w] = wl[w][hh];
+            e4[w] = wle[w][hh];
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+            if (l4[w] > 0.0f) M = fmaxf(M, m4[w]);
+        float L = 0.0f, Le = 0.0f, own = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = l4[w] > 0.0f ? exp2f(m4[w] - M) : 0.0f;
+            L += l4[w] * f;
+            Le += e4[w] * f;
+            own = w == wave ? f : own;
+        }
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        const int h = h0 + hh;
+        if (wave == 0 && grp == 0 && c == 0 && h < H) {
             if (S == 1) {
-                const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-                float* op = out + ((int64_t)r * H + h) * D + wave * DW + col;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) op[16 * dt] = o[ht][dt][i] * inv;
-                if (lse && wave == 0 && col == 0)
-                    lse[(int64_t)r * H + h] = L > 0.0f ? M * kLn2 + logf(Le) : -INFINITY;
+                if (lse) lse[(int64_t)r * H + h] = L > 0.0f ? M * kLn2 + logf(Le) : -INFINITY;
             } else {
-                float* op = part_o + (((int64_t)r * S + s) * H + h) * D + wave * DW + col;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) op[16 * dt] = o[ht][dt][i];
-                if (wave == 0 && col == 0) {
-                    *reinterpret_cast<float4*>(part_ml + (((int64_t)r * S + s) * H + h) * 4) =
-                        make_float4(M, L, Le, 0.0f);
-                }
+                *reinterpret_cast<float4*>(part_ml + (((int64_t)r * S + s) * H + h) * 4) = make_float4(M, L, Le, 0.0f);
             }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            own_o[ht][i] = __shfl(own, 4 * grp + i, CSA2_WAVE);
+            inv_o[ht][i] = S == 1 ? __shfl(inv, 4 * grp + i, CSA2_WAVE) : 1.0f;
+        }
+    }
+    // Rounds over RT output tiles at a time: every wave stores its weighted
+    // tiles of the round, then wave w sums the four waves' tiles
+    // [w RT/4, (w+1) RT/4) of it and writes them out (normalised when the row
+    // is not split, else as this split's partial output).
+    constexpr int RT = SM::RT;
+    constexpr int QW = RT / kWaves;
+    float* const dst = (S == 1 ? out + ((int64_t)r * H + h0) * D : part_o + (((int64_t)r * S + s) * H + h0) * D) +
+                       c * SM::DP;
+#pragma unroll
+    for (int rd = 0; rd < NDT / RT; ++rd) {
+        if (rd > 0) __syncthreads();   // the previous round's tiles are read
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int k = 0; k < RT; ++k) {
+                f32x4 v = o[ht][rd * RT + k];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] *= own_o[ht][i];
+                xo[((wave * HT + ht) * RT + k) * CSA2_WAVE + lane] = v;
+            }
+        __syncthreads();
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int k = 0; k < QW; ++k) {
+                const int tk = wave * QW + k;   // tile rd * RT + tk of the output
+                f32x4 acc = xo[((0 * HT + ht) * RT + tk) * CSA2_WAVE + lane];
+#pragma unroll
+                for (int w = 1; w < kWaves; ++w) acc += xo[((w * HT + ht) * RT + tk) * CSA2_WAVE + lane];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int hh = ht * 16 + 4 * grp + i;
+                    if (h0 + hh < H) dst[(int64_t)hh * D + 16 * (rd * RT + tk) + col] = acc[i] * inv_o[ht][i];
+                }
+            }
     }
 }
 
@@ -852,47 +780,56 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
 }
 
 struct AttnPlan {
-    int HT, HG, S, ntiles;
+    int HT, HG, CS, S, nfrag;
 };
 
-// Heads per workgroup (16 HT) and key splits per row.  A workgroup's cost is
-// dominated by per-tile latency (loads, four barriers) rather than by its
-// MFMA work, so the head count per group only grows (sharing each key's
-// dequantisation among more heads) once the rows alone give every compute
-// unit a workgroup; otherwise rows are spread over head groups and, as far as
-// needed to reach about one workgroup per compute unit, over key splits
-// (each split adds a partial output for the merge kernel).  Measured on
-// MI355X at 64 heads, D = 512, 640 keys per row: 32 rows -> 16 heads x 2
-// splits; 256 rows -> 32 heads, no split; 4 rows -> 16 heads x 8 splits.
+// Workgroup shape: heads per workgroup (16 HT), channel parts CS and key
+// splits S per row.  A workgroup dequantises and stages each of its keys once
+// and computes full scores, whatever its head count and channel part, so:
+//   * the head count per group is as large as the registers allow (each wave
+//     holds all D query channels and its part of the output of every head:
+//     HT <= 512 / D) while the rows alone give about one workgroup per
+//     compute unit;
+//   * otherwise HT = 1 and a row's keys are split over up to kMaxPlanSplits
+//     workgroups (each split adds a partial output for the merge kernel).
 AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
 {
     constexpr int64_t kTargetGroups = 256;
     AttnPlan p;
-    p.ntiles = (K + W + kTile - 1) / kTile;
-    if (p.ntiles < 1) p.ntiles = 1;
-    const int64_t rows_x_32 = (int64_t)R * ((H + 31) / 32);
-    const int64_t rows_x_64 = (int64_t)R * ((H + 63) / 64);
-    if (D <= 128 && H > 32 && rows_x_64 >= kTargetGroups) p.HT = 4;
-    else if (H > 16 && rows_x_32 >= kTargetGroups) p.HT = 2;
-    else p.HT = 1;
-    p.HG = (H + 16 * p.HT - 1) / (16 * p.HT);
+    p.nfrag = (K + W + kFrag - 1) / kFrag;
+    if (p.nfrag < 1) p.nfrag = 1;
+    const int heads16 = (H + 15) / 16;
+    int ht = 512 / D < heads16 ? 512 / D : heads16;
+    if (ht == 3) ht = 2;
+    p.HT = ht;
+    p.HG = (H + 16 * ht - 1) / (16 * ht);
+    p.CS = 1;
+    if ((int64_t)R * p.HG < kTargetGroups) {
+        p.HT = 1;
+        p.HG = heads16;
+    }
+    const int64_t smax = p.nfrag / kWaves > 1 ? p.nfrag / kWaves : 1;   // at least one fragment per wave
     const int64_t base = (int64_t)R * p.HG;
     int64_t S = base >= kTargetGroups ? 1 : (kTargetGroups + base - 1) / base;
     if (S > kMaxPlanSplits) S = kMaxPlanSplits;
-    if (S > p.ntiles) S = p.ntiles;
+    if (S > smax) S = smax;
+    // Channel parts repeat the whole score computation, which costs more
+    // than the merge of further key splits at every measured shape (4 to 256
+    // rows, 64 heads, D = 512), so they are not planned; the kernels support
+    // them (CS = 2, and 4 for D = 512).
     p.S = (int)S;
     return p;
 }
 
-template <int HT, int D>
+template <int HT, int D, int CS>
 void launch_attn(dim3 grid, hipStream_t st, const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
                  const int64_t* seq_start, const int32_t* row_seq, const int32_t* row_len, const int32_t* topk,
                  int32_t K, const uint8_t* swa, const int64_t* swa_row_start, const int32_t* swa_len, int32_t H,
-                 int32_t R, int32_t W, float sl2e, int HG, int S, int ntiles, float* out, float* lse, float* po,
+                 int32_t R, int32_t W, float sl2e, int HG, int S, int nfrag, float* out, float* lse, float* po,
                  float* pml)
 {
-    hipLaunchKernelGGL((k_sparse_attn<HT, D>), grid, dim3(256), 0, st, q, codes, scales, seq_start, row_seq,
-                       row_len, topk, K, swa, swa_row_start, swa_len, R, H, W, sl2e, HG, S, ntiles, out, lse, po,
+    hipLaunchKernelGGL((k_sparse_attn<HT, D, CS>), grid, dim3(64 * kWaves), 0, st, q, codes, scales, seq_start, row_seq,
+                       row_len, topk, K, swa, swa_row_start, swa_len, R, H, W, sl2e, HG, S, nfrag, out, lse, po,
                        pml);
 }
 
@@ -927,8 +864,11 @@ extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* code
     CSA2_REQUIRE(K == 0 || topk_idx, CSA2_ERR_NULL, "sparse_attn: topk_idx is NULL with K > 0");
     CSA2_REQUIRE(W == 0 || (swa && swa_row_start && swa_len), CSA2_ERR_NULL,
                  "sparse_attn: SWA pointers are NULL with W > 0");
+    CSA2_REQUIRE((((uintptr_t)q | (uintptr_t)codes | (uintptr_t)scales | (uintptr_t)(W > 0 ? swa : nullptr)) & 15) == 0,
+                 CSA2_ERR_UNSUPPORTED, "sparse_attn: q, codes, scales and swa must be 16-byte aligned");
     const AttnPlan p = plan_attn(R, H, D, K, W);
-    CSA2_REQUIRE(xcd_grid(R, (int64_t)p.HG * p.S) <= 0x7FFFFFFF, CSA2_ERR_UNSUPPORTED, "sparse_attn: grid too large");
+    CSA2_REQUIRE(xcd_grid(R, (int64_t)p.HG * p.CS * p.S) <= 0x7FFFFFFF, CSA2_ERR_UNSUPPORTED,
+                 "sparse_attn: grid too large");
     CSA2_REQUIRE(xcd_grid(R, H) <= 0x7FFFFFFF, CSA2_ERR_UNSUPPORTED, "sparse_attn: grid too large");
     const size_t need = csa2_sparse_attn_workspace_bytes(R, H, D, K, W);
     CSA2_REQUIRE(need == 0 || (workspace && workspace_bytes >= need && ((uintptr_t)workspace & 255) == 0),
@@ -944,15 +884,15 @@ extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* code
     // With W == 0 or K == 0 the kernels never dereference the unused pointers.
     hipStream_t st = csa2::as_stream(stream);
     const float sl2e = softmax_scale * 1.44269504088896340736f;
-    const dim3 grid((unsigned)xcd_grid(R, p.HG * p.S));
-#define CSA2_ATTN(ht, d)                                                                               \
-    if (p.HT == ht && D == d) {                                                                         \
-        launch_attn<ht, d>(grid, st, q, codes, scales, seq_start, row_seq, row_len, topk_idx, K, swa,   \
-                           swa_row_start, swa_len, H, R, W, sl2e, p.HG, p.S, p.ntiles, out, lse, po, pml); \
+    const dim3 grid((unsigned)xcd_grid(R, p.HG * p.CS * p.S));
+#define CSA2_ATTN(ht, d, cs)                                                                               \
+    if (p.HT == ht && D == d && p.CS == cs) {                                                               \
+        launch_attn<ht, d, cs>(grid, st, q, codes, scales, seq_start, row_seq, row_len, topk_idx, K, swa,   \
+                               swa_row_start, swa_len, H, R, W, sl2e, p.HG, p.S, p.nfrag, out, lse, po, pml); \
     }
-    CSA2_ATTN(1, 128) CSA2_ATTN(1, 256) CSA2_ATTN(1, 512)
-    CSA2_ATTN(2, 128) CSA2_ATTN(2, 256) CSA2_ATTN(2, 512)
-    CSA2_ATTN(4, 128)
+    CSA2_ATTN(1, 128, 1) CSA2_ATTN(2, 128, 1) CSA2_ATTN(4, 128, 1) CSA2_ATTN(1, 128, 2)
+    CSA2_ATTN(1, 256, 1) CSA2_ATTN(2, 256, 1) CSA2_ATTN(1, 256, 2)
+    CSA2_ATTN(1, 512, 1) CSA2_ATTN(1, 512, 2) CSA2_ATTN(1, 512, 4)
 #undef CSA2_ATTN
     if (p.S > 1)
         hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)xcd_grid(R, H)), dim3(128), 0, st, po, pml, R, H, D, p.S,

@@ -138,7 +138,7 @@ def test_sparse_attn_validation():
     assert f(*attn_args(topk=None)) == 1
     assert f(*attn_args(swa=None)) == 1
     assert f(*attn_args(out=None)) == 1
-    assert f(*attn_args(wsb=0)) == 4
+    assert f(*attn_args(R=2, wsb=0)) == 4   # few rows: split keys need a workspace
     assert f(*attn_args(R=0)) == 0
 
 
@@ -146,8 +146,8 @@ def test_attn_workspace_only_when_split():
     L = csa2.lib()
     # many rows: one workgroup per (row, head group) fills the GPU -> no split, no workspace
     assert L.csa2_sparse_attn_workspace_bytes(4096, 64, 512, 512, 128) == 0
-    # few rows: key tiles split across workgroups -> partial outputs need a workspace
-    assert L.csa2_sparse_attn_workspace_bytes(32, 64, 512, 512, 128) > 0
+    # few rows: keys split across workgroups -> partial outputs need a workspace
+    assert L.csa2_sparse_attn_workspace_bytes(2, 64, 512, 512, 128) > 0
 
 
 def test_python_binding_rejects_host_tensors():
