@@ -75,13 +75,24 @@ __device__ __forceinline__ constexpr int kperm(int t)
     return t < KS / 2 ? 2 * t : 2 * t - KS + 1;
 }
 
-// Zero bytes that slots without a key read instead of the cache, so that every
-// load is unconditional (a predicated load leaves part of its destination
-// registers as they were, and the compiler then copies and waits on them).
-// One SWA lane block at most: D/4 bytes for D <= 512.
-// (Not const: a const device array is placed outside the global address
-// space, and the selected pointers would turn into generic loads.)
-__device__ __attribute__((aligned(64))) uint8_t kZeroRow[128];
+// The cache is read with buffer loads: one descriptor per region (codes,
+// scales, SWA rows of the row) spans exactly the row's valid bytes, and the
+// hardware returns zeros for any dword outside it.  A slot without a key gets
+// the offset kNoKey, beyond every descriptor's range (each is kept below
+// 2^31 bytes), so every load is unconditional and a missing key reads as
+// zero bytes.
+constexpr uint32_t kNoKey = 0x80000000u;
+constexpr int32_t kBufConfig = 0x00020000;   // raw 32-bit buffer, as for gfx9 data loads
+// Descriptor of a buffer whose base and size are the same in every lane; the
+// values are passed through readfirstlane so that the compiler keeps the
+// descriptor in scalar registers.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int32_t bytes)
+{
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b), hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    void* const ub = reinterpret_cast<void*>((uint64_t)hi << 32 | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, __builtin_amdgcn_readfirstlane(bytes), kBufConfig);
+}
 
 // Raw bytes of one fragment held by one lane: the lane's channels of its key
 // (col): FP4 codes (one word per k-step) and the KS E4M3 scale bytes of a
@@ -96,46 +107,46 @@ struct FragRaw {
     f16x2 sp[KS / 2];   // scales of pieces 2u, 2u+1 as fp16 (set by unpair())
     bool valid, is_main;
 
-    // j: the slot's Top-K entry (only read for Top-K slots); crow / srow /
-    // wrow: code, scale and SWA pointers of the row's first entry, already
-    // offset to the lane's pair block.  The lane pair (p, 0), (p, 1) of a key
-    // needs one contiguous block (codes: D/4 bytes, SWA: D/2 bytes); each lane
-    // loads its half into consecutive words and unpair() exchanges the halves.
-    // The same straight-line loads serve every kind of slot (each address is
-    // chosen per lane), so every register is written by exactly one load and
-    // nothing waits for a load before its bytes are used.
-    __device__ __forceinline__ void load(int slot, int j, int hf, int K, int n, int nsw, const uint8_t* crow,
-                                         const uint8_t* srow, const uint8_t* wrow)
+    // kind (uniform): 0 a fragment of Top-K slots, 1 one of SWA rows.  j:
+    // the slot's Top-K entry (read only for Top-K slots); i: the SWA row.
+    // rc / rs / rw: buffers of the row's codes, scales and SWA rows.  The
+    // lane pair (p, 0), (p, 1) of a key needs one contiguous block (codes:
+    // D/4 bytes, SWA: D/2 bytes); each lane loads its half into consecutive
+    // words and unpair() exchanges the halves.  The same straight-line loads
+    // serve both kinds (offsets and descriptors are chosen per fragment), so
+    // every register is written by exactly one load and nothing waits for a
+    // load before its bytes are used.
+    __device__ __forceinline__ void load(int kind, bool vm, int j, bool vs, int i, int p, int hf,
+                                         __amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
+                                         __amdgpu_buffer_rsrc_t rw)
     {
-        const bool m = slot < K;
-        const int i = slot - K;
-        const bool vm = m && j >= 0 && j < n;
-        const bool vs = !m && i < nsw;
         valid = vm || vs;
-        is_main = m;
-        const uint8_t* ca = crow + (int64_t)(vm ? j : 0) * (D / 2) + (D / 8) * hf;
-        const uint8_t* sa = wrow + (int64_t)(vs ? i : 0) * D + (D / 4) * hf;
-        const uint8_t* a1 = vm ? ca : (vs ? sa : kZeroRow);
-        const uint8_t* a2 = vs ? sa + D / 8 : kZeroRow;      // second half of an SWA lane's bytes
-        const uint8_t* sp = vm ? srow + (int64_t)j * (D / 16) : kZeroRow;
+        is_main = kind == 0;
+        // (unsigned arithmetic: the offsets of absent slots are discarded)
+        const uint32_t uj = (uint32_t)j, ui = (uint32_t)i;
+        const uint32_t swa_off = vs ? ui * D + (D / 2) * p + (D / 4) * hf : kNoKey;
+        const uint32_t off1 = kind == 0 ? (vm ? uj * (D / 2) + (D / 4) * p + (D / 8) * hf : kNoKey) : swa_off;
+        const uint32_t off2 = kind == 0 ? kNoKey : swa_off + D / 8;   // second half of an SWA lane's bytes
+        const uint32_t offs = kind == 0 && vm ? uj * (D / 16) + KS * p : kNoKey;
 #pragma unroll
         for (int u = 0; u < KS / 4; ++u) {
-            const uint4 v = reinterpret_cast<const uint4*>(a1)[u];
-            raw[4 * u] = v.x; raw[4 * u + 1] = v.y; raw[4 * u + 2] = v.z; raw[4 * u + 3] = v.w;
+            const u32x4 v = kind == 0 ? __builtin_amdgcn_raw_buffer_load_b128(rc, off1 + 16 * u, 0, 0)
+                                      : __builtin_amdgcn_raw_buffer_load_b128(rw, off1 + 16 * u, 0, 0);
+            raw[4 * u] = v[0]; raw[4 * u + 1] = v[1]; raw[4 * u + 2] = v[2]; raw[4 * u + 3] = v[3];
         }
 #pragma unroll
         for (int u = 0; u < KS / 4; ++u) {
-            const uint4 v = reinterpret_cast<const uint4*>(a2)[u];
-            raw[KS + 4 * u] = v.x; raw[KS + 4 * u + 1] = v.y; raw[KS + 4 * u + 2] = v.z; raw[KS + 4 * u + 3] = v.w;
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, off2 + 16 * u, 0, 0);
+            raw[KS + 4 * u] = v[0]; raw[KS + 4 * u + 1] = v[1]; raw[KS + 4 * u + 2] = v[2]; raw[KS + 4 * u + 3] = v[3];
         }
         if constexpr (NSC == 4) {
-            const uint4 v = *reinterpret_cast<const uint4*>(sp);
-            sc[0] = v.x; sc[1] = v.y; sc[2] = v.z; sc[3] = v.w;
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, offs, 0, 0);
+            sc[0] = v[0]; sc[1] = v[1]; sc[2] = v[2]; sc[3] = v[3];
         } else if constexpr (NSC == 2) {
-            const uint2 v = *reinterpret_cast<const uint2*>(sp);
-            sc[0] = v.x; sc[1] = v.y;
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, offs, 0, 0);
+            sc[0] = v[0]; sc[1] = v[1];
         } else {
-            sc[0] = *reinterpret_cast<const uint32_t*>(sp);
+            sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, offs, 0, 0);
         }
     }
 
@@ -352,11 +363,11 @@ __device__ __forceinline__ int xcd_slot(unsigned id, int G, int& r)
     return slot % G;
 }
 
-// Kind of a fragment (uniform): 0 all Top-K slots, 1 all SWA rows, 2 both.
-__device__ __forceinline__ int frag_kind(int fr, int K)
-{
-    return (fr + 1) * kFrag <= K ? 0 : (fr * kFrag >= K ? 1 : 2);
-}
+// Slot layout of a row: the Top-K slots padded to Kp = a multiple of 16, then
+// the SWA rows, so that a fragment holds one kind of slot only.
+__host__ __device__ inline int pad_topk(int K) { return (K + kFrag - 1) / kFrag * kFrag; }
+// Kind of a fragment (uniform): 0 Top-K slots, 1 SWA rows.
+__device__ __forceinline__ int frag_kind(int fr, int Kp) { return fr * kFrag >= Kp ? 1 : 0; }
 
 // LDS of one workgroup: the waves' V tiles and the a-parts of the query during
 // the key loop, then the merge buffers.
@@ -371,8 +382,8 @@ struct AttnSmem {
     static constexpr int kLoop = kVBytes + kQaBytes;
     // Merge: rounds over RT output tiles at a time (a multiple of the wave
     // count); per round every wave stores its RT tiles per head tile,
-    // [wave][HT][RT][64] f32x4.
-    static constexpr int RT = NDT < 16 / HT ? NDT : 16 / HT;
+    // [wave][HT][RT][64] f32x4.  One round when that fits in 128 KB.
+    static constexpr int RT = HT * NDT <= 32 ? NDT : 32 / HT;
     static_assert(RT % kWaves == 0 && NDT % RT == 0, "merge rounds");
     static constexpr int kMerge = kWaves * HT * RT * CSA2_WAVE * 16;
     static constexpr int kBytes = kLoop > kMerge ? kLoop : kMerge;
@@ -419,21 +430,16 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     const int32_t* topk_row = topk + (int64_t)r * K;
 
     // Loads are issued in dependency order so that waiting for one never waits
-    // for a later chain: the query first, then the row's metadata and the
-    // wave's first two fragments' Top-K entries, then (once the sequence's
-    // first cache row is known) the first fragment's key bytes.  The query is
+    // for a later chain: the row's metadata and the wave's first two
+    // fragments' Top-K entries, the query, then (once the sequence's first
+    // cache row is known) the first fragment's key bytes.  The query is
     // converted while the sequence's first row is fetched.
-    uint4 qraw[HT][KS];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        const int h = h0 + ht * 16 + col;
-#pragma unroll
-        for (int t = 0; t < KS; ++t)
-            qraw[ht][t] = h < H ? *reinterpret_cast<const uint4*>(q + ((int64_t)r * H + h) * D + step_ch<D>(grp, t))
-                                : make_uint4(0u, 0u, 0u, 0u);
-    }
+    const int n = row_len[r];
+    const int seq = row_seq[r];
+    int nsw = W > 0 ? swa_len[r] : 0;
+    const int64_t swa0 = W > 0 ? swa_row_start[r] : 0;
     // Top-K entry of the lane's key in a fragment; SWA slots are left as they
-    // are (FragRaw::load never reads them), and no select on the loaded value
+    // are (the key loads never read them), and no select on the loaded value
     // so nothing waits for the load here.
     auto load_idx = [&](int fr, int& idx) {
         const int slot = fr * kFrag + col;
@@ -441,12 +447,23 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     };
     int fr = f_begin + wave;
     int idx_c = 0, idx_n = 0;
-    const int n = row_len[r];
-    const int seq = row_seq[r];
-    int nsw = W > 0 ? swa_len[r] : 0;
-    const int64_t swa0 = W > 0 ? swa_row_start[r] : 0;
     if (fr < f_end) load_idx(fr, idx_c);
     if (fr + kWaves < f_end) load_idx(fr + kWaves, idx_n);
+    // The row's query through a buffer over its H heads: heads past H read
+    // as zeros, with no branch around the loads.
+    uint4 qraw[HT][KS];
+    {
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + (int64_t)r * H * D, H * D * 2);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const uint32_t hoff = (uint32_t)(h0 + ht * 16 + col) * (D * 2);
+#pragma unroll
+            for (int t = 0; t < KS; ++t) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, hoff + 2 * step_ch<D>(grp, t), 0, 0);
+                qraw[ht][t] = make_uint4(v[0], v[1], v[2], v[3]);
+            }
+        }
+    }
     nsw = nsw < 0 ? 0 : (nsw > W ? W : nsw);
     const int64_t base = seq_start[seq];
     // Query heads (B operand): lane (head col, grp) holds channels
@@ -498,11 +515,19 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
         for (int t = 0; t < KS; ++t) asm volatile("" : "+a"(qf[ht][t]));
     }
     const int p = grp >> 1;
-    const uint8_t* const crow = codes + base * (D / 2) + (D / 4) * p;
-    const uint8_t* const srow = scales + base * (D / 16) + KS * p;
-    const uint8_t* const wrow = swa + swa0 * D + (D / 2) * p;   // not dereferenced when W == 0
-    auto load_frag = [&](FragRaw<D>& f, int fr_, int idx) {
-        f.load(fr_ * kFrag + col, idx, hf, K, n, nsw, crow, srow, wrow);
+    // Buffers over the row's visible entries and SWA rows; 32-bit offsets
+    // reach entries below 2^31 / (D/2) (8M entries at D = 512), later ones
+    // read as absent.
+    const int nb = n < 0 ? 0 : (n > 0x7FFFFFFF / (D / 2) ? 0x7FFFFFFF / (D / 2) : n);
+    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(codes + base * (D / 2), nb * (D / 2));
+    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales + base * (D / 16), nb * (D / 16));
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(W > 0 ? swa + swa0 * D : swa, nsw * D);   // empty when W == 0
+    const int Kp = pad_topk(K);
+    auto load_frag = [&](FragRaw<D>& f, int fr_, int j) {
+        const int slot = fr_ * kFrag + col, i = slot - Kp;
+        const bool vm = slot < K && j >= 0 && j < nb;
+        const bool vs = i >= 0 && i < nsw;
+        f.load(frag_kind(fr_, Kp), vm, j, vs, i, p, hf, rc, rs, rw);
     };
     FragRaw<D> cur, nxt;   // cur is unpaired in place at the start of its fragment
     if (fr < f_end) load_frag(cur, fr, idx_c);
@@ -537,12 +562,10 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
         // Large values (|v| > 8) make the output sensitive to logit rounding:
         // a logit error e moves the output by about e * |v - out|.  Such a
         // fragment gets exact scores and two-part probabilities.
-        const int kind = frag_kind(fr, K);
-        const bool precise = __ballot(kind == 0 ? cur.template big<0>() : (kind == 1 ? cur.template big<1>()
-                                                                                     : cur.template big<2>())) != 0ull;
+        const int kind = frag_kind(fr, Kp);
+        const bool precise = __ballot(kind == 0 ? cur.template big<0>() : cur.template big<1>()) != 0ull;
         if (kind == 0) cur.template unpair<0>();
-        else if (kind == 1) cur.template unpair<1>();
-        else cur.template unpair<2>();
+        else cur.template unpair<1>();
         const uint64_t vb = __ballot(cur.valid);   // bit k: key k of the fragment (lanes 0..15)
         // prefetch: raw bytes of the wave's next fragment, Top-K entry of the one after
         {
@@ -561,8 +584,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
         }
         if (precise) s_frag_exact<HT, D, CS>(cur, qa_lane, upper, vrow, grp, c, sh, sl);
         else if (kind == 0) s_frag<0, HT, D, CS>(cur, qf, vrow, grp, c, sh);
-        else if (kind == 1) s_frag<1, HT, D, CS>(cur, qf, vrow, grp, c, sh);
-        else s_frag<2, HT, D, CS>(cur, qf, vrow, grp, c, sh);
+        else s_frag<1, HT, D, CS>(cur, qf, vrow, grp, c, sh);
 
         // S^T lane layout: head h0 + 16 ht + col, keys 4 grp + i.
         // Probabilities enter PV as fp16, whose rounding (relative 2^-12)
@@ -796,7 +818,7 @@ AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
 {
     constexpr int64_t kTargetGroups = 256;
     AttnPlan p;
-    p.nfrag = (K + W + kFrag - 1) / kFrag;
+    p.nfrag = (pad_topk(K) + W + kFrag - 1) / kFrag;
     if (p.nfrag < 1) p.nfrag = 1;
     const int heads16 = (H + 15) / 16;
     int ht = 512 / D < heads16 ? 512 / D : heads16;
@@ -853,6 +875,7 @@ extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* code
 {
     CSA2_REQUIRE(R >= 0, CSA2_ERR_SHAPE, "sparse_attn: R=%d < 0", R);
     CSA2_REQUIRE(H >= 1, CSA2_ERR_SHAPE, "sparse_attn: H=%d < 1", H);
+    CSA2_REQUIRE(H <= 65536, CSA2_ERR_UNSUPPORTED, "sparse_attn: H=%d > 65536", H);
     CSA2_REQUIRE(D >= 16 && D % 16 == 0, CSA2_ERR_SHAPE, "sparse_attn: D=%d must be a positive multiple of 16", D);
     CSA2_REQUIRE(D == 128 || D == 256 || D == 512, CSA2_ERR_UNSUPPORTED,
                  "sparse_attn: D=%d (supported: 128, 256, 512)", D);
