@@ -46,7 +46,7 @@ HBM_PEAK_GBPS = 8000.0
 # were taken on).  Reported as null whenever that source has changed since.
 TRAFFIC = {
     # profiles/sparse_attn_decode_64k.md: k_sparse_attn + k_attn_combine per call
-    (2, "sparse_attn", "cb3b5b84310a4749"): 32055878,
+    (2, "sparse_attn", "5b72cc670004877c"): 32121861,
     # profiles/index_full_decode_64k.md: k_index_score (Full) + k_select (Full) per call
     (2, "index_full", "ebafcfd255f8f1e5"): 288803402,
 }
