@@ -16,15 +16,17 @@
 //                  inside a lane.  Full mode streams every visible key once
 //                  (coalesced 32-byte lane loads) and writes the fp32 scores
 //                  and the block maxima; Reindex mode gathers the pool's
-//                  1 KiB key blocks and writes one score per pool slot.
-//   k_select       One workgroup per query row: exact radix select (11/11/10
-//                  bit digits over order-preserving keys, histograms in LDS)
-//                  and an ordered compaction, so the outputs come out sorted
-//                  and ties resolve to the lowest index.  Full mode selects the
-//                  top max(P, K) blocks by block max, then the Top-K entries
-//                  inside those blocks only: every Top-K entry lies in one of
-//                  the top-K blocks under this order, so the result equals a
-//                  Top-K over all entries.
+//                  1 KiB key blocks and writes one score per pool slot plus
+//                  each pool block's maximum.
+//   k_select       One workgroup per query row: exact radix select (11-bit
+//                  digits over order-preserving keys, histograms in LDS) and
+//                  an ordered compaction, so the outputs come out sorted and
+//                  ties resolve to the lowest index.  Both modes first reduce
+//                  the candidates to the top-K blocks by block maximum (Full:
+//                  via the pool, which it also outputs), then select the Top-K
+//                  among those blocks' 8K entries: every Top-K entry lies in
+//                  one of them, so the result equals a Top-K over all
+//                  candidates.
 #include "csa2_device.h"
 #include "csa2_host.h"
 
@@ -35,7 +37,6 @@ constexpr int kSelWaves = kSelThreads / CSA2_WAVE;
 constexpr int kMaxK = 2048;
 constexpr int kMaxP = 2048;
 constexpr int kBins = 2048;
-constexpr int kLoadBatch = 16;      // global loads kept in flight per select thread
 constexpr int kFullChunk = 1024;     // entries per Full-score workgroup
 constexpr int kReChunk = 512;        // pool slots per Reindex-score workgroup
 
@@ -134,16 +135,19 @@ __global__ __launch_bounds__(256) void k_index_score(
             part += shfl_xor_f(part, 16);
             part += shfl_xor_f(part, 32);
             const int64_t slot = wbase + (int64_t)(it0 + u) * 16 + col;
+            // maximum over the visible entries of each 8-entry block (-inf if none)
+            float m = ok[u] ? part : -INFINITY;
+            m = fmaxf(m, shfl_xor_f(m, 1));
+            m = fmaxf(m, shfl_xor_f(m, 2));
+            m = fmaxf(m, shfl_xor_f(m, 4));
+            const bool lead = grp == 0 && (col & 7) == 0;
             if (REINDEX) {
                 if (grp == 0 && slot < (int64_t)P * 8) scores[(int64_t)r * ld_scores + slot] = part;
+                if (lead && slot < (int64_t)P * 8) bmax[(int64_t)r * ld_bmax + (slot >> 3)] = m;
             } else {
                 const int64_t j = ent[u];
                 if (grp == 0 && ok[u]) scores[(int64_t)r * ld_scores + j] = part;
-                float m = ok[u] ? part : -INFINITY;
-                m = fmaxf(m, shfl_xor_f(m, 1));
-                m = fmaxf(m, shfl_xor_f(m, 2));
-                m = fmaxf(m, shfl_xor_f(m, 4));
-                if (grp == 0 && (col & 7) == 0 && j < n) bmax[(int64_t)r * ld_bmax + (j >> 3)] = m;
+                if (lead && j < n) bmax[(int64_t)r * ld_bmax + (j >> 3)] = m;
             }
         }
     }
@@ -157,32 +161,55 @@ struct SelState {
     int need;
 };
 
+// Published per-wave values and the digit search result.  The per-wave slots
+// are double-buffered: every publish is followed by a barrier, so a slot set
+// is only rewritten after every wave has passed the barrier that follows the
+// reads of its previous contents.
 struct SelShared {
-    int hist[kBins];
-    int wave_a[kSelWaves];
-    int wave_b[kSelWaves];
-    int digit, above, nvalid;
+    int hist[kBins + kBins / 32 + CSA2_WAVE];   // digit histogram, bin b at b + b/32; then one
+                                                // discard word per lane
+    int wave_x[2][3][kSelWaves];
+    int digit, above, in_bin;
 };
 
-__device__ __forceinline__ uint64_t lanes_below() { const int l = lane_id(); return l ? (~0ull >> (64 - l)) : 0ull; }
+__device__ __forceinline__ int hist_at(int b) { return b + (b >> 5); }
+constexpr int kHistDiscard = kBins + kBins / 32;
 
-// Exclusive block-wide prefix sum of an int in thread order; returns the total.
-__device__ __forceinline__ int block_excl_sum(SelShared& sh, int v, int& excl)
+// Wave-wide inclusive scan with DPP: Hillis-Steele steps inside each row of
+// 16 lanes (row_shr 1, 2, 4, 8), then row 0's total to row 1 and row 2's to
+// row 3 (row_bcast:15), then lane 31's running total to rows 2 and 3
+// (row_bcast:31).  Lanes that receive nothing keep `id`, the identity of op.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x, uint32_t id, Op op)
+{
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xF, 0xF, false));
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xF, 0xF, false));
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xF, 0xF, false));
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xF, 0xF, false));
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xA, 0xF, false));
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xC, 0xF, false));
+    return x;
+}
+__device__ __forceinline__ int wave_incl_sum(int v)
+{
+    return (int)wave_scan((uint32_t)v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t wave_last(uint32_t v) { return (uint32_t)__builtin_amdgcn_readlane((int)v, CSA2_WAVE - 1); }
+
+// Exclusive block-wide prefix sum of an int in thread order; returns the
+// total.  `phase` selects the per-wave slot set and flips on every call.
+__device__ __forceinline__ int block_excl_sum(SelShared& sh, int& phase, int v, int& excl)
 {
     const int lane = lane_id(), wave = threadIdx.x / CSA2_WAVE;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < CSA2_WAVE; off <<= 1) {
-        const int y = __shfl_up(incl, off, CSA2_WAVE);
-        if (lane >= off) incl += y;
-    }
-    __syncthreads();
-    if (lane == CSA2_WAVE - 1) sh.wave_a[wave] = incl;
+    const int incl = wave_incl_sum(v);
+    int* slot = sh.wave_x[phase][0];
+    phase ^= 1;
+    if (lane == CSA2_WAVE - 1) slot[wave] = incl;
     __syncthreads();
     int before = 0, total = 0;
 #pragma unroll
     for (int i = 0; i < kSelWaves; ++i) {
-        const int x = sh.wave_a[i];
+        const int x = slot[i];
         if (i < wave) before += x;
         total += x;
     }
@@ -191,94 +218,180 @@ __device__ __forceinline__ int block_excl_sum(SelShared& sh, int v, int& excl)
 }
 
 // Items are processed in rounds of kRound; within a round thread t holds the
-// kE consecutive items t*kE .. t*kE+kE-1 in registers.  Key 0 marks an
-// invalid item (order_key never maps a finite float to 0).  Keys live in LDS
-// at padded positions (one spare word per 32) so that the 64 lanes reading
-// word t*kE + e of their own run hit 64 different banks.
-constexpr int kE = 32;
+// kE consecutive items t*kE .. t*kE+kE-1 in registers (one 8-entry block of
+// candidates, or eight block maxima: two 16-byte loads).  Key 0 marks an
+// invalid item (order_key never maps a finite float to 0).  The first
+// kRegRounds rounds stay in registers across all passes of a selection;
+// later rounds are read again from their source on every pass.
+constexpr int kE = 8;
 constexpr int kRound = kSelThreads * kE;
-constexpr int kPadded = kRound + kRound / 32;
-__device__ __forceinline__ int padded(int i) { return i + (i >> 5); }
+constexpr int kRegRounds = 4;
+// LDS key arrays: one spare word per 8 so that lane t reading word t*kE + e
+// lands in bank 9t + e (all 64 lanes distinct).
+__device__ __forceinline__ int padded(int i) { return i + (i >> 3); }
+constexpr int padded_size(int n) { return n + n / 8; }
 
-// Where the keys come from: an LDS array holding all of them (cnt <= kRound),
-// or global floats staged into the LDS array one round at a time.
-struct KeySource {
-    uint32_t* lds;
-    const float* gsrc;   // null when the keys are already in lds
+typedef uint32_t RegKeys[kRegRounds][kE];
+
+__device__ __forceinline__ void keys8(const float* p, uint32_t (&key)[kE], int valid)
+{
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    const float v[kE] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < kE; ++e) key[e] = e < valid ? order_key(v[e]) : 0u;
+}
+
+// Key sources.  Each gives rounds() and load(rd, key): the keys of items
+// rd*kRound + threadIdx.x*kE + e.
+
+// Block maxima of one Full row in global memory (item = block id).  The row
+// holds a multiple of 8 floats, so the last thread's 32-byte read stays inside
+// it; entries past `cnt` are masked.
+struct BlockMaxSrc {
+    const float* bm;
     int cnt;
-
     __device__ __forceinline__ int rounds() const { return (cnt + kRound - 1) / kRound; }
-
-    __device__ __forceinline__ void stage(int rd) const
-    {
-        if (!gsrc) return;
-        __syncthreads();
-        const int base = rd * kRound;
-        for (int c0 = 0; c0 < kRound; c0 += kSelThreads * kLoadBatch) {
-            float v[kLoadBatch];
-#pragma unroll
-            for (int u = 0; u < kLoadBatch; ++u) {
-                const int c = base + c0 + u * kSelThreads + threadIdx.x;
-                v[u] = c < cnt ? gsrc[c] : 0.0f;
-            }
-#pragma unroll
-            for (int u = 0; u < kLoadBatch; ++u) {
-                const int li = c0 + u * kSelThreads + threadIdx.x;
-                lds[padded(li)] = base + li < cnt ? order_key(v[u]) : 0u;
-            }
-        }
-        __syncthreads();
-    }
-
     __device__ __forceinline__ void load(int rd, uint32_t (&key)[kE]) const
     {
-        if (rounds() > 1) stage(rd);
-        const int l0 = threadIdx.x * kE;
-        const int i0 = rd * kRound + l0;
+        const int i0 = rd * kRound + (int)threadIdx.x * kE;
+        if (i0 < cnt) keys8(bm + i0, key, cnt - i0);
+        else
 #pragma unroll
-        for (int e = 0; e < kE; ++e) key[e] = (i0 + e < cnt) ? lds[padded(l0 + e)] : 0u;
+            for (int e = 0; e < kE; ++e) key[e] = 0u;
     }
 };
 
-// Finds the threshold of the k largest keys among the valid items 0..cnt-1.
-// The bits shared by every valid key are skipped first (an AND/OR reduction
-// finds the highest bit that differs), then radix passes over 11-bit digits
-// below it (LDS histograms) narrow to the digit holding the k-th largest key,
-// stopping early once a whole digit bin is taken.  get(i) returns the key of
-// item i, or 0 when the item is invalid.
-__device__ __forceinline__ SelState radix_select(SelShared& sh, const KeySource& src, int k)
+// Keys already in an LDS array at padded positions.
+struct LdsKeySrc {
+    const uint32_t* keys;
+    int cnt;
+    __device__ __forceinline__ int rounds() const { return (cnt + kRound - 1) / kRound; }
+    __device__ __forceinline__ void load(int rd, uint32_t (&key)[kE]) const
+    {
+        const int i0 = rd * kRound + (int)threadIdx.x * kE;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) key[e] = i0 + e < cnt ? keys[padded(i0 + e)] : 0u;
+    }
+};
+
+// Pool blocks of one Reindex row (item i = block blocks[i], whose maximum is
+// bm[slots[i]]; block -1 = no block).
+struct PoolBlockSrc {
+    const float* bm;
+    const int* blocks;
+    const int* slots;
+    int cnt;
+    __device__ __forceinline__ int rounds() const { return (cnt + kRound - 1) / kRound; }
+    __device__ __forceinline__ void load(int rd, uint32_t (&key)[kE]) const
+    {
+        const int i0 = rd * kRound + (int)threadIdx.x * kE;
+        float v[kE];
+        bool ok[kE];
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            ok[e] = i0 + e < cnt && blocks[i0 + e] >= 0;
+            v[e] = ok[e] ? bm[slots[i0 + e]] : 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < kE; ++e) key[e] = ok[e] && v[e] != -INFINITY ? order_key(v[e]) : 0u;
+    }
+};
+
+// Candidate entries: item c is position c % 8 of candidate block c / 8, i.e.
+// entry 8*blocks[c/8] + c%8, visible when below n.  Its score is at
+// sc[8*blocks[c/8] + c%8] (Full: scores by entry id) or sc[8*slots[c/8] + c%8]
+// (Reindex: scores by pool slot).  Thread t of round rd reads block
+// rd*kSelThreads + t: two 16-byte loads.
+struct CandSrc {
+    const float* sc;
+    const int* blocks;
+    const int* slots;    // null in Full mode
+    int nblk, n;
+    __device__ __forceinline__ int rounds() const { return (nblk + kSelThreads - 1) / kSelThreads; }
+    __device__ __forceinline__ void load(int rd, uint32_t (&key)[kE]) const
+    {
+        const int ci = rd * kSelThreads + (int)threadIdx.x;
+        if (ci < nblk) {
+            const int b = blocks[ci];
+            const int64_t at = 8 * (int64_t)(slots ? slots[ci] : b);
+            const int64_t vis = (int64_t)n - 8 * (int64_t)b;
+            keys8(sc + at, key, vis < kE ? (int)vis : kE);
+        } else {
+#pragma unroll
+            for (int e = 0; e < kE; ++e) key[e] = 0u;
+        }
+    }
+};
+
+// Calls f(rd, keys) for every round: the register rounds first, then the
+// rest read from the source.  Uniform across the block (f may synchronise).
+template <class Src, class F>
+__device__ __forceinline__ void for_rounds(const Src& src, const RegKeys& reg, F f)
 {
-    constexpr int BPT = kBins / kSelThreads;      // bins per thread in the digit search
-    const int lane = lane_id(), wave = threadIdx.x / CSA2_WAVE;
     const int rounds = src.rounds();
-    uint32_t key[kE];
-    if (rounds == 1) src.load(0, key);
+#pragma unroll
+    for (int rr = 0; rr < kRegRounds; ++rr)
+        if (rr < rounds) f(rr, reg[rr]);
+    for (int rd = kRegRounds; rd < rounds; ++rd) {
+        uint32_t key[kE];
+        src.load(rd, key);
+        f(rd, key);
+    }
+}
+
+template <class Src>
+__device__ __forceinline__ void load_regs(const Src& src, RegKeys& reg)
+{
+    const int rounds = src.rounds();
+#pragma unroll
+    for (int rr = 0; rr < kRegRounds; ++rr) {
+        if (rr < rounds) src.load(rr, reg[rr]);
+        else
+#pragma unroll
+            for (int e = 0; e < kE; ++e) reg[rr][e] = 0u;
+    }
+}
+
+// Finds the threshold of the k largest keys among the valid items.  The bits
+// shared by every valid key are skipped first (an AND/OR reduction finds the
+// highest bit that differs), then radix passes over 11-bit digits below it
+// narrow to the digit holding the k-th largest key, stopping early once a
+// whole digit bin is taken.  A pass is: LDS atomic histogram of the keys that
+// match the prefix so far (the others add into a discard word of their own
+// lane, so the loop has no branches), barrier, then wave 0 alone finds the
+// digit: each lane sums 32 contiguous bins (highest first), a wave scan and a
+// ballot pick the lane whose range holds the k-th key, a second scan over that
+// lane's 32 bins (one per lane) picks the bin; wave 0 also clears the bins for
+// the next pass and publishes the digit, barrier.  The histogram must be zero
+// on entry and is zero again on return.
+template <class Src>
+__device__ __forceinline__ SelState radix_select(SelShared& sh, int& phase, const Src& src, const RegKeys& reg,
+                                                 int k)
+{
+    const int lane = lane_id(), wave = threadIdx.x / CSA2_WAVE;
     // population and common prefix of the valid keys
     uint32_t kand = 0xFFFFFFFFu, kor = 0u;
     int nv = 0;
-    for (int rd = 0; rd < rounds; ++rd) {
-        if (rounds > 1) src.load(rd, key);
+    for_rounds(src, reg, [&](int, const uint32_t (&key)[kE]) {
 #pragma unroll
         for (int e = 0; e < kE; ++e)
             if (key[e]) { kand &= key[e]; kor |= key[e]; ++nv; }
-    }
-#pragma unroll
-    for (int off = 1; off < CSA2_WAVE; off <<= 1) {
-        kand &= (uint32_t)__shfl_xor((int)kand, off, CSA2_WAVE);
-        kor |= (uint32_t)__shfl_xor((int)kor, off, CSA2_WAVE);
-        nv += __shfl_xor(nv, off, CSA2_WAVE);
-    }
-    __syncthreads();
-    if (lane == 0) { sh.hist[wave] = (int)kand; sh.hist[kSelWaves + wave] = (int)kor; sh.wave_b[wave] = nv; }
+    });
+    kand = wave_last(wave_scan(kand, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a & b; }));
+    kor = wave_last(wave_scan(kor, 0u, [](uint32_t a, uint32_t b) { return a | b; }));
+    nv = (int)wave_last((uint32_t)wave_incl_sum(nv));
+    int (*slot)[kSelWaves] = sh.wave_x[phase];
+    phase ^= 1;
+    if (lane == 0) { slot[0][wave] = (int)kand; slot[1][wave] = (int)kor; slot[2][wave] = nv; }
     __syncthreads();
     kand = 0xFFFFFFFFu; kor = 0u; nv = 0;
 #pragma unroll
     for (int w = 0; w < kSelWaves; ++w) {
-        kand &= (uint32_t)sh.hist[w];
-        kor |= (uint32_t)sh.hist[kSelWaves + w];
-        nv += sh.wave_b[w];
+        kand &= (uint32_t)slot[0][w];
+        kor |= (uint32_t)slot[1][w];
+        nv += slot[2][w];
     }
-    __syncthreads();
     SelState st{0u, 0u, nv};
     if (nv <= k) return st;                       // everything valid is selected (mask 0)
     const uint32_t diff = kand ^ kor;             // bits that vary among valid keys
@@ -292,54 +405,57 @@ __device__ __forceinline__ SelState radix_select(SelShared& sh, const KeySource&
         const int width = top + 1 < 11 ? top + 1 : 11;
         const int shift = top + 1 - width;
         const uint32_t dmask = (1u << width) - 1u;
-        for (int i = threadIdx.x; i < kBins; i += kSelThreads) sh.hist[i] = 0;
+        for_rounds(src, reg, [&](int, const uint32_t (&key)[kE]) {
+#pragma unroll
+            for (int e = 0; e < kE; ++e) {
+                const bool hit = key[e] && (key[e] & st.mask) == st.prefix;
+                atomicAdd(&sh.hist[hit ? hist_at((int)((key[e] >> shift) & dmask)) : kHistDiscard + lane], 1);
+            }
+        });
         __syncthreads();
-        for (int rd = 0; rd < rounds; ++rd) {
-            if (rounds > 1) src.load(rd, key);
+        if (wave == 0) {
+            constexpr int BPL = kBins / CSA2_WAVE;    // bins per lane
+            const int b0 = kBins - 1 - BPL * lane;    // this lane's highest bin
+            int sum = 0;
 #pragma unroll
-            for (int e = 0; e < kE; ++e)
-                if (key[e] && (key[e] & st.mask) == st.prefix) atomicAdd(&sh.hist[(key[e] >> shift) & dmask], 1);
-        }
-        __syncthreads();
-        int h[BPT], sum = 0;
+            for (int m = 0; m < BPL; ++m) sum += sh.hist[hist_at(b0 - m)];
+            const int incl = wave_incl_sum(sum);
+            const int excl = incl - sum;
+            const uint64_t hit = __ballot(excl < krem && krem <= incl);   // exactly one lane
+            const int L = hit ? __builtin_ctzll(hit) : 0;
+            const int base = __builtin_amdgcn_readlane(excl, L);
+            const int bL = kBins - 1 - BPL * L;
+            const int v = lane < BPL ? sh.hist[hist_at(bL - lane)] : 0;
 #pragma unroll
-        for (int b = 0; b < BPT; ++b) { h[b] = sh.hist[kBins - 1 - BPT * threadIdx.x - b]; sum += h[b]; }
-        int before;
-        block_excl_sum(sh, sum, before);
-        int acc = before;
-#pragma unroll
-        for (int b = 0; b < BPT; ++b) {
-            if (acc < krem && krem <= acc + h[b]) { sh.digit = kBins - 1 - BPT * threadIdx.x - b; sh.above = acc; }
-            acc += h[b];
+            for (int m = 0; m < BPL; ++m) sh.hist[hist_at(b0 - m)] = 0;
+            const int a = base + wave_incl_sum(v) - v;
+            if (lane < BPL && a < krem && krem <= a + v) { sh.digit = bL - lane; sh.above = a; sh.in_bin = v; }
         }
         __syncthreads();
         const int d = sh.digit;
         krem -= sh.above;
-        const int in_bin = sh.hist[d];
+        const int in_bin = sh.in_bin;
         st.prefix |= (uint32_t)d << shift;
         st.mask |= dmask << shift;
         st.need = krem;
-        __syncthreads();
         if (in_bin == krem) break;   // the whole bin is taken: no tie to resolve
         top = shift - 1;
     }
     return st;
 }
 
-// Ordered compaction: emit(pos, i) for the selected items in item order.  A
-// thread counts the keys above the threshold and those equal to it among its
-// items; one block scan of the packed counts gives every thread the number of
-// selected items before its own (all keys above, plus the first `need` equal
-// keys: ties go to the lowest index), and the thread then writes its items in
-// order.  Returns the number selected.
-template <class Emit>
-__device__ __forceinline__ int select_compact(SelShared& sh, const KeySource& src, SelState st, Emit emit)
+// Ordered compaction: emit(pos, item, key) for the selected items in item
+// order.  A thread counts the keys above the threshold and those equal to it
+// among its items; one block scan of the packed counts per round gives every
+// thread the number of selected items before its own (all keys above, plus the
+// first `need` equal keys: ties go to the lowest item), and the thread then
+// writes its items in order.  Returns the number selected.
+template <class Src, class Emit>
+__device__ __forceinline__ int select_compact(SelShared& sh, int& phase, const Src& src, const RegKeys& reg,
+                                              SelState st, Emit emit)
 {
-    const int rounds = src.rounds();
     int gt_run = 0, eq_run = 0;
-    uint32_t key[kE];
-    for (int rd = 0; rd < rounds; ++rd) {
-        src.load(rd, key);
+    for_rounds(src, reg, [&](int rd, const uint32_t (&key)[kE]) {
         int gt = 0, eq = 0;
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
@@ -348,35 +464,35 @@ __device__ __forceinline__ int select_compact(SelShared& sh, const KeySource& sr
             eq += (key[e] && mk == st.prefix) ? 1 : 0;
         }
         int before;
-        const int total = block_excl_sum(sh, (gt << 16) | eq, before);   // counts < 2^15 per round
+        const int total = block_excl_sum(sh, phase, (gt << 16) | eq, before);   // counts <= kRound < 2^15
         const int gt_before = gt_run + (before >> 16), eq_before = eq_run + (before & 0xFFFF);
         int out = gt_before + (eq_before < st.need ? eq_before : st.need);
         int eq_seen = eq_before;
-        const int i0 = rd * kRound + threadIdx.x * kE;
+        const int i0 = rd * kRound + (int)threadIdx.x * kE;
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
             const uint32_t mk = key[e] & st.mask;
             const bool is_gt = key[e] && mk > st.prefix, is_eq = key[e] && mk == st.prefix;
             const bool sel = is_gt || (is_eq && eq_seen < st.need);
-            if (sel) emit(out++, i0 + e);
+            if (sel) emit(out++, i0 + e, key[e]);
             eq_seen += is_eq ? 1 : 0;
         }
         gt_run += total >> 16;
         eq_run += total & 0xFFFF;
-    }
+    });
     __syncthreads();
     return gt_run + (eq_run < st.need ? eq_run : st.need);
 }
 
-// Bitonic sort (ascending) of n_pow2 ints in LDS.
-__device__ void bitonic_sort(int* a, int n_pow2)
+// Bitonic sort (ascending) of n_pow2 64-bit keys in LDS.
+__device__ void bitonic_sort(unsigned long long* a, int n_pow2)
 {
     for (int k = 2; k <= n_pow2; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
             for (int i = threadIdx.x; i < n_pow2; i += kSelThreads) {
                 const int ixj = i ^ j;
                 if (ixj > i) {
-                    const int x = a[i], y = a[ixj];
+                    const unsigned long long x = a[i], y = a[ixj];
                     const bool up = (i & k) == 0;
                     if ((x > y) == up) { a[i] = y; a[ixj] = x; }
                 }
@@ -388,12 +504,21 @@ __device__ void bitonic_sort(int* a, int n_pow2)
 
 struct SelectLds {
     SelShared sh;
-    uint32_t keys[kPadded];     // block-max keys (Full), then candidate keys; padded positions
-    int blocks[kMaxP];
-    int outbuf[kMaxK];
+    uint32_t bkey[padded_size(kMaxP)];   // keys of the blocks in `blocks` (Full)
+    int blocks[kMaxP];                   // Full: selected blocks; Reindex: block of each item
+    int slots[kMaxP];                    // Reindex: pool slot of each item
+    int cblk[kMaxK];                     // candidate blocks (when not `blocks` itself)
+    int cslot[kMaxK];                    // Reindex: their pool slots
+    unsigned long long sortbuf[kMaxP];   // Reindex: pool sorted by block id
     int flag;
 };
 
+// Block-level reduction of the candidates.  Under the order (score desc,
+// entry id asc) every Top-K entry lies in one of the top-K blocks under the
+// order (block max desc, block id asc): if K blocks precede an entry's block,
+// each holds an entry at its maximum that precedes the entry itself (a larger
+// score, or an equal one at a lower id).  So the Top-K is taken among the
+// 8*K entries of those blocks only.
 template <bool FULL>
 __global__ __launch_bounds__(kSelThreads) void k_select(
     const float* __restrict__ scores, int64_t ld_scores, const float* __restrict__ bmax,
@@ -405,98 +530,118 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     const int n = row_len[r];
     const int nb = (n + 7) >> 3;
     const float* sc = scores + (int64_t)r * ld_scores;
-    int ncand_blocks;   // candidate blocks listed in L.blocks
+    const float* bm = bmax + (int64_t)r * ld_bmax;
+    RegKeys reg;
+    int phase = 0;
+    for (int i = threadIdx.x; i < kBins + kBins / 32; i += kSelThreads) L.sh.hist[i] = 0;
+    const int* cand;        // candidate blocks
+    const int* cand_slot;   // their pool slots (Reindex)
+    int ncb;                // number of candidate blocks
 
     if (FULL) {
-        const float* bm = bmax + (int64_t)r * ld_bmax;
-        // Block maxima: staged into LDS once when they fit in one round, else
-        // round by round inside each pass.
-        KeySource bsrc{L.keys, bm, nb};
-        if (nb <= kRound) {
-            bsrc.stage(0);
-            bsrc.gsrc = nullptr;
-        }
-        const int pint = K > P ? K : P;   // blocks that must hold the Top-K (and the pool)
-        if (pool_out && P < K && nb > P) {   // pool smaller than the Top-K block set: select it first
-            int32_t* po = pool_out + (int64_t)r * P;
-            SelState st = radix_select(L.sh, bsrc, P);
-            int np = select_compact(L.sh, bsrc, st, [&](int pos, int i) { if (pos < P) po[pos] = i; });
-            np = np < P ? np : P;
-            for (int i = np + threadIdx.x; i < P; i += kSelThreads) po[i] = -1;
-        }
-        if (nb <= pint) {
-            for (int i = threadIdx.x; i < nb; i += kSelThreads) L.blocks[i] = i;
-            ncand_blocks = nb;
-        } else {
-            SelState st = radix_select(L.sh, bsrc, pint);
-            ncand_blocks = select_compact(L.sh, bsrc, st, [&](int pos, int i) { if (pos < pint) L.blocks[pos] = i; });
-            ncand_blocks = ncand_blocks < pint ? ncand_blocks : pint;
-        }
+        // A = the top max(P, K) blocks (all of them when nb is smaller), with
+        // their keys; the pool and the candidate blocks are A and the top
+        // min(P, K) blocks of A, in the roles their sizes give.
+        const int big = K > P ? K : P;
+        const BlockMaxSrc bsrc{bm, nb};
+        load_regs(bsrc, reg);
+        SelState st = radix_select(L.sh, phase, bsrc, reg, big);
+        int na = select_compact(L.sh, phase, bsrc, reg, st, [&](int pos, int i, uint32_t key) {
+            if (pos < big) { L.blocks[pos] = i; L.bkey[padded(pos)] = key; }
+        });
+        na = na < big ? na : big;
         __syncthreads();
-        if (pool_out && (P >= K || nb <= P)) {
+        cand = L.blocks;
+        cand_slot = nullptr;
+        ncb = na;
+        if (P > 0) {
             int32_t* po = pool_out + (int64_t)r * P;
-            const int np = ncand_blocks < P ? ncand_blocks : P;
-            for (int i = threadIdx.x; i < P; i += kSelThreads) po[i] = i < np ? L.blocks[i] : -1;
+            const int small = K < P ? K : P;
+            const LdsKeySrc asrc{L.bkey, na};
+            if (na > small) {
+                load_regs(asrc, reg);
+                st = radix_select(L.sh, phase, asrc, reg, small);
+            }
+            if (P >= K) {   // pool = A, candidates = top-K of A
+                for (int i = threadIdx.x; i < P; i += kSelThreads) po[i] = i < na ? L.blocks[i] : -1;
+                if (na > K) {
+                    select_compact(L.sh, phase, asrc, reg, st, [&](int pos, int i, uint32_t) {
+                        if (pos < K) L.cblk[pos] = L.blocks[i];
+                    });
+                    cand = L.cblk;
+                    ncb = K;
+                }
+            } else {        // candidates = A, pool = top-P of A
+                int np = na;
+                if (na > P) {
+                    np = select_compact(L.sh, phase, asrc, reg, st, [&](int pos, int i, uint32_t) {
+                        if (pos < P) po[pos] = L.blocks[i];
+                    });
+                    np = np < P ? np : P;
+                } else {
+                    for (int i = threadIdx.x; i < na; i += kSelThreads) po[i] = L.blocks[i];
+                }
+                for (int i = np + threadIdx.x; i < P; i += kSelThreads) po[i] = -1;
+            }
         }
     } else {
+        // Items are the pool slots in block-id order: the pool as given when
+        // its valid ids already ascend, else sorted by id first, so that the
+        // lowest-item tie rule of the selections is the lowest-id rule.
         const int32_t* pl = pool_in + (int64_t)r * P;
         if (threadIdx.x == 0) L.flag = 0;
         __syncthreads();
         for (int i = threadIdx.x; i < P; i += kSelThreads) {
-            L.blocks[i] = pl[i];
+            const int b = pl[i];
+            const bool ok = b >= 0 && b < nb;
+            L.blocks[i] = ok ? b : -1;
+            L.slots[i] = i;
             if (i + 1 < P) {
-                const int a = pl[i], b = pl[i + 1];
-                if (b >= 0 && (a < 0 || a >= b)) L.flag = 1;   // not strictly ascending
+                const int b2 = pl[i + 1];
+                if (b2 >= 0 && b2 < nb && !(ok && b < b2)) L.flag = 1;
             }
         }
-        ncand_blocks = P;
+        __syncthreads();
+        if (L.flag) {
+            int np2 = 1;
+            while (np2 < P) np2 <<= 1;
+            for (int i = threadIdx.x; i < np2; i += kSelThreads) {
+                const unsigned hi = i < P && L.blocks[i] >= 0 ? (unsigned)L.blocks[i] : 0x7FFFFFFFu;
+                L.sortbuf[i] = i < P ? ((unsigned long long)hi << 32) | (unsigned)i : ~0ull;
+            }
+            __syncthreads();
+            bitonic_sort(L.sortbuf, np2);
+            for (int i = threadIdx.x; i < P; i += kSelThreads) {
+                const unsigned long long v = L.sortbuf[i];
+                const unsigned hi = (unsigned)(v >> 32);
+                L.blocks[i] = hi == 0x7FFFFFFFu ? -1 : (int)hi;
+                L.slots[i] = (int)(unsigned)v;
+            }
+            __syncthreads();
+        }
+        const PoolBlockSrc psrc{bm, L.blocks, L.slots, P};
+        load_regs(psrc, reg);
+        const SelState st = radix_select(L.sh, phase, psrc, reg, K);
+        ncb = select_compact(L.sh, phase, psrc, reg, st, [&](int pos, int i, uint32_t) {
+            if (pos < K) { L.cblk[pos] = L.blocks[i]; L.cslot[pos] = L.slots[i]; }
+        });
+        ncb = ncb < K ? ncb : K;
+        cand = L.cblk;
+        cand_slot = L.cslot;
     }
     __syncthreads();
 
-    // Candidate entries: slot c -> block L.blocks[c/8], position 8*block + c%8
-    const int ncand = ncand_blocks * 8;
-    // Key 0 marks a slot without a visible entry (every finite score maps above
-    // it).  Loads are batched so that many are in flight per thread.
-    for (int c0 = 0; c0 < ncand; c0 += kSelThreads * kLoadBatch) {
-        float v[kLoadBatch];
-        bool ok[kLoadBatch];
-#pragma unroll
-        for (int u = 0; u < kLoadBatch; ++u) {
-            const int c = c0 + u * kSelThreads + threadIdx.x;
-            const int b = c < ncand ? L.blocks[c >> 3] : -1;
-            const int64_t j = (int64_t)b * 8 + (c & 7);
-            ok[u] = b >= 0 && b < nb && j < n;
-            v[u] = ok[u] ? (FULL ? sc[j] : sc[c]) : 0.0f;
-        }
-#pragma unroll
-        for (int u = 0; u < kLoadBatch; ++u) {
-            const int c = c0 + u * kSelThreads + threadIdx.x;
-            if (c < ncand) L.keys[padded(c)] = ok[u] ? order_key(v[u]) : 0u;
-        }
-    }
-    __syncthreads();
-    const KeySource csrc{L.keys, nullptr, ncand};
+    // Top-K among the candidate blocks' entries, written in item order, which
+    // is ascending entry order.
+    const CandSrc csrc{sc, cand, cand_slot, ncb, n};
+    load_regs(csrc, reg);
+    const SelState st = radix_select(L.sh, phase, csrc, reg, K);
     int32_t* to = topk + (int64_t)r * K;
-    SelState st = radix_select(L.sh, csrc, K);
-    if (FULL) {
-        int nk = select_compact(L.sh, csrc, st,
-                                [&](int pos, int c) { if (pos < K) to[pos] = L.blocks[c >> 3] * 8 + (c & 7); });
-        nk = nk < K ? nk : K;
-        for (int i = nk + threadIdx.x; i < K; i += kSelThreads) to[i] = -1;
-    } else {
-        int nk = select_compact(L.sh, csrc, st,
-                                [&](int pos, int c) { if (pos < K) L.outbuf[pos] = L.blocks[c >> 3] * 8 + (c & 7); });
-        nk = nk < K ? nk : K;
-        __syncthreads();
-        if (L.flag) {   // pool not ascending: sort the selected ids
-            int np2 = 1;
-            while (np2 < nk) np2 <<= 1;
-            for (int i = nk + threadIdx.x; i < np2; i += kSelThreads) L.outbuf[i] = 0x7FFFFFFF;
-            __syncthreads();
-            bitonic_sort(L.outbuf, np2);
-        }
-        for (int i = threadIdx.x; i < K; i += kSelThreads) to[i] = i < nk ? L.outbuf[i] : -1;
-    }
+    int nk = select_compact(L.sh, phase, csrc, reg, st, [&](int pos, int c, uint32_t) {
+        if (pos < K) to[pos] = cand[c >> 3] * 8 + (c & 7);
+    });
+    nk = nk < K ? nk : K;
+    for (int i = nk + threadIdx.x; i < K; i += kSelThreads) to[i] = -1;
 }
 
 template <bool REINDEX>
@@ -517,6 +662,7 @@ void launch_score(int HT, int KS, dim3 grid, hipStream_t st, const uint8_t* qI, 
 }
 
 int64_t full_ld(int32_t max_len) { return ((int64_t)max_len + kFullChunk - 1) / kFullChunk * kFullChunk; }
+int64_t reindex_ld(int32_t P) { return ((int64_t)P * 8 + kReChunk - 1) / kReChunk * kReChunk; }
 
 csa2_status_t check_indexer_dims(const char* who, int32_t R, int32_t Hi, int32_t Di, int32_t K, int32_t block)
 {
@@ -585,8 +731,8 @@ extern "C" size_t csa2_index_reindex_workspace_bytes(int32_t R, int32_t K, int32
 {
     (void)K; (void)block;
     if (R < 0 || P < 0) return 0;
-    const int64_t ld = ((int64_t)P * 8 + kReChunk - 1) / kReChunk * kReChunk;
-    return csa2::align_up((size_t)R * ld * 4, 256);
+    const int64_t ld = reindex_ld(P);
+    return csa2::align_up((size_t)R * ld * 4, 256) + csa2::align_up((size_t)R * (ld / 8) * 4, 256);
 }
 
 extern "C" csa2_status_t csa2_index_reindex(const uint8_t* qI, const float* w, const uint8_t* ikeys,
@@ -608,14 +754,15 @@ extern "C" csa2_status_t csa2_index_reindex(const uint8_t* qI, const float* w, c
                  CSA2_ERR_WORKSPACE, "index_reindex: workspace needs %zu bytes, 256-byte aligned (got %zu)",
                  need, workspace_bytes);
     CSA2_REQUIRE(R <= 65535, CSA2_ERR_UNSUPPORTED, "index_reindex: R=%d > 65535", R);
-    const int64_t ld = ((int64_t)P * 8 + kReChunk - 1) / kReChunk * kReChunk;
+    const int64_t ld = reindex_ld(P);
     float* scores = static_cast<float*>(workspace);
+    float* bm = reinterpret_cast<float*>(static_cast<char*>(workspace) + csa2::align_up((size_t)R * ld * 4, 256));
     hipStream_t st = csa2::as_stream(stream);
     const int HT = (Hi + 15) / 16, KS = (Di + 127) / 128;
     dim3 grid((unsigned)(ld / kReChunk), (unsigned)R);
     launch_score<true>(HT, KS, grid, st, qI, w, ikeys, seq_start, row_seq, row_len, pool_blocks, Hi, Di, P,
-                       scores, ld, nullptr, 0);
-    hipLaunchKernelGGL(k_select<false>, dim3((unsigned)R), dim3(kSelThreads), 0, st, scores, ld, nullptr, 0,
+                       scores, ld, bm, ld / 8);
+    hipLaunchKernelGGL(k_select<false>, dim3((unsigned)R), dim3(kSelThreads), 0, st, scores, ld, bm, ld / 8,
                        row_len, pool_blocks, K, P, topk_idx, nullptr);
     return csa2::check_launch("index_reindex");
 }
