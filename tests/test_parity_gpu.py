@@ -145,6 +145,10 @@ def gpu_index_full(wl, layer, K, P):
     ("hi40_di256", [6000, 2500], 40, 256, 300, 500, "int3"),
     ("hi1_di64", [4096], 1, 64, 64, 256, "int3"),
     ("empty_row", [0, 900], 16, 64, 32, 40, "int3"),
+    # more than 4 rounds of 4,096 block maxima (later rounds re-read from memory); K = 2048 gives
+    # 16,384 candidates (4 register rounds)
+    ("long_k2048", [200000, 140000], 16, 64, 2048, 2048, "int3"),
+    ("long_k_above_p", [150000, 9000], 16, 64, 1500, 700, "ties"),
 ])
 def test_index_full_matches_oracle(name, lengths, Hi, Di, K, P, idx):
     log(f"index_full parity: {name}")
@@ -171,6 +175,8 @@ def test_index_full_all_equal_scores_and_no_pool():
     ("ragged_int3", [1, 7, 100, 1000, 4097, 20001], 64, 128, 512, 2048, "int3"),
     ("ties_alphabet", [30000, 17, 8191], 64, 128, 512, 2048, "ties"),
     ("small", [3000, 64, 9], 8, 64, 64, 256, "int3"),
+    ("k2048_all_pool", [70000, 20000, 5], 16, 64, 2048, 2048, "int3"),
+    ("k_above_pool", [40000, 3000], 16, 64, 700, 64, "ties"),
 ])
 def test_index_reindex_matches_oracle(name, lengths, Hi, Di, K, P, idx):
     log(f"index_reindex parity: {name}")
@@ -202,6 +208,31 @@ def test_index_reindex_unsorted_pool_with_invalid_ids():
                                   torch.tensor(pool, device=DEV), K)
     torch.cuda.synchronize()
     assert np.array_equal(np_(got), want)
+
+
+def test_index_reindex_unsorted_pool_all_ties():
+    # every score 0: the Top-K is the K lowest visible entry ids of the pool,
+    # whatever order the pool lists its blocks in
+    wl = small_workload([3000, 700], Hi=16, Di=64)
+    wl.w[1].zero_()
+    rng = np.random.default_rng(11)
+    K, P = 100, 64
+    pool = np.full((2, P), -1, np.int32)
+    for r, n in enumerate([3000, 700]):
+        nb = (n + 7) // 8
+        fixed = [nb - 1, 0, nb // 2]                  # the ragged last block, block 0, a middle one
+        ids = np.concatenate([fixed, rng.choice(np.setdiff1d(np.arange(nb), fixed), 37, replace=False)])
+        pool[r, rng.permutation(P)[:40]] = ids
+    packed = oracle_index_rows(wl, 0, [0, 1], K, P)[2]
+    want = oracle_reindex_rows(wl, 1, [0, 1], packed, pool, K)
+    got = csa2.csa2_index_reindex(wl.qI[1], wl.w[1], wl.ikeys, wl.seq_start, wl.row_seq, wl.row_len,
+                                  torch.tensor(pool, device=DEV), K)
+    torch.cuda.synchronize()
+    got = np_(got)
+    assert np.array_equal(got, want)
+    for r, n in enumerate([3000, 700]):
+        ent = sorted(j for b in pool[r] if b >= 0 for j in range(8 * b, min(8 * b + 8, n)))
+        assert got[r].tolist() == ent[:K] + [-1] * max(0, K - len(ent))
 
 
 # ----------------------------------------------------------------- attention
