@@ -759,7 +759,8 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
 // Merge of split partials: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),
 // lse from the unrounded sums.  Partial statistics per (row, split, head):
 // (m, l, l_exact, 0).  One workgroup per (row, head), placed on the row's XCD;
-// each thread owns four consecutive channels and requests all splits at once.
+// each thread owns four consecutive channels and requests the statistics and
+// its channels of every split at once, so the merge waits for one round trip.
 __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, int32_t R, int32_t H,
                                                       int32_t D, int32_t S, float* __restrict__ out,
@@ -769,36 +770,33 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
     const int h = xcd_slot(blockIdx.x, H, r);
     if (r >= R) return;
     const int64_t rh = (int64_t)r * H + h;
-    float4 st[kMaxPlanSplits];
-    float M = -INFINITY;
+    const int d = 4 * threadIdx.x;   // D <= 4 * blockDim.x
+    const bool has_d = d < D;
+    float4 st[kMaxPlanSplits], v[kMaxPlanSplits];
 #pragma unroll
     for (int k = 0; k < kMaxPlanSplits; ++k) {
         st[k] = k < S ? *reinterpret_cast<const float4*>(part_ml + (((int64_t)r * S + k) * H + h) * 4)
                       : make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
-        if (st[k].y > 0.0f) M = fmaxf(M, st[k].x);
+        v[k] = k < S && has_d ? *reinterpret_cast<const float4*>(part_o + (((int64_t)r * S + k) * H + h) * D + d)
+                              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
-    float L = 0.0f, Le = 0.0f, w[kMaxPlanSplits];
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kMaxPlanSplits; ++k)
+        if (st[k].y > 0.0f) M = fmaxf(M, st[k].x);
+    float L = 0.0f, Le = 0.0f;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
     for (int k = 0; k < kMaxPlanSplits; ++k) {
-        w[k] = st[k].y > 0.0f ? exp2f(st[k].x - M) : 0.0f;
-        L += st[k].y * w[k];
-        Le += st[k].z * w[k];
+        const float w = st[k].y > 0.0f ? exp2f(st[k].x - M) : 0.0f;
+        L += st[k].y * w;
+        Le += st[k].z * w;
+        acc.x += w * v[k].x; acc.y += w * v[k].y; acc.z += w * v[k].z; acc.w += w * v[k].w;
     }
     if (lse && threadIdx.x == 0) lse[rh] = L > 0.0f ? M * kLn2 + logf(Le) : -INFINITY;
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    for (int d = 4 * threadIdx.x; d < D; d += 4 * blockDim.x) {
-        float4 v[kMaxPlanSplits];
-#pragma unroll
-        for (int k = 0; k < kMaxPlanSplits; ++k)
-            v[k] = k < S ? *reinterpret_cast<const float4*>(part_o + (((int64_t)r * S + k) * H + h) * D + d)
-                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-#pragma unroll
-        for (int k = 0; k < kMaxPlanSplits; ++k) {
-            acc.x += w[k] * v[k].x; acc.y += w[k] * v[k].y; acc.z += w[k] * v[k].z; acc.w += w[k] * v[k].w;
-        }
+    if (has_d)
         *reinterpret_cast<float4*>(out + rh * D + d) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    }
 }
 
 struct AttnPlan {
