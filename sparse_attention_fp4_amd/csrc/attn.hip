@@ -369,8 +369,8 @@ __host__ __device__ inline int pad_topk(int K) { return (K + kFrag - 1) / kFrag 
 // Kind of a fragment (uniform): 0 Top-K slots, 1 SWA rows.
 __device__ __forceinline__ int frag_kind(int fr, int Kp) { return fr * kFrag >= Kp ? 1 : 0; }
 
-// LDS of one workgroup: the waves' V tiles and the a-parts of the query during
-// the key loop, then the merge buffers.
+// LDS of one workgroup: the waves' V tiles and the query (fp16, and its a-
+// and b-parts) during the key loop, then the merge buffers.
 template <int HT, int D, int CS>
 struct AttnSmem {
     static constexpr int KS = D / 32;
@@ -379,7 +379,8 @@ struct AttnSmem {
     static constexpr int VS = DP + 8;              // V row stride in halves (conflict-free rows and transposes)
     static constexpr int kVBytes = kWaves * kFrag * VS * 2;
     static constexpr int kQaBytes = 2 * HT * KS * CSA2_WAVE * 16;   // a and b parts
-    static constexpr int kLoop = kVBytes + kQaBytes;
+    static constexpr int kQfBytes = HT * KS * CSA2_WAVE * 16;       // the query as fp16
+    static constexpr int kLoop = kVBytes + kQaBytes + kQfBytes;
     // Merge: rounds over RT output tiles at a time (a multiple of the wave
     // count); per round every wave stores its RT tiles per head tile,
     // [wave][HT][RT][64] f32x4.  One round when that fits in 128 KB.
@@ -409,8 +410,10 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     __shared__ float wm[kWaves][NH];
     __shared__ float wl[kWaves][NH];
     __shared__ float wle[kWaves][NH];
+    __shared__ uint32_t wqm[kWaves][NH];   // per wave: bf16 bits of the max |q| of each head over its pieces
     _Float16* const vt = reinterpret_cast<_Float16*>(smem) + (threadIdx.x >> 6) * (kFrag * VS);
     f16x8* const qa_s = reinterpret_cast<f16x8*>(smem + SM::kVBytes);   // [2][HT * KS][64]: a, b
+    f16x8* const qf_s = reinterpret_cast<f16x8*>(smem + SM::kVBytes + SM::kQaBytes);   // [HT * KS][64]
     f32x4* const xo = reinterpret_cast<f32x4*>(smem);                    // merge buffers (after the loop)
 
     const int lane = lane_id();
@@ -430,10 +433,10 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     const int32_t* topk_row = topk + (int64_t)r * K;
 
     // Loads are issued in dependency order so that waiting for one never waits
-    // for a later chain: the row's metadata and the wave's first two
-    // fragments' Top-K entries, the query, then (once the sequence's first
-    // cache row is known) the first fragment's key bytes.  The query is
-    // converted while the sequence's first row is fetched.
+    // for a later chain: the row's metadata (scalar) and the wave's first two
+    // fragments' Top-K entries, the wave's quarter of the query, then the
+    // first fragment's key bytes, which arrive during the barriers that share
+    // the query.
     const int n = row_len[r];
     const int seq = row_seq[r];
     int nsw = W > 0 ? swa_len[r] : 0;
@@ -449,70 +452,76 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     int idx_c = 0, idx_n = 0;
     if (fr < f_end) load_idx(fr, idx_c);
     if (fr + kWaves < f_end) load_idx(fr + kWaves, idx_n);
-    // The row's query through a buffer over its H heads: heads past H read
-    // as zeros, with no branch around the loads.
-    uint4 qraw[HT][KS];
+    // The query is shared by the four waves: wave w loads and converts the
+    // pieces (ht, t) with (ht * KS + t) % 4 == w, i.e. piece k < NP of the
+    // wave is ht = k / (KS/4), t = 4k % KS + w; the pieces go to LDS and every
+    // wave reads the whole query back after the barrier.  The query is read
+    // through a buffer over its H heads: heads past H read as zeros.
+    constexpr int NP = HT * KS / kWaves;
+    static_assert(KS % kWaves == 0, "query pieces per wave");
+    uint4 qraw[NP];
     {
         const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + (int64_t)r * H * D, H * D * 2);
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
+        for (int k = 0; k < NP; ++k) {
+            const int ht = k / (KS / kWaves), t = (kWaves * k) % KS + wave;
             const uint32_t hoff = (uint32_t)(h0 + ht * 16 + col) * (D * 2);
-#pragma unroll
-            for (int t = 0; t < KS; ++t) {
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, hoff + 2 * step_ch<D>(grp, t), 0, 0);
-                qraw[ht][t] = make_uint4(v[0], v[1], v[2], v[3]);
-            }
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, hoff + 2 * step_ch<D>(grp, t), 0, 0);
+            qraw[k] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     }
     nsw = nsw < 0 ? 0 : (nsw > W ? W : nsw);
     const int64_t base = seq_start[seq];
-    // Query heads (B operand): lane (head col, grp) holds channels
-    // step_ch(grp, t) .. +8 for k-step t.  bf16 -> fp16 is exact for |q| in
-    // [2^-14, 65504].
-    f16x8 qf[HT][KS];
+    // Max |q| of each head over the wave's pieces: an integer max of the bf16
+    // magnitude bits (two per instruction), then over the lane groups.
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        float q32[KS][8];
-        float m = 0.0f;
+        u16x2 mx = {0, 0};
 #pragma unroll
-        for (int t = 0; t < KS; ++t) {
-            const uint32_t ws[4] = {qraw[ht][t].x, qraw[ht][t].y, qraw[ht][t].z, qraw[ht][t].w};
+        for (int k = ht * (KS / kWaves); k < (ht + 1) * (KS / kWaves); ++k) {
+            const uint32_t ws[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                q32[t][2 * e] = __uint_as_float(ws[e] << 16);
-                q32[t][2 * e + 1] = __uint_as_float(ws[e] & 0xFFFF0000u);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                qf[ht][t][e] = (_Float16)q32[t][e];
-                m = fmaxf(m, fabsf(q32[t][e]));
-            }
+            for (int e = 0; e < 4; ++e)
+                mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, ws[e] & 0x7FFF7FFFu));
         }
-        m = fmaxf(m, shfl_xor_f(m, 16));
-        m = fmaxf(m, shfl_xor_f(m, 32));
-        // a-part of the head: q rounded to a multiple of 2^(E-11), 2^E > max|q|
-        // (E >= -13 keeps the quantum within fp16's subnormal grid).  Adding
-        // and subtracting 1.5 * 2^(E+12) rounds to that multiple in fp32.
-        // Every wave holds the same query; wave w stores the pieces
-        // (ht * KS + t) % 4 == w.
+        uint32_t mb = mx[0] > mx[1] ? mx[0] : mx[1];
+        mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16, CSA2_WAVE));
+        mb = max(mb, (uint32_t)__shfl_xor((int)mb, 32, CSA2_WAVE));
+        if (grp == 0) wqm[wave][ht * 16 + col] = mb;
+    }
+    __syncthreads();
+    // Query heads (B operand): lane (head col, grp) holds channels
+    // step_ch(grp, t) .. +8 for k-step t.  bf16 -> fp16 is exact for |q| in
+    // [2^-14, 65504].  a-part of a head: q rounded to a multiple of 2^(E-11),
+    // 2^E > max|q| (E >= -13 keeps the quantum within fp16's subnormal grid).
+    // Adding and subtracting 1.5 * 2^(E+12) rounds to that multiple in fp32.
+    float Cq[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        uint32_t mb = 0u;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) mb = max(mb, wqm[w][ht * 16 + col]);
+        const float m = __uint_as_float(mb << 16);
         int E = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 0xFF) - 126 : -13;
         E = E < -13 ? -13 : E;
-        const float C = __uint_as_float((uint32_t)(E + 12 + 127) << 23 | 0x400000u);
+        Cq[ht] = __uint_as_float((uint32_t)(E + 12 + 127) << 23 | 0x400000u);
+    }
 #pragma unroll
-        for (int t = 0; t < KS; ++t) {
-            if ((ht * KS + t) % kWaves != wave) continue;
-            f16x8 av, bv;
+    for (int k = 0; k < NP; ++k) {
+        const int ht = k / (KS / kWaves), t = (kWaves * k) % KS + wave;
+        const uint32_t ws[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
+        f16x8 qv, av, bv;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float a = (q32[t][e] + C) - C;
-                av[e] = (_Float16)a;
-                bv[e] = (_Float16)(q32[t][e] - a);   // exact: the low bits of q
-            }
-            qa_s[(ht * KS + t) * CSA2_WAVE + lane] = av;
-            qa_s[((HT + ht) * KS + t) * CSA2_WAVE + lane] = bv;
+        for (int e = 0; e < 8; ++e) {
+            const float q32 = __uint_as_float(e & 1 ? ws[e >> 1] & 0xFFFF0000u : ws[e >> 1] << 16);
+            const float a = (q32 + Cq[ht]) - Cq[ht];
+            qv[e] = (_Float16)q32;
+            av[e] = (_Float16)a;
+            bv[e] = (_Float16)(q32 - a);   // exact: the low bits of q
         }
-#pragma unroll
-        for (int t = 0; t < KS; ++t) asm volatile("" : "+a"(qf[ht][t]));
+        qf_s[(ht * KS + t) * CSA2_WAVE + lane] = qv;
+        qa_s[(ht * KS + t) * CSA2_WAVE + lane] = av;
+        qa_s[((HT + ht) * KS + t) * CSA2_WAVE + lane] = bv;
     }
     const int p = grp >> 1;
     // Buffers over the row's visible entries and SWA rows; 32-bit offsets
@@ -533,6 +542,14 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     if (fr < f_end) load_frag(cur, fr, idx_c);
 
     __syncthreads();
+    f16x8 qf[HT][KS];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            qf[ht][t] = qf_s[(ht * KS + t) * CSA2_WAVE + lane];
+            asm volatile("" : "+a"(qf[ht][t]));
+        }
 
     // Online softmax state (log2 domain), per head in the S^T layout (lane
     // col = head).  The reference max of a head is raised only when a

@@ -12,6 +12,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __fp16 lds_f16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 
 #define CSA2_WAVE 64
