@@ -338,13 +338,21 @@ __device__ __forceinline__ void pv_frag(const f16x4 (&pa)[HT], const _Float16* v
                                         f32x4 (&o)[HT][NDT])
 {
     const _Float16* vr = vt + (4 * grp + (col >> 2)) * VS + 4 * (col & 3);
+    constexpr int B = NDT < 16 ? NDT : 16;   // reads in flight
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-        const lds_f16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-            (lds_f16x4 __attribute__((address_space(3)))*)(vr + 16 * dt));
-        const f16x4 vb = {(_Float16)b[0], (_Float16)b[1], (_Float16)b[2], (_Float16)b[3]};
+    for (int d0 = 0; d0 < NDT; d0 += B) {
+        lds_f16x4 b[B];
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) o[ht][dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa[ht], vb, o[ht][dt], 0, 0, 0);
+        for (int k = 0; k < B; ++k)
+            b[k] = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4 __attribute__((address_space(3)))*)(vr + 16 * (d0 + k)));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < B; ++k) {
+            const f16x4 vb = {(_Float16)b[k][0], (_Float16)b[k][1], (_Float16)b[k][2], (_Float16)b[k][3]};
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht)
+                o[ht][d0 + k] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa[ht], vb, o[ht][d0 + k], 0, 0, 0);
+        }
     }
 }
 
