@@ -46,9 +46,11 @@ HBM_PEAK_GBPS = 8000.0
 # were taken on).  Reported as null whenever that source has changed since.
 TRAFFIC = {
     # profiles/sparse_attn_decode_64k.md: k_sparse_attn + k_attn_combine per call
-    (2, "sparse_attn", "5b72cc670004877c"): 32121861,
+    (2, "sparse_attn", "867dfeaf2dad35ed"): 32087577,
     # profiles/index_full_decode_64k.md: k_index_score (Full) + k_select (Full) per call
-    (2, "index_full", "ebafcfd255f8f1e5"): 288803402,
+    (2, "index_full", "a214b6c6f4fd36c6"): 284882931,
+    # profiles/index_reindex_decode_64k.md: k_index_score (Reindex) + k_select (Reindex) per call
+    (2, "index_reindex", "a214b6c6f4fd36c6"): 74794183,
 }
 CALL_SOURCE = {"sparse_attn": "attn.hip", "index_full": "index.hip", "index_reindex": "index.hip",
                "quantize_append": "quantize.hip"}
@@ -302,7 +304,7 @@ def main():
     tokens_per_s = R / (ms / 1000.0) if not cfg.prefill_rows else cfg.prefill_rows / (ms / 1000.0)
     step_gbps = alg["total"] / (ms / 1000.0) / 1e9
 
-    breakdown, roofline, index_roofline, shares = {}, None, None, {}
+    breakdown, roofline, index_roofline, reindex_roofline, shares = {}, None, None, None, {}
     if not args.no_breakdown:
         log("bench: per-call timing")
         breakdown = per_call_times(step)
@@ -325,6 +327,8 @@ def main():
         dominant = max(shares, key=shares.get)
         roofline = roof(dominant)
         index_roofline = roof("index_full")
+        if calls_per_step["index_reindex"]:
+            reindex_roofline = roof("index_reindex")
     log("bench: cold-cache steps")
     cold_ms = cold_step_ms(g, min(args.steps, 10))
     extra = {}
@@ -364,6 +368,7 @@ def main():
         "per_call_us": {k: round(v, 2) for k, v in breakdown.items()},
         "roofline": roofline,
         "roofline_index_full": index_roofline,
+        "roofline_index_reindex": reindex_roofline,
         "cpu_baseline": cpu,
     }
     result.update(extra)
