@@ -493,8 +493,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
                 mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, ws[e] & 0x7FFF7FFFu));
         }
         uint32_t mb = mx[0] > mx[1] ? mx[0] : mx[1];
-        mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16, CSA2_WAVE));
-        mb = max(mb, (uint32_t)__shfl_xor((int)mb, 32, CSA2_WAVE));
+        mb = umax_xor32(umax_xor16(mb));
         if (grp == 0) wqm[wave][ht * 16 + col] = mb;
     }
     __syncthreads();
@@ -627,8 +626,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
                 x[i] = kv ? (sh[ht][i] + sl[ht][i]) * scale_log2e : -INFINITY;
                 mx = fmaxf(mx, x[i]);
             }
-            mx = fmaxf(mx, shfl_xor_f(mx, 16));
-            mx = fmaxf(mx, shfl_xor_f(mx, 32));
+            mx = max_xor32(max_xor16(mx));
             // Raise the head's reference when the fragment's max exceeds it by
             // more than kLazy (a head without any key so far has l = 0 and
             // o = 0: nothing to rescale).
@@ -689,11 +687,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     // ---- merge the four waves.  Per-head statistics first.
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        float lt = l_p[ht], le = l_e[ht];
-        lt += shfl_xor_f(lt, 16);
-        lt += shfl_xor_f(lt, 32);
-        le += shfl_xor_f(le, 16);
-        le += shfl_xor_f(le, 32);
+        const float lt = sum_xor32(sum_xor16(l_p[ht])), le = sum_xor32(sum_xor16(l_e[ht]));
         if (grp == 0) {
             wm[wave][ht * 16 + col] = m_p[ht];
             wl[wave][ht * 16 + col] = lt;

@@ -40,4 +40,41 @@ __device__ __forceinline__ uint32_t order_key(float f)
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, CSA2_WAVE); }
+
+// Reductions between lanes 16 (32) apart without an LDS round trip:
+// v_permlane16_swap(x, x) hands each lane of an even 16-lane row, in its
+// second result, the value of the lane 16 above (and each lane of an odd row,
+// in its first result, the value 16 below), while the other result keeps the
+// lane's own value; v_permlane32_swap does the same for the two halves of the
+// wave.  So op(first, second) is op(own, partner) in every lane.
+__device__ __forceinline__ float max_xor16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ uint32_t umax_xor16(uint32_t v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return r[0] > r[1] ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t umax_xor32(uint32_t v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return r[0] > r[1] ? r[0] : r[1];
+}
+__device__ __forceinline__ float sum_xor16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (CSA2_WAVE - 1)); }
