@@ -67,6 +67,15 @@ __device__ __forceinline__ uint32_t umax_xor32(uint32_t v)
     const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
     return r[0] > r[1] ? r[0] : r[1];
 }
+// Max over aligned groups of 8 lanes with DPP: quad permutations [1,0,3,2] and
+// [2,3,0,1], then the mirror within each half row (lane i <-> 7 - i, which
+// lies in the other quad of the same 8 lanes).
+__device__ __forceinline__ float max_over8(float v)
+{
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+}
 __device__ __forceinline__ float sum_xor16(float v)
 {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);

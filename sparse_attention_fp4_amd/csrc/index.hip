@@ -132,14 +132,10 @@ __global__ __launch_bounds__(256) void k_index_score(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) part += wv[t][i] * fmaxf(acc[i], 0.0f);
             }
-            part += shfl_xor_f(part, 16);
-            part += shfl_xor_f(part, 32);
+            part = sum_xor32(sum_xor16(part));
             const int64_t slot = wbase + (int64_t)(it0 + u) * 16 + col;
             // maximum over the visible entries of each 8-entry block (-inf if none)
-            float m = ok[u] ? part : -INFINITY;
-            m = fmaxf(m, shfl_xor_f(m, 1));
-            m = fmaxf(m, shfl_xor_f(m, 2));
-            m = fmaxf(m, shfl_xor_f(m, 4));
+            const float m = max_over8(ok[u] ? part : -INFINITY);
             const bool lead = grp == 0 && (col & 7) == 0;
             if (REINDEX) {
                 if (grp == 0 && slot < (int64_t)P * 8) scores[(int64_t)r * ld_scores + slot] = part;
