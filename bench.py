@@ -254,7 +254,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2, help="workload: 2 decode 64K (default), 3 decode 1M, "
-                                                          "5 ragged 256, 4 prefill chunk, 1 tiny")
+                                                          "5 ragged 256, 4 prefill chunk (Full layer), "
+                                                          "6 prefill chunk (all 20 layers), 1 tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--copy-check", action="store_true", help="also time a plain 1 GiB device copy")

@@ -38,10 +38,11 @@ SAMPLES = {
     3: dict(rows=[2], attn_layers=[0, 5, 19]),
     4: dict(rows=[0, 1234, 4095], attn_layers=[0]),
     5: dict(rows=None, attn_layers=[0, 10, 16]),
+    6: dict(rows=[0, 2047, 4095], attn_layers=[0, 3, 5, 19]),
 }
 
 
-@pytest.mark.parametrize("cid", [2, 5, 3, 4])
+@pytest.mark.parametrize("cid", [2, 5, 3, 4, 6])
 def test_full_size_workload(cid):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")

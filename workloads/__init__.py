@@ -61,6 +61,10 @@ CONFIGS = {
               layers="F", prefill_rows=4096),
     5: Config(5, "ragged_256", B=256, N=None, D=512, W=128, H=64, Hi=64, Di=128, K=512, P=2048,
               kv_dist="student_t_outliers", idx_dist="ties", ragged_lo=4096, ragged_hi=262144),
+    # the prefill chunk of config 4 run through the decode layer schedule: every chunk row gets the
+    # Full layer's pool, three pool-restricted Reindex layers and Reuse attention in the other layers
+    6: Config(6, "prefill_layers", B=1, N=131072, D=512, W=128, H=64, Hi=64, Di=128, K=512, P=2048,
+              prefill_rows=4096),
 }
 
 
@@ -159,7 +163,7 @@ def make(cfg: Config, device="cpu", layers: Optional[List[int]] = None,
     """Draw every input of one step of `cfg` on `device` with the config's seed.
 
     Decode configs: one query row per sequence seeing all its entries; the last
-    entry of each sequence is the one the step appends.  Prefill (config 4):
+    entry of each sequence is the one the step appends.  Prefill (configs 4, 6):
     the chunk's rows are appended after the 131,072 cached entries and query
     row i sees 131,072 + i + 1 entries; its SWA window is token rows
     [i, i + W) of one [W - 1 + rows, D] buffer.
