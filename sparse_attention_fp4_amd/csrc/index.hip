@@ -239,7 +239,9 @@ __device__ __forceinline__ void keys8(const float* p, uint32_t (&key)[kE], int v
 }
 
 // Key sources.  Each gives rounds() and load(rd, key): the keys of items
-// rd*kRound + threadIdx.x*kE + e.
+// rd*kRound + threadIdx.x*kE + e; load is fetch (issue the reads into a Raw)
+// followed by finish (turn the Raw into keys), and fetch may be issued for
+// rounds past the end (they finish as invalid items).
 
 // Block maxima of one Full row in global memory (item = block id).  The row
 // holds a multiple of 8 floats, so the last thread's 32-byte read stays inside
@@ -247,19 +249,48 @@ __device__ __forceinline__ void keys8(const float* p, uint32_t (&key)[kE], int v
 struct BlockMaxSrc {
     const float* bm;
     int cnt;
+    struct Raw { float4 a, b; };
     __device__ __forceinline__ int rounds() const { return (cnt + kRound - 1) / kRound; }
-    __device__ __forceinline__ void load(int rd, uint32_t (&key)[kE]) const
+    // Unconditional: items past the end read the row's last 8 floats
+    // (cnt >= 1 whenever there is a round), and finish() masks them.
+    __device__ __forceinline__ void fetch(int rd, Raw& raw) const
     {
         const int i0 = rd * kRound + (int)threadIdx.x * kE;
-        if (i0 < cnt) keys8(bm + i0, key, cnt - i0);
-        else
+        const int last = ((cnt + kE - 1) & ~(kE - 1)) - kE;
+        const float4* p = reinterpret_cast<const float4*>(bm + (i0 < last ? i0 : last));
+        raw.a = p[0];
+        raw.b = p[1];
+    }
+    __device__ __forceinline__ void finish(int rd, const Raw& raw, uint32_t (&key)[kE]) const
+    {
+        const int i0 = rd * kRound + (int)threadIdx.x * kE;
+        const float v[kE] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w, raw.b.x, raw.b.y, raw.b.z, raw.b.w};
 #pragma unroll
-            for (int e = 0; e < kE; ++e) key[e] = 0u;
+        for (int e = 0; e < kE; ++e) key[e] = i0 + e < cnt ? order_key(v[e]) : 0u;
+    }
+    __device__ __forceinline__ void load(int rd, uint32_t (&key)[kE]) const
+    {
+        Raw raw;
+        fetch(rd, raw);
+        finish(rd, raw, key);
+    }
+};
+
+// Sources whose loads are cheap to repeat (LDS, or small gathers that always
+// fit the register rounds) fetch by loading their keys directly.
+template <class Src>
+struct DirectFetch {
+    struct Raw { uint32_t k[kE]; };
+    __device__ __forceinline__ void fetch(int rd, Raw& raw) const { static_cast<const Src*>(this)->load(rd, raw.k); }
+    __device__ __forceinline__ void finish(int, const Raw& raw, uint32_t (&key)[kE]) const
+    {
+#pragma unroll
+        for (int e = 0; e < kE; ++e) key[e] = raw.k[e];
     }
 };
 
 // Keys already in an LDS array at padded positions.
-struct LdsKeySrc {
+struct LdsKeySrc : DirectFetch<LdsKeySrc> {
     const uint32_t* keys;
     int cnt;
     __device__ __forceinline__ int rounds() const { return (cnt + kRound - 1) / kRound; }
@@ -273,7 +304,7 @@ struct LdsKeySrc {
 
 // Pool blocks of one Reindex row (item i = block blocks[i], whose maximum is
 // bm[slots[i]]; block -1 = no block).
-struct PoolBlockSrc {
+struct PoolBlockSrc : DirectFetch<PoolBlockSrc> {
     const float* bm;
     const int* blocks;
     const int* slots;
@@ -299,7 +330,7 @@ struct PoolBlockSrc {
 // sc[8*blocks[c/8] + c%8] (Full: scores by entry id) or sc[8*slots[c/8] + c%8]
 // (Reindex: scores by pool slot).  Thread t of round rd reads block
 // rd*kSelThreads + t: two 16-byte loads.
-struct CandSrc {
+struct CandSrc : DirectFetch<CandSrc> {
     const float* sc;
     const int* blocks;
     const int* slots;    // null in Full mode
@@ -320,8 +351,28 @@ struct CandSrc {
     }
 };
 
+// Evenly spaced block maxima of a long Full row (cnt > kRound): item s of the
+// one round is block floor(s * cnt / kRound).
+struct SampleSrc : DirectFetch<SampleSrc> {
+    const float* bm;
+    int cnt;
+    __device__ __forceinline__ int rounds() const { return 1; }
+    __device__ __forceinline__ void load(int, uint32_t (&key)[kE]) const
+    {
+        const int s0 = (int)threadIdx.x * kE;
+        float v[kE];
+#pragma unroll
+        for (int e = 0; e < kE; ++e) v[e] = bm[(int)((int64_t)(s0 + e) * cnt / kRound)];
+#pragma unroll
+        for (int e = 0; e < kE; ++e) key[e] = order_key(v[e]);
+    }
+};
+
 // Calls f(rd, keys) for every round: the register rounds first, then the
-// rest read from the source.  Uniform across the block (f may synchronise).
+// rest read from the source with kPrefetch rounds in flight (their fetches
+// are unconditional, so every wait is for the oldest round only).  Uniform
+// across the block (f may synchronise).
+constexpr int kPrefetch = 4;
 template <class Src, class F>
 __device__ __forceinline__ void for_rounds(const Src& src, const RegKeys& reg, F f)
 {
@@ -329,10 +380,18 @@ __device__ __forceinline__ void for_rounds(const Src& src, const RegKeys& reg, F
 #pragma unroll
     for (int rr = 0; rr < kRegRounds; ++rr)
         if (rr < rounds) f(rr, reg[rr]);
-    for (int rd = kRegRounds; rd < rounds; ++rd) {
-        uint32_t key[kE];
-        src.load(rd, key);
-        f(rd, key);
+    if (rounds <= kRegRounds) return;
+    typename Src::Raw buf[kPrefetch];
+#pragma unroll
+    for (int q = 0; q < kPrefetch; ++q) src.fetch(kRegRounds + q, buf[q]);
+    for (int rd = kRegRounds; rd < rounds; rd += kPrefetch) {
+#pragma unroll
+        for (int q = 0; q < kPrefetch; ++q) {
+            uint32_t key[kE];
+            src.finish(rd + q, buf[q], key);
+            src.fetch(rd + q + kPrefetch, buf[q]);
+            if (rd + q < rounds) f(rd + q, key);
+        }
     }
 }
 
@@ -498,6 +557,8 @@ __device__ void bitonic_sort(unsigned long long* a, int n_pow2)
     }
 }
 
+constexpr int kGatherCap = 8192;   // blocks a long Full row's pre-filter may keep
+
 struct SelectLds {
     SelShared sh;
     uint32_t bkey[padded_size(kMaxP)];   // keys of the blocks in `blocks` (Full)
@@ -507,6 +568,10 @@ struct SelectLds {
     int cslot[kMaxK];                    // Reindex: their pool slots
     unsigned long long sortbuf[kMaxP];   // Reindex: pool sorted by block id
     int flag;
+};
+struct SelectLdsFull : SelectLds {
+    uint32_t gkey[padded_size(kGatherCap)];   // long rows: keys of the pre-filtered blocks
+    int gid[kGatherCap];                      // and their block ids, ascending
 };
 
 // Block-level reduction of the candidates.  Under the order (score desc,
@@ -521,7 +586,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     int64_t ld_bmax, const int32_t* __restrict__ row_len, const int32_t* __restrict__ pool_in,
     int32_t K, int32_t P, int32_t* __restrict__ topk, int32_t* __restrict__ pool_out)
 {
-    __shared__ SelectLds L;
+    __shared__ typename std::conditional<FULL, SelectLdsFull, SelectLds>::type L;
     const int r = blockIdx.x;
     const int n = row_len[r];
     const int nb = (n + 7) >> 3;
@@ -534,17 +599,65 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     const int* cand_slot;   // their pool slots (Reindex)
     int ncb;                // number of candidate blocks
 
-    if (FULL) {
+    if constexpr (FULL) {
         // A = the top max(P, K) blocks (all of them when nb is smaller), with
         // their keys; the pool and the candidate blocks are A and the top
         // min(P, K) blocks of A, in the roles their sizes give.
         const int big = K > P ? K : P;
         const BlockMaxSrc bsrc{bm, nb};
-        load_regs(bsrc, reg);
-        SelState st = radix_select(L.sh, phase, bsrc, reg, big);
-        int na = select_compact(L.sh, phase, bsrc, reg, st, [&](int pos, int i, uint32_t key) {
-            if (pos < big) { L.blocks[pos] = i; L.bkey[padded(pos)] = key; }
-        });
+        SelState st;
+        int na = -1;
+        if (nb > kRegRounds * kRound) {
+            // Long row: every pass over all block maxima re-reads memory, so a
+            // threshold is estimated first from kRound evenly spaced maxima (the
+            // key of the s-th largest sample, s chosen to expect about 2 * big
+            // blocks at or above it), the blocks at or above it are gathered in
+            // block order in one pass, and when that set holds at least `big`
+            // blocks (so the big-th largest key is at or above the threshold
+            // and every block of A is in the set, ties included) and fits, A
+            // is selected from it.  Otherwise the full selection below runs.
+            const SampleSrc ssrc{{}, bm, nb};
+            load_regs(ssrc, reg);
+            int s_target = (int)(((int64_t)2 * big * kRound + nb - 1) / nb);
+            s_target = s_target < 1 ? 1 : s_target;
+            const uint32_t thr = radix_select(L.sh, phase, ssrc, reg, s_target).prefix;
+            load_regs(bsrc, reg);
+            int cnt = 0;
+            for_rounds(bsrc, reg, [&](int rd, const uint32_t (&key)[kE]) {
+                int c = 0;
+#pragma unroll
+                for (int e = 0; e < kE; ++e) c += key[e] != 0u && key[e] >= thr ? 1 : 0;
+                int before;
+                const int total = block_excl_sum(L.sh, phase, c, before);
+                int pos = cnt + before;
+                const int i0 = rd * kRound + (int)threadIdx.x * kE;
+#pragma unroll
+                for (int e = 0; e < kE; ++e)
+                    if (key[e] != 0u && key[e] >= thr) {
+                        if (pos < kGatherCap) { L.gkey[padded(pos)] = key[e]; L.gid[pos] = i0 + e; }
+                        ++pos;
+                    }
+                cnt += total;
+            });
+            __syncthreads();
+            if (cnt >= big && cnt <= kGatherCap) {
+                const LdsKeySrc gsrc{{}, L.gkey, cnt};
+                RegKeys greg;
+                load_regs(gsrc, greg);
+                st = radix_select(L.sh, phase, gsrc, greg, big);
+                na = select_compact(L.sh, phase, gsrc, greg, st, [&](int pos, int i, uint32_t key) {
+                    if (pos < big) { L.blocks[pos] = L.gid[i]; L.bkey[padded(pos)] = key; }
+                });
+            }
+        } else {
+            load_regs(bsrc, reg);
+        }
+        if (na < 0) {
+            st = radix_select(L.sh, phase, bsrc, reg, big);
+            na = select_compact(L.sh, phase, bsrc, reg, st, [&](int pos, int i, uint32_t key) {
+                if (pos < big) { L.blocks[pos] = i; L.bkey[padded(pos)] = key; }
+            });
+        }
         na = na < big ? na : big;
         __syncthreads();
         cand = L.blocks;
@@ -553,7 +666,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
         if (P > 0) {
             int32_t* po = pool_out + (int64_t)r * P;
             const int small = K < P ? K : P;
-            const LdsKeySrc asrc{L.bkey, na};
+            const LdsKeySrc asrc{{}, L.bkey, na};
             if (na > small) {
                 load_regs(asrc, reg);
                 st = radix_select(L.sh, phase, asrc, reg, small);
@@ -615,7 +728,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
             }
             __syncthreads();
         }
-        const PoolBlockSrc psrc{bm, L.blocks, L.slots, P};
+        const PoolBlockSrc psrc{{}, bm, L.blocks, L.slots, P};
         load_regs(psrc, reg);
         const SelState st = radix_select(L.sh, phase, psrc, reg, K);
         ncb = select_compact(L.sh, phase, psrc, reg, st, [&](int pos, int i, uint32_t) {
@@ -629,7 +742,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
 
     // Top-K among the candidate blocks' entries, written in item order, which
     // is ascending entry order.
-    const CandSrc csrc{sc, cand, cand_slot, ncb, n};
+    const CandSrc csrc{{}, sc, cand, cand_slot, ncb, n};
     load_regs(csrc, reg);
     const SelState st = radix_select(L.sh, phase, csrc, reg, K);
     int32_t* to = topk + (int64_t)r * K;

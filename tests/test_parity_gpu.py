@@ -171,6 +171,17 @@ def test_index_full_all_equal_scores_and_no_pool():
     assert none is None and np.array_equal(topk2, rt)
 
 
+def test_index_full_long_row_all_ties_falls_back():
+    # a long row (more block maxima than the registers hold) whose scores are all equal: the sampled
+    # threshold keeps every block, more than the pre-filter holds, so the full selection runs
+    wl = small_workload([150000, 70000], Hi=8, Di=64)
+    wl.w[0].zero_()
+    topk, pool = gpu_index_full(wl, 0, 300, 2000)
+    rt, rp, _ = oracle_index_rows(wl, 0, [0, 1], 300, 2000)
+    assert np.array_equal(topk, rt) and np.array_equal(pool, rp)
+    assert topk[0].tolist() == list(range(300)) and pool[1].tolist() == list(range(2000))
+
+
 @pytest.mark.parametrize("name,lengths,Hi,Di,K,P,idx", [
     ("ragged_int3", [1, 7, 100, 1000, 4097, 20001], 64, 128, 512, 2048, "int3"),
     ("ties_alphabet", [30000, 17, 8191], 64, 128, 512, 2048, "ties"),
