@@ -389,6 +389,10 @@ __device__ __forceinline__ void for_rounds(const Src& src, const RegKeys& reg, F
         for (int q = 0; q < kPrefetch; ++q) {
             uint32_t key[kE];
             src.finish(rd + q, buf[q], key);
+            // the next fetch reuses buf[q]'s registers only if it stays after
+            // the finish; hoisted, it would land in other registers that the
+            // loop then copies back, waiting for loads still in flight
+            __builtin_amdgcn_sched_barrier(0);
             src.fetch(rd + q + kPrefetch, buf[q]);
             if (rd + q < rounds) f(rd + q, key);
         }
@@ -574,6 +578,64 @@ struct SelectLdsFull : SelectLds {
     int gid[kGatherCap];                      // and their block ids, ascending
 };
 
+// Threshold of the pre-filter of a long Full row (more block maxima than
+// the registers hold): the key of the s-th largest of kRound evenly spaced
+// block maxima, s chosen so that about 2 * big blocks are expected at or
+// above it.  Deterministic, so every workgroup of the row finds the same one.
+__device__ __forceinline__ uint32_t prefilter_threshold(SelShared& sh, int& phase, const float* bm, int nb, int big)
+{
+    const SampleSrc ssrc{{}, bm, nb};
+    RegKeys reg;
+    load_regs(ssrc, reg);
+    int s_target = (int)(((int64_t)2 * big * kRound + nb - 1) / nb);
+    s_target = s_target < 1 ? 1 : s_target;
+    const uint32_t thr = radix_select(sh, phase, ssrc, reg, s_target).prefix;
+    return thr > 1u ? thr : 1u;   // key 0 is an absent item
+}
+
+constexpr int kMaxSlices = 1024;    // slices of kRound block maxima a pre-filtered row may have
+constexpr int kPrefilterRows = 128;  // the separate pre-filter runs below this many rows
+
+// Pre-filter of long Full rows, one workgroup per (slice of kRound block
+// maxima, row): the blocks of the slice whose key is at or above the row's
+// threshold, in block order, go to gkey / gid at the slice's own offset, and
+// their number to gcount.  Rows that fit the registers are left to k_select.
+__global__ __launch_bounds__(kSelThreads) void k_prefilter(const float* __restrict__ bmax, int64_t ld_bmax,
+                                                           const int32_t* __restrict__ row_len, int32_t big,
+                                                           uint32_t* __restrict__ gkey, int32_t* __restrict__ gid,
+                                                           int32_t* __restrict__ gcount, int32_t nslices)
+{
+    __shared__ SelShared sh;
+    const int g = blockIdx.x, r = blockIdx.y;
+    const int n = row_len[r];
+    const int nb = (n + 7) >> 3;
+    const int ns = (nb + kRound - 1) / kRound;
+    if (nb <= kRegRounds * kRound || ns > kMaxSlices || g >= ns) return;   // uniform per workgroup
+    for (int i = threadIdx.x; i < kBins + kBins / 32; i += kSelThreads) sh.hist[i] = 0;
+    int phase = 0;
+    const float* bm = bmax + (int64_t)r * ld_bmax;
+    const uint32_t lo = prefilter_threshold(sh, phase, bm, nb, big);
+    const BlockMaxSrc bsrc{bm, nb};
+    uint32_t key[kE];
+    bsrc.load(g, key);
+    uint32_t hit = 0u;
+#pragma unroll
+    for (int e = 0; e < kE; ++e) hit |= (key[e] >= lo ? 1u : 0u) << e;
+    int before;
+    const int total = block_excl_sum(sh, phase, __builtin_popcount(hit), before);
+    const int64_t base = (int64_t)r * ld_bmax + (int64_t)g * kRound;
+    int pos = before;
+    const int i0 = g * kRound + (int)threadIdx.x * kE;
+#pragma unroll
+    for (int e = 0; e < kE; ++e)
+        if ((hit >> e) & 1u) {
+            gkey[base + pos] = key[e];
+            gid[base + pos] = i0 + e;
+            ++pos;
+        }
+    if (threadIdx.x == 0) gcount[(int64_t)r * nslices + g] = total;
+}
+
 // Block-level reduction of the candidates.  Under the order (score desc,
 // entry id asc) every Top-K entry lies in one of the top-K blocks under the
 // order (block max desc, block id asc): if K blocks precede an entry's block,
@@ -584,7 +646,9 @@ template <bool FULL>
 __global__ __launch_bounds__(kSelThreads) void k_select(
     const float* __restrict__ scores, int64_t ld_scores, const float* __restrict__ bmax,
     int64_t ld_bmax, const int32_t* __restrict__ row_len, const int32_t* __restrict__ pool_in,
-    int32_t K, int32_t P, int32_t* __restrict__ topk, int32_t* __restrict__ pool_out)
+    int32_t K, int32_t P, int32_t* __restrict__ topk, int32_t* __restrict__ pool_out,
+    const uint32_t* __restrict__ gkey_g, const int32_t* __restrict__ gid_g, const int32_t* __restrict__ gcount,
+    int32_t nslices)
 {
     __shared__ typename std::conditional<FULL, SelectLdsFull, SelectLds>::type L;
     const int r = blockIdx.x;
@@ -607,38 +671,63 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
         const BlockMaxSrc bsrc{bm, nb};
         SelState st;
         int na = -1;
-        if (nb > kRegRounds * kRound) {
-            // Long row: every pass over all block maxima re-reads memory, so a
-            // threshold is estimated first from kRound evenly spaced maxima (the
-            // key of the s-th largest sample, s chosen to expect about 2 * big
-            // blocks at or above it), the blocks at or above it are gathered in
-            // block order in one pass, and when that set holds at least `big`
-            // blocks (so the big-th largest key is at or above the threshold
-            // and every block of A is in the set, ties included) and fits, A
-            // is selected from it.  Otherwise the full selection below runs.
-            const SampleSrc ssrc{{}, bm, nb};
-            load_regs(ssrc, reg);
-            int s_target = (int)(((int64_t)2 * big * kRound + nb - 1) / nb);
-            s_target = s_target < 1 ? 1 : s_target;
-            const uint32_t thr = radix_select(L.sh, phase, ssrc, reg, s_target).prefix;
-            load_regs(bsrc, reg);
+        const int ns = (nb + kRound - 1) / kRound;
+        if (nb > kRegRounds * kRound && (!gcount || ns <= kMaxSlices)) {
+            // Long row: every pass over all block maxima re-reads memory, so
+            // the blocks whose key is at or above a sampled threshold are
+            // gathered first, in block order: by k_prefilter, slice by slice
+            // across many workgroups (when the rows are few), or here in one
+            // pass.  When that set holds at least `big` blocks (so the big-th
+            // largest key is at or above the threshold and every block of A is
+            // in the set, ties included) and fits, A is selected from it;
+            // otherwise the full selection below runs.
             int cnt = 0;
-            for_rounds(bsrc, reg, [&](int rd, const uint32_t (&key)[kE]) {
-                int c = 0;
-#pragma unroll
-                for (int e = 0; e < kE; ++e) c += key[e] != 0u && key[e] >= thr ? 1 : 0;
-                int before;
-                const int total = block_excl_sum(L.sh, phase, c, before);
-                int pos = cnt + before;
-                const int i0 = rd * kRound + (int)threadIdx.x * kE;
-#pragma unroll
-                for (int e = 0; e < kE; ++e)
-                    if (key[e] != 0u && key[e] >= thr) {
-                        if (pos < kGatherCap) { L.gkey[padded(pos)] = key[e]; L.gid[pos] = i0 + e; }
-                        ++pos;
+            if (gcount) {
+                int* off = L.blocks;   // slice offsets, ns <= kMaxSlices <= kMaxP
+                for (int c0 = 0; c0 < ns; c0 += kSelThreads) {
+                    const int gi = c0 + (int)threadIdx.x;
+                    const int c = gi < ns ? gcount[(int64_t)r * nslices + gi] : 0;
+                    int before;
+                    const int total = block_excl_sum(L.sh, phase, c, before);
+                    if (gi < ns) off[gi] = cnt + before;
+                    cnt += total;
+                }
+                __syncthreads();
+                if (cnt >= big && cnt <= kGatherCap) {
+                    for (int i = threadIdx.x; i < cnt; i += kSelThreads) {
+                        int lo_s = 0, hi_s = ns - 1;   // last slice whose offset is <= i
+                        while (lo_s < hi_s) {
+                            const int mid = (lo_s + hi_s + 1) >> 1;
+                            if (off[mid] <= i) lo_s = mid;
+                            else hi_s = mid - 1;
+                        }
+                        const int64_t at = (int64_t)r * ld_bmax + (int64_t)lo_s * kRound + (i - off[lo_s]);
+                        L.gkey[padded(i)] = gkey_g[at];
+                        L.gid[i] = gid_g[at];
                     }
-                cnt += total;
-            });
+                }
+            } else {
+                const uint32_t lo = prefilter_threshold(L.sh, phase, bm, nb, big);
+                load_regs(bsrc, reg);
+                for_rounds(bsrc, reg, [&](int rd, const uint32_t (&key)[kE]) {
+                    uint32_t hit = 0u;
+#pragma unroll
+                    for (int e = 0; e < kE; ++e) hit |= (key[e] >= lo ? 1u : 0u) << e;
+                    int before;
+                    const int total = block_excl_sum(L.sh, phase, __builtin_popcount(hit), before);
+                    if (hit != 0u) {   // few blocks pass: most lanes and waves skip the writes
+                        int pos = cnt + before;
+                        const int i0 = rd * kRound + (int)threadIdx.x * kE;
+#pragma unroll
+                        for (int e = 0; e < kE; ++e)
+                            if ((hit >> e) & 1u) {
+                                if (pos < kGatherCap) { L.gkey[padded(pos)] = key[e]; L.gid[pos] = i0 + e; }
+                                ++pos;
+                            }
+                    }
+                    cnt += total;
+                });
+            }
             __syncthreads();
             if (cnt >= big && cnt <= kGatherCap) {
                 const LdsKeySrc gsrc{{}, L.gkey, cnt};
@@ -649,6 +738,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
                     if (pos < big) { L.blocks[pos] = L.gid[i]; L.bkey[padded(pos)] = key; }
                 });
             }
+            if (na < 0 && gcount) load_regs(bsrc, reg);
         } else {
             load_regs(bsrc, reg);
         }
@@ -771,6 +861,10 @@ void launch_score(int HT, int KS, dim3 grid, hipStream_t st, const uint8_t* qI, 
 }
 
 int64_t full_ld(int32_t max_len) { return ((int64_t)max_len + kFullChunk - 1) / kFullChunk * kFullChunk; }
+// Slices of kRound block maxima per row, and whether rows this long use the
+// pre-filter (then the workspace also holds its gathered keys, ids and counts).
+int64_t full_slices(int64_t ld) { return (ld / 8 + kRound - 1) / kRound; }
+bool full_prefilter(int64_t ld) { return ld / 8 > (int64_t)kRegRounds * kRound; }
 int64_t reindex_ld(int32_t P) { return ((int64_t)P * 8 + kReChunk - 1) / kReChunk * kReChunk; }
 
 csa2_status_t check_indexer_dims(const char* who, int32_t R, int32_t Hi, int32_t Di, int32_t K, int32_t block)
@@ -795,7 +889,10 @@ extern "C" size_t csa2_index_full_workspace_bytes(int32_t R, int32_t max_len, in
     (void)K; (void)P; (void)block;
     if (R < 0 || max_len < 0) return 0;
     const int64_t ld = full_ld(max_len);
-    return csa2::align_up((size_t)R * ld * 4, 256) + csa2::align_up((size_t)R * (ld / 8) * 4, 256);
+    size_t b = csa2::align_up((size_t)R * ld * 4, 256) + csa2::align_up((size_t)R * (ld / 8) * 4, 256);
+    if (full_prefilter(ld) && R < kPrefilterRows)
+        b += 2 * csa2::align_up((size_t)R * (ld / 8) * 4, 256) + csa2::align_up((size_t)R * full_slices(ld) * 4, 256);
+    return b;
 }
 
 extern "C" csa2_status_t csa2_index_full(const uint8_t* qI, const float* w, const uint8_t* ikeys,
@@ -822,8 +919,25 @@ extern "C" csa2_status_t csa2_index_full(const uint8_t* qI, const float* w, cons
                  need, workspace_bytes);
     CSA2_REQUIRE(R <= 65535, CSA2_ERR_UNSUPPORTED, "index_full: R=%d > 65535", R);
     const int64_t ld = full_ld(max_len);
-    float* scores = static_cast<float*>(workspace);
-    float* bm = reinterpret_cast<float*>(static_cast<char*>(workspace) + csa2::align_up((size_t)R * ld * 4, 256));
+    char* w8 = static_cast<char*>(workspace);
+    float* scores = reinterpret_cast<float*>(w8);
+    w8 += csa2::align_up((size_t)R * ld * 4, 256);
+    float* bm = reinterpret_cast<float*>(w8);
+    w8 += csa2::align_up((size_t)R * (ld / 8) * 4, 256);
+    uint32_t* gkey = nullptr;
+    int32_t* gid = nullptr;
+    int32_t* gcount = nullptr;
+    const int64_t nslices = full_slices(ld);
+    // The separate pre-filter spreads long rows over many workgroups; with
+    // enough rows to occupy the GPU the selector's own one-pass gather is
+    // cheaper (it samples the threshold once per row instead of once per slice).
+    if (full_prefilter(ld) && R < kPrefilterRows) {
+        gkey = reinterpret_cast<uint32_t*>(w8);
+        w8 += csa2::align_up((size_t)R * (ld / 8) * 4, 256);
+        gid = reinterpret_cast<int32_t*>(w8);
+        w8 += csa2::align_up((size_t)R * (ld / 8) * 4, 256);
+        gcount = reinterpret_cast<int32_t*>(w8);
+    }
     hipStream_t st = csa2::as_stream(stream);
     const int HT = (Hi + 15) / 16, KS = (Di + 127) / 128;
     if (max_len > 0) {
@@ -831,8 +945,13 @@ extern "C" csa2_status_t csa2_index_full(const uint8_t* qI, const float* w, cons
         launch_score<false>(HT, KS, grid, st, qI, w, ikeys, seq_start, row_seq, row_len, nullptr, Hi, Di,
                             0, scores, ld, bm, ld / 8);
     }
+    if (gcount) {
+        const int32_t big = K > P ? K : P;
+        hipLaunchKernelGGL(k_prefilter, dim3((unsigned)nslices, (unsigned)R), dim3(kSelThreads), 0, st, bm, ld / 8,
+                           row_len, big, gkey, gid, gcount, (int32_t)nslices);
+    }
     hipLaunchKernelGGL(k_select<true>, dim3((unsigned)R), dim3(kSelThreads), 0, st, scores, ld, bm, ld / 8,
-                       row_len, nullptr, K, P, topk_idx, pool_blocks);
+                       row_len, nullptr, K, P, topk_idx, pool_blocks, gkey, gid, gcount, (int32_t)nslices);
     return csa2::check_launch("index_full");
 }
 
@@ -872,6 +991,6 @@ extern "C" csa2_status_t csa2_index_reindex(const uint8_t* qI, const float* w, c
     launch_score<true>(HT, KS, grid, st, qI, w, ikeys, seq_start, row_seq, row_len, pool_blocks, Hi, Di, P,
                        scores, ld, bm, ld / 8);
     hipLaunchKernelGGL(k_select<false>, dim3((unsigned)R), dim3(kSelThreads), 0, st, scores, ld, bm, ld / 8,
-                       row_len, pool_blocks, K, P, topk_idx, nullptr);
+                       row_len, pool_blocks, K, P, topk_idx, nullptr, nullptr, nullptr, nullptr, 0);
     return csa2::check_launch("index_reindex");
 }
