@@ -103,6 +103,27 @@ def build(cfg, dev):
     return wl, step
 
 
+def build_paged(cfg, wl, step, page_rows):
+    """The same step over a paged copy of the caches: pages of `page_rows`
+    entries in shuffled order, and (decode) each row's SWA window stored as a
+    ring with a seeded head."""
+    from sparse_attention_fp4_amd.step import CSA2Step
+    lay = workloads.paged_layout(wl.lengths, page_rows, cfg.seed + 7, device="cuda")
+    codes, scales, ikeys = (workloads.to_pages(lay, t) for t in (step.codes, step.scales, step.ikeys))
+    new_rows = lay.dst[wl.new_rows] if wl.new_rows is not None else None
+    swa, head = wl.swa, None
+    if not cfg.prefill_rows and cfg.W > 0:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(cfg.seed + 8)
+        head = torch.randint(0, cfg.W, (wl.R,), generator=g, device="cuda", dtype=torch.int32)
+        swa = {l: workloads.swa_ring(t, wl.swa_row_start, cfg.W, head) for l, t in wl.swa.items()}
+    return CSA2Step(list(cfg.layers), codes=codes, scales=scales, ikeys=ikeys, seq_start=None,
+                    row_seq=wl.row_seq, row_len=wl.row_len, max_len=step.max_len, new_kv=step.new_kv,
+                    new_rows=new_rows, qI=wl.qI, w=wl.w, q=wl.q, swa=swa, swa_row_start=wl.swa_row_start,
+                    swa_len=wl.swa_len, W=cfg.W, K=cfg.K, P=cfg.P, softmax_scale=step.scale,
+                    block_table=lay.block_table, page_rows=page_rows, swa_head=head)
+
+
 def graph_of(fn, reps=1):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -135,6 +156,8 @@ def per_call_times(step, reps=10):
     import sparse_attention_fp4_amd as csa2
     out = {}
     l_full = step.modes.index("F")
+    if step.paged:
+        return paged_call_times(step, reps)
     calls = {
         "quantize_append": lambda: csa2.csa2_quantize_append(step.new_kv, step.new_rows, step.codes, step.scales),
         "index_full": lambda: csa2.csa2_index_full(
@@ -156,6 +179,36 @@ def per_call_times(step, reps=10):
         g = graph_of(fn, reps=reps)
         time_graph(g, 2, reps)
         out[name] = time_graph(g, 5, reps) * 1000.0   # us per call
+    return out
+
+
+def paged_call_times(step, reps=10):
+    """per_call_times for a step in paged mode."""
+    import sparse_attention_fp4_amd as csa2
+    l_full = step.modes.index("F")
+    bt, pr = step.block_table, step.page_rows
+    calls = {
+        "quantize_append": lambda: csa2.csa2_quantize_append(step.new_kv, step.new_rows, step.codes, step.scales),
+        "index_full_paged": lambda: csa2.csa2_index_full_paged(
+            step.qI[l_full], step.w[l_full], step.ikeys, bt, pr, step.row_seq, step.row_len, step.max_len, step.K,
+            step.P, step.block, topk_idx=step.topk[l_full], pool_blocks=step.pool, topk_rows=step.phys[l_full],
+            workspace=step.workspace),
+    }
+    if "R" in step.modes:
+        lr = step.modes.index("R")
+        calls["index_reindex_paged"] = lambda: csa2.csa2_index_reindex_paged(
+            step.qI[lr], step.w[lr], step.ikeys, bt, pr, step.row_seq, step.row_len, step.pool, step.K, step.block,
+            topk_idx=step.topk[lr], topk_rows=step.phys[lr], workspace=step.workspace)
+    lu = len(step.modes) - 1
+    calls["sparse_attn_phys"] = lambda: csa2.csa2_sparse_attn_phys(
+        step.q[lu], step.codes, step.scales, step.phys[step.parents[lu]], step.swa[lu], step.swa_row_start,
+        step.swa_len, step.W, step.scale, swa_head=step.swa_head, out=step.out[lu], lse=step.lse[lu],
+        workspace=step.workspace)
+    out = {}
+    for name, fn in calls.items():
+        g = graph_of(fn, reps=reps)
+        time_graph(g, 2, reps)
+        out[name] = time_graph(g, 5, reps) * 1000.0
     return out
 
 
@@ -259,6 +312,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
     ap.add_argument("--copy-check", action="store_true", help="also time a plain 1 GiB device copy")
+    ap.add_argument("--page-rows", type=int, default=64, help="also time the step over a paged copy of the "
+                                                               "caches with pages of this many entries (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
@@ -333,6 +388,24 @@ def main():
     log("bench: cold-cache steps")
     cold_ms = cold_step_ms(g, min(args.steps, 10))
     extra = {}
+    if args.page_rows > 0:
+        log(f"bench: paged step ({args.page_rows} entries per page)")
+        pstep = build_paged(cfg, wl, step, args.page_rows)
+        for _ in range(max(args.warmup, 1)):
+            pstep.run()
+        pg = graph_of(pstep.run)
+        time_graph(pg, 2)
+        pms = time_graph(pg, args.steps)
+        extra["paged"] = {
+            "page_rows": args.page_rows,
+            "swa": "ring, seeded heads" if pstep.swa_head is not None else "packed",
+            "ms_per_step": round(pms, 4),
+            "value": round((cfg.prefill_rows or R) / (pms / 1000.0), 1),
+            "per_call_us": ({k: round(v, 2) for k, v in per_call_times(pstep).items()}
+                            if not args.no_breakdown else {}),
+        }
+        del pstep, pg
+        torch.cuda.empty_cache()
     if args.copy_check:
         extra["copy_check"] = copy_check()
 

@@ -183,6 +183,85 @@ csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* codes, const ui
                                int32_t W, float softmax_scale, float* out, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------- */
+/* Paged main cache and SWA ring.  The pages fix only what is cached (FP4    */
+/* main KV, FP8 SWA window, FP8 indexer keys; section 一 of the teardown);   */
+/* how a server lays those rows out is left open.  These calls compute       */
+/* exactly what the packed calls above compute, with different addressing.  */
+/* ---------------------------------------------------------------------- */
+/*
+ * Paged addressing, shared by the calls below:
+ *   block_table [S, max_pages] int32; page_rows a power of two in [8, 2^20].
+ *   Entry j of sequence s lives in cache row
+ *       block_table[s, j / page_rows] * page_rows + j % page_rows.
+ *   An entry whose page index is >= max_pages, whose table value is negative,
+ *   or whose row is >= cache_rows is not visible: it scores -inf, is never
+ *   selected, and counts as absent in its block (as an entry past row_len).
+ *   Visible entries need not be contiguous in the cache; pages may be shared.
+ *   row_seq[r] must be in [0, S) (not checkable on the host).
+ *
+ * csa2_index_full_paged / csa2_index_reindex_paged: csa2_index_full /
+ * csa2_index_reindex with `ikeys` [cache_rows, Di] addressed through the block
+ * table instead of seq_start.  Outputs are identical to those of the packed
+ * calls on a packed copy of the visible entries.  topk_rows [R, K] int32 (may
+ * be NULL) also receives the cache row of each Top-K entry, -1 padded (what
+ * csa2_paged_rows gives for topk_idx), ready for csa2_sparse_attn_phys.
+ * Workspace sizes are those of the packed calls; every other argument and
+ * limit is unchanged.
+ */
+csa2_status_t csa2_index_full_paged(const uint8_t* qI, const float* w, const uint8_t* ikeys,
+                                    int64_t cache_rows, const int32_t* block_table,
+                                    int32_t max_pages, int32_t page_rows,
+                                    const int32_t* row_seq, const int32_t* row_len,
+                                    int32_t R, int32_t Hi, int32_t Di, int32_t max_len,
+                                    int32_t K, int32_t P, int32_t block,
+                                    int32_t* topk_idx, int32_t* topk_rows, int32_t* pool_blocks,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+csa2_status_t csa2_index_reindex_paged(const uint8_t* qI, const float* w, const uint8_t* ikeys,
+                                       int64_t cache_rows, const int32_t* block_table,
+                                       int32_t max_pages, int32_t page_rows,
+                                       const int32_t* row_seq, const int32_t* row_len,
+                                       const int32_t* pool_blocks, int32_t R, int32_t Hi,
+                                       int32_t Di, int32_t K, int32_t P, int32_t block,
+                                       int32_t* topk_idx, int32_t* topk_rows,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Translate index lists into cache rows (for lists the paged index calls did
+ * not produce):
+ *   phys[r, k] = cache row of entry idx[r, k] of sequence row_seq[r], or -1
+ *   when idx[r, k] is -1, outside [0, row_len[r]), or not visible.
+ *   idx, phys [R, K] int32 (phys may not alias idx).  The order of idx is kept.
+ * Limits: R, K >= 0; cache rows above 2^31 - 1 map to -1.
+ */
+csa2_status_t csa2_paged_rows(const int32_t* block_table, int32_t max_pages, int32_t page_rows,
+                              int64_t cache_rows, const int32_t* row_seq, const int32_t* row_len,
+                              const int32_t* idx, int32_t R, int32_t K, int32_t* phys,
+                              void* stream);
+
+/*
+ * csa2_sparse_attn over cache rows: the main key set of row r is
+ *   { deq(cache row c) : c in phys_idx[r, :], 0 <= c < cache_rows },
+ * with codes [cache_rows, D/2] and scales [cache_rows, D/16].  Use
+ * csa2_paged_rows to build phys_idx from a Top-K list.  With swa_head == NULL
+ * the window is as in csa2_sparse_attn.  With swa_head [R] int32 the window of
+ * row r is a ring of W rows starting at swa_row_start[r]: its i-th oldest row
+ * (i < min(swa_len[r], W)) sits in slot (swa_head[r] + i) mod W, so the caller
+ * overwrites slot (head + len) mod W on append instead of moving rows.
+ * All W slots of a ring must lie inside `swa`.
+ * The keys are the packed call's (window unrolled), taken in the same order
+ * through the same arithmetic, so results are bit-identical to csa2_sparse_attn
+ * on a packed copy.  Workspace and limits as csa2_sparse_attn, plus
+ * cache_rows * D / 2 < 2^31.
+ */
+csa2_status_t csa2_sparse_attn_phys(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                                    int64_t cache_rows, const int32_t* phys_idx, int32_t K,
+                                    const uint8_t* swa, const int64_t* swa_row_start,
+                                    const int32_t* swa_len, const int32_t* swa_head, int32_t R,
+                                    int32_t H, int32_t D, int32_t W, float softmax_scale,
+                                    float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,8 @@ STATUS = {0: "CSA2_OK", 1: "CSA2_ERR_NULL", 2: "CSA2_ERR_SHAPE", 3: "CSA2_ERR_UN
 EXPORTS = ("csa2_status_string", "csa2_last_error", "csa2_abi_version", "csa2_quantize_append",
            "csa2_index_full_workspace_bytes", "csa2_index_full",
            "csa2_index_reindex_workspace_bytes", "csa2_index_reindex",
-           "csa2_sparse_attn_workspace_bytes", "csa2_sparse_attn")
+           "csa2_sparse_attn_workspace_bytes", "csa2_sparse_attn",
+           "csa2_index_full_paged", "csa2_index_reindex_paged", "csa2_paged_rows", "csa2_sparse_attn_phys")
 
 _lib = None
 
@@ -62,7 +63,15 @@ def lib() -> ctypes.CDLL:
         L.csa2_sparse_attn_workspace_bytes.restype = sz
         L.csa2_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, P, P, P, i32, i32, i32, i32, f32, P, P, P,
                                        sz, P]
-        for f in ("csa2_quantize_append", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn"):
+        L.csa2_index_full_paged.argtypes = [P, P, P, i64, P, i32, i32, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                            P, P, P, P, sz, P]
+        L.csa2_index_reindex_paged.argtypes = [P, P, P, i64, P, i32, i32, P, P, P, i32, i32, i32, i32, i32, i32, P,
+                                               P, P, sz, P]
+        L.csa2_paged_rows.argtypes = [P, i32, i32, i64, P, P, P, i32, i32, P, P]
+        L.csa2_sparse_attn_phys.argtypes = [P, P, P, i64, P, i32, P, P, P, P, i32, i32, i32, i32, f32, P, P, P,
+                                            sz, P]
+        for f in ("csa2_quantize_append", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
+                  "csa2_index_full_paged", "csa2_index_reindex_paged", "csa2_paged_rows", "csa2_sparse_attn_phys"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -252,4 +261,155 @@ def csa2_sparse_attn(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
                                 R, H, D, W, float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws),
                                 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
     _check("csa2_sparse_attn", st)
+    return out, lse
+
+
+# ----------------------------------------------------------------- paged cache
+
+def _pages(block_table: torch.Tensor, page_rows: int) -> int:
+    _dev(block_table, "block_table", torch.int32, 2)
+    if page_rows < 8 or page_rows & (page_rows - 1):
+        raise ValueError("page_rows must be a power of two >= 8")
+    return block_table.shape[1]
+
+
+def csa2_index_full_paged(qI: torch.Tensor, w: torch.Tensor, ikeys: torch.Tensor, block_table: torch.Tensor,
+                          page_rows: int, row_seq: torch.Tensor, row_len: torch.Tensor, max_len: int, K: int,
+                          P: int, block: int = 8, topk_idx: Optional[torch.Tensor] = None,
+                          pool_blocks: Optional[torch.Tensor] = None, want_pool: bool = True,
+                          topk_rows: Optional[torch.Tensor] = None, want_rows: bool = False,
+                          workspace: Optional[torch.Tensor] = None, stream=None):
+    """csa2_index_full over a paged key cache: entry j of sequence s is cache row
+    block_table[s, j // page_rows] * page_rows + j % page_rows.  Returns
+    (topk_idx, pool_blocks, topk_rows); topk_rows (the cache rows of the Top-K
+    entries) is None unless given or want_rows."""
+    qI = _dev(_u8(qI), "qI", torch.uint8, 3)
+    R, Hi, Di = qI.shape
+    _dev(w, "w", torch.float32, 2)
+    ikeys = _dev(_u8(ikeys), "ikeys", torch.uint8, 2)
+    max_pages = _pages(block_table, page_rows)
+    _dev(row_seq, "row_seq", torch.int32, 1)
+    _dev(row_len, "row_len", torch.int32, 1)
+    if tuple(w.shape) != (R, Hi) or ikeys.shape[1] != Di or row_seq.shape[0] != R or row_len.shape[0] != R:
+        raise ValueError("shape mismatch among qI, w, ikeys, row_seq, row_len")
+    dev = qI.device
+    if topk_idx is None:
+        topk_idx = torch.empty(R, K, dtype=torch.int32, device=dev)
+    _dev(topk_idx, "topk_idx", torch.int32, 2)
+    if want_pool and P > 0 and pool_blocks is None:
+        pool_blocks = torch.empty(R, P, dtype=torch.int32, device=dev)
+    if want_rows and topk_rows is None:
+        topk_rows = torch.empty(R, K, dtype=torch.int32, device=dev)
+    if topk_rows is not None:
+        _dev(topk_rows, "topk_rows", torch.int32, 2)
+        if tuple(topk_rows.shape) != (R, K):
+            raise ValueError("topk_rows must be [R, K]")
+    Pc = P if pool_blocks is not None else 0
+    ws = _workspace(csa2_index_full_workspace_bytes(R, max_len, K, Pc, block), dev, workspace)
+    st = lib().csa2_index_full_paged(_ptr(qI), _ptr(w), _ptr(ikeys), ikeys.shape[0], _ptr(block_table), max_pages,
+                                     page_rows, _ptr(row_seq), _ptr(row_len), R, Hi, Di, max_len, K, Pc, block,
+                                     _ptr(topk_idx), _ptr(topk_rows), _ptr(pool_blocks), _ptr(ws),
+                                     0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check("csa2_index_full_paged", st)
+    return topk_idx, pool_blocks, topk_rows
+
+
+def csa2_index_reindex_paged(qI: torch.Tensor, w: torch.Tensor, ikeys: torch.Tensor, block_table: torch.Tensor,
+                             page_rows: int, row_seq: torch.Tensor, row_len: torch.Tensor,
+                             pool_blocks: torch.Tensor, K: int, block: int = 8,
+                             topk_idx: Optional[torch.Tensor] = None, topk_rows: Optional[torch.Tensor] = None,
+                             want_rows: bool = False, workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """csa2_index_reindex over a paged key cache (addressing as
+    csa2_index_full_paged).  Returns (topk_idx, topk_rows)."""
+    qI = _dev(_u8(qI), "qI", torch.uint8, 3)
+    R, Hi, Di = qI.shape
+    _dev(w, "w", torch.float32, 2)
+    ikeys = _dev(_u8(ikeys), "ikeys", torch.uint8, 2)
+    max_pages = _pages(block_table, page_rows)
+    _dev(row_seq, "row_seq", torch.int32, 1)
+    _dev(row_len, "row_len", torch.int32, 1)
+    _dev(pool_blocks, "pool_blocks", torch.int32, 2)
+    P = pool_blocks.shape[1]
+    if tuple(w.shape) != (R, Hi) or ikeys.shape[1] != Di or pool_blocks.shape[0] != R:
+        raise ValueError("shape mismatch among qI, w, ikeys, pool_blocks")
+    dev = qI.device
+    if topk_idx is None:
+        topk_idx = torch.empty(R, K, dtype=torch.int32, device=dev)
+    _dev(topk_idx, "topk_idx", torch.int32, 2)
+    if want_rows and topk_rows is None:
+        topk_rows = torch.empty(R, K, dtype=torch.int32, device=dev)
+    if topk_rows is not None:
+        _dev(topk_rows, "topk_rows", torch.int32, 2)
+        if tuple(topk_rows.shape) != (R, K):
+            raise ValueError("topk_rows must be [R, K]")
+    ws = _workspace(csa2_index_reindex_workspace_bytes(R, K, P, block), dev, workspace)
+    st = lib().csa2_index_reindex_paged(_ptr(qI), _ptr(w), _ptr(ikeys), ikeys.shape[0], _ptr(block_table),
+                                        max_pages, page_rows, _ptr(row_seq), _ptr(row_len), _ptr(pool_blocks), R,
+                                        Hi, Di, K, P, block, _ptr(topk_idx), _ptr(topk_rows), _ptr(ws),
+                                        0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check("csa2_index_reindex_paged", st)
+    return topk_idx, topk_rows
+
+
+def csa2_paged_rows(block_table: torch.Tensor, page_rows: int, cache_rows: int, row_seq: torch.Tensor,
+                    row_len: torch.Tensor, idx: torch.Tensor, phys: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Cache rows [R, K] of the entries of index lists idx [R, K] over a paged cache (-1: none)."""
+    max_pages = _pages(block_table, page_rows)
+    _dev(row_seq, "row_seq", torch.int32, 1)
+    _dev(row_len, "row_len", torch.int32, 1)
+    _dev(idx, "idx", torch.int32, 2)
+    R, K = idx.shape
+    if row_seq.shape[0] != R or row_len.shape[0] != R:
+        raise ValueError("shape mismatch among idx, row_seq, row_len")
+    if phys is None:
+        phys = torch.empty(R, K, dtype=torch.int32, device=idx.device)
+    _dev(phys, "phys", torch.int32, 2)
+    st = lib().csa2_paged_rows(_ptr(block_table), max_pages, page_rows, int(cache_rows), _ptr(row_seq),
+                               _ptr(row_len), _ptr(idx), R, K, _ptr(phys), _stream(stream))
+    _check("csa2_paged_rows", st)
+    return phys
+
+
+def csa2_sparse_attn_phys(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, phys_idx: torch.Tensor,
+                          swa: Optional[torch.Tensor], swa_row_start: Optional[torch.Tensor],
+                          swa_len: Optional[torch.Tensor], W: int, softmax_scale: float,
+                          swa_head: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                          workspace: Optional[torch.Tensor] = None,
+                          stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """csa2_sparse_attn over cache rows (phys_idx from csa2_paged_rows), with an
+    optional SWA ring: window row i of row r in slot (swa_head[r] + i) % W."""
+    if q.dtype == torch.bfloat16:
+        q = q.view(torch.int16)
+    _dev(q, "q", torch.int16, 3)
+    R, H, D = q.shape
+    _dev(codes, "codes", torch.uint8, 2)
+    _dev(scales, "scales", torch.uint8, 2)
+    _dev(phys_idx, "phys_idx", torch.int32, 2)
+    K = phys_idx.shape[1]
+    if codes.shape[1] * 2 != D or scales.shape[1] * 16 != D or phys_idx.shape[0] != R:
+        raise ValueError("shape mismatch among q, codes, scales, phys_idx")
+    if W > 0:
+        swa = _dev(_u8(swa), "swa", torch.uint8, 2)
+        _dev(swa_row_start, "swa_row_start", torch.int64, 1)
+        _dev(swa_len, "swa_len", torch.int32, 1)
+        if swa_head is not None:
+            _dev(swa_head, "swa_head", torch.int32, 1)
+        if swa.shape[1] != D:
+            raise ValueError("swa rows must have D channels")
+    dev = q.device
+    if out is None:
+        out = torch.empty(R, H, D, dtype=torch.float32, device=dev)
+    _dev(out, "out", torch.float32, 3)
+    if want_lse and lse is None:
+        lse = torch.empty(R, H, dtype=torch.float32, device=dev)
+    ws = _workspace(csa2_sparse_attn_workspace_bytes(R, H, D, K, W), dev, workspace)
+    st = lib().csa2_sparse_attn_phys(_ptr(q), _ptr(codes), _ptr(scales), codes.shape[0], _ptr(phys_idx), K,
+                                     _ptr(swa if W > 0 else None), _ptr(swa_row_start if W > 0 else None),
+                                     _ptr(swa_len if W > 0 else None), _ptr(swa_head if W > 0 else None), R, H,
+                                     D, W, float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                     0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
+    _check("csa2_sparse_attn_phys", st)
     return out, lse

@@ -398,15 +398,18 @@ struct AttnSmem {
     static constexpr int kBytes = kLoop > kMerge ? kLoop : kMerge;
 };
 
-template <int HT, int D, int CS>
+// PG: the index lists hold cache rows (paged caches) and the SWA window may be
+// a ring; the packed form is a separate instantiation so that it carries none
+// of that addressing.
+template <int HT, int D, int CS, bool PG>
 __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const int64_t* __restrict__ seq_start, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ topk, int32_t K,
     const uint8_t* __restrict__ swa, const int64_t* __restrict__ swa_row_start,
-    const int32_t* __restrict__ swa_len, int32_t R, int32_t H, int32_t W, float scale_log2e, int32_t HG,
-    int32_t S, int32_t nfrag, float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_ml)
+    const int32_t* __restrict__ swa_len, const int32_t* __restrict__ swa_head, int64_t phys_rows, int32_t R,
+    int32_t H, int32_t W, float scale_log2e, int32_t HG, int32_t S, int32_t nfrag, float* __restrict__ out,
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml)
 {
     using SM = AttnSmem<HT, D, CS>;
     constexpr int KS = SM::KS;
@@ -445,9 +448,17 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     // fragments' Top-K entries, the wave's quarter of the query, then the
     // first fragment's key bytes, which arrive during the barriers that share
     // the query.
-    const int n = row_len[r];
-    const int seq = row_seq[r];
+    // PG: the index lists hold cache rows directly (paged caches),
+    // checked against the cache size; otherwise entries of the row's sequence.
+    const int n = PG ? (int)(phys_rows < 0x7FFFFFFF ? phys_rows : 0x7FFFFFFF) : row_len[r];
+    const int seq = PG ? 0 : row_seq[r];
     int nsw = W > 0 ? swa_len[r] : 0;
+    // SWA ring: window row i sits in slot (head + i) mod W of the row's W slots
+    int head = 0;
+    if constexpr (PG) {
+        head = W > 0 && swa_head ? swa_head[r] % W : 0;
+        head = head < 0 ? head + W : head;
+    }
     const int64_t swa0 = W > 0 ? swa_row_start[r] : 0;
     // Top-K entry of the lane's key in a fragment; SWA slots are left as they
     // are (the key loads never read them), and no select on the loaded value
@@ -479,7 +490,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
         }
     }
     nsw = nsw < 0 ? 0 : (nsw > W ? W : nsw);
-    const int64_t base = seq_start[seq];
+    const int64_t base = PG ? 0 : seq_start[seq];
     // Max |q| of each head over the wave's pieces: an integer max of the bf16
     // magnitude bits (two per instruction), then over the lane groups.
 #pragma unroll
@@ -537,13 +548,14 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     const int nb = n < 0 ? 0 : (n > 0x7FFFFFFF / (D / 2) ? 0x7FFFFFFF / (D / 2) : n);
     const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(codes + base * (D / 2), nb * (D / 2));
     const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales + base * (D / 16), nb * (D / 16));
-    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(W > 0 ? swa + swa0 * D : swa, nsw * D);   // empty when W == 0
+    const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(W > 0 ? swa + swa0 * D : swa, (PG && swa_head ? W : nsw) * D);   // empty when W == 0
     const int Kp = pad_topk(K);
     auto load_frag = [&](FragRaw<D>& f, int fr_, int j) {
         const int slot = fr_ * kFrag + col, i = slot - Kp;
         const bool vm = slot < K && j >= 0 && j < nb;
         const bool vs = i >= 0 && i < nsw;
-        f.load(frag_kind(fr_, Kp), vm, j, vs, i, p, hf, rc, rs, rw);
+        const int iw = PG ? (head + i >= W ? head + i - W : head + i) : i;
+        f.load(frag_kind(fr_, Kp), vm, j, vs, iw, p, hf, rc, rs, rw);
     };
     FragRaw<D> cur, nxt;   // cur is unpaired in place at the start of its fragment
     if (fr < f_end) load_frag(cur, fr, idx_c);
@@ -860,17 +872,50 @@ AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
     return p;
 }
 
-template <int HT, int D, int CS>
+template <int HT, int D, int CS, bool PG>
 void launch_attn(dim3 grid, hipStream_t st, const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
                  const int64_t* seq_start, const int32_t* row_seq, const int32_t* row_len, const int32_t* topk,
-                 int32_t K, const uint8_t* swa, const int64_t* swa_row_start, const int32_t* swa_len, int32_t H,
-                 int32_t R, int32_t W, float sl2e, int HG, int S, int nfrag, float* out, float* lse, float* po,
-                 float* pml)
+                 int32_t K, const uint8_t* swa, const int64_t* swa_row_start, const int32_t* swa_len,
+                 const int32_t* swa_head, int64_t phys_rows, int32_t H, int32_t R, int32_t W, float sl2e, int HG,
+                 int S, int nfrag, float* out, float* lse, float* po, float* pml)
 {
-    hipLaunchKernelGGL((k_sparse_attn<HT, D, CS>), grid, dim3(64 * kWaves), 0, st, q, codes, scales, seq_start, row_seq,
-                       row_len, topk, K, swa, swa_row_start, swa_len, R, H, W, sl2e, HG, S, nfrag, out, lse, po,
-                       pml);
+    hipLaunchKernelGGL((k_sparse_attn<HT, D, CS, PG>), grid, dim3(64 * kWaves), 0, st, q, codes, scales, seq_start, row_seq,
+                       row_len, topk, K, swa, swa_row_start, swa_len, swa_head, phys_rows, R, H, W, sl2e, HG, S,
+                       nfrag, out, lse, po, pml);
 }
+
+// Cache rows of the entries of index lists over a paged cache: entry j of the
+// row's sequence is in row bt[s * max_pages + j / page] * page + j % page;
+// -1 for absent entries, entries outside [0, row_len) and pages outside the
+// cache.
+__global__ __launch_bounds__(256) void k_paged_rows(const int32_t* __restrict__ bt, int32_t max_pages, int32_t shift,
+                                                    int64_t cache_rows, const int32_t* __restrict__ row_seq,
+                                                    const int32_t* __restrict__ row_len,
+                                                    const int32_t* __restrict__ idx, int32_t R, int32_t K,
+                                                    int32_t* __restrict__ phys)
+{
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= (int64_t)R * K) return;
+    const int r = (int)(e / K);
+    const int j = idx[e];
+    int32_t out = -1;
+    if (j >= 0 && j < row_len[r]) {
+        const int page = j >> shift;
+        if (page < max_pages) {
+            const int64_t pid = bt[(int64_t)row_seq[r] * max_pages + page];
+            const int64_t row = (pid << shift) | (j & ((1 << shift) - 1));
+            if (pid >= 0 && row < cache_rows && row <= 0x7FFFFFFF) out = (int32_t)row;
+        }
+    }
+    phys[e] = out;
+}
+
+csa2_status_t sparse_attn_impl(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                               const int64_t* seq_start, const int32_t* row_seq, const int32_t* row_len,
+                               int64_t phys_rows, const int32_t* topk_idx, int32_t K, const uint8_t* swa,
+                               const int64_t* swa_row_start, const int32_t* swa_len, const int32_t* swa_head,
+                               int32_t R, int32_t H, int32_t D, int32_t W, float softmax_scale, float* out,
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 }  // namespace
 
@@ -882,13 +927,13 @@ extern "C" size_t csa2_sparse_attn_workspace_bytes(int32_t R, int32_t H, int32_t
     return csa2::align_up((size_t)R * p.S * H * D * 4, 256) + csa2::align_up((size_t)R * p.S * H * 4 * 4, 256);
 }
 
-extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
-                                          const int64_t* seq_start, const int32_t* row_seq,
-                                          const int32_t* row_len, const int32_t* topk_idx, int32_t K,
-                                          const uint8_t* swa, const int64_t* swa_row_start,
-                                          const int32_t* swa_len, int32_t R, int32_t H, int32_t D, int32_t W,
-                                          float softmax_scale, float* out, float* lse, void* workspace,
-                                          size_t workspace_bytes, void* stream)
+namespace {
+csa2_status_t sparse_attn_impl(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                               const int64_t* seq_start, const int32_t* row_seq, const int32_t* row_len,
+                               int64_t phys_rows, const int32_t* topk_idx, int32_t K, const uint8_t* swa,
+                               const int64_t* swa_row_start, const int32_t* swa_len, const int32_t* swa_head,
+                               int32_t R, int32_t H, int32_t D, int32_t W, float softmax_scale, float* out,
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream)
 {
     CSA2_REQUIRE(R >= 0, CSA2_ERR_SHAPE, "sparse_attn: R=%d < 0", R);
     CSA2_REQUIRE(H >= 1, CSA2_ERR_SHAPE, "sparse_attn: H=%d < 1", H);
@@ -899,7 +944,7 @@ extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* code
     CSA2_REQUIRE(K >= 0 && W >= 0, CSA2_ERR_SHAPE, "sparse_attn: K=%d, W=%d must be >= 0", K, W);
     CSA2_REQUIRE(K <= 4096 && W <= 4096, CSA2_ERR_UNSUPPORTED, "sparse_attn: K=%d or W=%d > 4096", K, W);
     if (R == 0) return CSA2_OK;
-    CSA2_REQUIRE(q && codes && scales && seq_start && row_seq && row_len && out, CSA2_ERR_NULL,
+    CSA2_REQUIRE(q && codes && scales && out && (phys_rows > 0 || (seq_start && row_seq && row_len)), CSA2_ERR_NULL,
                  "sparse_attn: NULL pointer argument");
     CSA2_REQUIRE(K == 0 || topk_idx, CSA2_ERR_NULL, "sparse_attn: topk_idx is NULL with K > 0");
     CSA2_REQUIRE(W == 0 || (swa && swa_row_start && swa_len), CSA2_ERR_NULL,
@@ -927,8 +972,9 @@ extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* code
     const dim3 grid((unsigned)xcd_grid(R, p.HG * p.CS * p.S));
 #define CSA2_ATTN(ht, d, cs)                                                                               \
     if (p.HT == ht && D == d && p.CS == cs) {                                                               \
-        launch_attn<ht, d, cs>(grid, st, q, codes, scales, seq_start, row_seq, row_len, topk_idx, K, swa,   \
-                               swa_row_start, swa_len, H, R, W, sl2e, p.HG, p.S, p.nfrag, out, lse, po, pml); \
+        (phys_rows > 0 ? launch_attn<ht, d, cs, true> : launch_attn<ht, d, cs, false>)(grid, st, q, codes, scales, seq_start, row_seq, row_len, topk_idx, K, swa,   \
+                               swa_row_start, swa_len, swa_head, phys_rows, H, R, W, sl2e, p.HG, p.S, p.nfrag, \
+                               out, lse, po, pml);                                                          \
     }
     CSA2_ATTN(1, 128, 1) CSA2_ATTN(2, 128, 1) CSA2_ATTN(4, 128, 1) CSA2_ATTN(1, 128, 2)
     CSA2_ATTN(1, 256, 1) CSA2_ATTN(2, 256, 1) CSA2_ATTN(1, 256, 2)
@@ -938,4 +984,51 @@ extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* code
         hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)xcd_grid(R, H)), dim3(128), 0, st, po, pml, R, H, D, p.S,
                            out, lse);
     return csa2::check_launch("sparse_attn");
+}
+}  // namespace
+
+extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                                          const int64_t* seq_start, const int32_t* row_seq,
+                                          const int32_t* row_len, const int32_t* topk_idx, int32_t K,
+                                          const uint8_t* swa, const int64_t* swa_row_start,
+                                          const int32_t* swa_len, int32_t R, int32_t H, int32_t D, int32_t W,
+                                          float softmax_scale, float* out, float* lse, void* workspace,
+                                          size_t workspace_bytes, void* stream)
+{
+    return sparse_attn_impl(q, codes, scales, seq_start, row_seq, row_len, 0, topk_idx, K, swa, swa_row_start, swa_len,
+                            nullptr, R, H, D, W, softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" csa2_status_t csa2_sparse_attn_phys(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                                               int64_t cache_rows, const int32_t* phys_idx, int32_t K,
+                                               const uint8_t* swa, const int64_t* swa_row_start,
+                                               const int32_t* swa_len, const int32_t* swa_head, int32_t R, int32_t H,
+                                               int32_t D, int32_t W, float softmax_scale, float* out, float* lse,
+                                               void* workspace, size_t workspace_bytes, void* stream)
+{
+    CSA2_REQUIRE(cache_rows >= 1, CSA2_ERR_SHAPE, "sparse_attn_phys: cache_rows=%lld < 1", (long long)cache_rows);
+    CSA2_REQUIRE(D < 16 || cache_rows <= 0x7FFFFFFF / (D / 2), CSA2_ERR_UNSUPPORTED,
+                 "sparse_attn_phys: codes beyond 2^31 bytes (cache_rows=%lld)", (long long)cache_rows);
+    return sparse_attn_impl(q, codes, scales, nullptr, nullptr, nullptr, cache_rows, phys_idx, K, swa, swa_row_start,
+                            swa_len, swa_head, R, H, D, W, softmax_scale, out, lse, workspace, workspace_bytes,
+                            stream);
+}
+
+extern "C" csa2_status_t csa2_paged_rows(const int32_t* block_table, int32_t max_pages, int32_t page_rows,
+                                         int64_t cache_rows, const int32_t* row_seq, const int32_t* row_len,
+                                         const int32_t* idx, int32_t R, int32_t K, int32_t* phys, void* stream)
+{
+    CSA2_REQUIRE(R >= 0 && K >= 0, CSA2_ERR_SHAPE, "paged_rows: R=%d, K=%d must be >= 0", R, K);
+    CSA2_REQUIRE(max_pages >= 1, CSA2_ERR_SHAPE, "paged_rows: max_pages=%d < 1", max_pages);
+    CSA2_REQUIRE(cache_rows >= 1, CSA2_ERR_SHAPE, "paged_rows: cache_rows=%lld < 1", (long long)cache_rows);
+    CSA2_REQUIRE(page_rows >= 8 && page_rows <= (1 << 20) && (page_rows & (page_rows - 1)) == 0,
+                 CSA2_ERR_UNSUPPORTED, "paged_rows: page_rows=%d must be a power of two in [8, 2^20]", page_rows);
+    if ((int64_t)R * K == 0) return CSA2_OK;
+    CSA2_REQUIRE(block_table && row_seq && row_len && idx && phys, CSA2_ERR_NULL, "paged_rows: NULL pointer argument");
+    const int64_t total = (int64_t)R * K;
+    CSA2_REQUIRE((total + 255) / 256 <= 0x7FFFFFFF, CSA2_ERR_UNSUPPORTED, "paged_rows: too many entries");
+    hipLaunchKernelGGL(k_paged_rows, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, csa2::as_stream(stream),
+                       block_table, max_pages, __builtin_ctz((unsigned)page_rows), cache_rows, row_seq, row_len, idx, R,
+                       K, phys);
+    return csa2::check_launch("paged_rows");
 }

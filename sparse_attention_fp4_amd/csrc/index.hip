@@ -42,10 +42,31 @@ constexpr int kReChunk = 512;        // pool slots per Reindex-score workgroup
 
 // ------------------------------------------------------------------ scoring
 
-template <int HT, int KS, bool REINDEX>
+// Paged cache addressing: entry j of sequence s lives in cache row
+// bt[s * max_pages + (j >> shift)] * 2^shift + (j mod 2^shift).  A page id
+// outside the cache (or a page past max_pages) makes the entry not visible.
+struct PageMap {
+    const int32_t* bt;
+    int32_t max_pages;
+    int32_t shift;
+    int64_t cache_rows;
+    // Page id of page `page` of sequence `seq` (-1 if past the table).
+    __device__ __forceinline__ int32_t page_id(int seq, int64_t page) const
+    {
+        return page < max_pages ? bt[(int64_t)seq * max_pages + page] : -1;
+    }
+    // Cache row of entry j on page id pid, or -1 if not visible.
+    __device__ __forceinline__ int64_t row_on(int32_t pid, int64_t j) const
+    {
+        const int64_t phys = ((int64_t)pid << shift) | (j & (((int64_t)1 << shift) - 1));
+        return pid >= 0 && phys < cache_rows ? phys : -1;
+    }
+};
+
+template <int HT, int KS, bool REINDEX, bool PAGED>
 __global__ __launch_bounds__(256) void k_index_score(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ ikeys,
-    const int64_t* __restrict__ seq_start, const int32_t* __restrict__ row_seq,
+    const int64_t* __restrict__ seq_start, PageMap pm, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ pool, int32_t Hi, int32_t Di,
     int32_t P, float* __restrict__ scores, int64_t ld_scores, float* __restrict__ bmax,
     int64_t ld_bmax)
@@ -60,7 +81,32 @@ __global__ __launch_bounds__(256) void k_index_score(
     const int64_t first = (int64_t)blockIdx.x * chunk;
     if (!REINDEX && first >= n) return;
     const int nb = (n + 7) >> 3;
-    const uint8_t* keys = ikeys + seq_start[row_seq[r]] * (int64_t)Di;
+    const int seq = row_seq[r];
+    const uint8_t* keys = PAGED ? ikeys : ikeys + seq_start[seq] * (int64_t)Di;
+
+    // The workgroup's pool block ids (Reindex) and page ids (paged) are read
+    // once into LDS, so the loop's key loads wait for one LDS read instead of
+    // a dependent global load.  Reindex: per pool block of the chunk, the
+    // block id (-1 if absent or out of range) and the id of the page that
+    // holds it (a block never straddles pages).  Full, paged: the ids of the
+    // pages its entries cover (at most chunk / 8: pages hold at least 8).
+    constexpr int kPg = (REINDEX ? kReChunk : kFullChunk) / 8;
+    __shared__ int32_t pg_id[PAGED ? kPg : 1];
+    __shared__ int32_t pg_blk[REINDEX ? kPg : 1];
+    if constexpr (PAGED || REINDEX) {
+        for (int t = threadIdx.x; t < kPg; t += blockDim.x) {
+            if constexpr (REINDEX) {
+                const int64_t ps = (first >> 3) + t;
+                const int b = ps < P ? pool[(int64_t)r * P + ps] : -1;
+                const bool in = b >= 0 && b < nb;
+                pg_blk[t] = in ? b : -1;
+                if constexpr (PAGED) pg_id[t] = in ? pm.page_id(seq, ((int64_t)b * 8) >> pm.shift) : -1;
+            } else {
+                pg_id[t] = pm.page_id(seq, (first >> pm.shift) + t);
+            }
+        }
+        __syncthreads();
+    }
 
     // Query fragments (A operand: row = head, 32 bytes of the k-step per lane)
     i32x8 qa[HT][KS];
@@ -98,7 +144,7 @@ __global__ __launch_bounds__(256) void k_index_score(
             const int64_t slot = wbase + (int64_t)(it0 + u) * 16 + col;
             int64_t j;
             if (REINDEX) {
-                const int b = slot < (int64_t)P * 8 ? pool[(int64_t)r * P + (slot >> 3)] : -1;
+                const int b = pg_blk[(slot - first) >> 3];
                 j = (int64_t)b * 8 + (slot & 7);
                 ok[u] = b >= 0 && b < nb && j < n;
             } else {
@@ -106,7 +152,13 @@ __global__ __launch_bounds__(256) void k_index_score(
                 ok[u] = j < n;
             }
             ent[u] = j;
-            const int64_t jc = ok[u] ? j : 0;
+            int64_t jc = ok[u] ? j : 0;
+            if constexpr (PAGED) {
+                const int32_t pid = REINDEX ? pg_id[(slot - first) >> 3] : pg_id[(j >> pm.shift) - (first >> pm.shift)];
+                const int64_t ph = ok[u] ? pm.row_on(pid, j) : -1;
+                ok[u] = ph >= 0;
+                jc = ok[u] ? ph : 0;
+            }
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int d0 = ks * 128 + grp * 32;
@@ -137,12 +189,14 @@ __global__ __launch_bounds__(256) void k_index_score(
             // maximum over the visible entries of each 8-entry block (-inf if none)
             const float m = max_over8(ok[u] ? part : -INFINITY);
             const bool lead = grp == 0 && (col & 7) == 0;
+            // a slot without a visible entry scores -inf (never selected)
+            const float sv = ok[u] ? part : -INFINITY;
             if (REINDEX) {
-                if (grp == 0 && slot < (int64_t)P * 8) scores[(int64_t)r * ld_scores + slot] = part;
+                if (grp == 0 && slot < (int64_t)P * 8) scores[(int64_t)r * ld_scores + slot] = sv;
                 if (lead && slot < (int64_t)P * 8) bmax[(int64_t)r * ld_bmax + (slot >> 3)] = m;
             } else {
                 const int64_t j = ent[u];
-                if (grp == 0 && ok[u]) scores[(int64_t)r * ld_scores + j] = part;
+                if (grp == 0 && j < n) scores[(int64_t)r * ld_scores + j] = sv;
                 if (lead && j < n) bmax[(int64_t)r * ld_bmax + (j >> 3)] = m;
             }
         }
@@ -235,7 +289,7 @@ __device__ __forceinline__ void keys8(const float* p, uint32_t (&key)[kE], int v
     const float4 b = reinterpret_cast<const float4*>(p)[1];
     const float v[kE] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int e = 0; e < kE; ++e) key[e] = e < valid ? order_key(v[e]) : 0u;
+    for (int e = 0; e < kE; ++e) key[e] = e < valid && v[e] != -INFINITY ? order_key(v[e]) : 0u;
 }
 
 // Key sources.  Each gives rounds() and load(rd, key): the keys of items
@@ -266,7 +320,7 @@ struct BlockMaxSrc {
         const int i0 = rd * kRound + (int)threadIdx.x * kE;
         const float v[kE] = {raw.a.x, raw.a.y, raw.a.z, raw.a.w, raw.b.x, raw.b.y, raw.b.z, raw.b.w};
 #pragma unroll
-        for (int e = 0; e < kE; ++e) key[e] = i0 + e < cnt ? order_key(v[e]) : 0u;
+        for (int e = 0; e < kE; ++e) key[e] = i0 + e < cnt && v[e] != -INFINITY ? order_key(v[e]) : 0u;
     }
     __device__ __forceinline__ void load(int rd, uint32_t (&key)[kE]) const
     {
@@ -364,7 +418,7 @@ struct SampleSrc : DirectFetch<SampleSrc> {
 #pragma unroll
         for (int e = 0; e < kE; ++e) v[e] = bm[(int)((int64_t)(s0 + e) * cnt / kRound)];
 #pragma unroll
-        for (int e = 0; e < kE; ++e) key[e] = order_key(v[e]);
+        for (int e = 0; e < kE; ++e) key[e] = v[e] != -INFINITY ? order_key(v[e]) : 0u;
     }
 };
 
@@ -571,6 +625,7 @@ struct SelectLds {
     int cblk[kMaxK];                     // candidate blocks (when not `blocks` itself)
     int cslot[kMaxK];                    // Reindex: their pool slots
     unsigned long long sortbuf[kMaxP];   // Reindex: pool sorted by block id
+    int cpg[kMaxK];                      // paged caches: page id of each candidate block
     int flag;
 };
 struct SelectLdsFull : SelectLds {
@@ -648,7 +703,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     int64_t ld_bmax, const int32_t* __restrict__ row_len, const int32_t* __restrict__ pool_in,
     int32_t K, int32_t P, int32_t* __restrict__ topk, int32_t* __restrict__ pool_out,
     const uint32_t* __restrict__ gkey_g, const int32_t* __restrict__ gid_g, const int32_t* __restrict__ gcount,
-    int32_t nslices)
+    int32_t nslices, const int32_t* __restrict__ row_seq, PageMap pm, int32_t* __restrict__ rows_out)
 {
     __shared__ typename std::conditional<FULL, SelectLdsFull, SelectLds>::type L;
     const int r = blockIdx.x;
@@ -830,34 +885,96 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     }
     __syncthreads();
 
+    // Paged caches: the cache row of each selected entry is written too (-1
+    // when beyond 32-bit row numbers), so attention needs no separate
+    // translation.  The candidate blocks' page ids are loaded here and arrive
+    // in registers while the entries are selected.
+    int32_t* tr = rows_out ? rows_out + (int64_t)r * K : nullptr;
+    constexpr int kPgPer = kMaxK / kSelThreads;
+    int32_t pgr[kPgPer];
+    if (tr) {
+        const int seq = row_seq[r];
+#pragma unroll
+        for (int k = 0; k < kPgPer; ++k) {
+            const int i = threadIdx.x + k * kSelThreads;
+            const int b = i < ncb ? cand[i] : -1;
+            pgr[k] = b >= 0 ? pm.page_id(seq, ((int64_t)b * 8) >> pm.shift) : -1;
+        }
+    }
+
     // Top-K among the candidate blocks' entries, written in item order, which
     // is ascending entry order.
     const CandSrc csrc{{}, sc, cand, cand_slot, ncb, n};
     load_regs(csrc, reg);
     const SelState st = radix_select(L.sh, phase, csrc, reg, K);
     int32_t* to = topk + (int64_t)r * K;
+    if (tr) {
+#pragma unroll
+        for (int k = 0; k < kPgPer; ++k) L.cpg[threadIdx.x + k * kSelThreads] = pgr[k];
+        __syncthreads();
+    }
     int nk = select_compact(L.sh, phase, csrc, reg, st, [&](int pos, int c, uint32_t) {
-        if (pos < K) to[pos] = cand[c >> 3] * 8 + (c & 7);
+        if (pos < K) {
+            const int j = cand[c >> 3] * 8 + (c & 7);
+            to[pos] = j;
+            if (tr) {
+                const int64_t ph = pm.row_on(L.cpg[c >> 3], j);
+                tr[pos] = ph <= 0x7FFFFFFF ? (int32_t)ph : -1;
+            }
+        }
     });
     nk = nk < K ? nk : K;
-    for (int i = nk + threadIdx.x; i < K; i += kSelThreads) to[i] = -1;
+    for (int i = nk + threadIdx.x; i < K; i += kSelThreads) {
+        to[i] = -1;
+        if (tr) tr[i] = -1;
+    }
 }
 
-template <bool REINDEX>
+template <bool REINDEX, bool PAGED>
 void launch_score(int HT, int KS, dim3 grid, hipStream_t st, const uint8_t* qI, const float* w,
-                  const uint8_t* ikeys, const int64_t* seq_start, const int32_t* row_seq,
+                  const uint8_t* ikeys, const int64_t* seq_start, const PageMap& pm, const int32_t* row_seq,
                   const int32_t* row_len, const int32_t* pool, int32_t Hi, int32_t Di, int32_t P,
                   float* scores, int64_t lds, float* bm, int64_t ldb)
 {
-#define CSA2_SCORE(ht, ks)                                                                          \
-    if (HT == ht && KS == ks) {                                                                     \
-        hipLaunchKernelGGL((k_index_score<ht, ks, REINDEX>), grid, dim3(256), 0, st, qI, w, ikeys,   \
-                           seq_start, row_seq, row_len, pool, Hi, Di, P, scores, lds, bm, ldb);     \
-        return;                                                                                     \
+#define CSA2_SCORE(ht, ks)                                                                                 \
+    if (HT == ht && KS == ks) {                                                                            \
+        hipLaunchKernelGGL((k_index_score<ht, ks, REINDEX, PAGED>), grid, dim3(256), 0, st, qI, w, ikeys,   \
+                           seq_start, pm, row_seq, row_len, pool, Hi, Di, P, scores, lds, bm, ldb);        \
+        return;                                                                                            \
     }
     CSA2_SCORE(1, 1) CSA2_SCORE(2, 1) CSA2_SCORE(3, 1) CSA2_SCORE(4, 1)
     CSA2_SCORE(1, 2) CSA2_SCORE(2, 2) CSA2_SCORE(3, 2) CSA2_SCORE(4, 2)
 #undef CSA2_SCORE
+}
+
+template <bool REINDEX>
+void launch_score(bool paged, int HT, int KS, dim3 grid, hipStream_t st, const uint8_t* qI, const float* w,
+                  const uint8_t* ikeys, const int64_t* seq_start, const PageMap& pm, const int32_t* row_seq,
+                  const int32_t* row_len, const int32_t* pool, int32_t Hi, int32_t Di, int32_t P,
+                  float* scores, int64_t lds, float* bm, int64_t ldb)
+{
+    if (paged)
+        launch_score<REINDEX, true>(HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len, pool, Hi, Di,
+                                    P, scores, lds, bm, ldb);
+    else
+        launch_score<REINDEX, false>(HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len, pool, Hi,
+                                     Di, P, scores, lds, bm, ldb);
+}
+
+// Block-table arguments of the paged calls; shift = log2(page_rows).
+csa2_status_t check_pages(const char* who, const int32_t* bt, int32_t max_pages, int32_t page_rows,
+                          int64_t cache_rows, PageMap& pm)
+{
+    CSA2_REQUIRE(bt, CSA2_ERR_NULL, "%s: block_table is NULL", who);
+    CSA2_REQUIRE(max_pages >= 1, CSA2_ERR_SHAPE, "%s: max_pages=%d < 1", who, max_pages);
+    CSA2_REQUIRE(cache_rows >= 1, CSA2_ERR_SHAPE, "%s: cache_rows=%lld < 1", who, (long long)cache_rows);
+    CSA2_REQUIRE(page_rows >= 8 && page_rows <= (1 << 20) && (page_rows & (page_rows - 1)) == 0,
+                 CSA2_ERR_UNSUPPORTED, "%s: page_rows=%d must be a power of two in [8, 2^20]", who, page_rows);
+    pm.bt = bt;
+    pm.max_pages = max_pages;
+    pm.shift = __builtin_ctz((unsigned)page_rows);
+    pm.cache_rows = cache_rows;
+    return CSA2_OK;
 }
 
 int64_t full_ld(int32_t max_len) { return ((int64_t)max_len + kFullChunk - 1) / kFullChunk * kFullChunk; }
@@ -895,12 +1012,12 @@ extern "C" size_t csa2_index_full_workspace_bytes(int32_t R, int32_t max_len, in
     return b;
 }
 
-extern "C" csa2_status_t csa2_index_full(const uint8_t* qI, const float* w, const uint8_t* ikeys,
-                                         const int64_t* seq_start, const int32_t* row_seq,
-                                         const int32_t* row_len, int32_t R, int32_t Hi, int32_t Di,
-                                         int32_t max_len, int32_t K, int32_t P, int32_t block,
-                                         int32_t* topk_idx, int32_t* pool_blocks, void* workspace,
-                                         size_t workspace_bytes, void* stream)
+namespace {
+csa2_status_t index_full_impl(const uint8_t* qI, const float* w, const uint8_t* ikeys, const int64_t* seq_start,
+                              const PageMap* pmp, const int32_t* row_seq, const int32_t* row_len, int32_t R,
+                              int32_t Hi, int32_t Di, int32_t max_len, int32_t K, int32_t P, int32_t block,
+                              int32_t* topk_idx, int32_t* topk_rows, int32_t* pool_blocks, void* workspace,
+                              size_t workspace_bytes, void* stream)
 {
     csa2_status_t s = check_indexer_dims("index_full", R, Hi, Di, K, block);
     if (s != CSA2_OK) return s;
@@ -911,7 +1028,7 @@ extern "C" csa2_status_t csa2_index_full(const uint8_t* qI, const float* w, cons
     CSA2_REQUIRE(max_len >= 0, CSA2_ERR_SHAPE, "index_full: max_len=%d < 0", max_len);
     CSA2_REQUIRE(max_len <= 0x7FFFFFFF - 2 * kFullChunk, CSA2_ERR_UNSUPPORTED, "index_full: max_len too large");
     if (R == 0) return CSA2_OK;
-    CSA2_REQUIRE(qI && w && ikeys && seq_start && row_seq && row_len && topk_idx, CSA2_ERR_NULL,
+    CSA2_REQUIRE(qI && w && ikeys && (seq_start || pmp) && row_seq && row_len && topk_idx, CSA2_ERR_NULL,
                  "index_full: NULL pointer argument");
     const size_t need = csa2_index_full_workspace_bytes(R, max_len, K, P, block);
     CSA2_REQUIRE(workspace && workspace_bytes >= need && ((uintptr_t)workspace & 255) == 0,
@@ -940,10 +1057,11 @@ extern "C" csa2_status_t csa2_index_full(const uint8_t* qI, const float* w, cons
     }
     hipStream_t st = csa2::as_stream(stream);
     const int HT = (Hi + 15) / 16, KS = (Di + 127) / 128;
+    const PageMap pm = pmp ? *pmp : PageMap{nullptr, 0, 0, 0};
     if (max_len > 0) {
         dim3 grid((unsigned)(ld / kFullChunk), (unsigned)R);
-        launch_score<false>(HT, KS, grid, st, qI, w, ikeys, seq_start, row_seq, row_len, nullptr, Hi, Di,
-                            0, scores, ld, bm, ld / 8);
+        launch_score<false>(pmp != nullptr, HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len,
+                            nullptr, Hi, Di, 0, scores, ld, bm, ld / 8);
     }
     if (gcount) {
         const int32_t big = K > P ? K : P;
@@ -951,8 +1069,39 @@ extern "C" csa2_status_t csa2_index_full(const uint8_t* qI, const float* w, cons
                            row_len, big, gkey, gid, gcount, (int32_t)nslices);
     }
     hipLaunchKernelGGL(k_select<true>, dim3((unsigned)R), dim3(kSelThreads), 0, st, scores, ld, bm, ld / 8,
-                       row_len, nullptr, K, P, topk_idx, pool_blocks, gkey, gid, gcount, (int32_t)nslices);
+                       row_len, nullptr, K, P, topk_idx, pool_blocks, gkey, gid, gcount, (int32_t)nslices, row_seq, pm,
+                       pmp ? topk_rows : nullptr);
     return csa2::check_launch("index_full");
+}
+}  // namespace
+
+extern "C" csa2_status_t csa2_index_full(const uint8_t* qI, const float* w, const uint8_t* ikeys,
+                                         const int64_t* seq_start, const int32_t* row_seq,
+                                         const int32_t* row_len, int32_t R, int32_t Hi, int32_t Di,
+                                         int32_t max_len, int32_t K, int32_t P, int32_t block,
+                                         int32_t* topk_idx, int32_t* pool_blocks, void* workspace,
+                                         size_t workspace_bytes, void* stream)
+{
+    if (!seq_start && R > 0) return csa2::fail(CSA2_ERR_NULL, "index_full: seq_start is NULL");
+    return index_full_impl(qI, w, ikeys, seq_start, nullptr, row_seq, row_len, R, Hi, Di, max_len, K, P, block,
+                           topk_idx, nullptr, pool_blocks, workspace, workspace_bytes, stream);
+}
+
+extern "C" csa2_status_t csa2_index_full_paged(const uint8_t* qI, const float* w, const uint8_t* ikeys,
+                                               int64_t cache_rows, const int32_t* block_table, int32_t max_pages,
+                                               int32_t page_rows, const int32_t* row_seq, const int32_t* row_len,
+                                               int32_t R, int32_t Hi, int32_t Di, int32_t max_len, int32_t K,
+                                               int32_t P, int32_t block, int32_t* topk_idx, int32_t* topk_rows,
+                                               int32_t* pool_blocks, void* workspace, size_t workspace_bytes,
+                                               void* stream)
+{
+    PageMap pm;
+    if (R > 0) {
+        const csa2_status_t s = check_pages("index_full_paged", block_table, max_pages, page_rows, cache_rows, pm);
+        if (s != CSA2_OK) return s;
+    }
+    return index_full_impl(qI, w, ikeys, nullptr, &pm, row_seq, row_len, R, Hi, Di, max_len, K, P, block, topk_idx,
+                           topk_rows, pool_blocks, workspace, workspace_bytes, stream);
 }
 
 extern "C" size_t csa2_index_reindex_workspace_bytes(int32_t R, int32_t K, int32_t P, int32_t block)
@@ -963,19 +1112,19 @@ extern "C" size_t csa2_index_reindex_workspace_bytes(int32_t R, int32_t K, int32
     return csa2::align_up((size_t)R * ld * 4, 256) + csa2::align_up((size_t)R * (ld / 8) * 4, 256);
 }
 
-extern "C" csa2_status_t csa2_index_reindex(const uint8_t* qI, const float* w, const uint8_t* ikeys,
-                                            const int64_t* seq_start, const int32_t* row_seq,
-                                            const int32_t* row_len, const int32_t* pool_blocks,
-                                            int32_t R, int32_t Hi, int32_t Di, int32_t K, int32_t P,
-                                            int32_t block, int32_t* topk_idx, void* workspace,
-                                            size_t workspace_bytes, void* stream)
+namespace {
+csa2_status_t index_reindex_impl(const uint8_t* qI, const float* w, const uint8_t* ikeys, const int64_t* seq_start,
+                                 const PageMap* pmp, const int32_t* row_seq, const int32_t* row_len,
+                                 const int32_t* pool_blocks, int32_t R, int32_t Hi, int32_t Di, int32_t K, int32_t P,
+                                 int32_t block, int32_t* topk_idx, int32_t* topk_rows, void* workspace,
+                                 size_t workspace_bytes, void* stream)
 {
     csa2_status_t s = check_indexer_dims("index_reindex", R, Hi, Di, K, block);
     if (s != CSA2_OK) return s;
     CSA2_REQUIRE(P >= 1, CSA2_ERR_SHAPE, "index_reindex: P=%d < 1", P);
     CSA2_REQUIRE(P <= kMaxP, CSA2_ERR_UNSUPPORTED, "index_reindex: P=%d > %d", P, kMaxP);
     if (R == 0) return CSA2_OK;
-    CSA2_REQUIRE(qI && w && ikeys && seq_start && row_seq && row_len && pool_blocks && topk_idx,
+    CSA2_REQUIRE(qI && w && ikeys && (seq_start || pmp) && row_seq && row_len && pool_blocks && topk_idx,
                  CSA2_ERR_NULL, "index_reindex: NULL pointer argument");
     const size_t need = csa2_index_reindex_workspace_bytes(R, K, P, block);
     CSA2_REQUIRE(workspace && workspace_bytes >= need && ((uintptr_t)workspace & 255) == 0,
@@ -988,9 +1137,41 @@ extern "C" csa2_status_t csa2_index_reindex(const uint8_t* qI, const float* w, c
     hipStream_t st = csa2::as_stream(stream);
     const int HT = (Hi + 15) / 16, KS = (Di + 127) / 128;
     dim3 grid((unsigned)(ld / kReChunk), (unsigned)R);
-    launch_score<true>(HT, KS, grid, st, qI, w, ikeys, seq_start, row_seq, row_len, pool_blocks, Hi, Di, P,
-                       scores, ld, bm, ld / 8);
+    const PageMap pm = pmp ? *pmp : PageMap{nullptr, 0, 0, 0};
+    launch_score<true>(pmp != nullptr, HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len, pool_blocks,
+                       Hi, Di, P, scores, ld, bm, ld / 8);
     hipLaunchKernelGGL(k_select<false>, dim3((unsigned)R), dim3(kSelThreads), 0, st, scores, ld, bm, ld / 8,
-                       row_len, pool_blocks, K, P, topk_idx, nullptr, nullptr, nullptr, nullptr, 0);
+                       row_len, pool_blocks, K, P, topk_idx, nullptr, nullptr, nullptr, nullptr, 0, row_seq, pm,
+                       pmp ? topk_rows : nullptr);
     return csa2::check_launch("index_reindex");
+}
+}  // namespace
+
+extern "C" csa2_status_t csa2_index_reindex(const uint8_t* qI, const float* w, const uint8_t* ikeys,
+                                            const int64_t* seq_start, const int32_t* row_seq,
+                                            const int32_t* row_len, const int32_t* pool_blocks,
+                                            int32_t R, int32_t Hi, int32_t Di, int32_t K, int32_t P,
+                                            int32_t block, int32_t* topk_idx, void* workspace,
+                                            size_t workspace_bytes, void* stream)
+{
+    if (!seq_start && R > 0 && P >= 1) return csa2::fail(CSA2_ERR_NULL, "index_reindex: seq_start is NULL");
+    return index_reindex_impl(qI, w, ikeys, seq_start, nullptr, row_seq, row_len, pool_blocks, R, Hi, Di, K, P, block,
+                              topk_idx, nullptr, workspace, workspace_bytes, stream);
+}
+
+extern "C" csa2_status_t csa2_index_reindex_paged(const uint8_t* qI, const float* w, const uint8_t* ikeys,
+                                                  int64_t cache_rows, const int32_t* block_table, int32_t max_pages,
+                                                  int32_t page_rows, const int32_t* row_seq, const int32_t* row_len,
+                                                  const int32_t* pool_blocks, int32_t R, int32_t Hi, int32_t Di,
+                                                  int32_t K, int32_t P, int32_t block, int32_t* topk_idx,
+                                                  int32_t* topk_rows, void* workspace, size_t workspace_bytes,
+                                                  void* stream)
+{
+    PageMap pm;
+    if (R > 0) {
+        const csa2_status_t s = check_pages("index_reindex_paged", block_table, max_pages, page_rows, cache_rows, pm);
+        if (s != CSA2_OK) return s;
+    }
+    return index_reindex_impl(qI, w, ikeys, nullptr, &pm, row_seq, row_len, pool_blocks, R, Hi, Di, K, P, block,
+                              topk_idx, topk_rows, workspace, workspace_bytes, stream);
 }

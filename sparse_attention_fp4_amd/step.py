@@ -10,6 +10,12 @@ the pool of the Full layer.
 
 `CSA2Step` allocates every output and workspace once, so `run()` only enqueues
 kernels (nothing is allocated, copied or synchronised inside a step).
+
+Paged mode (block_table given): the main cache and the indexer keys are paged
+caches addressed through the block table, new_rows are cache rows, the two
+indexer calls take their paged forms and also write the cache rows of each
+Full/Reindex layer's Top-K entries, and every attention call reads those rows.
+With swa_head given the SWA window of each row is a ring of W slots.
 """
 from __future__ import annotations
 
@@ -17,9 +23,8 @@ from typing import Dict, List
 
 import torch
 
-from . import (csa2_index_full, csa2_index_full_workspace_bytes, csa2_index_reindex,
-               csa2_index_reindex_workspace_bytes, csa2_quantize_append, csa2_sparse_attn,
-               csa2_sparse_attn_workspace_bytes)
+from . import (csa2_index_full, csa2_index_full_paged, csa2_index_full_workspace_bytes, csa2_index_reindex,
+               csa2_index_reindex_paged, csa2_index_reindex_workspace_bytes, csa2_quantize_append, csa2_sparse_attn, csa2_sparse_attn_phys, csa2_sparse_attn_workspace_bytes)
 
 
 def parent_layers(modes: List[str]) -> List[int]:
@@ -49,12 +54,15 @@ class CSA2Step:
       qI[l], w[l]          indexer query/weights of Full and Reindex layers
       q[l], swa[l]         attention query and SWA rows of every layer
       swa_row_start, swa_len, W
+      block_table, page_rows   paged mode (seq_start unused)
+      swa_head             SWA ring heads [R] int32 (paged mode only)
     """
 
     def __init__(self, modes: List[str], *, codes, scales, ikeys, seq_start, row_seq, row_len, max_len,
                  new_kv, new_rows, qI: Dict[int, torch.Tensor], w: Dict[int, torch.Tensor],
                  q: Dict[int, torch.Tensor], swa: Dict[int, torch.Tensor], swa_row_start, swa_len, W: int,
-                 K: int, P: int, softmax_scale: float, block: int = 8):
+                 K: int, P: int, softmax_scale: float, block: int = 8, block_table=None, page_rows: int = 0,
+                 swa_head=None):
         self.modes = list(modes)
         self.parents = parent_layers(self.modes)
         self.codes, self.scales, self.ikeys = codes, scales, ikeys
@@ -63,6 +71,10 @@ class CSA2Step:
         self.qI, self.w, self.q, self.swa = qI, w, q, swa
         self.swa_row_start, self.swa_len, self.W = swa_row_start, swa_len, int(W)
         self.K, self.P, self.block, self.scale = int(K), int(P), int(block), float(softmax_scale)
+        self.block_table, self.page_rows, self.swa_head = block_table, int(page_rows), swa_head
+        self.paged = block_table is not None
+        if swa_head is not None and not self.paged:
+            raise ValueError("swa_head needs paged mode")
         dev = codes.device
         R = int(row_seq.shape[0])
         H, D = q[0].shape[1], q[0].shape[2]
@@ -70,6 +82,8 @@ class CSA2Step:
         self.topk = {l: torch.empty(R, self.K, dtype=torch.int32, device=dev)
                      for l, m in enumerate(self.modes) if m in "FR"}
         self.pool = torch.empty(R, self.P, dtype=torch.int32, device=dev)
+        self.phys = ({l: torch.empty(R, self.K, dtype=torch.int32, device=dev) for l in self.topk}
+                     if self.paged else self.topk)
         self.out = {l: torch.empty(R, H, D, dtype=torch.float32, device=dev) for l in range(len(self.modes))}
         self.lse = {l: torch.empty(R, H, dtype=torch.float32, device=dev) for l in range(len(self.modes))}
         nbytes = max(csa2_index_full_workspace_bytes(R, self.max_len, self.K, self.P, self.block),
@@ -92,21 +106,38 @@ class CSA2Step:
         for l, m in enumerate(self.modes):
             if m == "F":
                 _mark("index_full", "begin")
-                csa2_index_full(self.qI[l], self.w[l], self.ikeys, self.seq_start, self.row_seq, self.row_len,
-                                self.max_len, self.K, self.P, self.block, topk_idx=self.topk[l],
-                                pool_blocks=self.pool, workspace=self.workspace, stream=stream)
+                if self.paged:
+                    csa2_index_full_paged(self.qI[l], self.w[l], self.ikeys, self.block_table, self.page_rows,
+                                          self.row_seq, self.row_len, self.max_len, self.K, self.P, self.block,
+                                          topk_idx=self.topk[l], pool_blocks=self.pool, topk_rows=self.phys[l],
+                                          workspace=self.workspace, stream=stream)
+                else:
+                    csa2_index_full(self.qI[l], self.w[l], self.ikeys, self.seq_start, self.row_seq, self.row_len,
+                                    self.max_len, self.K, self.P, self.block, topk_idx=self.topk[l],
+                                    pool_blocks=self.pool, workspace=self.workspace, stream=stream)
                 _mark("index_full", "end")
             elif m == "R":
                 _mark("index_reindex", "begin")
-                csa2_index_reindex(self.qI[l], self.w[l], self.ikeys, self.seq_start, self.row_seq,
-                                   self.row_len, self.pool, self.K, self.block, topk_idx=self.topk[l],
-                                   workspace=self.workspace, stream=stream)
+                if self.paged:
+                    csa2_index_reindex_paged(self.qI[l], self.w[l], self.ikeys, self.block_table, self.page_rows,
+                                             self.row_seq, self.row_len, self.pool, self.K, self.block,
+                                             topk_idx=self.topk[l], topk_rows=self.phys[l], workspace=self.workspace,
+                                             stream=stream)
+                else:
+                    csa2_index_reindex(self.qI[l], self.w[l], self.ikeys, self.seq_start, self.row_seq,
+                                       self.row_len, self.pool, self.K, self.block, topk_idx=self.topk[l],
+                                       workspace=self.workspace, stream=stream)
                 _mark("index_reindex", "end")
             if layers is not None and l not in layers:
                 continue
             _mark("sparse_attn", "begin")
-            csa2_sparse_attn(self.q[l], self.codes, self.scales, self.seq_start, self.row_seq, self.row_len,
-                             self.topk[self.parents[l]], self.swa[l], self.swa_row_start, self.swa_len, self.W,
-                             self.scale, out=self.out[l], lse=self.lse[l], workspace=self.workspace,
-                             stream=stream)
+            if self.paged:
+                csa2_sparse_attn_phys(self.q[l], self.codes, self.scales, self.phys[self.parents[l]], self.swa[l],
+                                      self.swa_row_start, self.swa_len, self.W, self.scale, swa_head=self.swa_head,
+                                      out=self.out[l], lse=self.lse[l], workspace=self.workspace, stream=stream)
+            else:
+                csa2_sparse_attn(self.q[l], self.codes, self.scales, self.seq_start, self.row_seq, self.row_len,
+                                 self.topk[self.parents[l]], self.swa[l], self.swa_row_start, self.swa_len, self.W,
+                                 self.scale, out=self.out[l], lse=self.lse[l], workspace=self.workspace,
+                                 stream=stream)
             _mark("sparse_attn", "end")

@@ -150,6 +150,77 @@ def test_attn_workspace_only_when_split():
     assert L.csa2_sparse_attn_workspace_bytes(2, 64, 512, 512, 128) > 0
 
 
+def full_paged_args(**kw):
+    a = dict(qI=FAKE, w=FAKE, ikeys=FAKE, rows=1 << 20, bt=FAKE, mp=64, pr=64, rs=FAKE, rl=FAKE, R=2, Hi=64,
+             Di=128, max_len=100, K=512, P=2048, block=8, topk=FAKE, trows=None, pool=FAKE, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return [a[k] for k in ("qI", "w", "ikeys", "rows", "bt", "mp", "pr", "rs", "rl", "R", "Hi", "Di", "max_len",
+                           "K", "P", "block", "topk", "trows", "pool", "ws", "wsb")] + [None]
+
+
+def reindex_paged_args(**kw):
+    a = dict(qI=FAKE, w=FAKE, ikeys=FAKE, rows=1 << 20, bt=FAKE, mp=64, pr=64, rs=FAKE, rl=FAKE, pool=FAKE, R=2,
+             Hi=64, Di=128, K=512, P=2048, block=8, topk=FAKE, trows=None, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return [a[k] for k in ("qI", "w", "ikeys", "rows", "bt", "mp", "pr", "rs", "rl", "pool", "R", "Hi", "Di",
+                           "K", "P", "block", "topk", "trows", "ws", "wsb")] + [None]
+
+
+@pytest.mark.parametrize("which", ["full", "reindex"])
+def test_index_paged_validation(which):
+    L = csa2.lib()
+    f, args = ((L.csa2_index_full_paged, full_paged_args) if which == "full"
+               else (L.csa2_index_reindex_paged, reindex_paged_args))
+    assert f(*args(pr=48)) == 3                     # page_rows not a power of two
+    assert f(*args(pr=4)) == 3                      # below 8 rows per page
+    assert f(*args(pr=1 << 21)) == 3
+    assert "page_rows" in L.csa2_last_error().decode()
+    assert f(*args(mp=0)) == 2
+    assert f(*args(rows=0)) == 2
+    assert f(*args(bt=None)) == 1
+    assert f(*args(K=0)) == 2                       # the packed call's own checks still apply
+    assert f(*args(Hi=65)) == 3
+    assert f(*args(wsb=16)) == 4
+    assert f(*args(R=0, bt=None, pr=3)) == 0        # empty batch: nothing to check or do
+
+
+def test_paged_rows_validation():
+    f = csa2.lib().csa2_paged_rows
+    ok = dict(bt=FAKE, mp=64, pr=64, rows=1 << 20, rs=FAKE, rl=FAKE, idx=FAKE, R=4, K=512, phys=FAKE)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(*[a[k] for k in ("bt", "mp", "pr", "rows", "rs", "rl", "idx", "R", "K", "phys")], None)
+
+    assert call(pr=100) == 3
+    assert call(mp=0) == 2
+    assert call(rows=0) == 2
+    assert call(R=-1) == 2
+    assert call(idx=None) == 1
+    assert call(phys=None) == 1
+    assert call(R=0, idx=None, phys=None) == 0
+
+
+def test_sparse_attn_phys_validation():
+    f = csa2.lib().csa2_sparse_attn_phys
+    ok = dict(q=FAKE, codes=FAKE, scales=FAKE, rows=1 << 20, idx=FAKE, K=512, swa=FAKE, srs=FAKE, sl=FAKE,
+              head=None, R=32, H=64, D=512, W=128, scale=0.04, out=FAKE, lse=None, ws=FAKE, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(*[a[k] for k in ("q", "codes", "scales", "rows", "idx", "K", "swa", "srs", "sl", "head", "R",
+                                  "H", "D", "W", "scale", "out", "lse", "ws", "wsb")], None)
+
+    assert call(rows=0) == 2
+    assert call(rows=1 << 23) == 3                  # codes beyond 2^31 bytes at D = 512
+    assert call(D=96) == 3
+    assert call(idx=None) == 1
+    assert call(swa=None) == 1
+    assert call(out=None) == 1
+    assert call(R=2, wsb=0) == 4
+    assert call(R=0) == 0
+
+
 def test_python_binding_rejects_host_tensors():
     x = torch.zeros(4, 32, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):

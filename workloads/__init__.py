@@ -230,3 +230,56 @@ def make(cfg: Config, device="cpu", layers: Optional[List[int]] = None,
                     rows_total=rows_total, row_seq=row_seq, row_len=row_len, kv_raw=kv,
                     ikeys=ikeys, qI=qI, w=w, q=q, swa=swa, swa_row_start=swa_row_start,
                     swa_len=swa_len, new_rows=new_rows)
+
+
+# ----------------------------------------------------------------- paged layout
+
+@dataclasses.dataclass
+class PagedLayout:
+    """Where a workload's packed cache rows go in a paged cache.
+
+    Entry j of sequence s lives in cache row
+    block_table[s, j // page_rows] * page_rows + j % page_rows; dst[i] is the
+    cache row of packed row i.  Pages are handed out in a seeded random order,
+    so neighbouring pages of a sequence are far apart in memory."""
+    page_rows: int
+    block_table: torch.Tensor      # [S, max_pages] int32, -1 = unmapped
+    cache_rows: int
+    dst: torch.Tensor              # [rows_total] int64
+
+
+def paged_layout(lengths: np.ndarray, page_rows: int, seed: int, device="cpu", spare_pages: int = 0) -> PagedLayout:
+    lengths = np.asarray(lengths, np.int64)
+    npages = (lengths + page_rows - 1) // page_rows
+    max_pages = max(int(npages.max()) if len(npages) else 1, 1)
+    n_phys = int(npages.sum()) + spare_pages
+    perm = np.random.Generator(np.random.PCG64(seed)).permutation(n_phys)
+    bt = np.full((len(lengths), max_pages), -1, np.int64)
+    dst, k = [], 0
+    for s, (n, m) in enumerate(zip(lengths, npages)):
+        bt[s, :m] = perm[k:k + m]
+        k += int(m)
+        j = np.arange(int(n))
+        dst.append(bt[s, j // page_rows] * page_rows + j % page_rows)
+    dst = np.concatenate(dst) if dst else np.zeros(0, np.int64)
+    return PagedLayout(page_rows=page_rows, block_table=torch.tensor(bt.astype(np.int32), device=device),
+                       cache_rows=n_phys * page_rows, dst=torch.tensor(dst, device=device))
+
+
+def to_pages(layout: PagedLayout, packed: torch.Tensor) -> torch.Tensor:
+    """Copy of packed cache rows [rows_total, ...] in the paged layout
+    (unused rows zero)."""
+    out = torch.zeros((layout.cache_rows,) + tuple(packed.shape[1:]), dtype=packed.dtype, device=packed.device)
+    out[layout.dst] = packed
+    return out
+
+
+def swa_ring(swa: torch.Tensor, swa_row_start: torch.Tensor, W: int, heads: torch.Tensor) -> torch.Tensor:
+    """The W window rows of each query row r stored as a ring: window row i in
+    slot (heads[r] + i) mod W of the row's W slots."""
+    out = swa.clone()
+    i = torch.arange(W, device=swa.device)
+    src = swa_row_start[:, None] + i[None, :]
+    dst = swa_row_start[:, None] + (heads[:, None].long() + i[None, :]) % W
+    out[dst.reshape(-1)] = swa[src.reshape(-1)]
+    return out
