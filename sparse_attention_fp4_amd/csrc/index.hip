@@ -42,6 +42,14 @@ constexpr int kReChunk = 512;        // pool slots per Reindex-score workgroup
 
 // ------------------------------------------------------------------ scoring
 
+// max(x, 0) for a finite x as one integer max: the sign bit makes every
+// negative float (and -0) a negative integer, and non-negative floats keep
+// their order as integers.  (A float max would first canonicalise x.)
+__device__ __forceinline__ float relu(float x)
+{
+    return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // Paged cache addressing: entry j of sequence s lives in cache row
 // bt[s * max_pages + (j >> shift)] * 2^shift + (j mod 2^shift).  A page id
 // outside the cache (or a page past max_pages) makes the entry not visible.
@@ -182,7 +190,7 @@ __global__ __launch_bounds__(256) void k_index_score(
                     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[t][ks], kb[u][ks], acc,
                                                                            0, 0, 0, 127, 0, 127);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) part += wv[t][i] * fmaxf(acc[i], 0.0f);
+                for (int i = 0; i < 4; ++i) part += wv[t][i] * relu(acc[i]);
             }
             part = sum_xor32(sum_xor16(part));
             const int64_t slot = wbase + (int64_t)(it0 + u) * 16 + col;

@@ -182,6 +182,43 @@ def test_index_full_long_row_all_ties_falls_back():
     assert topk[0].tolist() == list(range(300)) and pool[1].tolist() == list(range(2000))
 
 
+def many_rows(seq_lengths, rows, Hi, Di, seed=21):
+    """A workload of several sequences with `rows` = [(sequence, visible
+    entries)] query rows (as in a prefill chunk), each with its own indexer
+    query and weights."""
+    wl = small_workload(seq_lengths, Hi=Hi, Di=Di)
+    g = gen(seed)
+    R = len(rows)
+    wl.row_seq = torch.tensor([s for s, _ in rows], dtype=torch.int32, device=DEV)
+    wl.row_len = torch.tensor([n for _, n in rows], dtype=torch.int32, device=DEV)
+    wl.qI[0] = workloads.to_e4m3_bytes(torch.randint(-3, 4, (R, Hi, Di), generator=g, device=DEV).float())
+    wl.w[0] = torch.round(torch.rand(R, Hi, generator=g, device=DEV) * 16.0) / 16.0
+    return wl
+
+
+@pytest.mark.parametrize("case", ["one_sequence_causal", "mixed_sequences"])
+def test_index_full_many_rows_matches_oracle(case):
+    """Many query rows per call: the causal rows of one sequence (a prefill
+    chunk), and rows of several sequences in arbitrary order."""
+    log(f"index_full many rows: {case}")
+    if case == "one_sequence_causal":
+        seq_lengths = [9000]
+        rows = [(0, 8000 + i + 1) for i in range(601)]      # row_len <= the sequence's 9,000 entries
+    else:
+        seq_lengths = [5000, 7777, 300]
+        rng = np.random.default_rng(8)
+        rows = []
+        for i in range(530):
+            s = int(rng.integers(0, 3)) if i % 7 else i % 3
+            rows.append((s, int(rng.integers(1, seq_lengths[s] + 1))))
+    wl = many_rows(seq_lengths, rows, Hi=16, Di=64)
+    K, P = 64, 100
+    topk, pool = gpu_index_full(wl, 0, K, P)
+    check = [0, 1, 2, 3, 4, 5, 6, 7, 250, 301, len(rows) - 2, len(rows) - 1]
+    rt, rp, _ = oracle_index_rows(wl, 0, check, K, P)
+    assert np.array_equal(topk[check], rt) and np.array_equal(pool[check], rp)
+
+
 @pytest.mark.parametrize("name,lengths,Hi,Di,K,P,idx", [
     ("ragged_int3", [1, 7, 100, 1000, 4097, 20001], 64, 128, 512, 2048, "int3"),
     ("ties_alphabet", [30000, 17, 8191], 64, 128, 512, 2048, "ties"),

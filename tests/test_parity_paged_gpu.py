@@ -140,9 +140,10 @@ def expected_reindex(scores, visible, pool_row, K):
     return out
 
 
-def expected_rows(pages, topk):
-    """Cache rows of index lists (rows of `topk` are sequences)."""
-    return np.array([[pages.phys_of(r, int(j)) for j in topk[r]] for r in range(topk.shape[0])], np.int32)
+def expected_rows(pages, topk, row_seq):
+    """Cache rows of the index lists of rows of sequences row_seq."""
+    return np.array([[pages.phys_of(int(row_seq[r]), int(j)) for j in topk[r]] for r in range(topk.shape[0])],
+                    np.int32)
 
 
 def run_full_paged(wl, pages, ikeys, layer, K, P):
@@ -151,7 +152,7 @@ def run_full_paged(wl, pages, ikeys, layer, K, P):
                                                   want_pool=P > 0, want_rows=True)
     torch.cuda.synchronize()
     topk = np_(topk)
-    assert np.array_equal(np_(rows), expected_rows(pages, topk)), "Full: cache rows differ"
+    assert np.array_equal(np_(rows), expected_rows(pages, topk, np_(wl.row_seq))), "Full: cache rows differ"
     return topk, (np_(pool) if pool is not None else None)
 
 
@@ -160,7 +161,7 @@ def run_reindex_paged(wl, pages, ikeys, layer, pool, K):
                                               wl.row_len, torch.tensor(pool, device=DEV), K, want_rows=True)
     torch.cuda.synchronize()
     got = np_(got)
-    assert np.array_equal(np_(rows), expected_rows(pages, got)), "Reindex: cache rows differ"
+    assert np.array_equal(np_(rows), expected_rows(pages, got, np_(wl.row_seq))), "Reindex: cache rows differ"
     return got
 
 
@@ -188,6 +189,31 @@ def test_index_paged_matches_oracle(name, lengths, pr, K, P, idx):
     want = oracle_reindex_rows(wl, 1, rows, packed, rp, K)
     got = run_reindex_paged(wl, pages, ikeys, 1, rp, K)
     assert np.array_equal(got, want), f"{name}: reindex differs"
+
+
+def test_index_paged_many_rows_one_sequence():
+    """Prefill-like rows (one sequence, causal lengths) over a paged cache
+    with an unmapped page."""
+    n_seq = 9000
+    R = 520
+    wl = small_workload([n_seq])
+    g = torch.Generator(device=DEV)
+    g.manual_seed(9)
+    wl.row_seq = torch.zeros(R, dtype=torch.int32, device=DEV)
+    wl.row_len = torch.arange(n_seq - R + 1, n_seq + 1, dtype=torch.int32, device=DEV)
+    wl.qI[0] = workloads.to_e4m3_bytes(torch.randint(-3, 4, (R, 16, 64), generator=g, device=DEV).float())
+    wl.w[0] = torch.round(torch.rand(R, 16, generator=g, device=DEV) * 16.0) / 16.0
+    pages = Pages([n_seq], 64, seed=4, holes={(0, 7): -1})
+    ikeys = paged_ikeys(wl, pages)
+    K, P = 64, 100
+    topk, pool = run_full_paged(wl, pages, ikeys, 0, K, P)
+    scores = oracle.index_scores(np_(wl.qI[0]), np_(wl.w[0]), np_(wl.ikeys), np_(wl.seq_start), np_(wl.row_seq),
+                                 np_(wl.row_len), n_seq)
+    vis = pages.visible(0)
+    for r in [0, 1, 2, 3, 4, 257, R - 2, R - 1]:
+        n = int(np_(wl.row_len)[r])
+        et, ep = expected_selection(scores[r, :n], vis[:n], K, P)
+        assert np.array_equal(topk[r], et) and np.array_equal(pool[r], ep), f"row {r} differs"
 
 
 def test_index_paged_unmapped_pages():
