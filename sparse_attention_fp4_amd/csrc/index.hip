@@ -16,17 +16,17 @@
 //                  inside a lane.  Full mode streams every visible key once
 //                  (coalesced 32-byte lane loads) and writes the fp32 scores
 //                  and the block maxima; Reindex mode gathers the pool's
-//                  1 KiB key blocks and writes one score per pool slot plus
-//                  each pool block's maximum.
+//                  1 KiB key blocks and writes one score per pool slot.
 //   k_select       One workgroup per query row: exact radix select (11-bit
 //                  digits over order-preserving keys, histograms in LDS) and
 //                  an ordered compaction, so the outputs come out sorted and
-//                  ties resolve to the lowest index.  Both modes first reduce
-//                  the candidates to the top-K blocks by block maximum (Full:
-//                  via the pool, which it also outputs), then select the Top-K
+//                  ties resolve to the lowest index.  Full mode first reduces
+//                  the candidates to the top-K blocks by block maximum (via
+//                  the pool, which it also outputs), then selects the Top-K
 //                  among those blocks' 8K entries: every Top-K entry lies in
 //                  one of them, so the result equals a Top-K over all
-//                  candidates.
+//                  entries.  Reindex mode selects among all 8P pool
+//                  positions at once (they fit in registers).
 #include "csa2_device.h"
 #include "csa2_host.h"
 
@@ -201,7 +201,6 @@ __global__ __launch_bounds__(256) void k_index_score(
             const float sv = ok[u] ? part : -INFINITY;
             if (REINDEX) {
                 if (grp == 0 && slot < (int64_t)P * 8) scores[(int64_t)r * ld_scores + slot] = sv;
-                if (lead && slot < (int64_t)P * 8) bmax[(int64_t)r * ld_bmax + (slot >> 3)] = m;
             } else {
                 const int64_t j = ent[u];
                 if (grp == 0 && j < n) scores[(int64_t)r * ld_scores + j] = sv;
@@ -364,34 +363,25 @@ struct LdsKeySrc : DirectFetch<LdsKeySrc> {
     }
 };
 
-// Pool blocks of one Reindex row (item i = block blocks[i], whose maximum is
-// bm[slots[i]]; block -1 = no block).
-struct PoolBlockSrc : DirectFetch<PoolBlockSrc> {
-    const float* bm;
-    const int* blocks;
-    const int* slots;
-    int cnt;
-    __device__ __forceinline__ int rounds() const { return (cnt + kRound - 1) / kRound; }
+// Pool positions of one Reindex row in slot order: item c is position c % 8
+// of pool slot c / 8, whose score is sc[c] (-inf where the slot holds no
+// visible entry), read as CandSrc reads a block.
+struct SlotSrc : DirectFetch<SlotSrc> {
+    const float* sc;
+    int nslot;
+    __device__ __forceinline__ int rounds() const { return (nslot + kSelThreads - 1) / kSelThreads; }
     __device__ __forceinline__ void load(int rd, uint32_t (&key)[kE]) const
     {
-        const int i0 = rd * kRound + (int)threadIdx.x * kE;
-        float v[kE];
-        bool ok[kE];
-#pragma unroll
-        for (int e = 0; e < kE; ++e) {
-            ok[e] = i0 + e < cnt && blocks[i0 + e] >= 0;
-            v[e] = ok[e] ? bm[slots[i0 + e]] : 0.0f;
-        }
-#pragma unroll
-        for (int e = 0; e < kE; ++e) key[e] = ok[e] && v[e] != -INFINITY ? order_key(v[e]) : 0u;
+        const int ci = rd * kSelThreads + (int)threadIdx.x;
+        keys8(sc + 8 * (int64_t)ci, key, ci < nslot ? kE : 0);
     }
 };
 
 // Candidate entries: item c is position c % 8 of candidate block c / 8, i.e.
-// entry 8*blocks[c/8] + c%8, visible when below n.  Its score is at
-// sc[8*blocks[c/8] + c%8] (Full: scores by entry id) or sc[8*slots[c/8] + c%8]
-// (Reindex: scores by pool slot).  Thread t of round rd reads block
-// rd*kSelThreads + t: two 16-byte loads.
+// entry 8*blocks[c/8] + c%8, visible when below n (block -1: none).  Its
+// score is at sc[8*blocks[c/8] + c%8] (Full: scores by entry id) or
+// sc[8*slots[c/8] + c%8] (Reindex: scores by pool slot).  Thread t of round rd
+// reads block rd*kSelThreads + t: two 16-byte loads.
 struct CandSrc : DirectFetch<CandSrc> {
     const float* sc;
     const int* blocks;
@@ -401,7 +391,7 @@ struct CandSrc : DirectFetch<CandSrc> {
     __device__ __forceinline__ void load(int rd, uint32_t (&key)[kE]) const
     {
         const int ci = rd * kSelThreads + (int)threadIdx.x;
-        if (ci < nblk) {
+        if (ci < nblk && blocks[ci] >= 0) {
             const int b = blocks[ci];
             const int64_t at = 8 * (int64_t)(slots ? slots[ci] : b);
             const int64_t vis = (int64_t)n - 8 * (int64_t)b;
@@ -718,13 +708,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     const int n = row_len[r];
     const int nb = (n + 7) >> 3;
     const float* sc = scores + (int64_t)r * ld_scores;
-    const float* bm = bmax + (int64_t)r * ld_bmax;
+    const float* bm = FULL ? bmax + (int64_t)r * ld_bmax : nullptr;
     RegKeys reg;
     int phase = 0;
     for (int i = threadIdx.x; i < kBins + kBins / 32; i += kSelThreads) L.sh.hist[i] = 0;
     const int* cand;        // candidate blocks
     const int* cand_slot;   // their pool slots (Reindex)
     int ncb;                // number of candidate blocks
+    bool preloaded = false; // reg already holds the candidates' keys
 
     if constexpr (FULL) {
         // A = the top max(P, K) blocks (all of them when nb is smaller), with
@@ -849,8 +840,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     } else {
         // Items are the pool slots in block-id order: the pool as given when
         // its valid ids already ascend, else sorted by id first, so that the
-        // lowest-item tie rule of the selections is the lowest-id rule.
+        // lowest-item tie rule of the selection is the lowest-id rule.  The
+        // scores are stored by pool slot with -inf where a slot holds no
+        // visible entry, so for a pool in order (the usual case: a Full
+        // layer's pool) the keys are the scores in slot order; they are
+        // requested before the order is checked.
         const int32_t* pl = pool_in + (int64_t)r * P;
+        load_regs(SlotSrc{{}, sc, P}, reg);
+        preloaded = true;
         if (threadIdx.x == 0) L.flag = 0;
         __syncthreads();
         for (int i = threadIdx.x; i < P; i += kSelThreads) {
@@ -880,16 +877,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
                 L.slots[i] = (int)(unsigned)v;
             }
             __syncthreads();
+            preloaded = false;   // keys in sorted order are read below
         }
-        const PoolBlockSrc psrc{{}, bm, L.blocks, L.slots, P};
-        load_regs(psrc, reg);
-        const SelState st = radix_select(L.sh, phase, psrc, reg, K);
-        ncb = select_compact(L.sh, phase, psrc, reg, st, [&](int pos, int i, uint32_t) {
-            if (pos < K) { L.cblk[pos] = L.blocks[i]; L.cslot[pos] = L.slots[i]; }
-        });
-        ncb = ncb < K ? ncb : K;
-        cand = L.cblk;
-        cand_slot = L.cslot;
+        // The pool holds at most 2048 x 8 positions, which the registers
+        // hold whole: the Top-K is selected among all of them at once.
+        cand = L.blocks;
+        cand_slot = L.slots;
+        ncb = P;
     }
     __syncthreads();
 
@@ -913,7 +907,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     // Top-K among the candidate blocks' entries, written in item order, which
     // is ascending entry order.
     const CandSrc csrc{{}, sc, cand, cand_slot, ncb, n};
-    load_regs(csrc, reg);
+    if (!preloaded) load_regs(csrc, reg);
     const SelState st = radix_select(L.sh, phase, csrc, reg, K);
     int32_t* to = topk + (int64_t)r * K;
     if (tr) {
@@ -1116,8 +1110,7 @@ extern "C" size_t csa2_index_reindex_workspace_bytes(int32_t R, int32_t K, int32
 {
     (void)K; (void)block;
     if (R < 0 || P < 0) return 0;
-    const int64_t ld = reindex_ld(P);
-    return csa2::align_up((size_t)R * ld * 4, 256) + csa2::align_up((size_t)R * (ld / 8) * 4, 256);
+    return csa2::align_up((size_t)R * reindex_ld(P) * 4, 256);   // one score per pool slot
 }
 
 namespace {
@@ -1141,14 +1134,13 @@ csa2_status_t index_reindex_impl(const uint8_t* qI, const float* w, const uint8_
     CSA2_REQUIRE(R <= 65535, CSA2_ERR_UNSUPPORTED, "index_reindex: R=%d > 65535", R);
     const int64_t ld = reindex_ld(P);
     float* scores = static_cast<float*>(workspace);
-    float* bm = reinterpret_cast<float*>(static_cast<char*>(workspace) + csa2::align_up((size_t)R * ld * 4, 256));
     hipStream_t st = csa2::as_stream(stream);
     const int HT = (Hi + 15) / 16, KS = (Di + 127) / 128;
     dim3 grid((unsigned)(ld / kReChunk), (unsigned)R);
     const PageMap pm = pmp ? *pmp : PageMap{nullptr, 0, 0, 0};
     launch_score<true>(pmp != nullptr, HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len, pool_blocks,
-                       Hi, Di, P, scores, ld, bm, ld / 8);
-    hipLaunchKernelGGL(k_select<false>, dim3((unsigned)R), dim3(kSelThreads), 0, st, scores, ld, bm, ld / 8,
+                       Hi, Di, P, scores, ld, nullptr, 0);
+    hipLaunchKernelGGL(k_select<false>, dim3((unsigned)R), dim3(kSelThreads), 0, st, scores, ld, nullptr, 0,
                        row_len, pool_blocks, K, P, topk_idx, nullptr, nullptr, nullptr, nullptr, 0, row_seq, pm,
                        pmp ? topk_rows : nullptr);
     return csa2::check_launch("index_reindex");
