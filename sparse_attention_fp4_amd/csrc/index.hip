@@ -71,8 +71,12 @@ struct PageMap {
     }
 };
 
+// Up to 4 query pieces (HT x KS) fit in 128 registers with no accumulation
+// registers: four workgroups per compute unit, MFMA results in ordinary
+// registers.  Larger queries (Di = 256 with 48 or more heads) keep the
+// compiler's own budget.
 template <int HT, int KS, bool REINDEX, bool PAGED>
-__global__ __launch_bounds__(256) void k_index_score(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HT * KS <= 4 ? 4 : 1))) void k_index_score(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ ikeys,
     const int64_t* __restrict__ seq_start, PageMap pm, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ pool, int32_t Hi, int32_t Di,
