@@ -226,15 +226,16 @@ struct SelState {
 // are double-buffered: every publish is followed by a barrier, so a slot set
 // is only rewritten after every wave has passed the barrier that follows the
 // reads of its previous contents.
+constexpr int kHistSpan = kBins + kBins / 32;   // one digit histogram, bin b at b + b/32
 struct SelShared {
-    int hist[kBins + kBins / 32 + CSA2_WAVE];   // digit histogram, bin b at b + b/32; then one
-                                                // discard word per lane
+    int hist[2 * kHistSpan + CSA2_WAVE];   // two histograms (two thresholds found in the same
+                                           // passes), then one discard word per lane
     int wave_x[2][3][kSelWaves];
-    int digit, above, in_bin;
+    int digit[2], above[2], in_bin[2];     // digit search results, one slot per threshold
 };
 
 __device__ __forceinline__ int hist_at(int b) { return b + (b >> 5); }
-constexpr int kHistDiscard = kBins + kBins / 32;
+constexpr int kHistDiscard = 2 * kHistSpan;
 
 // Wave-wide inclusive scan with DPP: Hillis-Steele steps inside each row of
 // 16 lanes (row_shr 1, 2, 4, 8), then row 0's total to row 1 and row 2's to
@@ -480,6 +481,37 @@ __device__ __forceinline__ void load_regs(const Src& src, RegKeys& reg)
 // lane's 32 bins (one per lane) picks the bin; wave 0 also clears the bins for
 // the next pass and publishes the digit, barrier.  The histogram must be zero
 // on entry and is zero again on return.
+
+// Run by one wave: the bin of histogram h holding the krem-th largest key
+// (bins taken from the highest digit down), the count of keys in higher bins
+// and the bin's own count go to result slot `res`.  Each lane sums 32 bins, a
+// scan and a ballot pick the lane whose bins span rank krem, and a second
+// scan over that lane's bins picks the bin.  With `clear` the wave zeroes the
+// histogram after reading it.
+__device__ __forceinline__ void digit_search(SelShared& sh, int h, int res, int krem, bool clear)
+{
+    const int lane = lane_id();
+    int* const hist = sh.hist + h * kHistSpan;
+    constexpr int BPL = kBins / CSA2_WAVE;    // bins per lane
+    const int b0 = kBins - 1 - BPL * lane;    // this lane's highest bin
+    int sum = 0;
+#pragma unroll
+    for (int m = 0; m < BPL; ++m) sum += hist[hist_at(b0 - m)];
+    const int incl = wave_incl_sum(sum);
+    const int excl = incl - sum;
+    const uint64_t hit = __ballot(excl < krem && krem <= incl);   // exactly one lane
+    const int L = hit ? __builtin_ctzll(hit) : 0;
+    const int base = __builtin_amdgcn_readlane(excl, L);
+    const int bL = kBins - 1 - BPL * L;
+    const int v = lane < BPL ? hist[hist_at(bL - lane)] : 0;
+    if (clear) {
+#pragma unroll
+        for (int m = 0; m < BPL; ++m) hist[hist_at(b0 - m)] = 0;
+    }
+    const int a = base + wave_incl_sum(v) - v;
+    if (lane < BPL && a < krem && krem <= a + v) { sh.digit[res] = bL - lane; sh.above[res] = a; sh.in_bin[res] = v; }
+}
+
 template <class Src>
 __device__ __forceinline__ SelState radix_select(SelShared& sh, int& phase, const Src& src, const RegKeys& reg,
                                                  int k)
@@ -528,28 +560,11 @@ __device__ __forceinline__ SelState radix_select(SelShared& sh, int& phase, cons
             }
         });
         __syncthreads();
-        if (wave == 0) {
-            constexpr int BPL = kBins / CSA2_WAVE;    // bins per lane
-            const int b0 = kBins - 1 - BPL * lane;    // this lane's highest bin
-            int sum = 0;
-#pragma unroll
-            for (int m = 0; m < BPL; ++m) sum += sh.hist[hist_at(b0 - m)];
-            const int incl = wave_incl_sum(sum);
-            const int excl = incl - sum;
-            const uint64_t hit = __ballot(excl < krem && krem <= incl);   // exactly one lane
-            const int L = hit ? __builtin_ctzll(hit) : 0;
-            const int base = __builtin_amdgcn_readlane(excl, L);
-            const int bL = kBins - 1 - BPL * L;
-            const int v = lane < BPL ? sh.hist[hist_at(bL - lane)] : 0;
-#pragma unroll
-            for (int m = 0; m < BPL; ++m) sh.hist[hist_at(b0 - m)] = 0;
-            const int a = base + wave_incl_sum(v) - v;
-            if (lane < BPL && a < krem && krem <= a + v) { sh.digit = bL - lane; sh.above = a; sh.in_bin = v; }
-        }
+        if (wave == 0) digit_search(sh, 0, 0, krem, true);
         __syncthreads();
-        const int d = sh.digit;
-        krem -= sh.above;
-        const int in_bin = sh.in_bin;
+        const int d = sh.digit[0];
+        krem -= sh.above[0];
+        const int in_bin = sh.in_bin[0];
         st.prefix |= (uint32_t)d << shift;
         st.mask |= dmask << shift;
         st.need = krem;
@@ -557,6 +572,91 @@ __device__ __forceinline__ SelState radix_select(SelShared& sh, int& phase, cons
         top = shift - 1;
     }
     return st;
+}
+
+// Thresholds of the k1 and of the k2 largest keys (k1 >= k2) in the same
+// passes.  Both searches take the same digit positions, so while their
+// prefixes agree one histogram serves both; once they differ, a key can match
+// at most one of them and counts in that one's histogram (the second half of
+// the LDS histogram space), so a pass still costs one atomic per key.
+template <class Src>
+__device__ __forceinline__ void radix_select2(SelShared& sh, int& phase, const Src& src, const RegKeys& reg, int k1,
+                                              int k2, SelState& s1, SelState& s2)
+{
+    const int lane = lane_id(), wave = threadIdx.x / CSA2_WAVE;
+    uint32_t kand = 0xFFFFFFFFu, kor = 0u;
+    int nv = 0;
+    for_rounds(src, reg, [&](int, const uint32_t (&key)[kE]) {
+#pragma unroll
+        for (int e = 0; e < kE; ++e)
+            if (key[e]) { kand &= key[e]; kor |= key[e]; ++nv; }
+    });
+    kand = wave_last(wave_scan(kand, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a & b; }));
+    kor = wave_last(wave_scan(kor, 0u, [](uint32_t a, uint32_t b) { return a | b; }));
+    nv = (int)wave_last((uint32_t)wave_incl_sum(nv));
+    int (*slot)[kSelWaves] = sh.wave_x[phase];
+    phase ^= 1;
+    if (lane == 0) { slot[0][wave] = (int)kand; slot[1][wave] = (int)kor; slot[2][wave] = nv; }
+    __syncthreads();
+    kand = 0xFFFFFFFFu; kor = 0u; nv = 0;
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) {
+        kand &= (uint32_t)slot[0][w];
+        kor |= (uint32_t)slot[1][w];
+        nv += slot[2][w];
+    }
+    s1 = SelState{0u, 0u, nv};
+    s2 = SelState{0u, 0u, nv};
+    bool done1 = nv <= k1, done2 = nv <= k2;     // everything valid is selected (mask 0)
+    if (done1 && done2) return;
+    const uint32_t diff = kand ^ kor;
+    const uint32_t mask0 = diff ? ~((2u << (31 - __builtin_clz(diff))) - 1u) : 0xFFFFFFFFu;
+    if (!done1) s1 = SelState{kand & mask0, mask0, k1};
+    if (!done2) s2 = SelState{kand & mask0, mask0, k2};
+    if (diff == 0u) return;                       // all valid keys equal: ties only
+    int top = 31 - __builtin_clz(diff);
+    int krem1 = k1, krem2 = k2;
+    while (top >= 0 && !(done1 && done2)) {
+        const int width = top + 1 < 11 ? top + 1 : 11;
+        const int shift = top + 1 - width;
+        const uint32_t dmask = (1u << width) - 1u;
+        const bool same = !done1 && !done2 && s1.prefix == s2.prefix;   // (the masks agree)
+        for_rounds(src, reg, [&](int, const uint32_t (&key)[kE]) {
+#pragma unroll
+            for (int e = 0; e < kE; ++e) {
+                const int dg = (int)((key[e] >> shift) & dmask);
+                const bool h1 = !done1 && key[e] && (key[e] & s1.mask) == s1.prefix;
+                const bool h2 = !done2 && !same && key[e] && (key[e] & s2.mask) == s2.prefix;
+                atomicAdd(&sh.hist[h1 ? hist_at(dg) : h2 ? kHistSpan + hist_at(dg) : kHistDiscard + lane], 1);
+            }
+        });
+        __syncthreads();
+        if (same) {
+            if (wave == 0) {
+                digit_search(sh, 0, 0, krem1, false);
+                digit_search(sh, 0, 1, krem2, true);
+            }
+        } else {
+            if (wave == 0 && !done1) digit_search(sh, 0, 0, krem1, true);
+            if (wave == 1 && !done2) digit_search(sh, 1, 1, krem2, true);
+        }
+        __syncthreads();
+        if (!done1) {
+            krem1 -= sh.above[0];
+            s1.prefix |= (uint32_t)sh.digit[0] << shift;
+            s1.mask |= dmask << shift;
+            s1.need = krem1;
+            done1 = sh.in_bin[0] == krem1;        // the whole bin is taken
+        }
+        if (!done2) {
+            krem2 -= sh.above[1];
+            s2.prefix |= (uint32_t)sh.digit[1] << shift;
+            s2.mask |= dmask << shift;
+            s2.need = krem2;
+            done2 = sh.in_bin[1] == krem2;
+        }
+        top = shift - 1;
+    }
 }
 
 // Ordered compaction: emit(pos, item, key) for the selected items in item
@@ -621,7 +721,6 @@ constexpr int kGatherCap = 8192;   // blocks a long Full row's pre-filter may ke
 
 struct SelectLds {
     SelShared sh;
-    uint32_t bkey[padded_size(kMaxP)];   // keys of the blocks in `blocks` (Full)
     int blocks[kMaxP];                   // Full: selected blocks; Reindex: block of each item
     int slots[kMaxP];                    // Reindex: pool slot of each item
     int cblk[kMaxK];                     // candidate blocks (when not `blocks` itself)
@@ -668,7 +767,7 @@ __global__ __launch_bounds__(kSelThreads) void k_prefilter(const float* __restri
     const int nb = (n + 7) >> 3;
     const int ns = (nb + kRound - 1) / kRound;
     if (nb <= kRegRounds * kRound || ns > kMaxSlices || g >= ns) return;   // uniform per workgroup
-    for (int i = threadIdx.x; i < kBins + kBins / 32; i += kSelThreads) sh.hist[i] = 0;
+    for (int i = threadIdx.x; i < 2 * kHistSpan; i += kSelThreads) sh.hist[i] = 0;
     int phase = 0;
     const float* bm = bmax + (int64_t)r * ld_bmax;
     const uint32_t lo = prefilter_threshold(sh, phase, bm, nb, big);
@@ -715,20 +814,46 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     const float* bm = FULL ? bmax + (int64_t)r * ld_bmax : nullptr;
     RegKeys reg;
     int phase = 0;
-    for (int i = threadIdx.x; i < kBins + kBins / 32; i += kSelThreads) L.sh.hist[i] = 0;
+    for (int i = threadIdx.x; i < 2 * kHistSpan; i += kSelThreads) L.sh.hist[i] = 0;
     const int* cand;        // candidate blocks
     const int* cand_slot;   // their pool slots (Reindex)
     int ncb;                // number of candidate blocks
     bool preloaded = false; // reg already holds the candidates' keys
 
     if constexpr (FULL) {
-        // A = the top max(P, K) blocks (all of them when nb is smaller), with
-        // their keys; the pool and the candidate blocks are A and the top
-        // min(P, K) blocks of A, in the roles their sizes give.
+        // A = the top max(P, K) blocks (all of them when nb is smaller) and B
+        // = the top min(P, K) blocks (B lies in A); the pool and the
+        // candidate blocks are A and B in the roles their sizes give.  Both
+        // thresholds come from one two-target radix select (one target when
+        // there is no pool); then A goes to L.blocks and B, when smaller, to
+        // the pool output or L.cblk.
         const int big = K > P ? K : P;
+        const int small = K < P ? K : P;
         const BlockMaxSrc bsrc{bm, nb};
-        SelState st;
-        int na = -1;
+        int na = -1, nsm = 0;
+        // Selection of A and B over the items of `src` (block id of item i:
+        // id(i)), whose keys `rg` holds.
+        auto select_ab = [&](const auto& src, const RegKeys& rg, auto id) {
+            SelState sa, sb;
+            if (P > 0) radix_select2(L.sh, phase, src, rg, big, small, sa, sb);
+            else sa = radix_select(L.sh, phase, src, rg, big);
+            na = select_compact(L.sh, phase, src, rg, sa, [&](int pos, int i, uint32_t) {
+                if (pos < big) L.blocks[pos] = id(i);
+            });
+            na = na < big ? na : big;
+            if (P > 0 && na > small) {
+                int32_t* po = pool_out + (int64_t)r * P;
+                nsm = select_compact(L.sh, phase, src, rg, sb, [&](int pos, int i, uint32_t) {
+                    if (pos < small) {
+                        if (P >= K) L.cblk[pos] = id(i);
+                        else po[pos] = id(i);
+                    }
+                });
+                nsm = nsm < small ? nsm : small;
+            } else {
+                nsm = na;   // B = A
+            }
+        };
         const int ns = (nb + kRound - 1) / kRound;
         if (nb > kRegRounds * kRound && (!gcount || ns <= kMaxSlices)) {
             // Long row: every pass over all block maxima re-reads memory, so
@@ -791,54 +916,29 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
                 const LdsKeySrc gsrc{{}, L.gkey, cnt};
                 RegKeys greg;
                 load_regs(gsrc, greg);
-                st = radix_select(L.sh, phase, gsrc, greg, big);
-                na = select_compact(L.sh, phase, gsrc, greg, st, [&](int pos, int i, uint32_t key) {
-                    if (pos < big) { L.blocks[pos] = L.gid[i]; L.bkey[padded(pos)] = key; }
-                });
+                select_ab(gsrc, greg, [&](int i) { return L.gid[i]; });
             }
             if (na < 0 && gcount) load_regs(bsrc, reg);
         } else {
             load_regs(bsrc, reg);
         }
-        if (na < 0) {
-            st = radix_select(L.sh, phase, bsrc, reg, big);
-            na = select_compact(L.sh, phase, bsrc, reg, st, [&](int pos, int i, uint32_t key) {
-                if (pos < big) { L.blocks[pos] = i; L.bkey[padded(pos)] = key; }
-            });
-        }
-        na = na < big ? na : big;
+        if (na < 0) select_ab(bsrc, reg, [](int i) { return i; });
         __syncthreads();
         cand = L.blocks;
         cand_slot = nullptr;
         ncb = na;
         if (P > 0) {
             int32_t* po = pool_out + (int64_t)r * P;
-            const int small = K < P ? K : P;
-            const LdsKeySrc asrc{{}, L.bkey, na};
-            if (na > small) {
-                load_regs(asrc, reg);
-                st = radix_select(L.sh, phase, asrc, reg, small);
-            }
-            if (P >= K) {   // pool = A, candidates = top-K of A
+            if (P >= K) {   // pool = A, candidates = B
                 for (int i = threadIdx.x; i < P; i += kSelThreads) po[i] = i < na ? L.blocks[i] : -1;
                 if (na > K) {
-                    select_compact(L.sh, phase, asrc, reg, st, [&](int pos, int i, uint32_t) {
-                        if (pos < K) L.cblk[pos] = L.blocks[i];
-                    });
                     cand = L.cblk;
-                    ncb = K;
+                    ncb = nsm;
                 }
-            } else {        // candidates = A, pool = top-P of A
-                int np = na;
-                if (na > P) {
-                    np = select_compact(L.sh, phase, asrc, reg, st, [&](int pos, int i, uint32_t) {
-                        if (pos < P) po[pos] = L.blocks[i];
-                    });
-                    np = np < P ? np : P;
-                } else {
+            } else {        // candidates = A, pool = B
+                if (na <= P)
                     for (int i = threadIdx.x; i < na; i += kSelThreads) po[i] = L.blocks[i];
-                }
-                for (int i = np + threadIdx.x; i < P; i += kSelThreads) po[i] = -1;
+                for (int i = nsm + threadIdx.x; i < P; i += kSelThreads) po[i] = -1;
             }
         }
     } else {
