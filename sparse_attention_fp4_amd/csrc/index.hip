@@ -726,7 +726,6 @@ struct SelectLds {
     int cblk[kMaxK];                     // candidate blocks (when not `blocks` itself)
     int cslot[kMaxK];                    // Reindex: their pool slots
     unsigned long long sortbuf[kMaxP];   // Reindex: pool sorted by block id
-    int cpg[kMaxK];                      // paged caches: page id of each candidate block
     int flag;
 };
 struct SelectLdsFull : SelectLds {
@@ -993,20 +992,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
 
     // Paged caches: the cache row of each selected entry is written too (-1
     // when beyond 32-bit row numbers), so attention needs no separate
-    // translation.  The candidate blocks' page ids are loaded here and arrive
-    // in registers while the entries are selected.
+    // translation.  The selected ids are kept in LDS (the sort buffer is free
+    // by now) and translated after the compaction.
     int32_t* tr = rows_out ? rows_out + (int64_t)r * K : nullptr;
-    constexpr int kPgPer = kMaxK / kSelThreads;
-    int32_t pgr[kPgPer];
-    if (tr) {
-        const int seq = row_seq[r];
-#pragma unroll
-        for (int k = 0; k < kPgPer; ++k) {
-            const int i = threadIdx.x + k * kSelThreads;
-            const int b = i < ncb ? cand[i] : -1;
-            pgr[k] = b >= 0 ? pm.page_id(seq, ((int64_t)b * 8) >> pm.shift) : -1;
-        }
-    }
+    int* const sel_ids = reinterpret_cast<int*>(L.sortbuf);   // kMaxP 64-bit words hold kMaxK ids
+    static_assert(sizeof(L.sortbuf) >= kMaxK * sizeof(int), "selected ids fit the sort buffer");
 
     // Top-K among the candidate blocks' entries, written in item order, which
     // is ascending entry order.
@@ -1014,25 +1004,25 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     if (!preloaded) load_regs(csrc, reg);
     const SelState st = radix_select(L.sh, phase, csrc, reg, K);
     int32_t* to = topk + (int64_t)r * K;
-    if (tr) {
-#pragma unroll
-        for (int k = 0; k < kPgPer; ++k) L.cpg[threadIdx.x + k * kSelThreads] = pgr[k];
-        __syncthreads();
-    }
     int nk = select_compact(L.sh, phase, csrc, reg, st, [&](int pos, int c, uint32_t) {
         if (pos < K) {
             const int j = cand[c >> 3] * 8 + (c & 7);
             to[pos] = j;
-            if (tr) {
-                const int64_t ph = pm.row_on(L.cpg[c >> 3], j);
-                tr[pos] = ph <= 0x7FFFFFFF ? (int32_t)ph : -1;
-            }
+            if (tr) sel_ids[pos] = j;
         }
     });
     nk = nk < K ? nk : K;
     for (int i = nk + threadIdx.x; i < K; i += kSelThreads) {
         to[i] = -1;
         if (tr) tr[i] = -1;
+    }
+    if (tr) {   // (select_compact ends with a barrier: sel_ids is complete)
+        const int seq = row_seq[r];
+        for (int i = threadIdx.x; i < nk; i += kSelThreads) {
+            const int j = sel_ids[i];
+            const int64_t ph = pm.row_on(pm.page_id(seq, j >> pm.shift), j);
+            tr[i] = ph <= 0x7FFFFFFF ? (int32_t)ph : -1;
+        }
     }
 }
 
