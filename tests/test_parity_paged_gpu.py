@@ -168,6 +168,7 @@ def run_reindex_paged(wl, pages, ikeys, layer, pool, K):
 FULL_CASES = [
     # name, lengths, page_rows, K, P, idx
     ("ragged_p64", [1, 7, 100, 1000, 4097, 20001], 64, 512, 2048, "int3"),
+    ("k_above_p_ties_p32", [40000, 3000, 90], 32, 700, 64, "ties"),
     ("ties_p16", [30000, 17, 8191], 16, 512, 2048, "ties"),
     ("p_below_k_p256", [5000, 3333], 256, 100, 10, "int3"),
     ("long_prefilter_p1024", [150000, 9000], 1024, 1500, 700, "int3"),
@@ -243,6 +244,27 @@ def test_index_paged_unmapped_pages():
     for r in range(R):
         er = expected_reindex(scores[1][r, :lengths[r]], pages.visible(r), pool[r], K)
         assert np.array_equal(got[r], er), f"row {r}: reindex differs"
+
+
+def test_index_reindex_paged_unsorted_pool():
+    """An out-of-order pool with -1 and out-of-range ids (sorted in the
+    selector) over a paged cache: the oracle's Top-K and the matching rows."""
+    lengths = [3000, 700]
+    wl = small_workload(lengths)
+    pages = Pages(lengths, 16, seed=12)
+    ikeys = paged_ikeys(wl, pages)
+    rng = np.random.default_rng(6)
+    K, P = 60, 48
+    pool = np.full((2, P), -1, np.int32)
+    for r, n in enumerate(lengths):
+        nb = (n + 7) // 8
+        ids = rng.choice(nb, 40, replace=False)
+        ids[5] = nb + 9                                  # out of range: skipped
+        pool[r, rng.permutation(P)[:40]] = ids
+    packed = oracle_index_rows(wl, 0, [0, 1], K, P)[2]
+    want = oracle_reindex_rows(wl, 1, [0, 1], packed, pool, K)
+    got = run_reindex_paged(wl, pages, ikeys, 1, pool, K)
+    assert np.array_equal(got, want)
 
 
 def test_paged_rows_formula():
