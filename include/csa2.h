@@ -251,8 +251,8 @@ csa2_status_t csa2_paged_rows(const int32_t* block_table, int32_t max_pages, int
  * All W slots of a ring must lie inside `swa`.
  * The keys are the packed call's (window unrolled), taken in the same order
  * through the same arithmetic, so results are bit-identical to csa2_sparse_attn
- * on a packed copy.  Workspace and limits as csa2_sparse_attn, plus
- * cache_rows * D / 2 < 2^31.
+ * on a packed copy.  Workspace and limits as csa2_sparse_attn; cache rows are
+ * int32 (below 2^31), with no limit on the cache's size in bytes.
  */
 csa2_status_t csa2_sparse_attn_phys(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
                                     int64_t cache_rows, const int32_t* phys_idx, int32_t K,

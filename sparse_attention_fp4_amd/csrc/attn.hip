@@ -75,11 +75,12 @@ __device__ __forceinline__ constexpr int kperm(int t)
     return t < KS / 2 ? 2 * t : 2 * t - KS + 1;
 }
 
-// The cache is read with buffer loads: one descriptor per region (codes,
-// scales, SWA rows of the row) spans exactly the row's valid bytes, and the
-// hardware returns zeros for any dword outside it.  A slot without a key gets
-// the offset kNoKey, beyond every descriptor's range (each is kept below
-// 2^31 bytes), so every load is unconditional and a missing key reads as
+// Main entries are read through 64-bit addresses once the slot's entry is
+// checked against the row (FragRaw::load_row).  A row's SWA window is read
+// with buffer loads: one descriptor spans exactly the window's valid bytes,
+// and the hardware returns zeros for any dword outside it.  A slot without an
+// SWA row gets the offset kNoKey, beyond the descriptor's range (kept below
+// 2^31 bytes), so those loads are unconditional and a missing row reads as
 // zero bytes.
 constexpr uint32_t kNoKey = 0x80000000u;
 constexpr int32_t kBufConfig = 0x00020000;   // raw 32-bit buffer, as for gfx9 data loads
@@ -107,46 +108,72 @@ struct FragRaw {
     f16x2 sp[KS / 2];   // scales of pieces 2u, 2u+1 as fp16 (set by unpair())
     bool valid, is_main;
 
-    // kind (uniform): 0 a fragment of Top-K slots, 1 one of SWA rows.  j:
-    // the slot's Top-K entry (read only for Top-K slots); i: the SWA row.
-    // rc / rs / rw: buffers of the row's codes, scales and SWA rows.  The
-    // lane pair (p, 0), (p, 1) of a key needs one contiguous block (codes:
-    // D/4 bytes, SWA: D/2 bytes); each lane loads its half into consecutive
-    // words and unpair() exchanges the halves.  The same straight-line loads
-    // serve both kinds (offsets and descriptors are chosen per fragment), so
-    // every register is written by exactly one load and nothing waits for a
-    // load before its bytes are used.
-    __device__ __forceinline__ void load(int kind, bool vm, int j, bool vs, int i, int p, int hf,
-                                         __amdgpu_buffer_rsrc_t rc, __amdgpu_buffer_rsrc_t rs,
-                                         __amdgpu_buffer_rsrc_t rw)
+    // SWA row i of the lane's slot (vs: the slot holds one) through rw, the
+    // buffer over the row's window.  The lane pair (p, 0), (p, 1) of a row
+    // needs one contiguous block of D/2 bytes; each lane loads its half into
+    // consecutive words and unpair() exchanges the halves.  An absent row
+    // gets the offset kNoKey and reads as zeros; the loads are unconditional.
+    __device__ __forceinline__ void load_swa(bool vs, int i, int p, int hf, __amdgpu_buffer_rsrc_t rw)
     {
-        valid = vm || vs;
-        is_main = kind == 0;
-        // (unsigned arithmetic: the offsets of absent slots are discarded)
-        const uint32_t uj = (uint32_t)j, ui = (uint32_t)i;
-        const uint32_t swa_off = vs ? ui * D + (D / 2) * p + (D / 4) * hf : kNoKey;
-        const uint32_t off1 = kind == 0 ? (vm ? uj * (D / 2) + (D / 4) * p + (D / 8) * hf : kNoKey) : swa_off;
-        const uint32_t off2 = kind == 0 ? kNoKey : swa_off + D / 8;   // second half of an SWA lane's bytes
-        const uint32_t offs = kind == 0 && vm ? uj * (D / 16) + KS * p : kNoKey;
+        valid = vs;
+        is_main = false;
+        const uint32_t off1 = vs ? (uint32_t)i * D + (D / 2) * p + (D / 4) * hf : kNoKey;
 #pragma unroll
         for (int u = 0; u < KS / 4; ++u) {
-            const u32x4 v = kind == 0 ? __builtin_amdgcn_raw_buffer_load_b128(rc, off1 + 16 * u, 0, 0)
-                                      : __builtin_amdgcn_raw_buffer_load_b128(rw, off1 + 16 * u, 0, 0);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, off1 + 16 * u, 0, 0);
             raw[4 * u] = v[0]; raw[4 * u + 1] = v[1]; raw[4 * u + 2] = v[2]; raw[4 * u + 3] = v[3];
         }
 #pragma unroll
-        for (int u = 0; u < KS / 4; ++u) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, off2 + 16 * u, 0, 0);
+        for (int u = 0; u < KS / 4; ++u) {   // second half of the lane's bytes
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, off1 + D / 8 + 16 * u, 0, 0);
             raw[KS + 4 * u] = v[0]; raw[KS + 4 * u + 1] = v[1]; raw[KS + 4 * u + 2] = v[2]; raw[KS + 4 * u + 3] = v[3];
         }
+        // (the scale words are loaded too, as zeros from past the buffer's
+        // end, so that on either kind of fragment every raw register is
+        // written by a load: the loop then waits on loads in issue order)
         if constexpr (NSC == 4) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, offs, 0, 0);
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, kNoKey, 0, 0);
             sc[0] = v[0]; sc[1] = v[1]; sc[2] = v[2]; sc[3] = v[3];
         } else if constexpr (NSC == 2) {
-            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, offs, 0, 0);
+            const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rw, kNoKey, 0, 0);
             sc[0] = v[0]; sc[1] = v[1];
         } else {
-            sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, offs, 0, 0);
+            sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rw, kNoKey, 0, 0);
+        }
+    }
+
+    // The lane's bytes of main entry j (vm: the slot holds a visible entry)
+    // from codes / scales, which start at the row's first entry (or at the
+    // cache's first row in the cache-row form): its D/4-byte half-block of
+    // codes (the lane pair exchanges halves in unpair()) and its KS scale
+    // bytes, through 64-bit addresses, so entries anywhere in a cache of any
+    // size are reachable; an absent slot loads nothing and keeps zeros.
+    __device__ __forceinline__ void load_row(bool vm, int j, int p, int hf, const uint8_t* codes,
+                                             const uint8_t* scales)
+    {
+        valid = vm;
+        is_main = true;
+#pragma unroll
+        for (int k = 0; k < 2 * KS; ++k) raw[k] = 0u;
+#pragma unroll
+        for (int w = 0; w < NSC; ++w) sc[w] = 0u;
+        if (vm) {
+            const uint8_t* pc = codes + (uint64_t)(uint32_t)j * (D / 2) + (D / 4) * p + (D / 8) * hf;
+#pragma unroll
+            for (int u = 0; u < KS / 4; ++u) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(pc + 16 * u);
+                raw[4 * u] = v[0]; raw[4 * u + 1] = v[1]; raw[4 * u + 2] = v[2]; raw[4 * u + 3] = v[3];
+            }
+            const uint8_t* ps = scales + (uint64_t)(uint32_t)j * (D / 16) + KS * p;
+            if constexpr (NSC == 4) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(ps);
+                sc[0] = v[0]; sc[1] = v[1]; sc[2] = v[2]; sc[3] = v[3];
+            } else if constexpr (NSC == 2) {
+                const u32x2 v = *reinterpret_cast<const u32x2*>(ps);
+                sc[0] = v[0]; sc[1] = v[1];
+            } else {
+                sc[0] = *reinterpret_cast<const uint32_t*>(ps);
+            }
         }
     }
 
@@ -542,12 +569,10 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
         qa_s[((HT + ht) * KS + t) * CSA2_WAVE + lane] = bv;
     }
     const int p = grp >> 1;
-    // Buffers over the row's visible entries and SWA rows; 32-bit offsets
-    // reach entries below 2^31 / (D/2) (8M entries at D = 512), later ones
-    // read as absent.
-    const int nb = n < 0 ? 0 : (n > 0x7FFFFFFF / (D / 2) ? 0x7FFFFFFF / (D / 2) : n);
-    const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(codes + base * (D / 2), nb * (D / 2));
-    const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(scales + base * (D / 16), nb * (D / 16));
+    // The row's SWA rows through a buffer (reads outside it return zeros);
+    // main entries are read through 64-bit addresses (FragRaw::load_row),
+    // so entry ids are bounded only by the row's length.
+    const int nb = n < 0 ? 0 : n;
     const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(W > 0 ? swa + swa0 * D : swa, (PG && swa_head ? W : nsw) * D);   // empty when W == 0
     const int Kp = pad_topk(K);
     auto load_frag = [&](FragRaw<D>& f, int fr_, int j) {
@@ -555,7 +580,10 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
         const bool vm = slot < K && j >= 0 && j < nb;
         const bool vs = i >= 0 && i < nsw;
         const int iw = PG ? (head + i >= W ? head + i - W : head + i) : i;
-        f.load(frag_kind(fr_, Kp), vm, j, vs, iw, p, hf, rc, rs, rw);
+        if (frag_kind(fr_, Kp) == 0)
+            f.load_row(vm, j, p, hf, codes + base * (D / 2), scales + base * (D / 16));
+        else
+            f.load_swa(vs, iw, p, hf, rw);
     };
     FragRaw<D> cur, nxt;   // cur is unpaired in place at the start of its fragment
     if (fr < f_end) load_frag(cur, fr, idx_c);
@@ -1007,8 +1035,6 @@ extern "C" csa2_status_t csa2_sparse_attn_phys(const uint16_t* q, const uint8_t*
                                                void* workspace, size_t workspace_bytes, void* stream)
 {
     CSA2_REQUIRE(cache_rows >= 1, CSA2_ERR_SHAPE, "sparse_attn_phys: cache_rows=%lld < 1", (long long)cache_rows);
-    CSA2_REQUIRE(D < 16 || cache_rows <= 0x7FFFFFFF / (D / 2), CSA2_ERR_UNSUPPORTED,
-                 "sparse_attn_phys: codes beyond 2^31 bytes (cache_rows=%lld)", (long long)cache_rows);
     return sparse_attn_impl(q, codes, scales, nullptr, nullptr, nullptr, cache_rows, phys_idx, K, swa, swa_row_start,
                             swa_len, swa_head, R, H, D, W, softmax_scale, out, lse, workspace, workspace_bytes,
                             stream);

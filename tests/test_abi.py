@@ -212,7 +212,7 @@ def test_sparse_attn_phys_validation():
                                   "H", "D", "W", "scale", "out", "lse", "ws", "wsb")], None)
 
     assert call(rows=0) == 2
-    assert call(rows=1 << 23) == 3                  # codes beyond 2^31 bytes at D = 512
+    assert call(K=5000) == 3
     assert call(D=96) == 3
     assert call(idx=None) == 1
     assert call(swa=None) == 1

@@ -378,6 +378,37 @@ def test_sparse_attn_phys_matches_packed_and_oracle(name, lengths, D, H, K, W, p
                np.stack([ref[r][1] for r in check_rows]), what=name)
 
 
+def test_sparse_attn_phys_cache_beyond_2gib():
+    """Cache rows past 2^31 bytes of codes (9.4M rows at D = 512): the row form
+    reads them through 64-bit addresses and matches the packed call."""
+    lengths = [3000, 5000]
+    D, H, K, W, pr = 512, 16, 128, 32, 64
+    wl = small_workload(lengths, D=D, H=H, W=W, Hi=8, Di=64)
+    pages = Pages(lengths, pr, seed=2)
+    off_pages = (9_400_000 + pr - 1) // pr                 # every page beyond 2^31 bytes of codes
+    rows_total = (off_pages + pages.n_phys) * pr
+    codes, scales, pc, ps = paged_kv(wl, pages)
+    big_c = torch.empty(rows_total, D // 2, dtype=torch.uint8, device=DEV)
+    big_s = torch.empty(rows_total, D // 16, dtype=torch.uint8, device=DEV)
+    big_c[off_pages * pr:] = pc
+    big_s[off_pages * pr:] = ps
+    bt = torch.where(pages.bt_dev >= 0, pages.bt_dev + off_pages, pages.bt_dev)
+    rng = np.random.default_rng(3)
+    topk = np.full((2, K), -1, np.int32)
+    for r, n in enumerate(lengths):
+        topk[r] = np.sort(rng.choice(n, K, replace=False))
+    topk_t = torch.tensor(topk, device=DEV)
+    phys = csa2.csa2_paged_rows(bt, pr, rows_total, wl.row_seq, wl.row_len, topk_t)
+    assert int(phys.min()) >= off_pages * pr
+    scale = 1.0 / math.sqrt(D)
+    out_p, lse_p = csa2.csa2_sparse_attn(wl.q[0], codes, scales, wl.seq_start, wl.row_seq, wl.row_len, topk_t,
+                                         wl.swa[0], wl.swa_row_start, wl.swa_len, W, scale)
+    out_f, lse_f = csa2.csa2_sparse_attn_phys(wl.q[0], big_c, big_s, phys, wl.swa[0], wl.swa_row_start, wl.swa_len,
+                                              W, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out_f, out_p) and torch.equal(lse_f, lse_p)
+
+
 @pytest.mark.parametrize("cid", [1, 2])
 def test_paged_step_matches_packed_step(cid):
     """The whole layer schedule over a paged cache (shuffled pages of 64
