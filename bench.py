@@ -46,11 +46,11 @@ HBM_PEAK_GBPS = 8000.0
 # were taken on).  Reported as null whenever that source has changed since.
 TRAFFIC = {
     # profiles/sparse_attn_decode_64k.md: k_sparse_attn + k_attn_combine per call
-    (2, "sparse_attn", "dbb3533f8d62e83a"): 32085053,
+    (2, "sparse_attn", "dbb3533f8d62e83a"): 32085347,
     # profiles/index_full_decode_64k.md: k_index_score (Full) + k_select (Full) per call
-    (2, "index_full", "a5c1f7b2fe638276"): 284828099,
+    (2, "index_full", "aac27b73117fbf0b"): 284857524,
     # profiles/index_reindex_decode_64k.md: k_index_score (Reindex) + k_select (Reindex) per call
-    (2, "index_reindex", "a5c1f7b2fe638276"): 74566773,
+    (2, "index_reindex", "aac27b73117fbf0b"): 74560284,
 }
 CALL_SOURCE = {"sparse_attn": "attn.hip", "index_full": "index.hip", "index_reindex": "index.hip",
                "quantize_append": "quantize.hip"}

@@ -471,8 +471,9 @@ __device__ __forceinline__ void load_regs(const Src& src, RegKeys& reg)
 
 // Finds the threshold of the k largest keys among the valid items.  The bits
 // shared by every valid key are skipped first (an AND/OR reduction finds the
-// highest bit that differs), then radix passes over 11-bit digits below it
-// narrow to the digit holding the k-th largest key, stopping early once a
+// highest and the lowest bit that differ: scores on a coarse grid leave their
+// low bits zero in every key), then radix passes over 11-bit digits between
+// them narrow to the digit holding the k-th largest key, stopping early once a
 // whole digit bin is taken.  A pass is: LDS atomic histogram of the keys that
 // match the prefix so far (the others add into a discard word of their own
 // lane, so the loop has no branches), barrier, then wave 0 alone finds the
@@ -481,6 +482,15 @@ __device__ __forceinline__ void load_regs(const Src& src, RegKeys& reg)
 // lane's 32 bins (one per lane) picks the bin; wave 0 also clears the bins for
 // the next pass and publishes the digit, barrier.  The histogram must be zero
 // on entry and is zero again on return.
+
+// Mask of the bits outside the varying range of the valid keys (diff: the bits
+// in which some valid keys differ): above its highest and below its lowest
+// bit.  Every valid key holds the same values there.
+__device__ __forceinline__ uint32_t common_bits(uint32_t diff)
+{
+    if (diff == 0u) return 0xFFFFFFFFu;
+    return ~((2u << (31 - __builtin_clz(diff))) - 1u) | ((1u << __builtin_ctz(diff)) - 1u);
+}
 
 // Run by one wave: the bin of histogram h holding the krem-th largest key
 // (bins taken from the highest digit down), the count of keys in higher bins
@@ -542,14 +552,15 @@ __device__ __forceinline__ SelState radix_select(SelShared& sh, int& phase, cons
     SelState st{0u, 0u, nv};
     if (nv <= k) return st;                       // everything valid is selected (mask 0)
     const uint32_t diff = kand ^ kor;             // bits that vary among valid keys
-    st.mask = diff ? ~((2u << (31 - __builtin_clz(diff))) - 1u) : 0xFFFFFFFFu;
+    st.mask = common_bits(diff);
     st.prefix = kand & st.mask;
     st.need = k;
     if (diff == 0u) return st;                    // all valid keys equal: ties only
     int top = 31 - __builtin_clz(diff);           // highest varying bit
+    const int low = __builtin_ctz(diff);          // lowest varying bit
     int krem = k;
-    while (top >= 0) {
-        const int width = top + 1 < 11 ? top + 1 : 11;
+    while (top >= low) {
+        const int width = top + 1 - low < 11 ? top + 1 - low : 11;
         const int shift = top + 1 - width;
         const uint32_t dmask = (1u << width) - 1u;
         for_rounds(src, reg, [&](int, const uint32_t (&key)[kE]) {
@@ -610,14 +621,15 @@ __device__ __forceinline__ void radix_select2(SelShared& sh, int& phase, const S
     bool done1 = nv <= k1, done2 = nv <= k2;     // everything valid is selected (mask 0)
     if (done1 && done2) return;
     const uint32_t diff = kand ^ kor;
-    const uint32_t mask0 = diff ? ~((2u << (31 - __builtin_clz(diff))) - 1u) : 0xFFFFFFFFu;
+    const uint32_t mask0 = common_bits(diff);
     if (!done1) s1 = SelState{kand & mask0, mask0, k1};
     if (!done2) s2 = SelState{kand & mask0, mask0, k2};
     if (diff == 0u) return;                       // all valid keys equal: ties only
     int top = 31 - __builtin_clz(diff);
+    const int low = __builtin_ctz(diff);
     int krem1 = k1, krem2 = k2;
-    while (top >= 0 && !(done1 && done2)) {
-        const int width = top + 1 < 11 ? top + 1 : 11;
+    while (top >= low && !(done1 && done2)) {
+        const int width = top + 1 - low < 11 ? top + 1 - low : 11;
         const int shift = top + 1 - width;
         const uint32_t dmask = (1u << width) - 1u;
         const bool same = !done1 && !done2 && s1.prefix == s2.prefix;   // (the masks agree)

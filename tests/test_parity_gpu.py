@@ -182,6 +182,37 @@ def test_index_full_long_row_all_ties_falls_back():
     assert topk[0].tolist() == list(range(300)) and pool[1].tolist() == list(range(2000))
 
 
+def test_index_scores_sharing_low_bits_below_their_varying_bits():
+    # every score is k[0] of its entry, one of 1.125, 1.375, 1.625, 1.875: their float bits differ only
+    # in bits 22..21 and all hold a 1 in bit 20, so the selector's common-bit mask reaches below the
+    # bits it resolves; heavy ties leave the lowest ids to decide
+    lengths = [5000, 777]
+    wl = small_workload(lengths, Hi=16, Di=64)
+    rng = np.random.default_rng(17)
+    vals = torch.tensor(rng.choice([1.125, 1.375, 1.625, 1.875], size=wl.ikeys.shape[0]), dtype=torch.float32)
+    k0 = vals.to(torch.float8_e4m3fn).view(torch.uint8).to(DEV)
+    assert torch.equal(k0.cpu().view(torch.float8_e4m3fn).float(), vals)
+    wl.ikeys[:, 0] = k0
+    for layer in (0, 1):
+        wl.w[layer].zero_()
+        wl.w[layer][:, 0] = 1.0
+        wl.qI[layer].zero_()
+        wl.qI[layer][:, 0, 0] = torch.tensor([1.0]).to(torch.float8_e4m3fn).view(torch.uint8).item()
+    K, P = 100, 64
+    rows = [0, 1]
+    topk, pool = gpu_index_full(wl, 0, K, P)
+    rt, rp, packed = oracle_index_rows(wl, 0, rows, K, P)
+    assert np.array_equal(topk, rt) and np.array_equal(pool, rp)
+    want = oracle_reindex_rows(wl, 1, rows, packed, rp, K)
+    got = csa2.csa2_index_reindex(wl.qI[1], wl.w[1], wl.ikeys, wl.seq_start, wl.row_seq, wl.row_len,
+                                  torch.tensor(rp, device=DEV), K)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(got), want)
+    # the Top-K holds the largest value's lowest ids first (the ids ascend within the list)
+    s0 = np.flatnonzero(vals.numpy()[:lengths[0]] == 1.875)
+    assert len(s0) >= K and rt[0].tolist() == s0[:K].tolist()
+
+
 def many_rows(seq_lengths, rows, Hi, Di, seed=21):
     """A workload of several sequences with `rows` = [(sequence, visible
     entries)] query rows (as in a prefill chunk), each with its own indexer
