@@ -38,7 +38,7 @@ constexpr int kMaxK = 2048;
 constexpr int kMaxP = 2048;
 constexpr int kBins = 2048;
 constexpr int kFullChunk = 1024;     // entries per Full-score workgroup
-constexpr int kReChunk = 512;        // pool slots per Reindex-score workgroup
+constexpr int kReChunkMax = 1024;    // pool slots per Reindex-score workgroup, at most (256, 512 or 1024)
 
 // ------------------------------------------------------------------ scoring
 
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HT * KS <= 
     const int64_t* __restrict__ seq_start, PageMap pm, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ pool, int32_t Hi, int32_t Di,
     int32_t P, float* __restrict__ scores, int64_t ld_scores, float* __restrict__ bmax,
-    int64_t ld_bmax)
+    int64_t ld_bmax, int32_t re_chunk)
 {
     const int r = blockIdx.y;
     const int n = row_len[r];
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HT * KS <= 
     const int wave = threadIdx.x / CSA2_WAVE;
     const int col = lane & 15;       // entry within a 16-entry tile / head within a head tile
     const int grp = lane >> 4;       // 32-byte slice of a 128-byte k-step
-    const int chunk = REINDEX ? kReChunk : kFullChunk;
+    const int chunk = REINDEX ? re_chunk : kFullChunk;
     const int64_t first = (int64_t)blockIdx.x * chunk;
     if (!REINDEX && first >= n) return;
     const int nb = (n + 7) >> 3;
@@ -102,11 +102,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HT * KS <= 
     // block id (-1 if absent or out of range) and the id of the page that
     // holds it (a block never straddles pages).  Full, paged: the ids of the
     // pages its entries cover (at most chunk / 8: pages hold at least 8).
-    constexpr int kPg = (REINDEX ? kReChunk : kFullChunk) / 8;
+    constexpr int kPg = (REINDEX ? kReChunkMax : kFullChunk) / 8;
     __shared__ int32_t pg_id[PAGED ? kPg : 1];
     __shared__ int32_t pg_blk[REINDEX ? kPg : 1];
     if constexpr (PAGED || REINDEX) {
-        for (int t = threadIdx.x; t < kPg; t += blockDim.x) {
+        for (int t = threadIdx.x; t < chunk / 8; t += blockDim.x) {
             if constexpr (REINDEX) {
                 const int64_t ps = (first >> 3) + t;
                 const int b = ps < P ? pool[(int64_t)r * P + ps] : -1;
@@ -1042,12 +1042,12 @@ template <bool REINDEX, bool PAGED>
 void launch_score(int HT, int KS, dim3 grid, hipStream_t st, const uint8_t* qI, const float* w,
                   const uint8_t* ikeys, const int64_t* seq_start, const PageMap& pm, const int32_t* row_seq,
                   const int32_t* row_len, const int32_t* pool, int32_t Hi, int32_t Di, int32_t P,
-                  float* scores, int64_t lds, float* bm, int64_t ldb)
+                  float* scores, int64_t lds, float* bm, int64_t ldb, int re_chunk)
 {
 #define CSA2_SCORE(ht, ks)                                                                                 \
     if (HT == ht && KS == ks) {                                                                            \
         hipLaunchKernelGGL((k_index_score<ht, ks, REINDEX, PAGED>), grid, dim3(256), 0, st, qI, w, ikeys,   \
-                           seq_start, pm, row_seq, row_len, pool, Hi, Di, P, scores, lds, bm, ldb);        \
+                           seq_start, pm, row_seq, row_len, pool, Hi, Di, P, scores, lds, bm, ldb, re_chunk); \
         return;                                                                                            \
     }
     CSA2_SCORE(1, 1) CSA2_SCORE(2, 1) CSA2_SCORE(3, 1) CSA2_SCORE(4, 1)
@@ -1059,14 +1059,14 @@ template <bool REINDEX>
 void launch_score(bool paged, int HT, int KS, dim3 grid, hipStream_t st, const uint8_t* qI, const float* w,
                   const uint8_t* ikeys, const int64_t* seq_start, const PageMap& pm, const int32_t* row_seq,
                   const int32_t* row_len, const int32_t* pool, int32_t Hi, int32_t Di, int32_t P,
-                  float* scores, int64_t lds, float* bm, int64_t ldb)
+                  float* scores, int64_t lds, float* bm, int64_t ldb, int re_chunk = 0)
 {
     if (paged)
         launch_score<REINDEX, true>(HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len, pool, Hi, Di,
-                                    P, scores, lds, bm, ldb);
+                                    P, scores, lds, bm, ldb, re_chunk);
     else
         launch_score<REINDEX, false>(HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len, pool, Hi,
-                                     Di, P, scores, lds, bm, ldb);
+                                     Di, P, scores, lds, bm, ldb, re_chunk);
 }
 
 // Block-table arguments of the paged calls; shift = log2(page_rows).
@@ -1090,7 +1090,19 @@ int64_t full_ld(int32_t max_len) { return ((int64_t)max_len + kFullChunk - 1) / 
 // pre-filter (then the workspace also holds its gathered keys, ids and counts).
 int64_t full_slices(int64_t ld) { return (ld / 8 + kRound - 1) / kRound; }
 bool full_prefilter(int64_t ld) { return ld / 8 > (int64_t)kRegRounds * kRound; }
-int64_t reindex_ld(int32_t P) { return ((int64_t)P * 8 + kReChunk - 1) / kReChunk * kReChunk; }
+int64_t reindex_ld(int32_t P) { return ((int64_t)P * 8 + kReChunkMax - 1) / kReChunkMax * kReChunkMax; }
+
+// Pool slots per Reindex-score workgroup: the largest of 1024, 512 and 256
+// that still gives at least two workgroups per compute unit (a few rows take
+// smaller chunks, so that their pools spread over the whole GPU; many rows
+// take larger ones, which load their keys with fewer, longer workgroups).
+// Every choice divides reindex_ld(P).
+int reindex_chunk(int32_t R, int64_t ld)
+{
+    for (int c = kReChunkMax; c > 256; c /= 2)
+        if ((int64_t)R * (ld / c) >= 512) return c;
+    return 256;
+}
 
 csa2_status_t check_indexer_dims(const char* who, int32_t R, int32_t Hi, int32_t Di, int32_t K, int32_t block)
 {
@@ -1242,10 +1254,11 @@ csa2_status_t index_reindex_impl(const uint8_t* qI, const float* w, const uint8_
     float* scores = static_cast<float*>(workspace);
     hipStream_t st = csa2::as_stream(stream);
     const int HT = (Hi + 15) / 16, KS = (Di + 127) / 128;
-    dim3 grid((unsigned)(ld / kReChunk), (unsigned)R);
+    const int chunk = reindex_chunk(R, ld);
+    dim3 grid((unsigned)(ld / chunk), (unsigned)R);
     const PageMap pm = pmp ? *pmp : PageMap{nullptr, 0, 0, 0};
     launch_score<true>(pmp != nullptr, HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len, pool_blocks,
-                       Hi, Di, P, scores, ld, nullptr, 0);
+                       Hi, Di, P, scores, ld, nullptr, 0, chunk);
     hipLaunchKernelGGL(k_select<false>, dim3((unsigned)R), dim3(kSelThreads), 0, st, scores, ld, nullptr, 0,
                        row_len, pool_blocks, K, P, topk_idx, nullptr, nullptr, nullptr, nullptr, 0, row_seq, pm,
                        pmp ? topk_rows : nullptr);
