@@ -46,11 +46,11 @@ HBM_PEAK_GBPS = 8000.0
 # were taken on).  Reported as null whenever that source has changed since.
 TRAFFIC = {
     # profiles/sparse_attn_decode_64k.md: k_sparse_attn + k_attn_combine per call
-    (2, "sparse_attn", "dbb3533f8d62e83a"): 32085347,
+    (2, "sparse_attn", "dbb3533f8d62e83a"): 32085009,
     # profiles/index_full_decode_64k.md: k_index_score (Full) + k_select (Full) per call
-    (2, "index_full", "aac27b73117fbf0b"): 284857524,
+    (2, "index_full", "3b324613329f3265"): 284831767,
     # profiles/index_reindex_decode_64k.md: k_index_score (Reindex) + k_select (Reindex) per call
-    (2, "index_reindex", "aac27b73117fbf0b"): 74560284,
+    (2, "index_reindex", "3b324613329f3265"): 74539671,
 }
 CALL_SOURCE = {"sparse_attn": "attn.hip", "index_full": "index.hip", "index_reindex": "index.hip",
                "quantize_append": "quantize.hip"}
