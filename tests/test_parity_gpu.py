@@ -256,6 +256,8 @@ def test_index_full_many_rows_matches_oracle(case):
     ("small", [3000, 64, 9], 8, 64, 64, 256, "int3"),
     ("k2048_all_pool", [70000, 20000, 5], 16, 64, 2048, 2048, "int3"),
     ("k_above_pool", [40000, 3000], 16, 64, 700, 64, "ties"),
+    # 16 rows of full pools: 512 pool positions per scoring workgroup (a few rows take 256, many 1,024)
+    ("rows16_full_pools", [17000] * 16, 16, 64, 512, 2048, "int3"),
 ])
 def test_index_reindex_matches_oracle(name, lengths, Hi, Di, K, P, idx):
     log(f"index_reindex parity: {name}")
