@@ -1,17 +1,24 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (one CSA2Step over all layers).  The oracle recomputes a seeded
-sample of rows (the whole row: every entry's score, the Top-K, the pool, each
-Reindex layer, and attention on sampled layers) and a sample of quantised cache
-rows; every sampled integer output must match exactly and every sampled
-attention output must meet the tolerance."""
+benchmark times (one CSA2Step over all layers).
+
+The oracle recomputes, for every query row of the decode workloads (decode-64K,
+decode-1M, the ragged batch) and for 64 seeded rows of the prefill chunk, the
+whole index path: every entry's score, the Top-K, the block pool and each
+Reindex layer's Top-K on the oracle's own pool.  Attention is checked on seeded
+(row, layer) pairs, each with the Top-K list the oracle's own layer schedule
+(`oracle.step.parents`) assigns to that layer, so a wrong inheritance link in
+the library's schedule fails here.  Integer outputs must match exactly;
+attention outputs must meet the tolerance of tests/helpers.py.  A sample of
+quantised cache rows is checked bit for bit as well."""
 import math
 
 import numpy as np
 import pytest
 import torch
 
+import oracle.step
 import sparse_attention_fp4_amd as csa2
-from sparse_attention_fp4_amd.step import CSA2Step, parent_layers
+from sparse_attention_fp4_amd.step import CSA2Step
 import workloads
 from helpers import (check_attn, log, np_, oracle_attn_rows, oracle_index_rows, oracle_quantize,
                      oracle_reindex_rows)
@@ -33,13 +40,40 @@ def build_step(cfg, wl):
     return step
 
 
-SAMPLES = {
-    2: dict(rows=[0, 17, 31], attn_layers=[0, 1, 5, 12, 19]),
-    3: dict(rows=[2], attn_layers=[0, 5, 19]),
-    4: dict(rows=[0, 1234, 4095], attn_layers=[0]),
-    5: dict(rows=None, attn_layers=[0, 10, 16]),
-    6: dict(rows=[0, 2047, 4095], attn_layers=[0, 3, 5, 19]),
+# index rows: "all" or a count of seeded rows (always including the first and
+# the last); attention: number of seeded (row, layer) pairs, always including
+# the first and last row, the Full layer, a Reindex layer, the last layer and
+# (ragged batch) the shortest and longest rows.
+PLAN = {
+    2: dict(index_rows="all", attn_pairs=16),
+    3: dict(index_rows="all", attn_pairs=8),
+    5: dict(index_rows="all", attn_pairs=16),
+    4: dict(index_rows=64, attn_pairs=16),
+    6: dict(index_rows=16, attn_pairs=16),
 }
+
+
+def index_rows_of(cfg, wl, spec):
+    R = wl.R
+    if spec == "all":
+        return list(range(R))
+    rng = np.random.default_rng(cfg.seed + 11)
+    pick = set(rng.choice(R, size=min(spec, R) - 2, replace=False).tolist()) | {0, R - 1}
+    return sorted(pick)[:spec] if len(pick) > spec else sorted(pick)
+
+
+def attn_pairs_of(cfg, wl, rows, npairs):
+    modes = list(cfg.layers)
+    L = len(modes)
+    rng = np.random.default_rng(cfg.seed + 13)
+    first_r = modes.index("R") if "R" in modes else 0
+    pairs = {(rows[0], 0), (rows[-1], L - 1), (rows[len(rows) // 2], first_r)}
+    if cfg.N is None:
+        lens = wl.lengths[np_(wl.row_seq)]
+        pairs |= {(int(np.argmin(lens)), int(rng.integers(0, L))), (int(np.argmax(lens)), int(rng.integers(0, L)))}
+    while len(pairs) < npairs:
+        pairs.add((int(rows[rng.integers(0, len(rows))]), int(rng.integers(0, L))))
+    return sorted(pairs)
 
 
 @pytest.mark.parametrize("cid", [2, 5, 3, 4, 6])
@@ -54,12 +88,8 @@ def test_full_size_workload(cid):
     step.run()
     torch.cuda.synchronize()
     modes = list(cfg.layers)
-    par = parent_layers(modes)
-    rows = SAMPLES[cid]["rows"]
-    if rows is None:
-        lens = wl.lengths
-        rng = np.random.default_rng(cfg.seed)
-        rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)), *rng.choice(len(lens), 2, replace=False).tolist()})
+    par = oracle.step.parents(modes)   # the oracle's own schedule, not the library's
+    rows = index_rows_of(cfg, wl, PLAN[cid]["index_rows"])
 
     # quantised cache: a seeded sample of rows
     rng = np.random.default_rng(cfg.seed + 7)
@@ -70,26 +100,44 @@ def test_full_size_workload(cid):
     assert np.array_equal(np_(step.scales[qrows_t]), rs), "scales differ"
     log("  quantised rows match")
 
-    # Full layer: Top-K and pool of the sampled rows
-    log(f"  oracle Full index for rows {rows}")
+    # Full layer: Top-K and pool of every checked row
+    log(f"  oracle Full index for {len(rows)} rows")
     rt, rp, packed = oracle_index_rows(wl, 0, rows, cfg.K, cfg.P)
-    assert np.array_equal(np_(step.topk[0])[rows], rt), "Full top-k differs"
-    assert np.array_equal(np_(step.pool)[rows], rp), "pool differs"
+    got_t, got_p = np_(step.topk[0])[rows], np_(step.pool)[rows]
+    bad = [rows[i] for i in range(len(rows)) if not np.array_equal(got_t[i], rt[i])]
+    assert not bad, f"Full top-k differs on rows {bad[:8]}"
+    bad = [rows[i] for i in range(len(rows)) if not np.array_equal(got_p[i], rp[i])]
+    assert not bad, f"pool differs on rows {bad[:8]}"
     oracle_topk = {0: rt}
     for l, m in enumerate(modes):
         if m == "R":
+            log(f"  oracle Reindex layer {l} for {len(rows)} rows")
             want = oracle_reindex_rows(wl, l, rows, packed, rp, cfg.K)
-            assert np.array_equal(np_(step.topk[l])[rows], want), f"Reindex layer {l} differs"
+            got = np_(step.topk[l])[rows]
+            bad = [rows[i] for i in range(len(rows)) if not np.array_equal(got[i], want[i])]
+            assert not bad, f"Reindex layer {l} differs on rows {bad[:8]}"
             oracle_topk[l] = want
     log("  index outputs match")
 
-    for l in SAMPLES[cid]["attn_layers"]:
-        parent = oracle_topk[par[l]]
-        ref = oracle_attn_rows(wl, {r: parent[i] for i, r in enumerate(rows)}, l, rows, cfg.W,
-                               1.0 / math.sqrt(cfg.D))
-        out = np_(step.out[l])[rows]
-        lse = np_(step.lse[l])[rows]
-        check_attn(out, np.stack([ref[r][0] for r in rows]), lse, np.stack([ref[r][1] for r in rows]),
-                   what=f"config {cid} layer {l}")
+    pos = {r: i for i, r in enumerate(rows)}
+    pairs = attn_pairs_of(cfg, wl, rows, PLAN[cid]["attn_pairs"])
+    missing = sorted({r for r, _ in pairs if r not in pos})
+    if missing:   # rows picked only for attention (ragged extremes): oracle index lists for them too
+        mt, mp, mpacked = oracle_index_rows(wl, 0, missing, cfg.K, cfg.P)
+        extra = {0: mt}
+        for l, m in enumerate(modes):
+            if m == "R":
+                extra[l] = oracle_reindex_rows(wl, l, missing, mpacked, mp, cfg.K)
+    by_layer = {}
+    for r, l in pairs:
+        by_layer.setdefault(l, []).append(r)
+    for l, rs_l in sorted(by_layer.items()):
+        lists = {r: (oracle_topk[par[l]][pos[r]] if r in pos else extra[par[l]][missing.index(r)]) for r in rs_l}
+        ref = oracle_attn_rows(wl, lists, l, rs_l, cfg.W, 1.0 / math.sqrt(cfg.D))
+        out = np_(step.out[l])[rs_l]
+        lse = np_(step.lse[l])[rs_l]
+        check_attn(out, np.stack([ref[r][0] for r in rs_l]), lse, np.stack([ref[r][1] for r in rs_l]),
+                   what=f"config {cid} layer {l} rows {rs_l}")
+    log(f"  attention matches on {len(pairs)} (row, layer) pairs")
     del step, wl
     torch.cuda.empty_cache()

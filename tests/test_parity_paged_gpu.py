@@ -21,6 +21,7 @@ import pytest
 import torch
 
 import oracle
+import oracle.step
 import sparse_attention_fp4_amd as csa2
 import workloads
 from helpers import check_attn, log, np_, oracle_attn_rows, oracle_index_rows, oracle_reindex_rows
@@ -413,8 +414,8 @@ def test_sparse_attn_phys_cache_beyond_2gib():
 def test_paged_step_matches_packed_step(cid):
     """The whole layer schedule over a paged cache (shuffled pages of 64
     entries, SWA windows as rings) gives the packed schedule's indices and
-    outputs bit for bit; the packed schedule is checked against the oracle in
-    the other parity tests."""
+    outputs bit for bit, and the paged step's own outputs match the oracle,
+    whose layer schedule decides which Top-K list each layer attends with."""
     from sparse_attention_fp4_amd.step import CSA2Step
     log(f"paged step vs packed step: config {cid}")
     cfg = workloads.CONFIGS[cid]
@@ -447,3 +448,21 @@ def test_paged_step_matches_packed_step(cid):
     for l in range(len(cfg.layers)):
         assert torch.equal(packed.out[l], paged.out[l]), f"layer {l}: output differs"
         assert torch.equal(packed.lse[l], paged.lse[l]), f"layer {l}: lse differs"
+    # the paged step against the oracle directly
+    modes = list(cfg.layers)
+    rows_chk = list(range(wl.R)) if wl.R <= 4 else [0, wl.R // 2, wl.R - 1]
+    rt, rp, packed_o = oracle_index_rows(wl, 0, rows_chk, cfg.K, cfg.P)
+    assert np.array_equal(np_(paged.topk[0])[rows_chk], rt), "paged Full top-k != oracle"
+    assert np.array_equal(np_(paged.pool)[rows_chk], rp), "paged pool != oracle"
+    otk = {0: rt}
+    for l, m in enumerate(modes):
+        if m == "R":
+            otk[l] = oracle_reindex_rows(wl, l, rows_chk, packed_o, rp, cfg.K)
+            assert np.array_equal(np_(paged.topk[l])[rows_chk], otk[l]), f"paged Reindex layer {l} != oracle"
+    par = oracle.step.parents(modes)
+    for l in sorted({0, modes.index("R"), len(modes) - 1}):
+        ref = oracle_attn_rows(wl, {r: otk[par[l]][i] for i, r in enumerate(rows_chk)}, l, rows_chk, cfg.W,
+                               1.0 / math.sqrt(D))
+        check_attn(np_(paged.out[l])[rows_chk], np.stack([ref[r][0] for r in rows_chk]),
+                   np_(paged.lse[l])[rows_chk], np.stack([ref[r][1] for r in rows_chk]),
+                   what=f"paged step config {cid} layer {l}")
