@@ -43,22 +43,22 @@ def lib():
         L = ctypes.CDLL(_LIB_PATH)
         P = ctypes.c_void_p
         i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
-        L.ora_e2m1_value.argtypes = [ctypes.c_int]
-        L.ora_e2m1_value.restype = ctypes.c_double
-        L.ora_e4m3_value.argtypes = [ctypes.c_int]
-        L.ora_e4m3_value.restype = ctypes.c_double
-        L.ora_e4m3_encode.argtypes = [ctypes.c_double]
-        L.ora_e4m3_encode.restype = ctypes.c_int
-        L.ora_quantize_append.argtypes = [P, ctypes.c_int, i32, i32, P, P, P, i64]
-        L.ora_dequant_rows.argtypes = [P, P, i64, i32, P]
-        L.ora_index_scores.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P]
-        L.ora_index_full.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, P, P]
-        L.ora_index_reindex.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, P]
-        L.ora_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, P, P, P, i32, i32, i32, i32, f32,
+        L.csa2_ref_e2m1_value.argtypes = [ctypes.c_int]
+        L.csa2_ref_e2m1_value.restype = ctypes.c_double
+        L.csa2_ref_e4m3_value.argtypes = [ctypes.c_int]
+        L.csa2_ref_e4m3_value.restype = ctypes.c_double
+        L.csa2_ref_e4m3_encode.argtypes = [ctypes.c_double]
+        L.csa2_ref_e4m3_encode.restype = ctypes.c_int
+        L.csa2_ref_quantize_append.argtypes = [P, ctypes.c_int, i32, i32, P, P, P, i64]
+        L.csa2_ref_dequant_rows.argtypes = [P, P, i64, i32, P]
+        L.csa2_ref_index_scores.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, P]
+        L.csa2_ref_index_full.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, P, P]
+        L.csa2_ref_index_reindex.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, P]
+        L.csa2_ref_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, P, P, P, i32, i32, i32, i32, f32,
                                       P, P, P]
-        L.ora_dense_attn.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, ctypes.c_double, P]
-        for f in ("ora_quantize_append", "ora_dequant_rows", "ora_index_scores", "ora_index_full",
-                  "ora_index_reindex", "ora_sparse_attn", "ora_dense_attn"):
+        L.csa2_ref_dense_attn.argtypes = [P, P, P, P, P, P, P, P, i32, i32, i32, ctypes.c_double, P]
+        for f in ("csa2_ref_quantize_append", "csa2_ref_dequant_rows", "csa2_ref_index_scores", "csa2_ref_index_full",
+                  "csa2_ref_index_reindex", "csa2_ref_sparse_attn", "csa2_ref_dense_attn"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -81,15 +81,15 @@ def _check(rc, name):
 # ---------------------------------------------------------------- formats
 
 def e2m1_value(code: int) -> float:
-    return lib().ora_e2m1_value(int(code))
+    return lib().csa2_ref_e2m1_value(int(code))
 
 
 def e4m3_value(bits: int) -> float:
-    return lib().ora_e4m3_value(int(bits))
+    return lib().csa2_ref_e4m3_value(int(bits))
 
 
 def e4m3_encode(v: float) -> int:
-    return lib().ora_e4m3_encode(float(v))
+    return lib().csa2_ref_e4m3_encode(float(v))
 
 
 # ---------------------------------------------------------------- a1
@@ -103,7 +103,7 @@ def quantize_append(x: np.ndarray, dtype: str, dst_row: np.ndarray, codes: np.nd
     dr = _c(dst_row, np.int64)
     assert codes.dtype == np.uint8 and scales.dtype == np.uint8
     assert codes.flags.c_contiguous and scales.flags.c_contiguous
-    rc = lib().ora_quantize_append(_p(xd), 0 if dtype == "f32" else 1, T, D, _p(dr),
+    rc = lib().csa2_ref_quantize_append(_p(xd), 0 if dtype == "f32" else 1, T, D, _p(dr),
                                    _p(codes), _p(scales), codes.shape[0])
     _check(rc, "quantize_append")
 
@@ -112,7 +112,7 @@ def dequant_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     rows, half = codes.shape
     D = half * 2
     out = np.empty((rows, D), np.float64)
-    rc = lib().ora_dequant_rows(_p(_c(codes, np.uint8)), _p(_c(scales, np.uint8)), rows, D, _p(out))
+    rc = lib().csa2_ref_dequant_rows(_p(_c(codes, np.uint8)), _p(_c(scales, np.uint8)), rows, D, _p(out))
     _check(rc, "dequant_rows")
     return out
 
@@ -122,7 +122,7 @@ def dequant_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 def index_scores(qI, w, ikeys, seq_start, row_seq, row_len, max_len):
     R, Hi, Di = qI.shape
     out = np.empty((R, max_len), np.float32)
-    rc = lib().ora_index_scores(_p(_c(qI, np.uint8)), _p(_c(w, np.float32)), _p(_c(ikeys, np.uint8)),
+    rc = lib().csa2_ref_index_scores(_p(_c(qI, np.uint8)), _p(_c(w, np.float32)), _p(_c(ikeys, np.uint8)),
                                 _p(_c(seq_start, np.int64)), _p(_c(row_seq, np.int32)),
                                 _p(_c(row_len, np.int32)), R, Hi, Di, max_len, _p(out))
     _check(rc, "index_scores")
@@ -133,7 +133,7 @@ def index_full(qI, w, ikeys, seq_start, row_seq, row_len, max_len, K, P, block=8
     R, Hi, Di = qI.shape
     topk = np.empty((R, K), np.int32)
     pool = np.empty((R, P), np.int32) if want_pool else None
-    rc = lib().ora_index_full(_p(_c(qI, np.uint8)), _p(_c(w, np.float32)), _p(_c(ikeys, np.uint8)),
+    rc = lib().csa2_ref_index_full(_p(_c(qI, np.uint8)), _p(_c(w, np.float32)), _p(_c(ikeys, np.uint8)),
                               _p(_c(seq_start, np.int64)), _p(_c(row_seq, np.int32)),
                               _p(_c(row_len, np.int32)), R, Hi, Di, max_len, K, P, block,
                               _p(topk), _p(pool))
@@ -145,7 +145,7 @@ def index_reindex(qI, w, ikeys, seq_start, row_seq, row_len, pool, K, block=8):
     R, Hi, Di = qI.shape
     P = pool.shape[1]
     topk = np.empty((R, K), np.int32)
-    rc = lib().ora_index_reindex(_p(_c(qI, np.uint8)), _p(_c(w, np.float32)), _p(_c(ikeys, np.uint8)),
+    rc = lib().csa2_ref_index_reindex(_p(_c(qI, np.uint8)), _p(_c(w, np.float32)), _p(_c(ikeys, np.uint8)),
                                  _p(_c(seq_start, np.int64)), _p(_c(row_seq, np.int32)),
                                  _p(_c(row_len, np.int32)), _p(_c(pool, np.int32)), R, Hi, Di,
                                  K, P, block, _p(topk))
@@ -168,7 +168,7 @@ def sparse_attn(q_bits, codes, scales, seq_start, row_seq, row_len, topk_idx, sw
     if rows is not None:
         mask = np.zeros(R, np.uint8)
         mask[np.asarray(list(rows), dtype=np.int64)] = 1
-    rc = lib().ora_sparse_attn(_p(_c(q_bits, np.uint16)), _p(_c(codes, np.uint8)), _p(_c(scales, np.uint8)),
+    rc = lib().csa2_ref_sparse_attn(_p(_c(q_bits, np.uint16)), _p(_c(codes, np.uint8)), _p(_c(scales, np.uint8)),
                                _p(_c(seq_start, np.int64)), _p(_c(row_seq, np.int32)),
                                _p(_c(row_len, np.int32)), _p(_c(topk_idx, np.int32)), K,
                                _p(_c(swa, np.uint8)), _p(_c(swa_row_start, np.int64)),
@@ -182,7 +182,7 @@ def dense_attn(q_bits, kv_vals, seq_start, row_seq, row_len, swa_vals, swa_row_s
                softmax_scale):
     R, H, D = q_bits.shape
     out = np.empty((R, H, D), np.float64)
-    rc = lib().ora_dense_attn(_p(_c(q_bits, np.uint16)), _p(_c(kv_vals, np.float64)),
+    rc = lib().csa2_ref_dense_attn(_p(_c(q_bits, np.uint16)), _p(_c(kv_vals, np.float64)),
                               _p(_c(seq_start, np.int64)), _p(_c(row_seq, np.int32)),
                               _p(_c(row_len, np.int32)), _p(_c(swa_vals, np.float64)),
                               _p(_c(swa_row_start, np.int64)), _p(_c(swa_len, np.int32)),

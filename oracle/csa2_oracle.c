@@ -24,6 +24,9 @@
  * is float.  Loops are plain; OpenMP only splits independent rows.
  * Every entry point returns 0 on success and a negative value on a violated
  * precondition (the oracle checks its inputs; it never guesses).
+ * The entry points are the twins of the library's calls: csa2_ref_<name> takes
+ * the arguments of csa2_<name> in the same order, as host arrays, without the
+ * stream and workspace (csa2_ref_sparse_attn adds an optional row mask).
  */
 #include <math.h>
 #include <stdint.h>
@@ -37,7 +40,7 @@
 /* E2M1 (FP4) value of a 4-bit code: bit 3 sign, bits 2..1 exponent with bias
  * 1, bit 0 mantissa.  Exponent field 0 is subnormal: m * 2^-1.
  * (FP4 KV cache paragraph: main KV codes are E2M1.) */
-double ora_e2m1_value(int code)
+double csa2_ref_e2m1_value(int code)
 {
     int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
     double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
@@ -48,7 +51,7 @@ double ora_e2m1_value(int code)
  * exponent with bias 7, bits 2..0 mantissa.  Exponent field 0 is subnormal:
  * m/8 * 2^-6.  0x7F and 0xFF are NaN.  (FP4 KV cache paragraph: one E4M3
  * scale per 16 channels; the SWA KV is FP8.) */
-double ora_e4m3_value(int bits)
+double csa2_ref_e4m3_value(int bits)
 {
     int s = (bits >> 7) & 1, e = (bits >> 3) & 15, m = bits & 7;
     double mag;
@@ -65,12 +68,12 @@ double ora_e4m3_value(int bits)
  * only if that lands on the even neighbour.  The grid is codes 0..126 (0 to
  * 448); midpoints are exact in double.  Any |v| above the last midpoint maps
  * to 448 (satfinite).  The sign bit is copied from v. */
-int ora_e4m3_encode(double v)
+int csa2_ref_e4m3_encode(double v)
 {
     double a = fabs(v);
     int code = 0;
     for (int k = 0; k < 126; ++k) {
-        double mid = 0.5 * (ora_e4m3_value(k) + ora_e4m3_value(k + 1));
+        double mid = 0.5 * (csa2_ref_e4m3_value(k) + csa2_ref_e4m3_value(k + 1));
         if (a > mid || (a == mid && (k & 1))) code = k + 1;
         else break;
     }
@@ -84,7 +87,7 @@ static int e2m1_mag_code(double a, double s)
 {
     int code = 0;
     for (int k = 0; k < 7; ++k) {
-        double mid = 0.5 * (ora_e2m1_value(k) + ora_e2m1_value(k + 1)) * s;
+        double mid = 0.5 * (csa2_ref_e2m1_value(k) + csa2_ref_e2m1_value(k + 1)) * s;
         if (a > mid || (a == mid && (k & 1))) code = k + 1;
         else break;
     }
@@ -100,8 +103,8 @@ static int g_tables_ready = 0;
 static void build_tables(void)
 {
     if (g_tables_ready) return;
-    for (int b = 0; b < 256; ++b) g_e4m3[b] = ora_e4m3_value(b);
-    for (int c = 0; c < 16; ++c) g_e2m1[c] = ora_e2m1_value(c);
+    for (int b = 0; b < 256; ++b) g_e4m3[b] = csa2_ref_e4m3_value(b);
+    for (int c = 0; c < 16; ++c) g_e2m1[c] = csa2_ref_e2m1_value(c);
     g_tables_ready = 1;
 }
 
@@ -135,8 +138,8 @@ static void quantize_group(const double* x, uint8_t* mag_sign /*16*/, uint8_t* s
 {
     double amax = 0.0;
     for (int c = 0; c < 16; ++c) if (fabs(x[c]) > amax) amax = fabs(x[c]);
-    int S = ora_e4m3_encode(amax / 6.0);
-    double s = ora_e4m3_value(S);
+    int S = csa2_ref_e4m3_encode(amax / 6.0);
+    double s = csa2_ref_e4m3_value(S);
     *scale_bits = (uint8_t)S;
     for (int c = 0; c < 16; ++c) {
         int mag = (s == 0.0) ? 0 : e2m1_mag_code(fabs(x[c]), s);
@@ -148,7 +151,7 @@ static void quantize_group(const double* x, uint8_t* mag_sign /*16*/, uint8_t* s
  * row dst_row[t].  Codes are packed two per byte, channel 2i in the low
  * nibble and 2i+1 in the high nibble; scales are one E4M3 byte per group.
  * Rows whose destination lies outside [0, cache_rows) are skipped. */
-int ora_quantize_append(const void* x, int dtype, int32_t T, int32_t D,
+int csa2_ref_quantize_append(const void* x, int dtype, int32_t T, int32_t D,
                         const int64_t* dst_row, uint8_t* codes, uint8_t* scales,
                         int64_t cache_rows)
 {
@@ -183,7 +186,7 @@ static inline double deq(const uint8_t* codes, const uint8_t* scales, int32_t D,
     return g_e2m1[code] * g_e4m3[scales[r * (D / 16) + c / 16]];
 }
 
-int ora_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t D, double* out)
+int csa2_ref_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t D, double* out)
 {
     if (D <= 0 || D % 16) return -1;
     build_tables();
@@ -215,7 +218,7 @@ static double index_score(const uint8_t* qI /*[Hi,Di]*/, const float* w /*[Hi]*/
 
 /* Scores of every visible entry of every row, rounded once to float.
  * scores is [R, max_len]; positions at or beyond row_len[r] are set to NaN. */
-int ora_index_scores(const uint8_t* qI, const float* w, const uint8_t* ikeys,
+int csa2_ref_index_scores(const uint8_t* qI, const float* w, const uint8_t* ikeys,
                      const int64_t* seq_start, const int32_t* row_seq, const int32_t* row_len,
                      int32_t R, int32_t Hi, int32_t Di, int32_t max_len, float* scores)
 {
@@ -275,7 +278,7 @@ static void take_first_k(item_t* it, int64_t n, int32_t K, int32_t* out)
  * ranked by the largest score among the block's visible positions (reading:
  * block-max), top P kept.  Both outputs are ascending and -1 padded.
  * pool_blocks may be NULL (no pool requested). */
-int ora_index_full(const uint8_t* qI, const float* w, const uint8_t* ikeys,
+int csa2_ref_index_full(const uint8_t* qI, const float* w, const uint8_t* ikeys,
                    const int64_t* seq_start, const int32_t* row_seq, const int32_t* row_len,
                    int32_t R, int32_t Hi, int32_t Di, int32_t max_len,
                    int32_t K, int32_t P, int32_t block,
@@ -319,7 +322,7 @@ int ora_index_full(const uint8_t* qI, const float* w, const uint8_t* ikeys,
  * is not -1, restricted to visible positions.  Pool ids outside
  * [0, ceil(n/block)) are ignored; duplicate pool ids are a precondition
  * violation. */
-int ora_index_reindex(const uint8_t* qI, const float* w, const uint8_t* ikeys,
+int csa2_ref_index_reindex(const uint8_t* qI, const float* w, const uint8_t* ikeys,
                       const int64_t* seq_start, const int32_t* row_seq, const int32_t* row_len,
                       const int32_t* pool_blocks, int32_t R, int32_t Hi, int32_t Di,
                       int32_t K, int32_t P, int32_t block, int32_t* topk_idx)
@@ -419,7 +422,7 @@ static void attend_one(const uint16_t* q /*[D]*/, const double* kbuf, int32_t nk
 /* q [R,H,D] bf16 bits; topk_idx [R,K]; out [R,H,D]; lse [R,H] or NULL.
  * `rows_mask` (may be NULL) selects which rows to compute; skipped rows are
  * left untouched. */
-int ora_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+int csa2_ref_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
                     const int64_t* seq_start, const int32_t* row_seq, const int32_t* row_len,
                     const int32_t* topk_idx, int32_t K,
                     const uint8_t* swa, const int64_t* swa_row_start, const int32_t* swa_len,
@@ -452,9 +455,9 @@ int ora_sparse_attn(const uint16_t* q, const uint8_t* codes, const uint8_t* scal
 }
 
 /* Dense attention over ALL of a row's visible entries plus its SWA rows, with
- * no selection at all.  Kept separate from ora_sparse_attn so that the
+ * no selection at all.  Kept separate from csa2_ref_sparse_attn so that the
  * "sparse equals dense when K >= n" check compares two independent loops. */
-int ora_dense_attn(const uint16_t* q, const double* kv /*[rows, D] dequantized*/,
+int csa2_ref_dense_attn(const uint16_t* q, const double* kv /*[rows, D] dequantized*/,
                    const int64_t* seq_start, const int32_t* row_seq, const int32_t* row_len,
                    const double* swa_vals /*[*, D]*/, const int64_t* swa_row_start,
                    const int32_t* swa_len, int32_t R, int32_t H, int32_t D, double scale,
