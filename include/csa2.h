@@ -33,6 +33,13 @@
  *     lists) cannot be validated on the host: kernels skip any index outside
  *     its valid range instead of reading or writing out of bounds.
  *   - Calls that share a workspace must not overlap on different streams.
+ *   - Debug builds (compiled with -DCSA2_DEBUG, shipped as libcsa2_debug.so)
+ *     also count, on the device, every out-of-range value that a kernel
+ *     skips (an index outside its list's range, a row length outside
+ *     [0, max_len], a destination row outside the cache, a window length
+ *     outside [0, W]); such a call synchronises its stream before returning
+ *     and returns CSA2_ERR_DEVICE_CHECK if the count is not zero.  Outputs are
+ *     still those of the release build.  Release builds never synchronise.
  */
 #ifndef CSA2_H
 #define CSA2_H
@@ -44,28 +51,38 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* Under C++ the enums take int as their fixed underlying type, so any int
+ * (e.g. a status code a C caller stored) is a valid value of the type. */
+#ifdef __cplusplus
+#define CSA2_ENUM_BASE : int
+#else
+#define CSA2_ENUM_BASE
+#endif
+
+typedef enum csa2_status_e CSA2_ENUM_BASE {
     CSA2_OK = 0,
     CSA2_ERR_NULL = 1,         /* a required pointer is NULL */
     CSA2_ERR_SHAPE = 2,        /* a size argument is negative or inconsistent */
     CSA2_ERR_UNSUPPORTED = 3,  /* well-defined, but outside this library's limits */
     CSA2_ERR_WORKSPACE = 4,    /* workspace missing, too small or not 256-byte aligned */
-    CSA2_ERR_LAUNCH = 5        /* a HIP launch failed (detail in csa2_last_error) */
+    CSA2_ERR_LAUNCH = 5,       /* a HIP launch failed (detail in csa2_last_error) */
+    CSA2_ERR_DEVICE_CHECK = 6  /* debug builds only: a kernel met an out-of-range
+                                  value in device memory and skipped it */
 } csa2_status_t;
 
-typedef enum {
+typedef enum csa2_dtype_e CSA2_ENUM_BASE {
     CSA2_F32 = 0,   /* IEEE binary32 */
     CSA2_BF16 = 1   /* bfloat16 */
 } csa2_dtype_t;
 
-/* Name of a status code (static storage). */
-const char* csa2_status_string(int status);
+/* Name of a status code (static storage); "CSA2_ERR_UNKNOWN" for any other value. */
+const char* csa2_status_string(csa2_status_t status);
 
 /* Detail of the last non-OK status returned on this thread ("" if none). */
 const char* csa2_last_error(void);
 
 /* ABI version of this header; bumped on any incompatible change. */
-#define CSA2_ABI_VERSION 1
+#define CSA2_ABI_VERSION 2
 int csa2_abi_version(void);
 
 /* ---------------------------------------------------------------------- */
@@ -102,7 +119,8 @@ csa2_status_t csa2_quantize_append(const void* x, int32_t x_dtype, int32_t T, in
  * the inputs are small integers, as in every shipped workload).
  *   qI        [R, Hi, Di] uint8 E4M3     w  [R, Hi] float32
  *   ikeys     [rows, Di] uint8 E4M3 (one key per cache row)
- *   seq_start [S] int64   row_seq [R] int32   row_len [R] int32 (<= max_len)
+ *   seq_start [S] int64   row_seq [R] int32   row_len [R] int32 in
+ *             [0, max_len] (values outside are clamped to that range)
  *   topk_idx  [R, K] int32 out: the min(K, n) entries first in the order
  *             (score descending, entry id ascending), written ascending and
  *             padded with -1.  Scores compare as reals (-0 == +0).
@@ -110,13 +128,13 @@ csa2_status_t csa2_quantize_append(const void* x, int32_t x_dtype, int32_t T, in
  *             [8b, 8b+8) first in the order (block max descending, block id
  *             ascending), where a block's max is over its visible entries;
  *             ascending, -1 padded.
- *   workspace: csa2_index_full_workspace_bytes(R, max_len, K, P, block)
+ *   workspace: csa2_index_full_workspace_bytes(R, max_len, Hi, K, P, block)
  *             bytes of device memory, 256-byte aligned, contents ignored.
  * Limits: block == 8; 1 <= K <= 2048; 0 <= P <= 2048 (P == 0 iff
  * pool_blocks == NULL); 1 <= Hi <= 64; 32 <= Di <= 256, Di % 32 == 0;
  * 0 <= max_len < 2^31 - 64.
  */
-size_t csa2_index_full_workspace_bytes(int32_t R, int32_t max_len, int32_t K, int32_t P,
+size_t csa2_index_full_workspace_bytes(int32_t R, int32_t max_len, int32_t Hi, int32_t K, int32_t P,
                                        int32_t block);
 csa2_status_t csa2_index_full(const uint8_t* qI, const float* w, const uint8_t* ikeys,
                               const int64_t* seq_start, const int32_t* row_seq,
@@ -132,12 +150,15 @@ csa2_status_t csa2_index_full(const uint8_t* qI, const float* w, const uint8_t* 
 /*
  * Candidates of row r are positions 8b + t (t < 8, 8b + t < row_len[r]) of
  * every pool block b = pool_blocks[r, p] that is in [0, ceil(n/8)); -1 and
- * out-of-range ids are skipped; ids must be distinct.  Scores use this call's
+ * out-of-range ids are skipped, and an id listed more than once counts once
+ * (debug builds report duplicates as out-of-range values).  Scores use this call's
  * qI / w with the shared ikeys (same formula as csa2_index_full); the output
  * is the Top-K of the candidates in the same order, ascending, -1 padded.
+ * Workspace: csa2_index_reindex_workspace_bytes(R, Hi, K, P, block) bytes,
+ * 256-byte aligned, contents ignored.
  * Limits: block == 8; 1 <= K <= 2048; 1 <= P <= 2048; Hi, Di as above.
  */
-size_t csa2_index_reindex_workspace_bytes(int32_t R, int32_t K, int32_t P, int32_t block);
+size_t csa2_index_reindex_workspace_bytes(int32_t R, int32_t Hi, int32_t K, int32_t P, int32_t block);
 csa2_status_t csa2_index_reindex(const uint8_t* qI, const float* w, const uint8_t* ikeys,
                                  const int64_t* seq_start, const int32_t* row_seq,
                                  const int32_t* row_len, const int32_t* pool_blocks,

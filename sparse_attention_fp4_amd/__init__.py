@@ -3,8 +3,12 @@
 Argument marshalling only: every step of the hot path runs in the HIP kernels
 behind the C ABI declared in include/csa2.h.  The functions below carry the
 same names as the C entry points; they take torch tensors that live on the
-GPU, check dtypes/shapes/contiguity, allocate outputs and workspaces when the
-caller does not pass them, and enqueue the call on torch's current stream.
+GPU, check the dtype, shape and contiguity of every input and every output
+the caller passes (the C ABI cannot see buffer sizes, so an undersized output
+would be written past its end) and that all of them live on one GPU, allocate
+outputs and workspaces the caller does not pass, and enqueue the call on
+torch's current stream.  Shapes are checked before devices, so the checks
+themselves run without a GPU.
 
 If the shared library has not been built, importing works but every call
 raises RuntimeError: there is no fallback of any kind.
@@ -22,7 +26,8 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 CSA2_F32, CSA2_BF16 = 0, 1
 STATUS = {0: "CSA2_OK", 1: "CSA2_ERR_NULL", 2: "CSA2_ERR_SHAPE", 3: "CSA2_ERR_UNSUPPORTED",
-          4: "CSA2_ERR_WORKSPACE", 5: "CSA2_ERR_LAUNCH"}
+          4: "CSA2_ERR_WORKSPACE", 5: "CSA2_ERR_LAUNCH", 6: "CSA2_ERR_DEVICE_CHECK"}
+ABI_VERSION = 2
 EXPORTS = ("csa2_status_string", "csa2_last_error", "csa2_abi_version", "csa2_quantize_append",
            "csa2_index_full_workspace_bytes", "csa2_index_full",
            "csa2_index_reindex_workspace_bytes", "csa2_index_reindex",
@@ -38,42 +43,49 @@ class Csa2Error(RuntimeError):
         self.status = status
 
 
+def load(path: str) -> ctypes.CDLL:
+    """Load a build of the library (release or debug) and declare its C signatures."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m sparse_attention_fp4_amd.build` (hipcc, gfx950)")
+    L = ctypes.CDLL(path)
+    P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.csa2_status_string.argtypes = [ctypes.c_int]
+    L.csa2_status_string.restype = ctypes.c_char_p
+    L.csa2_last_error.argtypes = []
+    L.csa2_last_error.restype = ctypes.c_char_p
+    L.csa2_abi_version.restype = ctypes.c_int
+    L.csa2_quantize_append.argtypes = [P, i32, i32, i32, P, P, P, i64, P]
+    L.csa2_index_full_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.csa2_index_full_workspace_bytes.restype = sz
+    L.csa2_index_full.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, sz, P]
+    L.csa2_index_reindex_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.csa2_index_reindex_workspace_bytes.restype = sz
+    L.csa2_index_reindex.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, P, P, sz, P]
+    L.csa2_sparse_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.csa2_sparse_attn_workspace_bytes.restype = sz
+    L.csa2_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, P, P, P, i32, i32, i32, i32, f32, P, P, P,
+                                   sz, P]
+    L.csa2_index_full_paged.argtypes = [P, P, P, i64, P, i32, i32, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                        P, P, P, P, sz, P]
+    L.csa2_index_reindex_paged.argtypes = [P, P, P, i64, P, i32, i32, P, P, P, i32, i32, i32, i32, i32, i32, P,
+                                           P, P, sz, P]
+    L.csa2_paged_rows.argtypes = [P, i32, i32, i64, P, P, P, i32, i32, P, P]
+    L.csa2_sparse_attn_phys.argtypes = [P, P, P, i64, P, i32, P, P, P, P, i32, i32, i32, i32, f32, P, P, P,
+                                        sz, P]
+    for f in ("csa2_quantize_append", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
+              "csa2_index_full_paged", "csa2_index_reindex_paged", "csa2_paged_rows", "csa2_sparse_attn_phys"):
+        getattr(L, f).restype = ctypes.c_int
+    if L.csa2_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path} has ABI version {L.csa2_abi_version()}, expected {ABI_VERSION}: rebuild it")
+    return L
+
+
 def lib() -> ctypes.CDLL:
     """Load libcsa2.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
-                               "`python -m sparse_attention_fp4_amd.build` (hipcc, gfx950)")
-        L = ctypes.CDLL(LIB_PATH)
-        P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
-        L.csa2_status_string.argtypes = [ctypes.c_int]
-        L.csa2_status_string.restype = ctypes.c_char_p
-        L.csa2_last_error.argtypes = []
-        L.csa2_last_error.restype = ctypes.c_char_p
-        L.csa2_abi_version.restype = ctypes.c_int
-        L.csa2_quantize_append.argtypes = [P, i32, i32, i32, P, P, P, i64, P]
-        L.csa2_index_full_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
-        L.csa2_index_full_workspace_bytes.restype = sz
-        L.csa2_index_full.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, sz, P]
-        L.csa2_index_reindex_workspace_bytes.argtypes = [i32, i32, i32, i32]
-        L.csa2_index_reindex_workspace_bytes.restype = sz
-        L.csa2_index_reindex.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, P, P, sz, P]
-        L.csa2_sparse_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
-        L.csa2_sparse_attn_workspace_bytes.restype = sz
-        L.csa2_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, P, P, P, i32, i32, i32, i32, f32, P, P, P,
-                                       sz, P]
-        L.csa2_index_full_paged.argtypes = [P, P, P, i64, P, i32, i32, P, P, i32, i32, i32, i32, i32, i32, i32,
-                                            P, P, P, P, sz, P]
-        L.csa2_index_reindex_paged.argtypes = [P, P, P, i64, P, i32, i32, P, P, P, i32, i32, i32, i32, i32, i32, P,
-                                               P, P, sz, P]
-        L.csa2_paged_rows.argtypes = [P, i32, i32, i64, P, P, P, i32, i32, P, P]
-        L.csa2_sparse_attn_phys.argtypes = [P, P, P, i64, P, i32, P, P, P, P, i32, i32, i32, i32, f32, P, P, P,
-                                            sz, P]
-        for f in ("csa2_quantize_append", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
-                  "csa2_index_full_paged", "csa2_index_reindex_paged", "csa2_paged_rows", "csa2_sparse_attn_phys"):
-            getattr(L, f).restype = ctypes.c_int
-        _lib = L
+        _lib = load(LIB_PATH)
     return _lib
 
 
@@ -86,18 +98,39 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _dev(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None) -> torch.Tensor:
+def _dev(t: torch.Tensor, name: str, dtype, ndim: Optional[int] = None, shape=None) -> torch.Tensor:
+    """Type, dtype, rank, shape (None entries match any size) and contiguity of
+    one argument.  The device is checked by _same_gpu once every argument has
+    passed these checks."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
-        raise ValueError(f"{name} must live on the GPU (got {t.device})")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
-    if ndim is not None and t.dim() != ndim:
+    if shape is not None:
+        shape = tuple(shape)
+        if t.dim() != len(shape) or any(w is not None and int(g) != int(w) for g, w in zip(t.shape, shape)):
+            want = tuple("*" if w is None else int(w) for w in shape)
+            raise ValueError(f"{name} must have shape {want} (got {tuple(t.shape)})")
+    elif ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims (got {tuple(t.shape)})")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _same_gpu(**tensors) -> torch.device:
+    """Every given tensor lives on the GPU, all on the same one; returns it."""
+    dev = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must live on the GPU (got {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, the other arguments on {dev}")
+    return dev
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -113,6 +146,8 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torc
         return torch.empty(nbytes, dtype=torch.uint8, device=device)
     if ws.numel() * ws.element_size() < nbytes:
         raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, needs {nbytes}")
+    if not ws.is_contiguous() or ws.device != device:
+        raise ValueError(f"workspace must be contiguous and on {device}")
     return ws
 
 
@@ -131,12 +166,12 @@ def csa2_quantize_append(x: torch.Tensor, dst_row: torch.Tensor, codes: torch.Te
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("x must be float32 or bfloat16")
     T, D = x.shape
-    _dev(dst_row, "dst_row", torch.int64, 1)
-    _dev(codes, "codes", torch.uint8, 2)
-    _dev(scales, "scales", torch.uint8, 2)
-    if dst_row.shape[0] != T or codes.shape[1] * 2 != D or scales.shape[1] * 16 != D \
-            or codes.shape[0] != scales.shape[0]:
-        raise ValueError("shape mismatch between x, dst_row, codes and scales")
+    _dev(dst_row, "dst_row", torch.int64, shape=(T,))
+    _dev(codes, "codes", torch.uint8, shape=(None, D // 2))
+    _dev(scales, "scales", torch.uint8, shape=(codes.shape[0], D // 16))
+    if D % 16:
+        raise ValueError("D must be a multiple of 16")
+    _same_gpu(x=x, dst_row=dst_row, codes=codes, scales=scales)
     st = lib().csa2_quantize_append(_ptr(x), CSA2_F32 if x.dtype == torch.float32 else CSA2_BF16,
                                     T, D, _ptr(dst_row), _ptr(codes), _ptr(scales), codes.shape[0],
                                     _stream(stream))
@@ -145,8 +180,8 @@ def csa2_quantize_append(x: torch.Tensor, dst_row: torch.Tensor, codes: torch.Te
 
 # ----------------------------------------------------------------------- a2 + a3
 
-def csa2_index_full_workspace_bytes(R: int, max_len: int, K: int, P: int, block: int = 8) -> int:
-    return int(lib().csa2_index_full_workspace_bytes(R, max_len, K, P, block))
+def csa2_index_full_workspace_bytes(R: int, max_len: int, Hi: int, K: int, P: int, block: int = 8) -> int:
+    return int(lib().csa2_index_full_workspace_bytes(R, max_len, Hi, K, P, block))
 
 
 def csa2_index_full(qI: torch.Tensor, w: torch.Tensor, ikeys: torch.Tensor, seq_start: torch.Tensor,
@@ -157,21 +192,23 @@ def csa2_index_full(qI: torch.Tensor, w: torch.Tensor, ikeys: torch.Tensor, seq_
     """Full-mode indexer: returns (topk_idx [R, K], pool_blocks [R, P] or None)."""
     qI = _dev(_u8(qI), "qI", torch.uint8, 3)
     R, Hi, Di = qI.shape
-    _dev(w, "w", torch.float32, 2)
-    ikeys = _dev(_u8(ikeys), "ikeys", torch.uint8, 2)
+    _dev(w, "w", torch.float32, shape=(R, Hi))
+    ikeys = _dev(_u8(ikeys), "ikeys", torch.uint8, shape=(None, Di))
     _dev(seq_start, "seq_start", torch.int64, 1)
-    _dev(row_seq, "row_seq", torch.int32, 1)
-    _dev(row_len, "row_len", torch.int32, 1)
-    if tuple(w.shape) != (R, Hi) or ikeys.shape[1] != Di or row_seq.shape[0] != R or row_len.shape[0] != R:
-        raise ValueError("shape mismatch among qI, w, ikeys, row_seq, row_len")
-    dev = qI.device
+    _dev(row_seq, "row_seq", torch.int32, shape=(R,))
+    _dev(row_len, "row_len", torch.int32, shape=(R,))
+    if topk_idx is not None:
+        _dev(topk_idx, "topk_idx", torch.int32, shape=(R, K))
+    if pool_blocks is not None:
+        _dev(pool_blocks, "pool_blocks", torch.int32, shape=(R, P))
+    dev = _same_gpu(qI=qI, w=w, ikeys=ikeys, seq_start=seq_start, row_seq=row_seq, row_len=row_len,
+                    topk_idx=topk_idx, pool_blocks=pool_blocks)
     if topk_idx is None:
         topk_idx = torch.empty(R, K, dtype=torch.int32, device=dev)
-    _dev(topk_idx, "topk_idx", torch.int32, 2)
     if want_pool and P > 0 and pool_blocks is None:
         pool_blocks = torch.empty(R, P, dtype=torch.int32, device=dev)
     Pc = P if pool_blocks is not None else 0
-    ws = _workspace(csa2_index_full_workspace_bytes(R, max_len, K, Pc, block), dev, workspace)
+    ws = _workspace(csa2_index_full_workspace_bytes(R, max_len, Hi, K, Pc, block), dev, workspace)
     st = lib().csa2_index_full(_ptr(qI), _ptr(w), _ptr(ikeys), _ptr(seq_start), _ptr(row_seq), _ptr(row_len),
                                R, Hi, Di, max_len, K, Pc, block, _ptr(topk_idx), _ptr(pool_blocks),
                                _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
@@ -181,8 +218,8 @@ def csa2_index_full(qI: torch.Tensor, w: torch.Tensor, ikeys: torch.Tensor, seq_
 
 # ----------------------------------------------------------------------- a4
 
-def csa2_index_reindex_workspace_bytes(R: int, K: int, P: int, block: int = 8) -> int:
-    return int(lib().csa2_index_reindex_workspace_bytes(R, K, P, block))
+def csa2_index_reindex_workspace_bytes(R: int, Hi: int, K: int, P: int, block: int = 8) -> int:
+    return int(lib().csa2_index_reindex_workspace_bytes(R, Hi, K, P, block))
 
 
 def csa2_index_reindex(qI: torch.Tensor, w: torch.Tensor, ikeys: torch.Tensor, seq_start: torch.Tensor,
@@ -192,20 +229,20 @@ def csa2_index_reindex(qI: torch.Tensor, w: torch.Tensor, ikeys: torch.Tensor, s
     """Reindex-mode rescoring of the pool: returns topk_idx [R, K]."""
     qI = _dev(_u8(qI), "qI", torch.uint8, 3)
     R, Hi, Di = qI.shape
-    _dev(w, "w", torch.float32, 2)
-    ikeys = _dev(_u8(ikeys), "ikeys", torch.uint8, 2)
+    _dev(w, "w", torch.float32, shape=(R, Hi))
+    ikeys = _dev(_u8(ikeys), "ikeys", torch.uint8, shape=(None, Di))
     _dev(seq_start, "seq_start", torch.int64, 1)
-    _dev(row_seq, "row_seq", torch.int32, 1)
-    _dev(row_len, "row_len", torch.int32, 1)
-    _dev(pool_blocks, "pool_blocks", torch.int32, 2)
+    _dev(row_seq, "row_seq", torch.int32, shape=(R,))
+    _dev(row_len, "row_len", torch.int32, shape=(R,))
+    _dev(pool_blocks, "pool_blocks", torch.int32, shape=(R, None))
     P = pool_blocks.shape[1]
-    if tuple(w.shape) != (R, Hi) or ikeys.shape[1] != Di or pool_blocks.shape[0] != R:
-        raise ValueError("shape mismatch among qI, w, ikeys, pool_blocks")
-    dev = qI.device
+    if topk_idx is not None:
+        _dev(topk_idx, "topk_idx", torch.int32, shape=(R, K))
+    dev = _same_gpu(qI=qI, w=w, ikeys=ikeys, seq_start=seq_start, row_seq=row_seq, row_len=row_len,
+                    pool_blocks=pool_blocks, topk_idx=topk_idx)
     if topk_idx is None:
         topk_idx = torch.empty(R, K, dtype=torch.int32, device=dev)
-    _dev(topk_idx, "topk_idx", torch.int32, 2)
-    ws = _workspace(csa2_index_reindex_workspace_bytes(R, K, P, block), dev, workspace)
+    ws = _workspace(csa2_index_reindex_workspace_bytes(R, Hi, K, P, block), dev, workspace)
     st = lib().csa2_index_reindex(_ptr(qI), _ptr(w), _ptr(ikeys), _ptr(seq_start), _ptr(row_seq),
                                   _ptr(row_len), _ptr(pool_blocks), R, Hi, Di, K, P, block, _ptr(topk_idx),
                                   _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
@@ -233,25 +270,26 @@ def csa2_sparse_attn(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
         q = q.view(torch.int16)
     _dev(q, "q", torch.int16, 3)
     R, H, D = q.shape
-    _dev(codes, "codes", torch.uint8, 2)
-    _dev(scales, "scales", torch.uint8, 2)
+    _dev(codes, "codes", torch.uint8, shape=(None, D // 2))
+    _dev(scales, "scales", torch.uint8, shape=(codes.shape[0], D // 16))
     _dev(seq_start, "seq_start", torch.int64, 1)
-    _dev(row_seq, "row_seq", torch.int32, 1)
-    _dev(row_len, "row_len", torch.int32, 1)
-    _dev(topk_idx, "topk_idx", torch.int32, 2)
+    _dev(row_seq, "row_seq", torch.int32, shape=(R,))
+    _dev(row_len, "row_len", torch.int32, shape=(R,))
+    _dev(topk_idx, "topk_idx", torch.int32, shape=(R, None))
     K = topk_idx.shape[1]
-    if codes.shape[1] * 2 != D or scales.shape[1] * 16 != D or topk_idx.shape[0] != R:
-        raise ValueError("shape mismatch among q, codes, scales, topk_idx")
     if W > 0:
-        swa = _dev(_u8(swa), "swa", torch.uint8, 2)
-        _dev(swa_row_start, "swa_row_start", torch.int64, 1)
-        _dev(swa_len, "swa_len", torch.int32, 1)
-        if swa.shape[1] != D:
-            raise ValueError("swa rows must have D channels")
-    dev = q.device
+        swa = _dev(_u8(swa), "swa", torch.uint8, shape=(None, D))
+        _dev(swa_row_start, "swa_row_start", torch.int64, shape=(R,))
+        _dev(swa_len, "swa_len", torch.int32, shape=(R,))
+    if out is not None:
+        _dev(out, "out", torch.float32, shape=(R, H, D))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, shape=(R, H))
+    dev = _same_gpu(q=q, codes=codes, scales=scales, seq_start=seq_start, row_seq=row_seq, row_len=row_len,
+                    topk_idx=topk_idx, swa=swa if W > 0 else None, swa_row_start=swa_row_start if W > 0 else None,
+                    swa_len=swa_len if W > 0 else None, out=out, lse=lse)
     if out is None:
         out = torch.empty(R, H, D, dtype=torch.float32, device=dev)
-    _dev(out, "out", torch.float32, 3)
     if want_lse and lse is None:
         lse = torch.empty(R, H, dtype=torch.float32, device=dev)
     ws = _workspace(csa2_sparse_attn_workspace_bytes(R, H, D, K, W), dev, workspace)
@@ -268,6 +306,8 @@ def csa2_sparse_attn(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
 
 def _pages(block_table: torch.Tensor, page_rows: int) -> int:
     _dev(block_table, "block_table", torch.int32, 2)
+    if block_table.shape[1] < 1:
+        raise ValueError("block_table needs at least one page column")
     if page_rows < 8 or page_rows & (page_rows - 1):
         raise ValueError("page_rows must be a power of two >= 8")
     return block_table.shape[1]
@@ -285,27 +325,25 @@ def csa2_index_full_paged(qI: torch.Tensor, w: torch.Tensor, ikeys: torch.Tensor
     entries) is None unless given or want_rows."""
     qI = _dev(_u8(qI), "qI", torch.uint8, 3)
     R, Hi, Di = qI.shape
-    _dev(w, "w", torch.float32, 2)
-    ikeys = _dev(_u8(ikeys), "ikeys", torch.uint8, 2)
+    _dev(w, "w", torch.float32, shape=(R, Hi))
+    ikeys = _dev(_u8(ikeys), "ikeys", torch.uint8, shape=(None, Di))
     max_pages = _pages(block_table, page_rows)
-    _dev(row_seq, "row_seq", torch.int32, 1)
-    _dev(row_len, "row_len", torch.int32, 1)
-    if tuple(w.shape) != (R, Hi) or ikeys.shape[1] != Di or row_seq.shape[0] != R or row_len.shape[0] != R:
-        raise ValueError("shape mismatch among qI, w, ikeys, row_seq, row_len")
-    dev = qI.device
+    _dev(row_seq, "row_seq", torch.int32, shape=(R,))
+    _dev(row_len, "row_len", torch.int32, shape=(R,))
+    for name, t, shp in (("topk_idx", topk_idx, (R, K)), ("pool_blocks", pool_blocks, (R, P)),
+                         ("topk_rows", topk_rows, (R, K))):
+        if t is not None:
+            _dev(t, name, torch.int32, shape=shp)
+    dev = _same_gpu(qI=qI, w=w, ikeys=ikeys, block_table=block_table, row_seq=row_seq, row_len=row_len,
+                    topk_idx=topk_idx, pool_blocks=pool_blocks, topk_rows=topk_rows)
     if topk_idx is None:
         topk_idx = torch.empty(R, K, dtype=torch.int32, device=dev)
-    _dev(topk_idx, "topk_idx", torch.int32, 2)
     if want_pool and P > 0 and pool_blocks is None:
         pool_blocks = torch.empty(R, P, dtype=torch.int32, device=dev)
     if want_rows and topk_rows is None:
         topk_rows = torch.empty(R, K, dtype=torch.int32, device=dev)
-    if topk_rows is not None:
-        _dev(topk_rows, "topk_rows", torch.int32, 2)
-        if tuple(topk_rows.shape) != (R, K):
-            raise ValueError("topk_rows must be [R, K]")
     Pc = P if pool_blocks is not None else 0
-    ws = _workspace(csa2_index_full_workspace_bytes(R, max_len, K, Pc, block), dev, workspace)
+    ws = _workspace(csa2_index_full_workspace_bytes(R, max_len, Hi, K, Pc, block), dev, workspace)
     st = lib().csa2_index_full_paged(_ptr(qI), _ptr(w), _ptr(ikeys), ikeys.shape[0], _ptr(block_table), max_pages,
                                      page_rows, _ptr(row_seq), _ptr(row_len), R, Hi, Di, max_len, K, Pc, block,
                                      _ptr(topk_idx), _ptr(topk_rows), _ptr(pool_blocks), _ptr(ws),
@@ -324,26 +362,23 @@ def csa2_index_reindex_paged(qI: torch.Tensor, w: torch.Tensor, ikeys: torch.Ten
     csa2_index_full_paged).  Returns (topk_idx, topk_rows)."""
     qI = _dev(_u8(qI), "qI", torch.uint8, 3)
     R, Hi, Di = qI.shape
-    _dev(w, "w", torch.float32, 2)
-    ikeys = _dev(_u8(ikeys), "ikeys", torch.uint8, 2)
+    _dev(w, "w", torch.float32, shape=(R, Hi))
+    ikeys = _dev(_u8(ikeys), "ikeys", torch.uint8, shape=(None, Di))
     max_pages = _pages(block_table, page_rows)
-    _dev(row_seq, "row_seq", torch.int32, 1)
-    _dev(row_len, "row_len", torch.int32, 1)
-    _dev(pool_blocks, "pool_blocks", torch.int32, 2)
+    _dev(row_seq, "row_seq", torch.int32, shape=(R,))
+    _dev(row_len, "row_len", torch.int32, shape=(R,))
+    _dev(pool_blocks, "pool_blocks", torch.int32, shape=(R, None))
     P = pool_blocks.shape[1]
-    if tuple(w.shape) != (R, Hi) or ikeys.shape[1] != Di or pool_blocks.shape[0] != R:
-        raise ValueError("shape mismatch among qI, w, ikeys, pool_blocks")
-    dev = qI.device
+    for name, t in (("topk_idx", topk_idx), ("topk_rows", topk_rows)):
+        if t is not None:
+            _dev(t, name, torch.int32, shape=(R, K))
+    dev = _same_gpu(qI=qI, w=w, ikeys=ikeys, block_table=block_table, row_seq=row_seq, row_len=row_len,
+                    pool_blocks=pool_blocks, topk_idx=topk_idx, topk_rows=topk_rows)
     if topk_idx is None:
         topk_idx = torch.empty(R, K, dtype=torch.int32, device=dev)
-    _dev(topk_idx, "topk_idx", torch.int32, 2)
     if want_rows and topk_rows is None:
         topk_rows = torch.empty(R, K, dtype=torch.int32, device=dev)
-    if topk_rows is not None:
-        _dev(topk_rows, "topk_rows", torch.int32, 2)
-        if tuple(topk_rows.shape) != (R, K):
-            raise ValueError("topk_rows must be [R, K]")
-    ws = _workspace(csa2_index_reindex_workspace_bytes(R, K, P, block), dev, workspace)
+    ws = _workspace(csa2_index_reindex_workspace_bytes(R, Hi, K, P, block), dev, workspace)
     st = lib().csa2_index_reindex_paged(_ptr(qI), _ptr(w), _ptr(ikeys), ikeys.shape[0], _ptr(block_table),
                                         max_pages, page_rows, _ptr(row_seq), _ptr(row_len), _ptr(pool_blocks), R,
                                         Hi, Di, K, P, block, _ptr(topk_idx), _ptr(topk_rows), _ptr(ws),
@@ -357,15 +392,17 @@ def csa2_paged_rows(block_table: torch.Tensor, page_rows: int, cache_rows: int, 
                     stream=None) -> torch.Tensor:
     """Cache rows [R, K] of the entries of index lists idx [R, K] over a paged cache (-1: none)."""
     max_pages = _pages(block_table, page_rows)
-    _dev(row_seq, "row_seq", torch.int32, 1)
-    _dev(row_len, "row_len", torch.int32, 1)
     _dev(idx, "idx", torch.int32, 2)
     R, K = idx.shape
-    if row_seq.shape[0] != R or row_len.shape[0] != R:
-        raise ValueError("shape mismatch among idx, row_seq, row_len")
+    _dev(row_seq, "row_seq", torch.int32, shape=(R,))
+    _dev(row_len, "row_len", torch.int32, shape=(R,))
+    if phys is not None:
+        _dev(phys, "phys", torch.int32, shape=(R, K))
+        if phys.data_ptr() == idx.data_ptr() and R * K > 0:
+            raise ValueError("phys may not alias idx")
+    dev = _same_gpu(block_table=block_table, row_seq=row_seq, row_len=row_len, idx=idx, phys=phys)
     if phys is None:
-        phys = torch.empty(R, K, dtype=torch.int32, device=idx.device)
-    _dev(phys, "phys", torch.int32, 2)
+        phys = torch.empty(R, K, dtype=torch.int32, device=dev)
     st = lib().csa2_paged_rows(_ptr(block_table), max_pages, page_rows, int(cache_rows), _ptr(row_seq),
                                _ptr(row_len), _ptr(idx), R, K, _ptr(phys), _stream(stream))
     _check("csa2_paged_rows", st)
@@ -385,24 +422,25 @@ def csa2_sparse_attn_phys(q: torch.Tensor, codes: torch.Tensor, scales: torch.Te
         q = q.view(torch.int16)
     _dev(q, "q", torch.int16, 3)
     R, H, D = q.shape
-    _dev(codes, "codes", torch.uint8, 2)
-    _dev(scales, "scales", torch.uint8, 2)
-    _dev(phys_idx, "phys_idx", torch.int32, 2)
+    _dev(codes, "codes", torch.uint8, shape=(None, D // 2))
+    _dev(scales, "scales", torch.uint8, shape=(codes.shape[0], D // 16))
+    _dev(phys_idx, "phys_idx", torch.int32, shape=(R, None))
     K = phys_idx.shape[1]
-    if codes.shape[1] * 2 != D or scales.shape[1] * 16 != D or phys_idx.shape[0] != R:
-        raise ValueError("shape mismatch among q, codes, scales, phys_idx")
     if W > 0:
-        swa = _dev(_u8(swa), "swa", torch.uint8, 2)
-        _dev(swa_row_start, "swa_row_start", torch.int64, 1)
-        _dev(swa_len, "swa_len", torch.int32, 1)
+        swa = _dev(_u8(swa), "swa", torch.uint8, shape=(None, D))
+        _dev(swa_row_start, "swa_row_start", torch.int64, shape=(R,))
+        _dev(swa_len, "swa_len", torch.int32, shape=(R,))
         if swa_head is not None:
-            _dev(swa_head, "swa_head", torch.int32, 1)
-        if swa.shape[1] != D:
-            raise ValueError("swa rows must have D channels")
-    dev = q.device
+            _dev(swa_head, "swa_head", torch.int32, shape=(R,))
+    if out is not None:
+        _dev(out, "out", torch.float32, shape=(R, H, D))
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, shape=(R, H))
+    dev = _same_gpu(q=q, codes=codes, scales=scales, phys_idx=phys_idx, swa=swa if W > 0 else None,
+                    swa_row_start=swa_row_start if W > 0 else None, swa_len=swa_len if W > 0 else None,
+                    swa_head=swa_head if W > 0 else None, out=out, lse=lse)
     if out is None:
         out = torch.empty(R, H, D, dtype=torch.float32, device=dev)
-    _dev(out, "out", torch.float32, 3)
     if want_lse and lse is None:
         lse = torch.empty(R, H, dtype=torch.float32, device=dev)
     ws = _workspace(csa2_sparse_attn_workspace_bytes(R, H, D, K, W), dev, workspace)

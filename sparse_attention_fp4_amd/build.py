@@ -8,6 +8,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa2.so")
+# the same sources with device-side range checks (-DCSA2_DEBUG): every call
+# synchronises and reports skipped out-of-range values as CSA2_ERR_DEVICE_CHECK
+LIB_DEBUG = os.path.join(HERE, "libcsa2_debug.so")
 SOURCES = ["status.hip", "quantize.hip", "index.hip", "attn.hip"]
 
 HIPCC_FLAGS = [
@@ -18,15 +21,23 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def _compile(out: str, extra, verbose: bool) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-o", tmp, *srcs]
+    tmp = out + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, *extra, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Compile libcsa2.so and (debug=True) libcsa2_debug.so; returns the release path."""
+    _compile(LIB, [], verbose)
+    if debug:
+        _compile(LIB_DEBUG, ["-DCSA2_DEBUG"], verbose)
     return LIB
 
 

@@ -458,12 +458,15 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: branches on it are scalar
     const int col = lane & 15, grp = lane >> 4, hf = grp & 1;
     int r, hg, c, s;   // row, head group, channel part, key split
+    bool g_first;      // the row's first workgroup
     {
         const int g = xcd_slot(blockIdx.x, HG * CS * S, r);
         hg = g % HG;
         c = g / HG % CS;
         s = g / (HG * CS);
+        g_first = g == 0;
     }
+    (void)g_first;
     if (r >= R) return;   // padding of the XCD mapping (whole workgroup, before any barrier)
     const int h0 = hg * NH;
     const bool upper = lane >= 32;
@@ -516,6 +519,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
             qraw[k] = make_uint4(v[0], v[1], v[2], v[3]);
         }
     }
+    CSA2_DCHECK(g_first && threadIdx.x == 0 && (nsw < 0 || nsw > W));
     nsw = nsw < 0 ? 0 : (nsw > W ? W : nsw);
     const int64_t base = PG ? 0 : seq_start[seq];
     // Max |q| of each head over the wave's pieces: an integer max of the bf16
@@ -578,6 +582,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     auto load_frag = [&](FragRaw<D>& f, int fr_, int j) {
         const int slot = fr_ * kFrag + col, i = slot - Kp;
         const bool vm = slot < K && j >= 0 && j < nb;
+        CSA2_DCHECK(hg == 0 && c == 0 && slot < K && j != -1 && !vm);
         const bool vs = i >= 0 && i < nsw;
         const int iw = PG ? (head + i >= W ? head + i - W : head + i) : i;
         if (frag_kind(fr_, Kp) == 0)
@@ -927,6 +932,7 @@ __global__ __launch_bounds__(256) void k_paged_rows(const int32_t* __restrict__ 
     const int r = (int)(e / K);
     const int j = idx[e];
     int32_t out = -1;
+    CSA2_DCHECK(j != -1 && !(j >= 0 && j < row_len[r]));
     if (j >= 0 && j < row_len[r]) {
         const int page = j >> shift;
         if (page < max_pages) {
@@ -949,7 +955,10 @@ csa2_status_t sparse_attn_impl(const uint16_t* q, const uint8_t* codes, const ui
 
 extern "C" size_t csa2_sparse_attn_workspace_bytes(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
 {
-    if (R <= 0 || H <= 0 || D <= 0 || K < 0 || W < 0) return 0;
+    // arguments the call rejects need no workspace
+    if (R <= 0 || H <= 0 || H > 65536 || (D != 128 && D != 256 && D != 512) || K < 0 || K > 4096 || W < 0 ||
+        W > 4096)
+        return 0;
     const AttnPlan p = plan_attn(R, H, D, K, W);
     if (p.S <= 1) return 0;
     return csa2::align_up((size_t)R * p.S * H * D * 4, 256) + csa2::align_up((size_t)R * p.S * H * 4 * 4, 256);
@@ -1011,7 +1020,7 @@ csa2_status_t sparse_attn_impl(const uint16_t* q, const uint8_t* codes, const ui
     if (p.S > 1)
         hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)xcd_grid(R, H)), dim3(128), 0, st, po, pml, R, H, D, p.S,
                            out, lse);
-    return csa2::check_launch("sparse_attn");
+    return CSA2_FINISH(st, "sparse_attn");
 }
 }  // namespace
 
@@ -1056,5 +1065,5 @@ extern "C" csa2_status_t csa2_paged_rows(const int32_t* block_table, int32_t max
     hipLaunchKernelGGL(k_paged_rows, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, csa2::as_stream(stream),
                        block_table, max_pages, __builtin_ctz((unsigned)page_rows), cache_rows, row_seq, row_len, idx, R,
                        K, phys);
-    return csa2::check_launch("paged_rows");
+    return CSA2_FINISH(csa2::as_stream(stream), "paged_rows");
 }

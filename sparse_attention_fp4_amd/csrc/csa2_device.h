@@ -17,6 +17,38 @@ typedef __fp16 lds_f16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
 
 #define CSA2_WAVE 64
 
+#include "csa2_host.h"
+
+// Debug builds (-DCSA2_DEBUG): each translation unit counts, in a device word
+// of its own, the out-of-range values that its kernels skip (CSA2_DCHECK), and
+// an entry point ends with CSA2_FINISH, which then waits for the stream, reads
+// and clears the count, and returns CSA2_ERR_DEVICE_CHECK when it is not zero.
+// Release builds compile the checks away and CSA2_FINISH only checks the
+// launch status.
+#ifdef CSA2_DEBUG
+static __device__ unsigned int csa2_dbg_skipped;
+#define CSA2_DCHECK(bad) do { if (bad) atomicAdd(&csa2_dbg_skipped, 1u); } while (0)
+static inline csa2_status_t csa2_debug_finish(hipStream_t st, const char* who)
+{
+    const csa2_status_t ls = ::csa2::check_launch(who);
+    if (ls != CSA2_OK) return ls;
+    if (hipStreamSynchronize(st) != hipSuccess)
+        return ::csa2::fail(CSA2_ERR_LAUNCH, "%s: stream synchronisation failed (debug build)", who);
+    unsigned int c = 0, z = 0;
+    if (hipMemcpyFromSymbol(&c, HIP_SYMBOL(csa2_dbg_skipped), sizeof c, 0, hipMemcpyDeviceToHost) != hipSuccess)
+        return ::csa2::fail(CSA2_ERR_LAUNCH, "%s: reading the device check count failed", who);
+    if (c == 0) return CSA2_OK;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(csa2_dbg_skipped), &z, sizeof z, 0, hipMemcpyHostToDevice) != hipSuccess)
+        return ::csa2::fail(CSA2_ERR_LAUNCH, "%s: clearing the device check count failed", who);
+    return ::csa2::fail(CSA2_ERR_DEVICE_CHECK, "%s: kernels skipped %u out-of-range values in device memory", who,
+                        c);
+}
+#define CSA2_FINISH(st, who) csa2_debug_finish((st), (who))
+#else
+#define CSA2_DCHECK(bad) ((void)0)
+#define CSA2_FINISH(st, who) ::csa2::check_launch(who)
+#endif
+
 // Value of a non-negative OCP E4M3 magnitude code (0..126), exact in fp32.
 __device__ __forceinline__ float e4m3_mag_value(int b)
 {

@@ -79,12 +79,14 @@ template <int HT, int KS, bool REINDEX, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HT * KS <= 4 ? 4 : 1))) void k_index_score(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ ikeys,
     const int64_t* __restrict__ seq_start, PageMap pm, const int32_t* __restrict__ row_seq,
-    const int32_t* __restrict__ row_len, const int32_t* __restrict__ pool, int32_t Hi, int32_t Di,
-    int32_t P, float* __restrict__ scores, int64_t ld_scores, float* __restrict__ bmax,
+    const int32_t* __restrict__ row_len, int32_t n_cap, const int32_t* __restrict__ pool, int32_t Hi,
+    int32_t Di, int32_t P, float* __restrict__ scores, int64_t ld_scores, float* __restrict__ bmax,
     int64_t ld_bmax, int32_t re_chunk)
 {
     const int r = blockIdx.y;
-    const int n = row_len[r];
+    const int n_raw = row_len[r];
+    CSA2_DCHECK(blockIdx.x == 0 && threadIdx.x == 0 && (n_raw < 0 || n_raw > n_cap));
+    const int n = n_raw < 0 ? 0 : (n_raw > n_cap ? n_cap : n_raw);   // row lengths are clamped to [0, n_cap]
     const int lane = lane_id();
     const int wave = threadIdx.x / CSA2_WAVE;
     const int col = lane & 15;       // entry within a 16-entry tile / head within a head tile
@@ -111,6 +113,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HT * KS <= 
                 const int64_t ps = (first >> 3) + t;
                 const int b = ps < P ? pool[(int64_t)r * P + ps] : -1;
                 const bool in = b >= 0 && b < nb;
+                CSA2_DCHECK(b != -1 && !in);
                 pg_blk[t] = in ? b : -1;
                 if constexpr (PAGED) pg_id[t] = in ? pm.page_id(seq, ((int64_t)b * 8) >> pm.shift) : -1;
             } else {
@@ -768,13 +771,14 @@ constexpr int kPrefilterRows = 128;  // the separate pre-filter runs below this 
 // threshold, in block order, go to gkey / gid at the slice's own offset, and
 // their number to gcount.  Rows that fit the registers are left to k_select.
 __global__ __launch_bounds__(kSelThreads) void k_prefilter(const float* __restrict__ bmax, int64_t ld_bmax,
-                                                           const int32_t* __restrict__ row_len, int32_t big,
+                                                           const int32_t* __restrict__ row_len, int32_t n_cap,
+                                                           int32_t big,
                                                            uint32_t* __restrict__ gkey, int32_t* __restrict__ gid,
                                                            int32_t* __restrict__ gcount, int32_t nslices)
 {
     __shared__ SelShared sh;
     const int g = blockIdx.x, r = blockIdx.y;
-    const int n = row_len[r];
+    const int n = min(max(row_len[r], 0), n_cap);
     const int nb = (n + 7) >> 3;
     const int ns = (nb + kRound - 1) / kRound;
     if (nb <= kRegRounds * kRound || ns > kMaxSlices || g >= ns) return;   // uniform per workgroup
@@ -812,14 +816,14 @@ __global__ __launch_bounds__(kSelThreads) void k_prefilter(const float* __restri
 template <bool FULL>
 __global__ __launch_bounds__(kSelThreads) void k_select(
     const float* __restrict__ scores, int64_t ld_scores, const float* __restrict__ bmax,
-    int64_t ld_bmax, const int32_t* __restrict__ row_len, const int32_t* __restrict__ pool_in,
+    int64_t ld_bmax, const int32_t* __restrict__ row_len, int32_t n_cap, const int32_t* __restrict__ pool_in,
     int32_t K, int32_t P, int32_t* __restrict__ topk, int32_t* __restrict__ pool_out,
     const uint32_t* __restrict__ gkey_g, const int32_t* __restrict__ gid_g, const int32_t* __restrict__ gcount,
     int32_t nslices, const int32_t* __restrict__ row_seq, PageMap pm, int32_t* __restrict__ rows_out)
 {
     __shared__ typename std::conditional<FULL, SelectLdsFull, SelectLds>::type L;
     const int r = blockIdx.x;
-    const int n = row_len[r];
+    const int n = min(max(row_len[r], 0), n_cap);   // as the score kernel clamps it
     const int nb = (n + 7) >> 3;
     const float* sc = scores + (int64_t)r * ld_scores;
     const float* bm = FULL ? bmax + (int64_t)r * ld_bmax : nullptr;
@@ -985,10 +989,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
             }
             __syncthreads();
             bitonic_sort(L.sortbuf, np2);
+            // a block listed more than once counts once: after the sort its
+            // copies are adjacent, and only the first (lowest slot) is kept
             for (int i = threadIdx.x; i < P; i += kSelThreads) {
                 const unsigned long long v = L.sortbuf[i];
                 const unsigned hi = (unsigned)(v >> 32);
-                L.blocks[i] = hi == 0x7FFFFFFFu ? -1 : (int)hi;
+                const bool dup = i > 0 && hi != 0x7FFFFFFFu && (unsigned)(L.sortbuf[i - 1] >> 32) == hi;
+                CSA2_DCHECK(dup);
+                L.blocks[i] = hi == 0x7FFFFFFFu || dup ? -1 : (int)hi;
                 L.slots[i] = (int)(unsigned)v;
             }
             __syncthreads();
@@ -1041,13 +1049,14 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
 template <bool REINDEX, bool PAGED>
 void launch_score(int HT, int KS, dim3 grid, hipStream_t st, const uint8_t* qI, const float* w,
                   const uint8_t* ikeys, const int64_t* seq_start, const PageMap& pm, const int32_t* row_seq,
-                  const int32_t* row_len, const int32_t* pool, int32_t Hi, int32_t Di, int32_t P,
+                  const int32_t* row_len, int32_t n_cap, const int32_t* pool, int32_t Hi, int32_t Di, int32_t P,
                   float* scores, int64_t lds, float* bm, int64_t ldb, int re_chunk)
 {
 #define CSA2_SCORE(ht, ks)                                                                                 \
     if (HT == ht && KS == ks) {                                                                            \
         hipLaunchKernelGGL((k_index_score<ht, ks, REINDEX, PAGED>), grid, dim3(256), 0, st, qI, w, ikeys,   \
-                           seq_start, pm, row_seq, row_len, pool, Hi, Di, P, scores, lds, bm, ldb, re_chunk); \
+                           seq_start, pm, row_seq, row_len, n_cap, pool, Hi, Di, P, scores, lds, bm, ldb,    \
+                           re_chunk);                                                                      \
         return;                                                                                            \
     }
     CSA2_SCORE(1, 1) CSA2_SCORE(2, 1) CSA2_SCORE(3, 1) CSA2_SCORE(4, 1)
@@ -1058,15 +1067,15 @@ void launch_score(int HT, int KS, dim3 grid, hipStream_t st, const uint8_t* qI, 
 template <bool REINDEX>
 void launch_score(bool paged, int HT, int KS, dim3 grid, hipStream_t st, const uint8_t* qI, const float* w,
                   const uint8_t* ikeys, const int64_t* seq_start, const PageMap& pm, const int32_t* row_seq,
-                  const int32_t* row_len, const int32_t* pool, int32_t Hi, int32_t Di, int32_t P,
+                  const int32_t* row_len, int32_t n_cap, const int32_t* pool, int32_t Hi, int32_t Di, int32_t P,
                   float* scores, int64_t lds, float* bm, int64_t ldb, int re_chunk = 0)
 {
     if (paged)
-        launch_score<REINDEX, true>(HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len, pool, Hi, Di,
-                                    P, scores, lds, bm, ldb, re_chunk);
+        launch_score<REINDEX, true>(HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len, n_cap, pool,
+                                    Hi, Di, P, scores, lds, bm, ldb, re_chunk);
     else
-        launch_score<REINDEX, false>(HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len, pool, Hi,
-                                     Di, P, scores, lds, bm, ldb, re_chunk);
+        launch_score<REINDEX, false>(HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len, n_cap, pool,
+                                     Hi, Di, P, scores, lds, bm, ldb, re_chunk);
 }
 
 // Block-table arguments of the paged calls; shift = log2(page_rows).
@@ -1120,10 +1129,10 @@ csa2_status_t check_indexer_dims(const char* who, int32_t R, int32_t Hi, int32_t
 
 }  // namespace
 
-extern "C" size_t csa2_index_full_workspace_bytes(int32_t R, int32_t max_len, int32_t K, int32_t P,
+extern "C" size_t csa2_index_full_workspace_bytes(int32_t R, int32_t max_len, int32_t Hi, int32_t K, int32_t P,
                                                   int32_t block)
 {
-    (void)K; (void)P; (void)block;
+    (void)Hi; (void)K; (void)P; (void)block;
     if (R < 0 || max_len < 0) return 0;
     const int64_t ld = full_ld(max_len);
     size_t b = csa2::align_up((size_t)R * ld * 4, 256) + csa2::align_up((size_t)R * (ld / 8) * 4, 256);
@@ -1150,11 +1159,11 @@ csa2_status_t index_full_impl(const uint8_t* qI, const float* w, const uint8_t* 
     if (R == 0) return CSA2_OK;
     CSA2_REQUIRE(qI && w && ikeys && (seq_start || pmp) && row_seq && row_len && topk_idx, CSA2_ERR_NULL,
                  "index_full: NULL pointer argument");
-    const size_t need = csa2_index_full_workspace_bytes(R, max_len, K, P, block);
+    CSA2_REQUIRE(R <= 65535, CSA2_ERR_UNSUPPORTED, "index_full: R=%d > 65535", R);
+    const size_t need = csa2_index_full_workspace_bytes(R, max_len, Hi, K, P, block);
     CSA2_REQUIRE(workspace && workspace_bytes >= need && ((uintptr_t)workspace & 255) == 0,
                  CSA2_ERR_WORKSPACE, "index_full: workspace needs %zu bytes, 256-byte aligned (got %zu)",
                  need, workspace_bytes);
-    CSA2_REQUIRE(R <= 65535, CSA2_ERR_UNSUPPORTED, "index_full: R=%d > 65535", R);
     const int64_t ld = full_ld(max_len);
     char* w8 = static_cast<char*>(workspace);
     float* scores = reinterpret_cast<float*>(w8);
@@ -1181,17 +1190,17 @@ csa2_status_t index_full_impl(const uint8_t* qI, const float* w, const uint8_t* 
     if (max_len > 0) {
         dim3 grid((unsigned)(ld / kFullChunk), (unsigned)R);
         launch_score<false>(pmp != nullptr, HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len,
-                            nullptr, Hi, Di, 0, scores, ld, bm, ld / 8);
+                            max_len, nullptr, Hi, Di, 0, scores, ld, bm, ld / 8);
     }
     if (gcount) {
         const int32_t big = K > P ? K : P;
         hipLaunchKernelGGL(k_prefilter, dim3((unsigned)nslices, (unsigned)R), dim3(kSelThreads), 0, st, bm, ld / 8,
-                           row_len, big, gkey, gid, gcount, (int32_t)nslices);
+                           row_len, max_len, big, gkey, gid, gcount, (int32_t)nslices);
     }
     hipLaunchKernelGGL(k_select<true>, dim3((unsigned)R), dim3(kSelThreads), 0, st, scores, ld, bm, ld / 8,
-                       row_len, nullptr, K, P, topk_idx, pool_blocks, gkey, gid, gcount, (int32_t)nslices, row_seq, pm,
+                       row_len, max_len, nullptr, K, P, topk_idx, pool_blocks, gkey, gid, gcount, (int32_t)nslices, row_seq, pm,
                        pmp ? topk_rows : nullptr);
-    return csa2::check_launch("index_full");
+    return CSA2_FINISH(st, "index_full");
 }
 }  // namespace
 
@@ -1224,9 +1233,9 @@ extern "C" csa2_status_t csa2_index_full_paged(const uint8_t* qI, const float* w
                            topk_rows, pool_blocks, workspace, workspace_bytes, stream);
 }
 
-extern "C" size_t csa2_index_reindex_workspace_bytes(int32_t R, int32_t K, int32_t P, int32_t block)
+extern "C" size_t csa2_index_reindex_workspace_bytes(int32_t R, int32_t Hi, int32_t K, int32_t P, int32_t block)
 {
-    (void)K; (void)block;
+    (void)Hi; (void)K; (void)block;
     if (R < 0 || P < 0) return 0;
     return csa2::align_up((size_t)R * reindex_ld(P) * 4, 256);   // one score per pool slot
 }
@@ -1245,11 +1254,11 @@ csa2_status_t index_reindex_impl(const uint8_t* qI, const float* w, const uint8_
     if (R == 0) return CSA2_OK;
     CSA2_REQUIRE(qI && w && ikeys && (seq_start || pmp) && row_seq && row_len && pool_blocks && topk_idx,
                  CSA2_ERR_NULL, "index_reindex: NULL pointer argument");
-    const size_t need = csa2_index_reindex_workspace_bytes(R, K, P, block);
+    CSA2_REQUIRE(R <= 65535, CSA2_ERR_UNSUPPORTED, "index_reindex: R=%d > 65535", R);
+    const size_t need = csa2_index_reindex_workspace_bytes(R, Hi, K, P, block);
     CSA2_REQUIRE(workspace && workspace_bytes >= need && ((uintptr_t)workspace & 255) == 0,
                  CSA2_ERR_WORKSPACE, "index_reindex: workspace needs %zu bytes, 256-byte aligned (got %zu)",
                  need, workspace_bytes);
-    CSA2_REQUIRE(R <= 65535, CSA2_ERR_UNSUPPORTED, "index_reindex: R=%d > 65535", R);
     const int64_t ld = reindex_ld(P);
     float* scores = static_cast<float*>(workspace);
     hipStream_t st = csa2::as_stream(stream);
@@ -1257,12 +1266,12 @@ csa2_status_t index_reindex_impl(const uint8_t* qI, const float* w, const uint8_
     const int chunk = reindex_chunk(R, ld);
     dim3 grid((unsigned)(ld / chunk), (unsigned)R);
     const PageMap pm = pmp ? *pmp : PageMap{nullptr, 0, 0, 0};
-    launch_score<true>(pmp != nullptr, HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len, pool_blocks,
-                       Hi, Di, P, scores, ld, nullptr, 0, chunk);
+    launch_score<true>(pmp != nullptr, HT, KS, grid, st, qI, w, ikeys, seq_start, pm, row_seq, row_len, 0x7FFFFFFF,
+                       pool_blocks, Hi, Di, P, scores, ld, nullptr, 0, chunk);
     hipLaunchKernelGGL(k_select<false>, dim3((unsigned)R), dim3(kSelThreads), 0, st, scores, ld, nullptr, 0,
-                       row_len, pool_blocks, K, P, topk_idx, nullptr, nullptr, nullptr, nullptr, 0, row_seq, pm,
+                       row_len, 0x7FFFFFFF, pool_blocks, K, P, topk_idx, nullptr, nullptr, nullptr, nullptr, 0, row_seq, pm,
                        pmp ? topk_rows : nullptr);
-    return csa2::check_launch("index_reindex");
+    return CSA2_FINISH(st, "index_reindex");
 }
 }  // namespace
 

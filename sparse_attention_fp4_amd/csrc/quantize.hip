@@ -60,6 +60,7 @@ __global__ __launch_bounds__(256) void k_quantize_append(const void* __restrict_
     const int64_t t = gid / G;
     const int g = (int)(gid - t * G);
     const int64_t r = dst_row[t];
+    CSA2_DCHECK(g == 0 && (r < 0 || r >= cache_rows));
     if (r < 0 || r >= cache_rows) return;
 
     float v[16];
@@ -122,5 +123,5 @@ extern "C" csa2_status_t csa2_quantize_append(const void* x, int32_t x_dtype, in
     else
         hipLaunchKernelGGL(k_quantize_append<false>, dim3((unsigned)blocks), dim3(256), 0, st, x, T, D,
                            dst_row, codes, scales, cache_rows);
-    return csa2::check_launch("quantize_append");
+    return CSA2_FINISH(st, "quantize_append");
 }

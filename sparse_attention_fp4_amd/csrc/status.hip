@@ -27,7 +27,7 @@ csa2_status_t check_launch(const char* what)
 
 }  // namespace csa2
 
-extern "C" const char* csa2_status_string(int status)
+extern "C" const char* csa2_status_string(csa2_status_t status)
 {
     switch (status) {
         case CSA2_OK: return "CSA2_OK";
@@ -36,6 +36,7 @@ extern "C" const char* csa2_status_string(int status)
         case CSA2_ERR_UNSUPPORTED: return "CSA2_ERR_UNSUPPORTED";
         case CSA2_ERR_WORKSPACE: return "CSA2_ERR_WORKSPACE";
         case CSA2_ERR_LAUNCH: return "CSA2_ERR_LAUNCH";
+        case CSA2_ERR_DEVICE_CHECK: return "CSA2_ERR_DEVICE_CHECK";
         default: return "CSA2_ERR_UNKNOWN";
     }
 }

@@ -86,8 +86,9 @@ class CSA2Step:
                      if self.paged else self.topk)
         self.out = {l: torch.empty(R, H, D, dtype=torch.float32, device=dev) for l in range(len(self.modes))}
         self.lse = {l: torch.empty(R, H, dtype=torch.float32, device=dev) for l in range(len(self.modes))}
-        nbytes = max(csa2_index_full_workspace_bytes(R, self.max_len, self.K, self.P, self.block),
-                     csa2_index_reindex_workspace_bytes(R, self.K, self.P, self.block),
+        Hi = int(qI[self.modes.index("F")].shape[1])
+        nbytes = max(csa2_index_full_workspace_bytes(R, self.max_len, Hi, self.K, self.P, self.block),
+                     csa2_index_reindex_workspace_bytes(R, Hi, self.K, self.P, self.block),
                      csa2_sparse_attn_workspace_bytes(R, H, D, self.K, self.W), 256)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
 

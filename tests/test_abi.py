@@ -32,10 +32,24 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     L = csa2.lib()
-    assert L.csa2_abi_version() == 1
+    assert L.csa2_abi_version() == 2 == csa2.ABI_VERSION
     for code, name in csa2.STATUS.items():
         assert L.csa2_status_string(code).decode() == name
     assert L.csa2_status_string(99).decode() == "CSA2_ERR_UNKNOWN"
+    # the header's enum and the binding's table agree
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    enum = dict((int(v), k) for k, v in re.findall(r"\b(CSA2_(?:OK|ERR_\w+))\s*=\s*(\d+)", text))
+    assert enum == csa2.STATUS
+
+
+def test_debug_build_exports_the_same_abi():
+    from sparse_attention_fp4_amd.build import LIB_DEBUG
+    D = csa2.load(LIB_DEBUG)
+    for n in declared_functions():
+        assert hasattr(D, n), n
+    assert D.csa2_abi_version() == csa2.ABI_VERSION
+    # host validation is the release build's
+    assert D.csa2_index_full(*full_args(K=0)) == 2
 
 
 V = ctypes.c_void_p
@@ -95,9 +109,16 @@ def test_index_full_validation():
 def test_index_full_workspace_formula():
     L = csa2.lib()
     # scores padded to 1024 entries per row plus block maxima, each 256-byte aligned
-    assert L.csa2_index_full_workspace_bytes(32, 65536, 512, 2048, 8) == 32 * 65536 * 4 + 32 * 8192 * 4
-    assert L.csa2_index_full_workspace_bytes(1, 1, 64, 256, 8) == 4096 + 512
-    assert L.csa2_index_full_workspace_bytes(-1, 1, 1, 1, 8) == 0
+    assert L.csa2_index_full_workspace_bytes(32, 65536, 64, 512, 2048, 8) == 32 * 65536 * 4 + 32 * 8192 * 4
+    assert L.csa2_index_full_workspace_bytes(1, 1, 1, 64, 256, 8) == 4096 + 512
+    assert L.csa2_index_full_workspace_bytes(-1, 1, 1, 1, 1, 8) == 0
+
+
+def test_index_reindex_workspace_formula():
+    L = csa2.lib()
+    # one fp32 score per pool slot, rows padded to whole scoring chunks
+    assert L.csa2_index_reindex_workspace_bytes(32, 64, 512, 2048, 8) == 32 * 16384 * 4
+    assert L.csa2_index_reindex_workspace_bytes(-1, 64, 512, 2048, 8) == 0
 
 
 def reindex_args(**kw):
