@@ -7,21 +7,30 @@ entry and selects its Top-K and block pool, each Reindex layer rescores the
 pool, and every layer (Full, Reindex and Reuse) runs sparse attention over its
 selected entries plus its FP8 sliding window.  Inputs are seeded synthetic
 data already resident in HBM.  The step is captured once as a HIP graph and
-replayed; `value` is whole-job decode throughput (query rows per second).
+replayed.
 
-Also reported: the algorithmic HBM bytes moved per step and the achieved
-fraction of the 8 TB/s peak, a per-call breakdown, a cold-cache step time
-(L2 and Infinity Cache flushed before every step), the roofline of the call
-that takes most of the step (by measured time x calls per step; sparse
-attention, which every layer runs, on the decode workloads) and of the
-Full-mode index call, and the CPU oracle timed on a bounded sample of the
-same workload on this host.
+Headline (`value`, `ms_per_step`): cold-cache steps -- before each timed step a
+1 GiB buffer is written (outside the timed events), which evicts the L2 caches
+and the Infinity Cache, so a step cannot re-read the previous step's keys from
+cache.  `ms_per_step` is the median of the K timed steps (p10 and p90 beside
+it); `value` is whole-job decode throughput, query rows per second (prefill:
+chunk tokens per second).  Warm (back-to-back) replays are reported as well.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|5|4]
+Also reported: the algorithmic HBM bytes per step and their fraction of the
+8 TB/s peak and of a measured device-copy ceiling, a per-call breakdown (HIP
+events around graph replays of each call alone), the kernel launches per step
+(nodes of the captured graph) and the measured cost of one launch boundary, a
+roofline object for the call that takes most of the step and for the index
+calls (HBM-bound on decode; matrix-core bound on the prefill chunk), the same
+step over a paged copy of the caches, the decode-1M workload (default run), and
+the CPU oracle timed on a bounded sample of the same workload on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2|3|5|4|6|1]
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -39,6 +48,7 @@ import workloads  # noqa: E402
 
 METRIC = "CSA2 decode tokens/s + achieved HBM GB/s (% of peak) at 64K and 1M KV entries"
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp16": 2500.0}   # dense, MI355X
 
 # HBM traffic per call measured with rocprofv3 --pmc (FETCH_SIZE and
 # WRITE_SIZE per dispatch, scaled by the same counters on a plain 1 GiB device
@@ -86,6 +96,18 @@ def algorithmic_bytes(cfg, lengths, R, row_len):
     return dict(a1=a1, a2=a2, a4_per_layer=a4_one, a5_per_layer=a5_one, total=total)
 
 
+def algorithmic_flops(cfg, R, row_len):
+    """Matrix-core work per call: the indexer takes Hi x Di multiply-adds (FP8)
+    per scored entry; attention 2 x H x D multiply-adds (QK^T and PV, fp16) per
+    key (selected entries plus the window)."""
+    n = np.asarray(row_len, np.int64)
+    per_entry = 2 * cfg.Hi * cfg.Di
+    return dict(index_full=int(n.sum()) * per_entry,
+                index_reindex=int(np.minimum(cfg.P * 8, n).sum()) * per_entry,
+                sparse_attn=int((np.minimum(cfg.K, n) + cfg.W).sum()) * 4 * cfg.H * cfg.D,
+                quantize_append=0)
+
+
 def build(cfg, dev):
     import sparse_attention_fp4_amd as csa2
     from sparse_attention_fp4_amd.step import CSA2Step
@@ -124,19 +146,50 @@ def build_paged(cfg, wl, step, page_rows):
                     block_table=lay.block_table, page_rows=page_rows, swa_head=head)
 
 
-def graph_of(fn, reps=1):
+def new_graph(keep=False):
+    if keep:
+        try:
+            return torch.cuda.CUDAGraph(keep_graph=True)
+        except TypeError:
+            pass
+    return torch.cuda.CUDAGraph()
+
+
+def graph_of(fn, reps=1, keep=False):
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         fn()                                   # warm the allocator / code objects outside capture
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
+    g = new_graph(keep)
     with torch.cuda.graph(g):
         for _ in range(reps):
             fn()
     torch.cuda.synchronize()
     return g
+
+
+def graph_kernel_nodes(g):
+    """(kernel nodes, all nodes) of a captured graph, from the HIP runtime."""
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        graph = ctypes.c_void_p(g.raw_cuda_graph())
+        n = ctypes.c_size_t(0)
+        if hip.hipGraphGetNodes(graph, None, ctypes.byref(n)) != 0:
+            return None
+        nodes = (ctypes.c_void_p * n.value)()
+        if hip.hipGraphGetNodes(graph, nodes, ctypes.byref(n)) != 0:
+            return None
+        kernels = 0
+        for nd in nodes[:n.value]:
+            t = ctypes.c_int(-1)
+            hip.hipGraphNodeGetType(ctypes.c_void_p(nd), ctypes.byref(t))
+            kernels += t.value == 0   # hipGraphNodeTypeKernel
+        return kernels, int(n.value)
+    except Exception as e:  # noqa: BLE001 - reporting only
+        log(f"bench: graph node count unavailable ({e})")
+        return None
 
 
 def time_graph(g, reps, inner=1):
@@ -148,6 +201,21 @@ def time_graph(g, reps, inner=1):
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / (reps * inner)
+
+
+def launch_boundary_us(reps=64):
+    """Device time per launch of a graph of back-to-back one-thread kernels
+    (csa2_paged_rows over a single entry): the fixed cost of one kernel
+    boundary inside a graph."""
+    import sparse_attention_fp4_amd as csa2
+    bt = torch.zeros(1, 1, dtype=torch.int32, device="cuda")
+    one = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ln = torch.ones(1, dtype=torch.int32, device="cuda")
+    idx = torch.zeros(1, 1, dtype=torch.int32, device="cuda")
+    phys = torch.empty(1, 1, dtype=torch.int32, device="cuda")
+    g = graph_of(lambda: csa2.csa2_paged_rows(bt, 8, 8, one, ln, idx, phys=phys), reps=reps)
+    time_graph(g, 3, reps)
+    return time_graph(g, 10, reps) * 1000.0
 
 
 def per_call_times(step, reps=10):
@@ -212,25 +280,36 @@ def paged_call_times(step, reps=10):
     return out
 
 
-def cold_step_ms(g, steps):
-    """Step time with L2 and Infinity Cache flushed (1 GiB write) before each step."""
-    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    times = []
-    for _ in range(steps):
-        flush.fill_(1.0)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+class Flusher:
+    """Writes 1 GiB before a cold step: more than the L2 caches and the
+    256 MB Infinity Cache hold together."""
+
+    def __init__(self):
+        self.buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        self.buf.fill_(1.0)
+
+
+def timed_steps(g, steps, flush=None):
+    """Per-step device times (ms) of `steps` graph replays, each bracketed by
+    its own HIP events; with `flush`, the flush runs before each step, outside
+    the events.  The whole loop is bracketed by synchronisations."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        if flush is not None:
+            flush()
         a.record()
         g.replay()
         b.record()
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b))
-    del flush
-    return float(np.median(times))
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs])
 
 
 def copy_check():
-    """Plain device copy of 1 GiB (reference kernel for counter scaling) and the
-    achieved copy bandwidth."""
+    """Plain device copy of 1 GiB (the reference kernel for counter scaling)
+    and its achieved bandwidth: the practical HBM ceiling of this device."""
     n = 1 << 28
     a = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
@@ -244,7 +323,19 @@ def copy_check():
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / 10
-    return dict(bytes_read=n * 4, bytes_written=n * 4, ms=ms, gbps=2 * n * 4 / ms / 1e6)
+    del a, b
+    torch.cuda.empty_cache()
+    return dict(bytes_read=n * 4, bytes_written=n * 4, ms=round(ms, 4), gbps=round(2 * n * 4 / ms / 1e6, 1))
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(cfg, wl, budget_s=15.0):
@@ -291,6 +382,7 @@ def cpu_baseline(cfg, wl, budget_s=15.0):
         if t_total >= budget_s:
             break
     return dict(value=rows_done / t_total, unit="tokens/s", cores=nthreads, kind="oracle",
+                cpu_model=cpu_model(),
                 sample=f"{rows_done} query-row steps over the {wl.R} rows of the same workload, each a whole step "
                        f"(append + Full + {modes.count('R')} Reindex + {len(modes)} attention layers), "
                        f"{t_total:.1f} s of CPU time with {nthreads} OpenMP threads")
@@ -299,6 +391,132 @@ def cpu_baseline(cfg, wl, budget_s=15.0):
 def source_hash(name):
     p = os.path.join(ROOT, "sparse_attention_fp4_amd", "csrc", name)
     return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def pct(a, q):
+    return round(float(np.percentile(a, q)), 4)
+
+
+def measure(cfg, args, flusher, copy_gbps, with_paged=True):
+    """Build one workload and measure its step: cold (headline) and warm step
+    times, the per-call breakdown, launches per step and the rooflines."""
+    log(f"bench: config {cfg.cid} ({cfg.name}) generating inputs")
+    wl, step = build(cfg, "cuda")
+    R = wl.R
+    row_len = wl.row_len.cpu().numpy()
+    alg = algorithmic_bytes(cfg, wl.lengths, R, row_len)
+    flops = algorithmic_flops(cfg, R, row_len)
+    prefill = bool(cfg.prefill_rows)
+    rows_per_step = cfg.prefill_rows if prefill else R
+
+    log("bench: eager warmup")
+    for _ in range(max(args.warmup, 1)):
+        step.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        step.run()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) / 3 * 1000
+
+    log("bench: capturing the step as a HIP graph")
+    g = graph_of(step.run, keep=True)
+    nodes = graph_kernel_nodes(g)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    log(f"bench: timing {args.steps} cold-cache steps")
+    cold = timed_steps(g, args.steps, flusher)
+    log(f"bench: timing {args.steps} warm steps")
+    warm_ms = time_graph(g, args.steps)
+    ms = float(np.median(cold))
+    res = {
+        "value": round(rows_per_step / (ms / 1000.0), 1),
+        "ms_per_step": round(ms, 4),
+        "ms_per_step_p10": pct(cold, 10),
+        "ms_per_step_p90": pct(cold, 90),
+        "timing": "cold cache: 1 GiB written before each step outside its events; median over the timed steps",
+        "value_warm": round(rows_per_step / (warm_ms / 1000.0), 1),
+        "ms_per_step_warm": round(warm_ms, 4),
+        "ms_per_step_eager": round(eager_ms, 3),
+        "algorithmic_bytes_per_step": alg["total"],
+    }
+    step_gbps = alg["total"] / (ms / 1000.0) / 1e9
+    res["hbm_gbps_step"] = round(step_gbps, 1)
+    res["hbm_frac_step"] = round(step_gbps / HBM_PEAK_GBPS, 4)
+    if copy_gbps:
+        res["copy_ceiling_frac_step"] = round(step_gbps / copy_gbps, 4)
+    if nodes is not None:
+        res["launches_per_step"] = nodes[0]
+        res["graph_nodes_per_step"] = nodes[1]
+
+    if not args.no_breakdown:
+        log("bench: per-call timing")
+        breakdown = per_call_times(step)
+        modes = list(cfg.layers)
+        calls_per_step = {"quantize_append": 1, "index_full": modes.count("F"),
+                          "index_reindex": modes.count("R"), "sparse_attn": len(modes)}
+        call_bytes = {"quantize_append": alg["a1"], "index_full": alg["a2"],
+                      "index_reindex": alg["a4_per_layer"], "sparse_attn": alg["a5_per_layer"]}
+        shares = {k: breakdown[k] * calls_per_step[k] / 1000.0 / warm_ms for k in breakdown}
+
+        def roof(call):
+            us = breakdown[call]
+            tr = TRAFFIC.get((cfg.cid, call, source_hash(CALL_SOURCE[call])))
+            extra = dict(kernel=f"csa2_{call}: {CALL_KERNELS[call]}", us_per_launch=round(us, 2),
+                         launches_per_step=calls_per_step[call], share_of_warm_step=round(shares[call], 3))
+            if prefill and call != "quantize_append":
+                # the chunk's rows share one key set: bound by the matrix cores
+                dt = "fp16" if call == "sparse_attn" else "fp8"
+                achieved = flops[call] / (us / 1e6) / 1e12
+                peak = MFMA_PEAK_TFLOPS[dt]
+                return dict(bound="mfma", achieved=round(achieved, 1), peak=peak, unit="TFLOP/s",
+                            frac=round(achieved / peak, 4), traffic=tr, dtype=dt,
+                            algorithmic_flops_per_launch=int(flops[call]),
+                            algorithmic_bytes_per_launch=int(call_bytes[call]), **extra)
+            achieved = call_bytes[call] / (us / 1e6) / 1e9
+            r = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                     frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=tr,
+                     algorithmic_bytes_per_launch=int(call_bytes[call]), **extra)
+            if copy_gbps:
+                r["copy_ceiling_frac"] = round(achieved / copy_gbps, 4)
+            return r
+
+        dominant = max(shares, key=shares.get)
+        res["per_call_us"] = {k: round(v, 2) for k, v in breakdown.items()}
+        res["roofline"] = roof(dominant)
+        res["roofline_index_full"] = roof("index_full")
+        if calls_per_step["index_reindex"]:
+            res["roofline_index_reindex"] = roof("index_reindex")
+        if not prefill:
+            res["roofline_sparse_attn"] = roof("sparse_attn")
+
+    if with_paged and args.page_rows > 0:
+        log(f"bench: paged step ({args.page_rows} entries per page)")
+        pstep = build_paged(cfg, wl, step, args.page_rows)
+        for _ in range(max(args.warmup, 1)):
+            pstep.run()
+        pg = graph_of(pstep.run)
+        pg.replay()
+        pcold = timed_steps(pg, args.steps, flusher)
+        pms = float(np.median(pcold))
+        res["paged"] = {
+            "page_rows": args.page_rows,
+            "swa": "ring, seeded heads" if pstep.swa_head is not None else "packed",
+            "ms_per_step": round(pms, 4),
+            "value": round(rows_per_step / (pms / 1000.0), 1),
+            "ms_per_step_warm": round(time_graph(pg, args.steps), 4),
+            "per_call_us": ({k: round(v, 2) for k, v in per_call_times(pstep).items()}
+                            if not args.no_breakdown else {}),
+        }
+        del pstep, pg
+    return wl, step, res
+
+
+def workload_name(cfg, R, row_len):
+    return (f"{cfg.name}: {R} query rows x {int(row_len.max())} max entries, D={cfg.D} FP4 (E2M1 + E4M3/16ch), "
+            f"SWA {cfg.W} FP8, {cfg.H} heads, indexer {cfg.Hi}x{cfg.Di} FP8, Top-{cfg.K}, pool {cfg.P}x8, "
+            f"layers {cfg.layers}")
 
 
 def main():
@@ -311,7 +529,7 @@ def main():
                                                           "6 prefill chunk (all 20 layers), 1 tiny")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-breakdown", action="store_true")
-    ap.add_argument("--copy-check", action="store_true", help="also time a plain 1 GiB device copy")
+    ap.add_argument("--no-1m", action="store_true", help="skip the decode-1M object of the default run")
     ap.add_argument("--page-rows", type=int, default=64, help="also time the step over a paged copy of the "
                                                                "caches with pages of this many entries (0: skip)")
     args = ap.parse_args()
@@ -326,126 +544,57 @@ def main():
     import sparse_attention_fp4_amd as csa2
     csa2.lib()
 
+    log("bench: device copy ceiling")
+    copy = copy_check()
+    boundary = launch_boundary_us()
+    flusher = Flusher()
+
     cfg = workloads.CONFIGS[args.config]
-    log(f"bench: config {cfg.cid} ({cfg.name}) generating inputs")
-    wl, step = build(cfg, "cuda")
+    wl, step, res = measure(cfg, args, flusher, copy["gbps"])
     R = wl.R
     row_len = wl.row_len.cpu().numpy()
-    alg = algorithmic_bytes(cfg, wl.lengths, R, row_len)
-
-    log("bench: eager warmup")
-    for _ in range(max(args.warmup, 1)):
-        step.run()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(3):
-        step.run()
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) / 3 * 1000
-
-    log("bench: capturing the step as a HIP graph")
-    g = graph_of(step.run)
-    for _ in range(args.warmup):
-        g.replay()
-    torch.cuda.synchronize()
-    log(f"bench: timing {args.steps} steps")
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        g.replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    tokens_per_s = R / (ms / 1000.0) if not cfg.prefill_rows else cfg.prefill_rows / (ms / 1000.0)
-    step_gbps = alg["total"] / (ms / 1000.0) / 1e9
-
-    breakdown, roofline, index_roofline, reindex_roofline, shares = {}, None, None, None, {}
-    if not args.no_breakdown:
-        log("bench: per-call timing")
-        breakdown = per_call_times(step)
-        modes = list(cfg.layers)
-        calls_per_step = {"quantize_append": 1, "index_full": modes.count("F"),
-                          "index_reindex": modes.count("R"), "sparse_attn": len(modes)}
-        call_bytes = {"quantize_append": alg["a1"], "index_full": alg["a2"],
-                      "index_reindex": alg["a4_per_layer"], "sparse_attn": alg["a5_per_layer"]}
-        shares = {k: breakdown[k] * calls_per_step[k] / 1000.0 / ms for k in breakdown}
-
-        def roof(call):
-            us = breakdown[call]
-            achieved = call_bytes[call] / (us / 1e6) / 1e9
-            tr = TRAFFIC.get((cfg.cid, call, source_hash(CALL_SOURCE[call])))
-            return dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
-                        frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=tr,
-                        kernel=f"csa2_{call}: {CALL_KERNELS[call]}", us_per_launch=round(us, 2),
-                        launches_per_step=calls_per_step[call], share_of_step=round(shares[call], 3),
-                        algorithmic_bytes_per_launch=int(call_bytes[call]))
-        dominant = max(shares, key=shares.get)
-        roofline = roof(dominant)
-        index_roofline = roof("index_full")
-        if calls_per_step["index_reindex"]:
-            reindex_roofline = roof("index_reindex")
-    log("bench: cold-cache steps")
-    cold_ms = cold_step_ms(g, min(args.steps, 10))
-    extra = {}
-    if args.page_rows > 0:
-        log(f"bench: paged step ({args.page_rows} entries per page)")
-        pstep = build_paged(cfg, wl, step, args.page_rows)
-        for _ in range(max(args.warmup, 1)):
-            pstep.run()
-        pg = graph_of(pstep.run)
-        time_graph(pg, 2)
-        pms = time_graph(pg, args.steps)
-        extra["paged"] = {
-            "page_rows": args.page_rows,
-            "swa": "ring, seeded heads" if pstep.swa_head is not None else "packed",
-            "ms_per_step": round(pms, 4),
-            "value": round((cfg.prefill_rows or R) / (pms / 1000.0), 1),
-            "per_call_us": ({k: round(v, 2) for k, v in per_call_times(pstep).items()}
-                            if not args.no_breakdown else {}),
-        }
-        del pstep, pg
-        torch.cuda.empty_cache()
-    if args.copy_check:
-        extra["copy_check"] = copy_check()
-
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: CPU oracle baseline")
         cpu = cpu_baseline(cfg, wl)
+    del step, wl
+    torch.cuda.empty_cache()
 
-    D = cfg.D
+    decode_1m = None
+    if args.config == 2 and not args.no_1m:
+        cfg3 = workloads.CONFIGS[3]
+        wl3, step3, r3 = measure(cfg3, args, flusher, copy["gbps"], with_paged=False)
+        r3["workload"] = workload_name(cfg3, wl3.R, wl3.row_len.cpu().numpy())
+        decode_1m = r3
+        del step3, wl3
+        torch.cuda.empty_cache()
+
     result = {
         "metric": METRIC,
-        "value": round(tokens_per_s, 1),
+        "value": res.pop("value"),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": res.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8+fp16 mfma, f32 accumulate",
         "data": "synthetic (seeded, generated on the GPU)",
         "config": {
-            "workload": (f"{cfg.name}: {R} query rows x {int(row_len.max())} max entries, D={D} FP4 (E2M1 + "
-                         f"E4M3/16ch), SWA {cfg.W} FP8, {cfg.H} heads, indexer {cfg.Hi}x{cfg.Di} FP8, "
-                         f"Top-{cfg.K}, pool {cfg.P}x8, layers {cfg.layers}"),
+            "workload": workload_name(cfg, R, row_len),
             "rows": R, "entries_per_row": int(row_len.max()), "layers": cfg.layers,
         },
-        "hbm_gbps_step": round(step_gbps, 1),
-        "hbm_frac_step": round(step_gbps / HBM_PEAK_GBPS, 4),
-        "algorithmic_bytes_per_step": alg["total"],
-        "ms_per_step_cold": round(cold_ms, 4),
-        "ms_per_step_eager": round(eager_ms, 3),
-        "per_call_us": {k: round(v, 2) for k, v in breakdown.items()},
-        "roofline": roofline,
-        "roofline_index_full": index_roofline,
-        "roofline_index_reindex": reindex_roofline,
-        "cpu_baseline": cpu,
     }
-    result.update(extra)
+    result.update(res)
+    if "launches_per_step" in result:
+        result["launch_boundary_us"] = round(boundary, 3)
+        result["launch_boundaries_us_per_step"] = round(boundary * result["launches_per_step"], 1)
+    result["copy_ceiling"] = copy
+    result["cpu_baseline"] = cpu
+    if decode_1m is not None:
+        result["decode_1m"] = decode_1m
     print(json.dumps(result), flush=True)
 
 
