@@ -166,6 +166,28 @@ csa2_status_t csa2_index_reindex(const uint8_t* qI, const float* w, const uint8_
                                  int32_t block, int32_t* topk_idx,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * csa2_index_reindex with the score buffer in a fixed device array of
+ * CSA2_NOALLOC_SCRATCH_BYTES inside the library instead of a workspace.
+ * Arguments, outputs and limits are those of csa2_index_reindex (without
+ * workspace / workspace_bytes); the outputs are identical.  The call also
+ * needs csa2_index_reindex_workspace_bytes(R, Hi, K, P, block) to be at most
+ * CSA2_NOALLOC_SCRATCH_BYTES (at P = 2048: up to 256 rows) and returns
+ * CSA2_ERR_UNSUPPORTED otherwise, before any HIP call.  It allocates nothing:
+ * each GPU holds one copy of the array from its first use until the process
+ * ends, found on the first call on that device.  Every call on a GPU shares
+ * that GPU's copy, so calls that overlap on one GPU (different streams or
+ * threads) race; calls in one stream are ordered as usual.
+ */
+#define CSA2_NOALLOC_SCRATCH_BYTES (16u << 20)
+csa2_status_t csa2_index_reindex_noalloc(const uint8_t* qI, const float* w, const uint8_t* ikeys,
+                                         const int64_t* seq_start, const int32_t* row_seq,
+                                         const int32_t* row_len, const int32_t* pool_blocks,
+                                         int32_t R, int32_t Hi, int32_t Di, int32_t K, int32_t P,
+                                         int32_t block, int32_t* topk_idx, void* stream);
+
 /* ---------------------------------------------------------------------- */
 /* Sparse attention (Reuse mode = this call with inherited indices).        */
 /* CSA2 modes paragraph; FP4 main KV and FP8 SWA KV.                         */

@@ -32,7 +32,9 @@ EXPORTS = ("csa2_status_string", "csa2_last_error", "csa2_abi_version", "csa2_qu
            "csa2_index_full_workspace_bytes", "csa2_index_full",
            "csa2_index_reindex_workspace_bytes", "csa2_index_reindex",
            "csa2_sparse_attn_workspace_bytes", "csa2_sparse_attn",
-           "csa2_index_full_paged", "csa2_index_reindex_paged", "csa2_paged_rows", "csa2_sparse_attn_phys")
+           "csa2_index_full_paged", "csa2_index_reindex_paged", "csa2_paged_rows", "csa2_sparse_attn_phys",
+           "csa2_index_reindex_noalloc")
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
 
@@ -62,6 +64,7 @@ def load(path: str) -> ctypes.CDLL:
     L.csa2_index_reindex_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.csa2_index_reindex_workspace_bytes.restype = sz
     L.csa2_index_reindex.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, P, P, sz, P]
+    L.csa2_index_reindex_noalloc.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, P, P]
     L.csa2_sparse_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.csa2_sparse_attn_workspace_bytes.restype = sz
     L.csa2_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, P, P, P, i32, i32, i32, i32, f32, P, P, P,
@@ -73,8 +76,9 @@ def load(path: str) -> ctypes.CDLL:
     L.csa2_paged_rows.argtypes = [P, i32, i32, i64, P, P, P, i32, i32, P, P]
     L.csa2_sparse_attn_phys.argtypes = [P, P, P, i64, P, i32, P, P, P, P, i32, i32, i32, i32, f32, P, P, P,
                                         sz, P]
-    for f in ("csa2_quantize_append", "csa2_index_full", "csa2_index_reindex", "csa2_sparse_attn",
-              "csa2_index_full_paged", "csa2_index_reindex_paged", "csa2_paged_rows", "csa2_sparse_attn_phys"):
+    for f in ("csa2_quantize_append", "csa2_index_full", "csa2_index_reindex", "csa2_index_reindex_noalloc",
+              "csa2_sparse_attn", "csa2_index_full_paged", "csa2_index_reindex_paged", "csa2_paged_rows",
+              "csa2_sparse_attn_phys"):
         getattr(L, f).restype = ctypes.c_int
     if L.csa2_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{path} has ABI version {L.csa2_abi_version()}, expected {ABI_VERSION}: rebuild it")
@@ -248,6 +252,30 @@ def csa2_index_reindex(qI: torch.Tensor, w: torch.Tensor, ikeys: torch.Tensor, s
                                   _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                   _stream(stream))
     _check("csa2_index_reindex", st)
+    return topk_idx
+
+
+def csa2_index_reindex_noalloc(qI: torch.Tensor, w: torch.Tensor, ikeys: torch.Tensor, seq_start: torch.Tensor,
+                               row_seq: torch.Tensor, row_len: torch.Tensor, pool_blocks: torch.Tensor, K: int,
+                               topk_idx: torch.Tensor, block: int = 8, stream=None) -> torch.Tensor:
+    """csa2_index_reindex with the library's fixed device scratch array instead
+    of a workspace; the caller passes topk_idx [R, K] int32, so nothing is
+    allocated.  Calls that overlap on one GPU share the array and race."""
+    qI = _dev(_u8(qI), "qI", torch.uint8, 3)
+    R, Hi, Di = qI.shape
+    _dev(w, "w", torch.float32, shape=(R, Hi))
+    ikeys = _dev(_u8(ikeys), "ikeys", torch.uint8, shape=(None, Di))
+    _dev(seq_start, "seq_start", torch.int64, 1)
+    _dev(row_seq, "row_seq", torch.int32, shape=(R,))
+    _dev(row_len, "row_len", torch.int32, shape=(R,))
+    _dev(pool_blocks, "pool_blocks", torch.int32, shape=(R, None))
+    _dev(topk_idx, "topk_idx", torch.int32, shape=(R, K))
+    _same_gpu(qI=qI, w=w, ikeys=ikeys, seq_start=seq_start, row_seq=row_seq, row_len=row_len,
+              pool_blocks=pool_blocks, topk_idx=topk_idx)
+    st = lib().csa2_index_reindex_noalloc(_ptr(qI), _ptr(w), _ptr(ikeys), _ptr(seq_start), _ptr(row_seq),
+                                          _ptr(row_len), _ptr(pool_blocks), R, Hi, Di, K, pool_blocks.shape[1],
+                                          block, _ptr(topk_idx), _stream(stream))
+    _check("csa2_index_reindex_noalloc", st)
     return topk_idx
 
 

@@ -27,6 +27,8 @@
 //                  one of them, so the result equals a Top-K over all
 //                  entries.  Reindex mode selects among all 8P pool
 //                  positions at once (they fit in registers).
+#include <mutex>
+
 #include "csa2_device.h"
 #include "csa2_host.h"
 
@@ -1302,4 +1304,73 @@ extern "C" csa2_status_t csa2_index_reindex_paged(const uint8_t* qI, const float
     }
     return index_reindex_impl(qI, w, ikeys, nullptr, &pm, row_seq, row_len, pool_blocks, R, Hi, Di, K, P, block,
                               topk_idx, topk_rows, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------------------------ no-allocation Reindex
+//
+// csa2_index_reindex_noalloc runs the Reindex kernels with their score buffer
+// in a fixed device array instead of a caller workspace, for callers that
+// cannot allocate (code under graph capture, tight serving loops).  The array
+// lives in this file's device code, one copy per GPU the library runs on, for
+// the life of the process; host code never passes its name to a kernel (the
+// name is a host-side stand-in): the device address of each GPU's copy is
+// looked up once with hipGetSymbolAddress, with that GPU current, and kept.
+// The kernels write every score slot they later read, so the array needs no
+// clearing between calls; calls that overlap on one GPU share it and race.
+
+static __device__ __align__(256) uint8_t scratch[CSA2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices];   // device address of `scratch`, per device id
+
+// Device address of this GPU's `scratch` (the current device), looked up on
+// the first call on that device.
+csa2_status_t scratch_address(const char* who, void** out)
+{
+    int dev = -1;
+    const hipError_t e0 = hipGetDevice(&dev);
+    if (e0 != hipSuccess) return csa2::fail(CSA2_ERR_LAUNCH, "%s: hipGetDevice: %s", who, hipGetErrorString(e0));
+    CSA2_REQUIRE(dev >= 0 && dev < kMaxScratchDevices, CSA2_ERR_UNSUPPORTED, "%s: device %d >= %d", who, dev,
+                 kMaxScratchDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return csa2::fail(CSA2_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch) on device %d: %s", who, dev,
+                              hipGetErrorString(e));
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return CSA2_OK;
+}
+
+}  // namespace
+
+extern "C" csa2_status_t csa2_index_reindex_noalloc(const uint8_t* qI, const float* w, const uint8_t* ikeys,
+                                                    const int64_t* seq_start, const int32_t* row_seq,
+                                                    const int32_t* row_len, const int32_t* pool_blocks, int32_t R,
+                                                    int32_t Hi, int32_t Di, int32_t K, int32_t P, int32_t block,
+                                                    int32_t* topk_idx, void* stream)
+{
+    // every argument check of the workspace form runs first (the workspace one
+    // is met by construction), then the size limit, then the device lookup
+    const size_t need = csa2_index_reindex_workspace_bytes(R, Hi, K, P, block);
+    CSA2_REQUIRE(R >= 0 && P >= 1 && P <= kMaxP, R < 0 || P < 1 ? CSA2_ERR_SHAPE : CSA2_ERR_UNSUPPORTED,
+                 "index_reindex_noalloc: R=%d, P=%d out of range", R, P);
+    CSA2_REQUIRE(need <= (size_t)CSA2_NOALLOC_SCRATCH_BYTES, CSA2_ERR_UNSUPPORTED,
+                 "index_reindex_noalloc: R=%d rows with P=%d pool blocks need %zu bytes of scratch, more than the "
+                 "fixed %zu (call csa2_index_reindex with a workspace, or split the rows)",
+                 R, P, need, (size_t)CSA2_NOALLOC_SCRATCH_BYTES);
+    if (R == 0) return index_reindex_impl(qI, w, ikeys, seq_start, nullptr, row_seq, row_len, pool_blocks, R, Hi,
+                                          Di, K, P, block, topk_idx, nullptr, nullptr, 0, stream);
+    if (!seq_start) return csa2::fail(CSA2_ERR_NULL, "index_reindex_noalloc: seq_start is NULL");
+    void* ws = nullptr;
+    const csa2_status_t s = scratch_address("index_reindex_noalloc", &ws);
+    if (s != CSA2_OK) return s;
+    return index_reindex_impl(qI, w, ikeys, seq_start, nullptr, row_seq, row_len, pool_blocks, R, Hi, Di, K, P,
+                              block, topk_idx, nullptr, ws, (size_t)CSA2_NOALLOC_SCRATCH_BYTES, stream);
 }
