@@ -14,22 +14,43 @@ LIB_DEBUG = os.path.join(HERE, "libcsa2_debug.so")
 SOURCES = ["status.hip", "quantize.hip", "index.hip", "attn.hip"]
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from emitting packed-fp32 VALU instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
 ]
+# Per-source flags.  attn.hip keeps matrix-core operands and accumulators in
+# ordinary VGPRs: its kernels run two waves per SIMD, and at that occupancy the
+# compiler would otherwise split the 256 registers evenly between VGPRs and
+# AGPRs, which its working set does not fit.
+SOURCE_FLAGS = {"attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(out: str, extra, verbose: bool) -> str:
+    """Compile every source to its own object (in parallel), then link."""
+    from concurrent.futures import ThreadPoolExecutor
+
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = out + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *extra, "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
-    os.replace(tmp, out)
+    objs = [f"{out}.{os.path.splitext(s)[0]}.o" for s in SOURCES]
+
+    def run(cmd):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+
+    cmds = [[hipcc, *HIPCC_FLAGS, *SOURCE_FLAGS.get(s, []), *extra, "-c", "-o", o, os.path.join(CSRC, s)]
+            for s, o in zip(SOURCES, objs)]
+    try:
+        with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+            for f in [ex.submit(run, c) for c in cmds]:
+                f.result()
+        run([hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+        os.replace(tmp, out)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return out
 
 

@@ -8,28 +8,29 @@
 // is shared by all query heads; the selected entries and the SWA rows form one
 // key set under one softmax.
 //
-// Work decomposition.  One workgroup (4 waves) = one query row x NH = 16*HT
-// heads x a contiguous range of 16-key fragments.  The waves take the range's
-// fragments in turn and each runs a complete online softmax over its own
-// fragments, so no wave waits for another before the final merge:
-//   * S^T = K Q^T: lane (key col, grp) dequantises D/4 channels of key col
-//     straight from the cache to fp16 in registers (E2M1 -> fp16 by the
-//     hardware converter, times the E4M3 scale; the product is exact in fp16)
-//     and feeds them as the A operand of v_mfma_f32_16x16x32_f16 against the
-//     NH query heads (B operand, all D channels held in registers).  The
-//     contraction order only has to agree between the two operands; it is
-//     chosen so that in every MFMA lanes 0-31 carry the two halves of one
-//     16-channel scale group and lanes 32-63 those of another (see below).
-//   * The same fp16 values go to the wave's own LDS tile [16 keys][D] and come
-//     back transposed (ds_read_b64_tr_b16) as the B operand of PV.
-//   * The S^T accumulator (lane = head, 4 keys) is already the A operand
-//     layout of v_mfma_f32_16x16x16_f16, so probabilities never leave the
-//     registers.  Online softmax in the log2 domain with a lazily raised
-//     reference max.
-//   * At the end the four waves' (max, sums, O) are merged through LDS; wave w
-//     writes output channels [w*D/4, (w+1)*D/4).  Rows whose fragments are
-//     split across workgroups write unnormalised partial outputs plus (max,
-//     sums); k_attn_combine merges them.
+// Work decomposition.  One workgroup (8 waves, two per SIMD) = one query row
+// x NH = 16*HT heads x a contiguous range of 16-key fragments, taken in rounds
+// of 8 fragments, fragment f0 + w of a round by wave w:
+//   * scores: wave w dequantises its fragment's 16 keys straight from the
+//     cache to fp16 in registers (E2M1 -> fp16 by the hardware converter,
+//     times the E4M3 scale; the product is exact in fp16) and feeds them as the
+//     A operand of v_mfma_f32_16x16x32_f16 against the NH query heads (B
+//     operand, all D channels held in registers): S^T of the fragment.  The
+//     same fp16 values go to the wave's V tile in LDS.
+//   * softmax: the waves publish each fragment's per-head maximum; every wave
+//     derives the same reference maximum per head from them (raised lazily,
+//     log2 domain, so the output is rarely rescaled), and the owner turns its
+//     scores into fp16 probabilities, published in the A operand layout of
+//     v_mfma_f32_16x16x16_f16 (the S^T accumulator already has it).
+//   * PV: output channels are split between the waves (D/8 each); every wave
+//     multiplies the probabilities of all 8 fragments of the round into its
+//     channels, reading its columns of the 8 V tiles transposed
+//     (ds_read_b64_tr_b16).
+// So each key is dequantised once per workgroup, a wave's accumulators hold
+// only its channels (two waves fit one SIMD and hide each other's latency),
+// and the end needs no merge of outputs between waves.  Rows whose fragments
+// are split across workgroups write unnormalised partial outputs plus (max,
+// sums); k_attn_combine merges them.
 //
 // Exact scores for keys with large values.  The matrix cores sum products
 // with errors of a few units in the last place of the largest addend, and
@@ -51,7 +52,7 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kFrag = 16;           // keys per fragment (one MFMA row block)
-constexpr int kWaves = 4;           // waves per workgroup
+constexpr int kWaves = 8;           // waves per workgroup (two per SIMD), fragments per round
 constexpr float kLazy = 8.0f;       // log2-domain slack before a running max is raised
 constexpr int kMaxPlanSplits = 8;   // key splits per row, at most
 
@@ -278,44 +279,36 @@ __device__ __forceinline__ f16x8 dequant_step(const FragRaw<D>& fr, int t)
     return fr.is_main ? a : b;
 }
 
-// The workgroup's output channels are part c of CS equal parts of D; its V
-// tile holds only those.  k-step t of lane group grp falls in part
-// (D/2 * p + 16 t) / (D/CS), p = grp / 2.
-template <int D, int CS>
-__device__ __forceinline__ bool in_part(int grp, int t, int c)
+// Store k-step t of the lane's key to its row (vrow) of the wave's V tile.
+template <int D>
+__device__ __forceinline__ void v_store(_Float16* vrow, int grp, int t, f16x8 kf)
 {
-    return step_ch<D>(grp, t) / (D / CS) == c;
+    *reinterpret_cast<f16x8*>(vrow + step_ch<D>(grp, t)) = kf;
 }
 
-// Store k-step t of the lane's key to the V tile (vrow: the lane's key row of
-// the tile, already offset by -c D/CS) if it belongs to the part.
-template <int D, int CS>
-__device__ __forceinline__ void v_store(_Float16* vrow, int grp, int t, int c, f16x8 kf)
-{
-    if (in_part<D, CS>(grp, t, c)) *reinterpret_cast<f16x8*>(vrow + step_ch<D>(grp, t)) = kf;
-}
-
-// S^T of one fragment, fp32 MFMA chain; the dequantised keys of the
-// workgroup's channel part also go to the wave's V tile.
-template <int MODE, int HT, int D, int CS>
+// S^T of one fragment, fp32 MFMA chain; the dequantised keys also go to the
+// wave's V tile.
+template <int MODE, int HT, int D>
 __device__ __forceinline__ void s_frag(const FragRaw<D>& fr, const f16x8 (&qf)[HT][D / 32], _Float16* vrow, int grp,
-                                       int c, f32x4 (&acc)[HT])
+                                       f32x4 (&acc)[HT])
 {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
         const f16x8 kf = dequant_step<MODE, D>(fr, t);
-        v_store<D, CS>(vrow, grp, t, c, kf);
+        v_store<D>(vrow, grp, t, kf);
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ht][t], acc[ht], 0, 0, 0);
     }
 }
 
 // The same fragment with S computed exactly as (hi, lo) = K a^T + K b^T
-// (split of q described at the top of the file).  qab: this lane's a- and
-// b-part pieces in LDS, [2][HT * KS][64 lanes]; upper: lane >= 32.
-template <int HT, int D, int CS>
-__device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const f16x8* qab, bool upper, _Float16* vrow,
-                                             int grp, int c, f32x4 (&acc)[HT], f32x4 (&lo)[HT])
+// (split of q described at the top of the file).  qa: this lane's a-part
+// pieces in LDS, [HT * KS][64 lanes]; b = q - a is formed from the query
+// registers (an exact fp16 subtraction: the difference is q's bits below the
+// quantum of a).  upper: lane >= 32.
+template <int HT, int D>
+__device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const f16x8* qa, const f16x8 (&qf)[HT][D / 32],
+                                             bool upper, _Float16* vrow, int grp, f32x4 (&acc)[HT], f32x4 (&lo)[HT])
 {
     constexpr int KS = D / 32;
     double ex[HT][4];
@@ -330,13 +323,13 @@ __device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const f16x8* 
 #pragma unroll
     for (int t = 0; t < KS; ++t) {
         const f16x8 kf = dequant_step<2, D>(fr, t);
-        v_store<D, CS>(vrow, grp, t, c, kf);
+        v_store<D>(vrow, grp, t, kf);
         const f16x8 k_lo = upper ? zero : kf;     // scale group t (p = 0)
         const f16x8 k_hi = upper ? kf : zero;     // and scale group KS + t (p = 1)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-            const f16x8 a = qab[(ht * KS + t) * CSA2_WAVE];
-            const f16x8 b = qab[((HT + ht) * KS + t) * CSA2_WAVE];
+            const f16x8 a = qa[(ht * KS + t) * CSA2_WAVE];
+            const f16x8 b = qf[ht][t] - a;
             sb[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, b, sb[ht], 0, 0, 0);
             const f32x4 g0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_lo, a, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
             const f32x4 g1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_hi, a, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
@@ -355,39 +348,47 @@ __device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const f16x8* 
         }
 }
 
-// O[heads x the part's channels] += P V for one fragment.  The B operand is read with
-// ds_read_b64_tr_b16: within each 16-lane group, lane l receives element l%4
-// of the 8-byte rows addressed by lanes 4i + l/4, so addressing row (key
-// 4g + l/4, channels c0 + 4(l%4)) hands lane l the 4 keys 4g + 0..3 of channel
-// c0 + l, the key order of the probability operand.
-template <int HT, int NDT, int VS>
-__device__ __forceinline__ void pv_frag(const f16x4 (&pa)[HT], const _Float16* vt, int col, int grp,
-                                        f32x4 (&o)[HT][NDT])
+// O[heads x the wave's channels] += P V for G fragment slots of the round,
+// all of whose LDS reads are issued before the first product.  The B operand
+// is read with ds_read_b64_tr_b16: within each 16-lane group, lane l receives
+// element l%4 of the 8-byte rows addressed by lanes 4i + l/4, so addressing
+// row (key 4g + l/4, channels c0 + 4(l%4)) hands lane l the 4 keys 4g + 0..3
+// of channel c0 + l, the key order of the probability operand.
+// pp: this lane's probabilities of the first slot, [HT][64] apart by head
+// tile, pstride apart by slot; vr: this lane's address in the first slot's
+// tile at the wave's first channel, vstride apart by slot.
+constexpr int kPvGroup = 4;
+template <int G, int HT, int NDT>
+__device__ __forceinline__ void pv_slots(const f16x4* pp, int pstride, const _Float16* vr, int vstride,
+                                         f32x4 (&o)[HT][NDT])
 {
-    const _Float16* vr = vt + (4 * grp + (col >> 2)) * VS + 4 * (col & 3);
-    constexpr int B = NDT < 16 ? NDT : 16;   // reads in flight
+    f16x4 pa[G][HT];
+    lds_f16x4 b[G][NDT];
 #pragma unroll
-    for (int d0 = 0; d0 < NDT; d0 += B) {
-        lds_f16x4 b[B];
+    for (int u = 0; u < G; ++u) {
 #pragma unroll
-        for (int k = 0; k < B; ++k)
-            b[k] = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4 __attribute__((address_space(3)))*)(vr + 16 * (d0 + k)));
-        __builtin_amdgcn_sched_barrier(0);
+        for (int ht = 0; ht < HT; ++ht) pa[u][ht] = pp[u * pstride + ht * CSA2_WAVE];
 #pragma unroll
-        for (int k = 0; k < B; ++k) {
-            const f16x4 vb = {(_Float16)b[k][0], (_Float16)b[k][1], (_Float16)b[k][2], (_Float16)b[k][3]};
+        for (int k = 0; k < NDT; ++k)
+            b[u][k] = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                (lds_f16x4 __attribute__((address_space(3)))*)(vr + u * vstride + 16 * k));
+    }
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+#pragma unroll
+        for (int k = 0; k < NDT; ++k) {
+            const f16x4 vb = {(_Float16)b[u][k][0], (_Float16)b[u][k][1], (_Float16)b[u][k][2], (_Float16)b[u][k][3]};
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht)
-                o[ht][d0 + k] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa[ht], vb, o[ht][d0 + k], 0, 0, 0);
+                o[ht][k] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa[u][ht], vb, o[ht][k], 0, 0, 0);
         }
-    }
 }
 
 // Workgroups are handed to the 8 XCDs of the chip round-robin by linear id,
 // and each XCD has its own L2.  All G workgroups of a row are placed on one
 // XCD (row r on XCD r % 8, at consecutive slots there), so the head groups and
-// key splits of a row share its key bytes in one L2 and the merge kernel finds
-// the row's partial outputs there.
+// key splits of a row share its key bytes in one L2, where the merge kernel
+// finds the row's partial outputs.
 constexpr int kXcds = 8;
 __host__ __device__ inline int64_t xcd_grid(int64_t R, int64_t G) { return (R + kXcds - 1) / kXcds * kXcds * G; }
 // workgroup id -> (row, index g < G within the row)
@@ -404,32 +405,30 @@ __host__ __device__ inline int pad_topk(int K) { return (K + kFrag - 1) / kFrag 
 // Kind of a fragment (uniform): 0 Top-K slots, 1 SWA rows.
 __device__ __forceinline__ int frag_kind(int fr, int Kp) { return fr * kFrag >= Kp ? 1 : 0; }
 
-// LDS of one workgroup: the waves' V tiles and the query (fp16, and its a-
-// and b-parts) during the key loop, then the merge buffers.
-template <int HT, int D, int CS>
+// LDS of one workgroup: one V tile per fragment slot of a round (slot w
+// filled by wave w), the a-part of the query (exact scores) and the round's
+// probabilities; before the loop the query is staged where the tiles go.
+template <int HT, int D>
 struct AttnSmem {
     static constexpr int KS = D / 32;
-    static constexpr int DP = D / CS;              // channels of the workgroup's part
-    static constexpr int NDT = DP / 16;            // output tiles per head tile
-    static constexpr int VS = DP + 8;              // V row stride in halves (conflict-free rows and transposes)
-    static constexpr int kVBytes = kWaves * kFrag * VS * 2;
-    static constexpr int kQaBytes = 2 * HT * KS * CSA2_WAVE * 16;   // a and b parts
-    static constexpr int kQfBytes = HT * KS * CSA2_WAVE * 16;       // the query as fp16
-    static constexpr int kLoop = kVBytes + kQaBytes + kQfBytes;
-    // Merge: rounds over RT output tiles at a time (a multiple of the wave
-    // count); per round every wave stores its RT tiles per head tile,
-    // [wave][HT][RT][64] f32x4.  One round when that fits in 128 KB.
-    static constexpr int RT = HT * NDT <= 32 ? NDT : 32 / HT;
-    static_assert(RT % kWaves == 0 && NDT % RT == 0, "merge rounds");
-    static constexpr int kMerge = kWaves * HT * RT * CSA2_WAVE * 16;
-    static constexpr int kBytes = kLoop > kMerge ? kLoop : kMerge;
+    static constexpr int NH = HT * 16;
+    static constexpr int CW = D / kWaves;          // output channels of a wave
+    static constexpr int NDT = CW / 16;            // its output tiles per head tile
+    static constexpr int VS = D + 8;               // V row stride in halves (conflict-free rows and transposes)
+    static constexpr int kTile = kFrag * VS;       // halves per V tile
+    static constexpr int kVBytes = kWaves * kTile * 2;
+    static constexpr int kQaBytes = HT * KS * CSA2_WAVE * 16;         // [HT * KS][64] f16x8
+    static constexpr int kPBytes = kWaves * 2 * HT * CSA2_WAVE * 8;   // [slot][hi, lo][HT][64] f16x4
+    static constexpr int kBytes = kVBytes + kQaBytes + kPBytes;
+    static_assert(HT * KS * CSA2_WAVE * 16 <= kVBytes, "the query staging fits the V tiles");
+    static_assert(D % (16 * kWaves) == 0 && NDT >= 1, "whole output tiles per wave");
 };
 
 // PG: the index lists hold cache rows (paged caches) and the SWA window may be
 // a ring; the packed form is a separate instantiation so that it carries none
 // of that addressing.
-template <int HT, int D, int CS, bool PG>
-__global__ __launch_bounds__(256, 1) void k_sparse_attn(
+template <int HT, int D, bool PG>
+__global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const int64_t* __restrict__ seq_start, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ topk, int32_t K,
@@ -438,32 +437,31 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     int32_t H, int32_t W, float scale_log2e, int32_t HG, int32_t S, int32_t nfrag, float* __restrict__ out,
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml)
 {
-    using SM = AttnSmem<HT, D, CS>;
+    using SM = AttnSmem<HT, D>;
     constexpr int KS = SM::KS;
+    constexpr int NH = SM::NH;
     constexpr int NDT = SM::NDT;
     constexpr int VS = SM::VS;
-    constexpr int NH = HT * 16;
 
     __shared__ __attribute__((aligned(16))) char smem[SM::kBytes];
-    __shared__ float wm[kWaves][NH];
-    __shared__ float wl[kWaves][NH];
-    __shared__ float wle[kWaves][NH];
-    __shared__ uint32_t wqm[kWaves][NH];   // per wave: bf16 bits of the max |q| of each head over its pieces
-    _Float16* const vt = reinterpret_cast<_Float16*>(smem) + (threadIdx.x >> 6) * (kFrag * VS);
-    f16x8* const qa_s = reinterpret_cast<f16x8*>(smem + SM::kVBytes);   // [2][HT * KS][64]: a, b
-    f16x8* const qf_s = reinterpret_cast<f16x8*>(smem + SM::kVBytes + SM::kQaBytes);   // [HT * KS][64]
-    f32x4* const xo = reinterpret_cast<f32x4*>(smem);                    // merge buffers (after the loop)
+    __shared__ float4 fmx[NH][kWaves / 4];   // per head: each slot's largest logit of the head
+    __shared__ float wsum[2][kWaves][NH];    // at the end: each wave's sums (PV weights, unrounded)
+    __shared__ uint32_t wqm[kWaves][NH];     // per wave: bf16 bits of the max |q| of each head over its pieces
+    __shared__ int fprec[kWaves];            // per slot: exact scores, two-part probabilities
+    _Float16* const vtiles = reinterpret_cast<_Float16*>(smem);
+    f16x8* const qa_s = reinterpret_cast<f16x8*>(smem + SM::kVBytes);                  // [HT * KS][64]
+    f16x4* const p_s = reinterpret_cast<f16x4*>(smem + SM::kVBytes + SM::kQaBytes);   // [slot][2][HT][64]
+    f16x8* const qf_s = reinterpret_cast<f16x8*>(smem);                                // staging (before the loop)
 
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: branches on it are scalar
     const int col = lane & 15, grp = lane >> 4, hf = grp & 1;
-    int r, hg, c, s;   // row, head group, channel part, key split
-    bool g_first;      // the row's first workgroup
+    int r, hg, s;   // row, head group, key split
+    bool g_first;   // the row's first workgroup
     {
-        const int g = xcd_slot(blockIdx.x, HG * CS * S, r);
+        const int g = xcd_slot(blockIdx.x, HG * S, r);
         hg = g % HG;
-        c = g / HG % CS;
-        s = g / (HG * CS);
+        s = g / HG;
         g_first = g == 0;
     }
     (void)g_first;
@@ -475,9 +473,9 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
 
     // Loads are issued in dependency order so that waiting for one never waits
     // for a later chain: the row's metadata (scalar) and the wave's first two
-    // fragments' Top-K entries, the wave's quarter of the query, then the
-    // first fragment's key bytes, which arrive during the barriers that share
-    // the query.
+    // fragments' Top-K entries, the wave's pieces of the query, then the first
+    // fragment's key bytes, which arrive during the barriers that share the
+    // query.
     // PG: the index lists hold cache rows directly (paged caches),
     // checked against the cache size; otherwise entries of the row's sequence.
     const int n = PG ? (int)(phys_rows < 0x7FFFFFFF ? phys_rows : 0x7FFFFFFF) : row_len[r];
@@ -493,30 +491,33 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     // Top-K entry of the lane's key in a fragment; SWA slots are left as they
     // are (the key loads never read them), and no select on the loaded value
     // so nothing waits for the load here.
-    auto load_idx = [&](int fr, int& idx) {
-        const int slot = fr * kFrag + col;
+    auto load_idx = [&](int fr_, int& idx) {
+        const int slot = fr_ * kFrag + col;
         if (slot < K) idx = topk_row[slot];
     };
-    int fr = f_begin + wave;
+    const int fw = f_begin + wave;   // the wave's fragment in the first round
     int idx_c = 0, idx_n = 0;
-    if (fr < f_end) load_idx(fr, idx_c);
-    if (fr + kWaves < f_end) load_idx(fr + kWaves, idx_n);
-    // The query is shared by the four waves: wave w loads and converts the
-    // pieces (ht, t) with (ht * KS + t) % 4 == w, i.e. piece k < NP of the
-    // wave is ht = k / (KS/4), t = 4k % KS + w; the pieces go to LDS and every
-    // wave reads the whole query back after the barrier.  The query is read
-    // through a buffer over its H heads: heads past H read as zeros.
-    constexpr int NP = HT * KS / kWaves;
-    static_assert(KS % kWaves == 0, "query pieces per wave");
-    uint4 qraw[NP];
+    if (fw < f_end) load_idx(fw, idx_c);
+    if (fw + kWaves < f_end) load_idx(fw + kWaves, idx_n);
+    // The query, as NQP pieces (piece P = ht * KS + t: k-step t of head tile
+    // ht, the B operand layout); wave w loads and converts pieces w, w + 8, ...,
+    // which go to LDS; every wave reads the whole query back after the
+    // barrier.  The query is read through a buffer over its H heads: heads past
+    // H read as zeros.
+    constexpr int NQP = HT * KS;
+    constexpr int NPW = (NQP + kWaves - 1) / kWaves;
+    uint4 qraw[NPW];
     {
         const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + (int64_t)r * H * D, H * D * 2);
 #pragma unroll
-        for (int k = 0; k < NP; ++k) {
-            const int ht = k / (KS / kWaves), t = (kWaves * k) % KS + wave;
-            const uint32_t hoff = (uint32_t)(h0 + ht * 16 + col) * (D * 2);
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, hoff + 2 * step_ch<D>(grp, t), 0, 0);
-            qraw[k] = make_uint4(v[0], v[1], v[2], v[3]);
+        for (int k = 0; k < NPW; ++k) {
+            const int P = k * kWaves + wave;
+            qraw[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (P < NQP) {
+                const uint32_t hoff = (uint32_t)(h0 + (P / KS) * 16 + col) * (D * 2);
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, hoff + 2 * step_ch<D>(grp, P % KS), 0, 0);
+                qraw[k] = make_uint4(v[0], v[1], v[2], v[3]);
+            }
         }
     }
     CSA2_DCHECK(g_first && threadIdx.x == 0 && (nsw < 0 || nsw > W));
@@ -528,11 +529,14 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     for (int ht = 0; ht < HT; ++ht) {
         u16x2 mx = {0, 0};
 #pragma unroll
-        for (int k = ht * (KS / kWaves); k < (ht + 1) * (KS / kWaves); ++k) {
-            const uint32_t ws[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
+        for (int k = 0; k < NPW; ++k) {
+            const int P = k * kWaves + wave;
+            if (P < NQP && P / KS == ht) {
+                const uint32_t ws[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, ws[e] & 0x7FFF7FFFu));
+                for (int e = 0; e < 4; ++e)
+                    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, ws[e] & 0x7FFF7FFFu));
+            }
         }
         uint32_t mb = mx[0] > mx[1] ? mx[0] : mx[1];
         mb = umax_xor32(umax_xor16(mb));
@@ -556,21 +560,22 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
         Cq[ht] = __uint_as_float((uint32_t)(E + 12 + 127) << 23 | 0x400000u);
     }
 #pragma unroll
-    for (int k = 0; k < NP; ++k) {
-        const int ht = k / (KS / kWaves), t = (kWaves * k) % KS + wave;
+    for (int k = 0; k < NPW; ++k) {
+        const int P = k * kWaves + wave;
+        if (P >= NQP) continue;
+        float C = Cq[0];
+#pragma unroll
+        for (int ht = 1; ht < HT; ++ht) C = P / KS == ht ? Cq[ht] : C;
         const uint32_t ws[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
-        f16x8 qv, av, bv;
+        f16x8 qv, av;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float q32 = __uint_as_float(e & 1 ? ws[e >> 1] & 0xFFFF0000u : ws[e >> 1] << 16);
-            const float a = (q32 + Cq[ht]) - Cq[ht];
             qv[e] = (_Float16)q32;
-            av[e] = (_Float16)a;
-            bv[e] = (_Float16)(q32 - a);   // exact: the low bits of q
+            av[e] = (_Float16)((q32 + C) - C);
         }
-        qf_s[(ht * KS + t) * CSA2_WAVE + lane] = qv;
-        qa_s[(ht * KS + t) * CSA2_WAVE + lane] = av;
-        qa_s[((HT + ht) * KS + t) * CSA2_WAVE + lane] = bv;
+        qf_s[P * CSA2_WAVE + lane] = qv;
+        qa_s[P * CSA2_WAVE + lane] = av;
     }
     const int p = grp >> 1;
     // The row's SWA rows through a buffer (reads outside it return zeros);
@@ -582,7 +587,7 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
     auto load_frag = [&](FragRaw<D>& f, int fr_, int j) {
         const int slot = fr_ * kFrag + col, i = slot - Kp;
         const bool vm = slot < K && j >= 0 && j < nb;
-        CSA2_DCHECK(hg == 0 && c == 0 && slot < K && j != -1 && !vm);
+        CSA2_DCHECK(hg == 0 && slot < K && j != -1 && !vm);
         const bool vs = i >= 0 && i < nsw;
         const int iw = PG ? (head + i >= W ? head + i - W : head + i) : i;
         if (frag_kind(fr_, Kp) == 0)
@@ -590,97 +595,116 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
         else
             f.load_swa(vs, iw, p, hf, rw);
     };
-    FragRaw<D> cur, nxt;   // cur is unpaired in place at the start of its fragment
-    if (fr < f_end) load_frag(cur, fr, idx_c);
+    FragRaw<D> cur, nxt;   // cur is unpaired in place at the start of its round
+    if (fw < f_end) load_frag(cur, fw, idx_c);
 
-    __syncthreads();
+    __syncthreads();   // the query is staged
     f16x8 qf[HT][KS];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
             qf[ht][t] = qf_s[(ht * KS + t) * CSA2_WAVE + lane];
-            asm volatile("" : "+a"(qf[ht][t]));
         }
+    __syncthreads();   // every wave holds the query: its staging space becomes the V tiles
 
-    // Online softmax state (log2 domain), per head in the S^T layout (lane
-    // col = head).  The reference max of a head is raised only when a
-    // fragment's max exceeds it by more than kLazy, so the accumulated output
-    // is rarely rescaled; probabilities stay <= 2^kLazy.
-    // l_p: sum of the probabilities as PV weights them (normalises the
-    // output); l_e: sum of the unrounded probabilities (for lse).  Both are
-    // per-lane partial sums over the lane's keys.
-    float m_p[HT], l_p[HT], l_e[HT];
+    // Softmax state (log2 domain), per head in the S^T layout (lane col =
+    // head).  m_run, the reference maximum, is the same in every wave.  l_p:
+    // sum of the probabilities as PV weights them (normalises the output);
+    // l_e: sum of the unrounded probabilities (for lse).  Both are per-lane
+    // partial sums over the keys of the fragments this wave scored.
+    float m_run[HT], l_p[HT], l_e[HT];
     f32x4 o[HT][NDT];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-        m_p[ht] = -INFINITY;
+        m_run[ht] = -INFINITY;
         l_p[ht] = 0.0f;
         l_e[ht] = 0.0f;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) o[ht][dt] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
     }
-    _Float16* const vrow = vt + col * VS - c * SM::DP;   // indexed by the key's channel
+    _Float16* const vrow = vtiles + wave * SM::kTile + col * VS;   // the lane's key row of the wave's tile
     const f16x8* const qa_lane = qa_s + lane;
+    // the lane's PV operand address in slot 0's tile, at the wave's first channel
+    const _Float16* const vr0 = vtiles + (4 * grp + (col >> 2)) * VS + 4 * (col & 3) + wave * SM::CW;
 
-    // Register classes: the query pieces (MFMA B operands) and the output
-    // accumulators stay in the matrix-core registers (AGPRs) for the whole
-    // loop, leaving the VGPRs to the raw bytes and the dequantisation.  The
-    // empty asm statements only name that class for the compiler.
-    for (; fr < f_end; fr += kWaves) {
+    // Registers: this file is compiled with the matrix-core operands and
+    // accumulators in ordinary VGPRs (-amdgpu-mfma-vgpr-form), so that the
+    // query (64 registers at HT * D = 512), the output and the fragment bytes
+    // share one budget of 256 per wave, two waves per SIMD.
+    for (int f0 = f_begin; f0 < f_end; f0 += kWaves) {
+        const int fr = f0 + wave;
+        const bool has = fr < f_end;                               // uniform in the wave
+        const int nslot = f_end - f0 < kWaves ? f_end - f0 : kWaves;   // uniform in the workgroup
+        // ---- the wave's fragment: scores, V tile, per-head maximum.
         // Large values (|v| > 8) make the output sensitive to logit rounding:
         // a logit error e moves the output by about e * |v - out|.  Such a
         // fragment gets exact scores and two-part probabilities.
-        const int kind = frag_kind(fr, Kp);
-        const bool precise = __ballot(kind == 0 ? cur.template big<0>() : cur.template big<1>()) != 0ull;
-        if (kind == 0) cur.template unpair<0>();
-        else cur.template unpair<1>();
-        const uint64_t vb = __ballot(cur.valid);   // bit k: key k of the fragment (lanes 0..15)
-        // prefetch: raw bytes of the wave's next fragment, Top-K entry of the one after
-        {
-            const int f1 = fr + kWaves;
-            if (f1 < f_end) {
-                load_frag(nxt, f1, idx_n);
-                if (f1 + kWaves < f_end) load_idx(f1 + kWaves, idx_n);
-            }
-        }
-
         f32x4 sh[HT], sl[HT];
+        float x[HT][4];
+        bool precise = false;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
             sh[ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
             sl[ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[ht][i] = -INFINITY;
         }
-        if (precise) s_frag_exact<HT, D, CS>(cur, qa_lane, upper, vrow, grp, c, sh, sl);
-        else if (kind == 0) s_frag<0, HT, D, CS>(cur, qf, vrow, grp, c, sh);
-        else s_frag<1, HT, D, CS>(cur, qf, vrow, grp, c, sh);
+        if (has) {
+            const int kind = frag_kind(fr, Kp);
+            precise = __ballot(kind == 0 ? cur.template big<0>() : cur.template big<1>()) != 0ull;
+            if (kind == 0) cur.template unpair<0>();
+            else cur.template unpair<1>();
+            const uint64_t vb = __ballot(cur.valid);   // bit k: key k of the fragment (lanes 0..15)
+            // prefetch: raw bytes of the wave's next fragment, Top-K entry of the one after
+            {
+                const int f1 = fr + kWaves;
+                if (f1 < f_end) {
+                    load_frag(nxt, f1, idx_n);
+                    if (f1 + kWaves < f_end) load_idx(f1 + kWaves, idx_n);
+                }
+            }
+            if (precise) s_frag_exact<HT, D>(cur, qa_lane, qf, upper, vrow, grp, sh, sl);
+            else if (kind == 0) s_frag<0, HT, D>(cur, qf, vrow, grp, sh);
+            else s_frag<1, HT, D>(cur, qf, vrow, grp, sh);
+            // S^T lane layout: head h0 + 16 ht + col, keys 4 grp + i.
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if ((vb >> (4 * grp + i)) & 1ull) x[ht][i] = (sh[ht][i] + sl[ht][i]) * scale_log2e;
+        }
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            float mx = fmaxf(fmaxf(x[ht][0], x[ht][1]), fmaxf(x[ht][2], x[ht][3]));
+            mx = max_xor32(max_xor16(mx));
+            if (grp == 0) reinterpret_cast<float*>(fmx[ht * 16 + col])[wave] = mx;
+        }
+        if (lane == 0) fprec[wave] = precise ? 1 : 0;
+        __syncthreads();   // the round's V tiles, maxima and flags
 
-        // S^T lane layout: head h0 + 16 ht + col, keys 4 grp + i.
+        // ---- reference maximum of each head (the same in every wave): raised
+        // to the round's maximum when that exceeds it by more than kLazy (a
+        // head without any key so far has l = 0 and o = 0: nothing to
+        // rescale).  Then the wave's own probabilities.
         // Probabilities enter PV as fp16, whose rounding (relative 2^-12)
         // moves the output by up to 2^-12 * |v - out|; in a precise fragment
         // they are split into fp16 hi + lo parts and PV runs twice (rounding
         // ~2^-23).
-        f16x4 pa[HT], pl[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-            float x[4];
-            float mx = -INFINITY;
+            float rm = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool kv = (vb >> (4 * grp + i)) & 1ull;
-                x[i] = kv ? (sh[ht][i] + sl[ht][i]) * scale_log2e : -INFINITY;
-                mx = fmaxf(mx, x[i]);
+            for (int w4 = 0; w4 < kWaves / 4; ++w4) {
+                const float4 v = fmx[ht * 16 + col][w4];
+                rm = fmaxf(rm, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
             }
-            mx = max_xor32(max_xor16(mx));
-            // Raise the head's reference when the fragment's max exceeds it by
-            // more than kLazy (a head without any key so far has l = 0 and
-            // o = 0: nothing to rescale).
-            const bool raise = mx > m_p[ht] + kLazy;
+            const bool raise = rm > m_run[ht] + kLazy;
             if (__ballot(raise) != 0ull) {
-                const float al = (raise && m_p[ht] != -INFINITY) ? __builtin_amdgcn_exp2f(m_p[ht] - mx) : 1.0f;
+                const float al = (raise && m_run[ht] != -INFINITY) ? __builtin_amdgcn_exp2f(m_run[ht] - rm) : 1.0f;
                 l_p[ht] *= al;
                 l_e[ht] *= al;
-                if (raise) m_p[ht] = mx;
+                if (raise) m_run[ht] = rm;
                 // O lane layout: channel 16 dt + col, heads 4 grp + i; the
                 // factor of head 4 grp + i sits in lane 4 grp + i.
                 float ai[4];
@@ -692,132 +716,100 @@ __global__ __launch_bounds__(256, 1) void k_sparse_attn(
                 }
                 if (__ballot(rescale) != 0ull) {
 #pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) {
-                        asm volatile("" : "+a"(o[ht][dt]));   // copies out of the AGPRs happen only here
+                    for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) o[ht][dt][i] *= ai[i];
-                        asm volatile("" : "+a"(o[ht][dt]));
-                    }
                 }
             }
-            const float mn = m_p[ht];
-            float ps = 0.0f, pe = 0.0f;
+            if (has) {
+                const float mn = m_run[ht];
+                float ps = 0.0f, pe = 0.0f;
+                f16x4 pa, pl;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                // the exponent's argument is formed with one rounding at its own
-                // (small) magnitude; the reference itself only has to be consistent
-                const float d = fmaf(sh[ht][i], scale_log2e, -mn) + sl[ht][i] * scale_log2e;
-                const float pf = x[i] != -INFINITY ? __builtin_amdgcn_exp2f(d) : 0.0f;
-                const _Float16 ph = (_Float16)pf;
-                pa[ht][i] = ph;
-                pl[ht][i] = (_Float16)(pf - (float)ph);
-                ps += precise ? pf : (float)ph;   // normalise by what PV actually weights
-                pe += pf;
+                for (int i = 0; i < 4; ++i) {
+                    // the exponent's argument is formed with one rounding at its own
+                    // (small) magnitude; the reference itself only has to be consistent
+                    const float d = fmaf(sh[ht][i], scale_log2e, -mn) + sl[ht][i] * scale_log2e;
+                    const float pf = x[ht][i] != -INFINITY ? __builtin_amdgcn_exp2f(d) : 0.0f;
+                    const _Float16 ph = (_Float16)pf;
+                    pa[i] = ph;
+                    pl[i] = (_Float16)(pf - (float)ph);
+                    ps += precise ? pf : (float)ph;   // normalise by what PV actually weights
+                    pe += pf;
+                }
+                l_p[ht] += ps;
+                l_e[ht] += pe;
+                p_s[((wave * 2 + 0) * HT + ht) * CSA2_WAVE + lane] = pa;
+                if (precise) p_s[((wave * 2 + 1) * HT + ht) * CSA2_WAVE + lane] = pl;
             }
-            l_p[ht] += ps;
-            l_e[ht] += pe;
         }
-        pv_frag<HT, NDT, VS>(pa, vt, col, grp, o);
-        if (precise) pv_frag<HT, NDT, VS>(pl, vt, col, grp, o);
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(o[ht][dt]));
-#pragma unroll
-            for (int t = 0; t < KS; ++t) asm volatile("" : "+a"(qf[ht][t]));
+        __syncthreads();   // the round's probabilities
+
+        // ---- PV: the probabilities of every slot into the wave's channels
+        // (then the low parts of precise slots).
+        for (int j0 = 0; j0 < nslot; j0 += kPvGroup) {
+            if (j0 + kPvGroup <= nslot)
+                pv_slots<kPvGroup, HT, NDT>(p_s + (j0 * 2 * HT) * CSA2_WAVE + lane, 2 * HT * CSA2_WAVE,
+                                            vr0 + j0 * SM::kTile, SM::kTile, o);
+            else
+                for (int j = j0; j < nslot; ++j)
+                    pv_slots<1, HT, NDT>(p_s + (j * 2 * HT) * CSA2_WAVE + lane, 0, vr0 + j * SM::kTile, 0, o);
+        }
+        for (int j = 0; j < nslot; ++j) {
+            if (fprec[j]) {
+                pv_slots<1, HT, NDT>(p_s + ((j * 2 + 1) * HT) * CSA2_WAVE + lane, 0, vr0 + j * SM::kTile, 0, o);
+            }
         }
         cur = nxt;
+        __syncthreads();   // the round's tiles and probabilities are consumed
     }
 
-    // ---- merge the four waves.  Per-head statistics first.
+    // ---- the end: per-head sums over the waves; each wave writes its
+    // channels (normalised when the row is not split, else as this split's
+    // partial output with its statistics).
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const float lt = sum_xor32(sum_xor16(l_p[ht])), le = sum_xor32(sum_xor16(l_e[ht]));
         if (grp == 0) {
-            wm[wave][ht * 16 + col] = m_p[ht];
-            wl[wave][ht * 16 + col] = lt;
-            wle[wave][ht * 16 + col] = le;
+            wsum[0][wave][ht * 16 + col] = lt;
+            wsum[1][wave][ht * 16 + col] = le;
         }
     }
-    __syncthreads();   // statistics visible; every wave is done with its V tile and qa
-    // Per head (S^T layout, lane col = head): the merged max M, the sums and
-    // this wave's weight 2^(m_w - M).  The O layout (lane (col, grp) holds
-    // heads 4 grp + i) takes the weight and 1 / L of head 4 grp + i from lane
-    // 4 grp + i.
-    float own_o[HT][4], inv_o[HT][4];
+    __syncthreads();
+    float inv_o[HT][4];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const int hh = ht * 16 + col;
-        float m4[kWaves], l4[kWaves], e4[kWaves];
+        float L = 0.0f, Le = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            m4[w] = wm[w][hh];
-            l4[w] = wl[w][hh];
-            e4[w] = wle[w][hh];
+            L += wsum[0][w][hh];
+            Le += wsum[1][w][hh];
         }
-        float M = -INFINITY;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-            if (l4[w] > 0.0f) M = fmaxf(M, m4[w]);
-        float L = 0.0f, Le = 0.0f, own = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float f = l4[w] > 0.0f ? exp2f(m4[w] - M) : 0.0f;
-            L += l4[w] * f;
-            Le += e4[w] * f;
-            own = w == wave ? f : own;
-        }
-        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        const float M = m_run[ht];
         const int h = h0 + hh;
-        if (wave == 0 && grp == 0 && c == 0 && h < H) {
+        if (wave == 0 && grp == 0 && h < H) {
             if (S == 1) {
                 if (lse) lse[(int64_t)r * H + h] = L > 0.0f ? M * kLn2 + logf(Le) : -INFINITY;
             } else {
                 *reinterpret_cast<float4*>(part_ml + (((int64_t)r * S + s) * H + h) * 4) = make_float4(M, L, Le, 0.0f);
             }
         }
+        const float inv = S == 1 ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            own_o[ht][i] = __shfl(own, 4 * grp + i, CSA2_WAVE);
-            inv_o[ht][i] = S == 1 ? __shfl(inv, 4 * grp + i, CSA2_WAVE) : 1.0f;
-        }
+        for (int i = 0; i < 4; ++i) inv_o[ht][i] = __shfl(inv, 4 * grp + i, CSA2_WAVE);
     }
-    // Rounds over RT output tiles at a time: every wave stores its weighted
-    // tiles of the round, then wave w sums the four waves' tiles
-    // [w RT/4, (w+1) RT/4) of it and writes them out (normalised when the row
-    // is not split, else as this split's partial output).
-    constexpr int RT = SM::RT;
-    constexpr int QW = RT / kWaves;
     float* const dst = (S == 1 ? out + ((int64_t)r * H + h0) * D : part_o + (((int64_t)r * S + s) * H + h0) * D) +
-                       c * SM::DP;
+                       wave * SM::CW;
 #pragma unroll
-    for (int rd = 0; rd < NDT / RT; ++rd) {
-        if (rd > 0) __syncthreads();   // the previous round's tiles are read
+    for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int k = 0; k < RT; ++k) {
-                f32x4 v = o[ht][rd * RT + k];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] *= own_o[ht][i];
-                xo[((wave * HT + ht) * RT + k) * CSA2_WAVE + lane] = v;
+            for (int i = 0; i < 4; ++i) {
+                const int hh = ht * 16 + 4 * grp + i;
+                if (h0 + hh < H) dst[(int64_t)hh * D + 16 * dt + col] = o[ht][dt][i] * inv_o[ht][i];
             }
-        __syncthreads();
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-            for (int k = 0; k < QW; ++k) {
-                const int tk = wave * QW + k;   // tile rd * RT + tk of the output
-                f32x4 acc = xo[((0 * HT + ht) * RT + tk) * CSA2_WAVE + lane];
-#pragma unroll
-                for (int w = 1; w < kWaves; ++w) acc += xo[((w * HT + ht) * RT + tk) * CSA2_WAVE + lane];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int hh = ht * 16 + 4 * grp + i;
-                    if (h0 + hh < H) dst[(int64_t)hh * D + 16 * (rd * RT + tk) + col] = acc[i] * inv_o[ht][i];
-                }
-            }
-    }
 }
 
 // Merge of split partials: o = sum_s O_s 2^(m_s - M) / sum_s l_s 2^(m_s - M),
@@ -864,18 +856,18 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
 }
 
 struct AttnPlan {
-    int HT, HG, CS, S, nfrag;
+    int HT, HG, S, nfrag;
 };
 
-// Workgroup shape: heads per workgroup (16 HT), channel parts CS and key
-// splits S per row.  A workgroup dequantises and stages each of its keys once
-// and computes full scores, whatever its head count and channel part, so:
+// Workgroup shape: heads per workgroup (16 HT) and key splits S per row.  A
+// workgroup dequantises and stages each of its keys once and computes full
+// scores, whatever its head count, so:
 //   * the head count per group is as large as the registers allow (each wave
-//     holds all D query channels and its part of the output of every head:
-//     HT <= 512 / D) while the rows alone give about one workgroup per
-//     compute unit;
+//     holds all D query channels of every head: HT <= 512 / D) while the rows
+//     alone give about one workgroup per compute unit;
 //   * otherwise HT = 1 and a row's keys are split over up to kMaxPlanSplits
-//     workgroups (each split adds a partial output for the merge kernel).
+//     workgroups, keeping at least one fragment per wave (each split adds a
+//     partial output for the merge kernel).
 AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
 {
     constexpr int64_t kTargetGroups = 256;
@@ -887,34 +879,29 @@ AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
     if (ht == 3) ht = 2;
     p.HT = ht;
     p.HG = (H + 16 * ht - 1) / (16 * ht);
-    p.CS = 1;
     if ((int64_t)R * p.HG < kTargetGroups) {
         p.HT = 1;
         p.HG = heads16;
     }
-    const int64_t smax = p.nfrag / kWaves > 1 ? p.nfrag / kWaves : 1;   // at least one fragment per wave
+    const int64_t smax = p.nfrag / kWaves > 1 ? p.nfrag / kWaves : 1;
     const int64_t base = (int64_t)R * p.HG;
     int64_t S = base >= kTargetGroups ? 1 : (kTargetGroups + base - 1) / base;
     if (S > kMaxPlanSplits) S = kMaxPlanSplits;
     if (S > smax) S = smax;
-    // Channel parts repeat the whole score computation, which costs more
-    // than the merge of further key splits at every measured shape (4 to 256
-    // rows, 64 heads, D = 512), so they are not planned; the kernels support
-    // them (CS = 2, and 4 for D = 512).
     p.S = (int)S;
     return p;
 }
 
-template <int HT, int D, int CS, bool PG>
+template <int HT, int D, bool PG>
 void launch_attn(dim3 grid, hipStream_t st, const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
                  const int64_t* seq_start, const int32_t* row_seq, const int32_t* row_len, const int32_t* topk,
                  int32_t K, const uint8_t* swa, const int64_t* swa_row_start, const int32_t* swa_len,
                  const int32_t* swa_head, int64_t phys_rows, int32_t H, int32_t R, int32_t W, float sl2e, int HG,
                  int S, int nfrag, float* out, float* lse, float* po, float* pml)
 {
-    hipLaunchKernelGGL((k_sparse_attn<HT, D, CS, PG>), grid, dim3(64 * kWaves), 0, st, q, codes, scales, seq_start, row_seq,
-                       row_len, topk, K, swa, swa_row_start, swa_len, swa_head, phys_rows, R, H, W, sl2e, HG, S,
-                       nfrag, out, lse, po, pml);
+    hipLaunchKernelGGL((k_sparse_attn<HT, D, PG>), grid, dim3(CSA2_WAVE * kWaves), 0, st, q, codes, scales, seq_start,
+                       row_seq, row_len, topk, K, swa, swa_row_start, swa_len, swa_head, phys_rows, R, H, W, sl2e,
+                       HG, S, nfrag, out, lse, po, pml);
 }
 
 // Cache rows of the entries of index lists over a paged cache: entry j of the
@@ -989,7 +976,7 @@ csa2_status_t sparse_attn_impl(const uint16_t* q, const uint8_t* codes, const ui
     CSA2_REQUIRE((((uintptr_t)q | (uintptr_t)codes | (uintptr_t)scales | (uintptr_t)(W > 0 ? swa : nullptr)) & 15) == 0,
                  CSA2_ERR_UNSUPPORTED, "sparse_attn: q, codes, scales and swa must be 16-byte aligned");
     const AttnPlan p = plan_attn(R, H, D, K, W);
-    CSA2_REQUIRE(xcd_grid(R, (int64_t)p.HG * p.CS * p.S) <= 0x7FFFFFFF, CSA2_ERR_UNSUPPORTED,
+    CSA2_REQUIRE(xcd_grid(R, (int64_t)p.HG * p.S) <= 0x7FFFFFFF, CSA2_ERR_UNSUPPORTED,
                  "sparse_attn: grid too large");
     CSA2_REQUIRE(xcd_grid(R, H) <= 0x7FFFFFFF, CSA2_ERR_UNSUPPORTED, "sparse_attn: grid too large");
     const size_t need = csa2_sparse_attn_workspace_bytes(R, H, D, K, W);
@@ -1006,16 +993,15 @@ csa2_status_t sparse_attn_impl(const uint16_t* q, const uint8_t* codes, const ui
     // With W == 0 or K == 0 the kernels never dereference the unused pointers.
     hipStream_t st = csa2::as_stream(stream);
     const float sl2e = softmax_scale * 1.44269504088896340736f;
-    const dim3 grid((unsigned)xcd_grid(R, p.HG * p.CS * p.S));
-#define CSA2_ATTN(ht, d, cs)                                                                               \
-    if (p.HT == ht && D == d && p.CS == cs) {                                                               \
-        (phys_rows > 0 ? launch_attn<ht, d, cs, true> : launch_attn<ht, d, cs, false>)(grid, st, q, codes, scales, seq_start, row_seq, row_len, topk_idx, K, swa,   \
-                               swa_row_start, swa_len, swa_head, phys_rows, H, R, W, sl2e, p.HG, p.S, p.nfrag, \
-                               out, lse, po, pml);                                                          \
-    }
-    CSA2_ATTN(1, 128, 1) CSA2_ATTN(2, 128, 1) CSA2_ATTN(4, 128, 1) CSA2_ATTN(1, 128, 2)
-    CSA2_ATTN(1, 256, 1) CSA2_ATTN(2, 256, 1) CSA2_ATTN(1, 256, 2)
-    CSA2_ATTN(1, 512, 1) CSA2_ATTN(1, 512, 2) CSA2_ATTN(1, 512, 4)
+    const dim3 grid((unsigned)xcd_grid(R, p.HG * p.S));
+#define CSA2_ATTN(ht, d)                                                                                    \
+    if (p.HT == ht && D == d)                                                                               \
+        (phys_rows > 0 ? launch_attn<ht, d, true> : launch_attn<ht, d, false>)(                             \
+            grid, st, q, codes, scales, seq_start, row_seq, row_len, topk_idx, K, swa, swa_row_start, swa_len, \
+            swa_head, phys_rows, H, R, W, sl2e, p.HG, p.S, p.nfrag, out, lse, po, pml);
+    CSA2_ATTN(1, 128) CSA2_ATTN(2, 128) CSA2_ATTN(4, 128)
+    CSA2_ATTN(1, 256) CSA2_ATTN(2, 256)
+    CSA2_ATTN(1, 512)
 #undef CSA2_ATTN
     if (p.S > 1)
         hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)xcd_grid(R, H)), dim3(128), 0, st, po, pml, R, H, D, p.S,
