@@ -64,7 +64,7 @@ TRAFFIC = {
 }
 CALL_SOURCE = {"sparse_attn": "attn.hip", "index_full": "index.hip", "index_reindex": "index.hip",
                "quantize_append": "quantize.hip"}
-CALL_KERNELS = {"sparse_attn": "k_sparse_attn (+ k_attn_combine when key tiles are split)",
+CALL_KERNELS = {"sparse_attn": "k_sparse_attn (+ k_attn_combine when a row's keys are split more than twice)",
                 "index_full": "k_index_score + k_select (Full)",
                 "index_reindex": "k_index_score + k_select (Reindex)",
                 "quantize_append": "k_quantize_append"}
@@ -242,7 +242,7 @@ def per_call_times(step, reps=10):
     calls["sparse_attn"] = lambda: csa2.csa2_sparse_attn(
         step.q[lu], step.codes, step.scales, step.seq_start, step.row_seq, step.row_len,
         step.topk[step.parents[lu]], step.swa[lu], step.swa_row_start, step.swa_len, step.W, step.scale,
-        out=step.out[lu], lse=step.lse[lu], workspace=step.workspace)
+        out=step.out[lu], lse=step.lse[lu], workspace=step.attn_workspace)
     for name, fn in calls.items():
         g = graph_of(fn, reps=reps)
         time_graph(g, 2, reps)
@@ -271,7 +271,7 @@ def paged_call_times(step, reps=10):
     calls["sparse_attn_phys"] = lambda: csa2.csa2_sparse_attn_phys(
         step.q[lu], step.codes, step.scales, step.phys[step.parents[lu]], step.swa[lu], step.swa_row_start,
         step.swa_len, step.W, step.scale, swa_head=step.swa_head, out=step.out[lu], lse=step.lse[lu],
-        workspace=step.workspace)
+        workspace=step.attn_workspace)
     out = {}
     for name, fn in calls.items():
         g = graph_of(fn, reps=reps)

@@ -209,6 +209,13 @@ csa2_status_t csa2_index_reindex_noalloc(const uint8_t* qI, const float* w, cons
  *   out      [R, H, D] float32;  lse [R, H] float32 (may be NULL).
  *   workspace: csa2_sparse_attn_workspace_bytes(R, H, D, K, W) bytes,
  *            256-byte aligned (may be 0 bytes and NULL when that is 0).
+ *            Its first 1 KiB holds arrival words of the merge of a row's key
+ *            splits: they must be zero before the first call, and every
+ *            call leaves them zero again, so a workspace is zero-filled once
+ *            and then reused by attention calls (the index calls' workspaces
+ *            carry no such state; one they used must be zeroed again).  Other
+ *            contents give wrong outputs (debug builds report
+ *            CSA2_ERR_DEVICE_CHECK).
  * Arithmetic: dequantised keys are exact in fp16; logits accumulate in fp32,
  * and are exact (then rounded once) for key tiles whose scales or FP8 bytes
  * allow |value| > 8; softmax in fp32; probabilities enter the PV product

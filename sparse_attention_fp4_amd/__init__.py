@@ -143,11 +143,11 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor], zeroed: bool = False) -> Optional[torch.Tensor]:
     if nbytes == 0:
         return ws
     if ws is None:
-        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return (torch.zeros if zeroed else torch.empty)(nbytes, dtype=torch.uint8, device=device)
     if ws.numel() * ws.element_size() < nbytes:
         raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, needs {nbytes}")
     if not ws.is_contiguous() or ws.device != device:
@@ -320,7 +320,7 @@ def csa2_sparse_attn(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
         out = torch.empty(R, H, D, dtype=torch.float32, device=dev)
     if want_lse and lse is None:
         lse = torch.empty(R, H, dtype=torch.float32, device=dev)
-    ws = _workspace(csa2_sparse_attn_workspace_bytes(R, H, D, K, W), dev, workspace)
+    ws = _workspace(csa2_sparse_attn_workspace_bytes(R, H, D, K, W), dev, workspace, zeroed=True)
     st = lib().csa2_sparse_attn(_ptr(q), _ptr(codes), _ptr(scales), _ptr(seq_start), _ptr(row_seq),
                                 _ptr(row_len), _ptr(topk_idx), K, _ptr(swa if W > 0 else None),
                                 _ptr(swa_row_start if W > 0 else None), _ptr(swa_len if W > 0 else None),
@@ -471,7 +471,7 @@ def csa2_sparse_attn_phys(q: torch.Tensor, codes: torch.Tensor, scales: torch.Te
         out = torch.empty(R, H, D, dtype=torch.float32, device=dev)
     if want_lse and lse is None:
         lse = torch.empty(R, H, dtype=torch.float32, device=dev)
-    ws = _workspace(csa2_sparse_attn_workspace_bytes(R, H, D, K, W), dev, workspace)
+    ws = _workspace(csa2_sparse_attn_workspace_bytes(R, H, D, K, W), dev, workspace, zeroed=True)
     st = lib().csa2_sparse_attn_phys(_ptr(q), _ptr(codes), _ptr(scales), codes.shape[0], _ptr(phys_idx), K,
                                      _ptr(swa if W > 0 else None), _ptr(swa_row_start if W > 0 else None),
                                      _ptr(swa_len if W > 0 else None), _ptr(swa_head if W > 0 else None), R, H,

@@ -30,7 +30,9 @@
 // only its channels (two waves fit one SIMD and hide each other's latency),
 // and the end needs no merge of outputs between waves.  Rows whose fragments
 // are split across workgroups write unnormalised partial outputs plus (max,
-// sums); k_attn_combine merges them.
+// sums): with two splits the second workgroup of the pair to finish merges
+// the first's partial into its own output; with more, k_attn_combine merges
+// them.
 //
 // Exact scores for keys with large values.  The matrix cores sum products
 // with errors of a few units in the last place of the largest addend, and
@@ -387,8 +389,7 @@ __device__ __forceinline__ void pv_slots(const f16x4* pp, int pstride, const _Fl
 // Workgroups are handed to the 8 XCDs of the chip round-robin by linear id,
 // and each XCD has its own L2.  All G workgroups of a row are placed on one
 // XCD (row r on XCD r % 8, at consecutive slots there), so the head groups and
-// key splits of a row share its key bytes in one L2, where the merge kernel
-// finds the row's partial outputs.
+// key splits of a row share its key bytes in one L2.
 constexpr int kXcds = 8;
 __host__ __device__ inline int64_t xcd_grid(int64_t R, int64_t G) { return (R + kXcds - 1) / kXcds * kXcds * G; }
 // workgroup id -> (row, index g < G within the row)
@@ -398,6 +399,20 @@ __device__ __forceinline__ int xcd_slot(unsigned id, int G, int& r)
     r = slot / G * kXcds + xcd;
     return slot % G;
 }
+
+// Relaxed device-scope store: written through to the device's coherence point,
+// so that a workgroup on any XCD reads it with a device-scope load once the
+// store has completed.
+__device__ __forceinline__ void store_coherent(float* p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Rows with exactly two key splits have fewer than 256 (row, head group)
+// pairs (the plan splits only below 256 groups): the arrival words of the
+// pair merge fit in the first 1 KiB of the workspace.
+constexpr int kPairWords = 256;
+// Bound of a wait that always ends; running into it is counted as a device check.
+constexpr int kSpinLimit = 1 << 22;
 
 // Slot layout of a row: the Top-K slots padded to Kp = a multiple of 16, then
 // the SWA rows, so that a fragment holds one kind of slot only.
@@ -435,7 +450,7 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
     const uint8_t* __restrict__ swa, const int64_t* __restrict__ swa_row_start,
     const int32_t* __restrict__ swa_len, const int32_t* __restrict__ swa_head, int64_t phys_rows, int32_t R,
     int32_t H, int32_t W, float scale_log2e, int32_t HG, int32_t S, int32_t nfrag, float* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml)
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml, int32_t* __restrict__ pair_sync)
 {
     using SM = AttnSmem<HT, D>;
     constexpr int KS = SM::KS;
@@ -776,30 +791,119 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
         }
     }
     __syncthreads();
+    float Lh[HT], Leh[HT], Mh[HT];   // per head (S^T layout): the workgroup's statistics
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        Lh[ht] = 0.0f;
+        Leh[ht] = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            Lh[ht] += wsum[0][w][ht * 16 + col];
+            Leh[ht] += wsum[1][w][ht * 16 + col];
+        }
+        Mh[ht] = m_run[ht];
+    }
+    if (S == 2) {
+        // Two splits: the first of the pair to get here publishes its partial
+        // (device-coherent stores, in this register layout) and leaves; the
+        // second merges it into its own registers and writes the output.  The
+        // arrival word of the (row, head group) counts arrivals (+1) and the
+        // published partial (+4); the second resets it to zero.  The second
+        // waits only for a workgroup that has arrived and waits for nothing,
+        // so the wait ends (it is bounded all the same).
+        __shared__ int second;
+        int32_t* const sync = pair_sync + (r * HG + hg);
+        CSA2_DCHECK(threadIdx.x == 0 && r * HG + hg >= kPairWords);
+        constexpr int NE = HT * NDT * 4;   // output values per lane
+        float* const po = part_o + ((int64_t)r * HG + hg) * (kWaves * CSA2_WAVE * NE) + wave * CSA2_WAVE + lane;
+        float* const pml = part_ml + ((int64_t)r * HG + hg) * (NH * 4);
+        if (threadIdx.x == 0)
+            second = __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 ? 0 : 1;
+        __syncthreads();
+        if (!second) {
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        store_coherent(po + ((ht * NDT + dt) * 4 + i) * (kWaves * CSA2_WAVE), o[ht][dt][i]);
+                if (wave == 0 && grp == 0) {
+                    float* const ml = pml + (ht * 16 + col) * 4;
+                    store_coherent(ml + 0, Mh[ht]);
+                    store_coherent(ml + 1, Lh[ht]);
+                    store_coherent(ml + 2, Leh[ht]);
+                }
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's partial is complete
+            __syncthreads();
+            if (threadIdx.x == 0) __hip_atomic_fetch_add(sync, 4, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        if (threadIdx.x == 0) {
+            int n = 0;
+            while ((__hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 4) == 0 && n < kSpinLimit) {
+                __builtin_amdgcn_s_sleep(2);
+                ++n;
+            }
+            CSA2_DCHECK(n >= kSpinLimit);
+            __hip_atomic_store(sync, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        // merge: o = (o_a 2^(m_a - M) + o_b 2^(m_b - M)) / L, per head; each
+        // product is rounded on its own (no contraction into an fma) and the
+        // sum commutes, so the result does not depend on which split arrived
+        // first.
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+#pragma clang fp contract(off)
+            const float* const ml = pml + (ht * 16 + col) * 4;
+            const float Mb = __hip_atomic_load(ml + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float Lb = __hip_atomic_load(ml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float Leb = __hip_atomic_load(ml + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            float M = -INFINITY;
+            if (Lh[ht] > 0.0f) M = Mh[ht];
+            if (Lb > 0.0f) M = fmaxf(M, Mb);
+            const float wa = Lh[ht] > 0.0f ? exp2f(Mh[ht] - M) : 0.0f;
+            const float wb = Lb > 0.0f ? exp2f(Mb - M) : 0.0f;
+            Lh[ht] = Lh[ht] * wa + Lb * wb;
+            Leh[ht] = Leh[ht] * wa + Leb * wb;
+            Mh[ht] = M;
+            float wai[4], wbi[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                wai[i] = __shfl(wa, 4 * grp + i, CSA2_WAVE);
+                wbi[i] = __shfl(wb, 4 * grp + i, CSA2_WAVE);
+            }
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float ob = __hip_atomic_load(po + ((ht * NDT + dt) * 4 + i) * (kWaves * CSA2_WAVE),
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    o[ht][dt][i] = o[ht][dt][i] * wai[i] + ob * wbi[i];
+                }
+        }
+    }
+    const bool whole = S <= 2;   // this workgroup writes the normalised output
     float inv_o[HT][4];
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const int hh = ht * 16 + col;
-        float L = 0.0f, Le = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            L += wsum[0][w][hh];
-            Le += wsum[1][w][hh];
-        }
-        const float M = m_run[ht];
+        const float L = Lh[ht], Le = Leh[ht], M = Mh[ht];
         const int h = h0 + hh;
         if (wave == 0 && grp == 0 && h < H) {
-            if (S == 1) {
+            if (whole) {
                 if (lse) lse[(int64_t)r * H + h] = L > 0.0f ? M * kLn2 + logf(Le) : -INFINITY;
             } else {
                 *reinterpret_cast<float4*>(part_ml + (((int64_t)r * S + s) * H + h) * 4) = make_float4(M, L, Le, 0.0f);
             }
         }
-        const float inv = S == 1 ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f;
+        const float inv = whole ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) inv_o[ht][i] = __shfl(inv, 4 * grp + i, CSA2_WAVE);
     }
-    float* const dst = (S == 1 ? out + ((int64_t)r * H + h0) * D : part_o + (((int64_t)r * S + s) * H + h0) * D) +
+    float* const dst = (whole ? out + ((int64_t)r * H + h0) * D : part_o + (((int64_t)r * S + s) * H + h0) * D) +
                        wave * SM::CW;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
@@ -867,7 +971,7 @@ struct AttnPlan {
 //     alone give about one workgroup per compute unit;
 //   * otherwise HT = 1 and a row's keys are split over up to kMaxPlanSplits
 //     workgroups, keeping at least one fragment per wave (each split adds a
-//     partial output for the merge kernel).
+//     partial output to the merge).
 AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
 {
     constexpr int64_t kTargetGroups = 256;
@@ -885,7 +989,8 @@ AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
     }
     const int64_t smax = p.nfrag / kWaves > 1 ? p.nfrag / kWaves : 1;
     const int64_t base = (int64_t)R * p.HG;
-    int64_t S = base >= kTargetGroups ? 1 : (kTargetGroups + base - 1) / base;
+    // no more workgroups than compute units: each holds a whole one (LDS)
+    int64_t S = base >= kTargetGroups ? 1 : kTargetGroups / base;
     if (S > kMaxPlanSplits) S = kMaxPlanSplits;
     if (S > smax) S = smax;
     p.S = (int)S;
@@ -897,11 +1002,11 @@ void launch_attn(dim3 grid, hipStream_t st, const uint16_t* q, const uint8_t* co
                  const int64_t* seq_start, const int32_t* row_seq, const int32_t* row_len, const int32_t* topk,
                  int32_t K, const uint8_t* swa, const int64_t* swa_row_start, const int32_t* swa_len,
                  const int32_t* swa_head, int64_t phys_rows, int32_t H, int32_t R, int32_t W, float sl2e, int HG,
-                 int S, int nfrag, float* out, float* lse, float* po, float* pml)
+                 int S, int nfrag, float* out, float* lse, float* po, float* pml, int32_t* sync)
 {
     hipLaunchKernelGGL((k_sparse_attn<HT, D, PG>), grid, dim3(CSA2_WAVE * kWaves), 0, st, q, codes, scales, seq_start,
                        row_seq, row_len, topk, K, swa, swa_row_start, swa_len, swa_head, phys_rows, R, H, W, sl2e,
-                       HG, S, nfrag, out, lse, po, pml);
+                       HG, S, nfrag, out, lse, po, pml, sync);
 }
 
 // Cache rows of the entries of index lists over a paged cache: entry j of the
@@ -948,7 +1053,13 @@ extern "C" size_t csa2_sparse_attn_workspace_bytes(int32_t R, int32_t H, int32_t
         return 0;
     const AttnPlan p = plan_attn(R, H, D, K, W);
     if (p.S <= 1) return 0;
-    return csa2::align_up((size_t)R * p.S * H * D * 4, 256) + csa2::align_up((size_t)R * p.S * H * 4 * 4, 256);
+    // the pair-merge arrival words, then the partial outputs and statistics
+    const size_t head = (size_t)kPairWords * 4;
+    if (p.S == 2) {
+        const size_t nh = (size_t)16 * p.HT;
+        return head + csa2::align_up((size_t)R * p.HG * nh * D * 4, 256) + csa2::align_up((size_t)R * p.HG * nh * 16, 256);
+    }
+    return head + csa2::align_up((size_t)R * p.S * H * D * 4, 256) + csa2::align_up((size_t)R * p.S * H * 4 * 4, 256);
 }
 
 namespace {
@@ -985,10 +1096,14 @@ csa2_status_t sparse_attn_impl(const uint16_t* q, const uint8_t* codes, const ui
                  workspace_bytes);
     float* po = nullptr;
     float* pml = nullptr;
+    int32_t* sync = nullptr;
     if (p.S > 1) {
-        po = static_cast<float*>(workspace);
-        pml = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                       csa2::align_up((size_t)R * p.S * H * D * 4, 256));
+        char* w8 = static_cast<char*>(workspace);
+        sync = reinterpret_cast<int32_t*>(w8);
+        w8 += (size_t)kPairWords * 4;
+        po = reinterpret_cast<float*>(w8);
+        const size_t po_bytes = p.S == 2 ? (size_t)R * p.HG * 16 * p.HT * D * 4 : (size_t)R * p.S * H * D * 4;
+        pml = reinterpret_cast<float*>(w8 + csa2::align_up(po_bytes, 256));
     }
     // With W == 0 or K == 0 the kernels never dereference the unused pointers.
     hipStream_t st = csa2::as_stream(stream);
@@ -998,12 +1113,12 @@ csa2_status_t sparse_attn_impl(const uint16_t* q, const uint8_t* codes, const ui
     if (p.HT == ht && D == d)                                                                               \
         (phys_rows > 0 ? launch_attn<ht, d, true> : launch_attn<ht, d, false>)(                             \
             grid, st, q, codes, scales, seq_start, row_seq, row_len, topk_idx, K, swa, swa_row_start, swa_len, \
-            swa_head, phys_rows, H, R, W, sl2e, p.HG, p.S, p.nfrag, out, lse, po, pml);
+            swa_head, phys_rows, H, R, W, sl2e, p.HG, p.S, p.nfrag, out, lse, po, pml, sync);
     CSA2_ATTN(1, 128) CSA2_ATTN(2, 128) CSA2_ATTN(4, 128)
     CSA2_ATTN(1, 256) CSA2_ATTN(2, 256)
     CSA2_ATTN(1, 512)
 #undef CSA2_ATTN
-    if (p.S > 1)
+    if (p.S > 2)
         hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)xcd_grid(R, H)), dim3(128), 0, st, po, pml, R, H, D, p.S,
                            out, lse);
     return CSA2_FINISH(st, "sparse_attn");

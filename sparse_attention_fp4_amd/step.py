@@ -88,9 +88,11 @@ class CSA2Step:
         self.lse = {l: torch.empty(R, H, dtype=torch.float32, device=dev) for l in range(len(self.modes))}
         Hi = int(qI[self.modes.index("F")].shape[1])
         nbytes = max(csa2_index_full_workspace_bytes(R, self.max_len, Hi, self.K, self.P, self.block),
-                     csa2_index_reindex_workspace_bytes(R, Hi, self.K, self.P, self.block),
-                     csa2_sparse_attn_workspace_bytes(R, H, D, self.K, self.W), 256)
+                     csa2_index_reindex_workspace_bytes(R, Hi, self.K, self.P, self.block), 256)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        # the attention calls keep arrival words in theirs: zeroed once, left zero by every call
+        self.attn_workspace = torch.zeros(max(csa2_sparse_attn_workspace_bytes(R, H, D, self.K, self.W), 256),
+                                          dtype=torch.uint8, device=dev)
 
     def run(self, stream=None, layers=None, mark=None) -> None:
         """Enqueue the step.  `mark(label, phase)` (optional) is called right
@@ -135,10 +137,11 @@ class CSA2Step:
             if self.paged:
                 csa2_sparse_attn_phys(self.q[l], self.codes, self.scales, self.phys[self.parents[l]], self.swa[l],
                                       self.swa_row_start, self.swa_len, self.W, self.scale, swa_head=self.swa_head,
-                                      out=self.out[l], lse=self.lse[l], workspace=self.workspace, stream=stream)
+                                      out=self.out[l], lse=self.lse[l], workspace=self.attn_workspace,
+                                      stream=stream)
             else:
                 csa2_sparse_attn(self.q[l], self.codes, self.scales, self.seq_start, self.row_seq, self.row_len,
                                  self.topk[self.parents[l]], self.swa[l], self.swa_row_start, self.swa_len, self.W,
-                                 self.scale, out=self.out[l], lse=self.lse[l], workspace=self.workspace,
+                                 self.scale, out=self.out[l], lse=self.lse[l], workspace=self.attn_workspace,
                                  stream=stream)
             _mark("sparse_attn", "end")

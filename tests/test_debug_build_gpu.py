@@ -120,7 +120,7 @@ def call_attn(L, q, codes, scales, row_len, topk, swa, swa_len, W):
     out = torch.empty(R, H, D, device=DEV)
     lse = torch.empty(R, H, device=DEV)
     nb = L.csa2_sparse_attn_workspace_bytes(R, H, D, K, W)
-    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=DEV)
     st = L.csa2_sparse_attn(p(q), p(codes), p(scales), p(ss), p(rs), p(row_len), p(topk), K, p(swa), p(srs),
                             p(swa_len), R, H, D, W, ctypes.c_float(D ** -0.5), p(out), p(lse), p(ws), ws.numel(),
                             stream())

@@ -335,7 +335,10 @@ def with_cache(wl):
 
 
 @pytest.mark.parametrize("name,lengths,D,H,K,W", [
-    ("d128_h8_k64_w32_single_row_split", [4096], 128, 8, 64, 32),
+    ("d128_h8_k64_w32_single_row", [4096], 128, 8, 64, 32),
+    ("d128_h8_k512_w64_single_row_4_splits", [4096], 128, 8, 512, 64),
+    ("d512_h64_rows24_2_splits", [60 + (977 * i) % 20000 for i in range(24)], 512, 64, 512, 128),
+    ("d512_h64_rows24_2_splits_one_empty", [5] + [3000 + 11 * i for i in range(23)], 512, 64, 512, 128),
     ("d512_h64_student_outliers", [9000, 3000, 20000], 512, 64, 512, 128),
     ("d128_h8_student_outliers_nosplit_rows", [500 + 11 * i for i in range(140)], 128, 8, 64, 32),
     ("d512_h64_k512_w128_split", [9000, 700, 30000], 512, 64, 512, 128),
@@ -374,6 +377,36 @@ def test_sparse_attn_matches_oracle(name, lengths, D, H, K, W):
     ref = oracle_attn_rows(wl, {r: topk[r] for r in range(R)}, 0, list(range(R)), W, scale)
     check_attn(out, np.stack([ref[r][0] for r in range(R)]), lse, np.stack([ref[r][1] for r in range(R)]),
                what=name)
+
+
+def test_sparse_attn_pair_merge_is_deterministic_and_leaves_its_workspace_zero():
+    """Two key splits per row (24 rows x 4 head groups): the second split of a
+    pair merges the first's partial.  Two calls on one workspace give
+    bit-identical outputs, and the workspace's arrival words end at zero."""
+    lengths = [60 + (977 * i) % 20000 for i in range(24)]
+    R, D, H, K, W = len(lengths), 512, 64, 512, 128
+    wl = with_cache(small_workload(lengths, Hi=8, Di=64, D=D, H=H, W=W, layers="F"))
+    rng = np.random.default_rng(5)
+    topk = np.full((R, K), -1, np.int32)
+    for r, n in enumerate(lengths):
+        k = min(K, n)
+        topk[r, :k] = np.sort(rng.choice(n, k, replace=False))
+    topk = torch.tensor(topk, device=DEV)
+    nb = csa2.csa2_sparse_attn_workspace_bytes(R, H, D, K, W)
+    assert nb > 1024
+    ws = torch.zeros(nb, dtype=torch.uint8, device=DEV)
+    outs = []
+    for _ in range(2):
+        out, lse = csa2.csa2_sparse_attn(wl.q[0], wl.codes_dev, wl.scales_dev, wl.seq_start, wl.row_seq,
+                                         wl.row_len, topk, wl.swa[0], wl.swa_row_start, wl.swa_len, W,
+                                         1.0 / math.sqrt(D), workspace=ws)
+        torch.cuda.synchronize()
+        outs.append((out.clone(), lse.clone()))
+        assert int(ws[:1024].count_nonzero()) == 0
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    ref = oracle_attn_rows(wl, {r: np_(topk)[r] for r in (0, 17, 23)}, 0, [0, 17, 23], W, 1.0 / math.sqrt(D))
+    check_attn(np_(outs[0][0])[[0, 17, 23]], np.stack([ref[r][0] for r in (0, 17, 23)]),
+               np_(outs[0][1])[[0, 17, 23]], np.stack([ref[r][1] for r in (0, 17, 23)]), what="pair merge rows")
 
 
 def test_sparse_attn_empty_key_set():
