@@ -52,6 +52,23 @@ __device__ __forceinline__ float relu(float x)
     return __int_as_float(max(__float_as_int(x), 0));
 }
 
+// Maximum over the 8 lanes of each 8-lane group (lanes 8g .. 8g+7 of every
+// row), as integer maxima of an order-preserving image of the float bits
+// (negative floats have their magnitude bits flipped), which fold into DPP
+// operands and need no canonicalisation.  Exact: the result is one of the
+// inputs.  NaN inputs are not expected.
+__device__ __forceinline__ float block_max8(float v)
+{
+    int k = __float_as_int(v);
+    k ^= (k >> 31) & 0x7FFFFFFF;
+    constexpr int kLow = (int)0x80000000;   // identity of max (every lane is written anyway)
+    k = max(k, __builtin_amdgcn_update_dpp(kLow, k, 0xB1, 0xF, 0xF, false));    // quad_perm [1,0,3,2]
+    k = max(k, __builtin_amdgcn_update_dpp(kLow, k, 0x4E, 0xF, 0xF, false));    // quad_perm [2,3,0,1]
+    k = max(k, __builtin_amdgcn_update_dpp(kLow, k, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    k ^= (k >> 31) & 0x7FFFFFFF;
+    return __int_as_float(k);
+}
+
 // Paged cache addressing: entry j of sequence s lives in cache row
 // bt[s * max_pages + (j >> shift)] * 2^shift + (j mod 2^shift).  A page id
 // outside the cache (or a page past max_pages) makes the entry not visible.
@@ -215,6 +232,227 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HT * KS <= 
                 if (grp == 0 && j < n) scores[(int64_t)r * ld_scores + j] = sv;
                 if (lead && j < n) bmax[(int64_t)r * ld_bmax + (j >> 3)] = m;
             }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ prefill block maxima (GEMM)
+// A prefill chunk has many query rows of one sequence that see (nearly) the
+// same keys.  A workgroup takes kGemmRows consecutive rows (one per wave) and
+// one range of at most kGemmSplitKeys keys, and stages each 64-key tile in LDS
+// once for all its rows: the keys are read once per kGemmRows rows instead of
+// once per row.  Per 16 keys a wave runs its row's HT x KS MFMAs and the same
+// epilogue as k_index_score, in the same order (so an entry's score is
+// bit-identical to the one k_index_score gives it), but keeps only the
+// 8-entry block maxima: the Full selection needs the entries' own scores only
+// within its candidate blocks, which are rescored afterwards.  A wave whose row
+// belongs to another sequence than the tile's reads its keys directly.
+constexpr int kGemmRows = 8;             // query rows per workgroup, one per wave
+constexpr int kGemmTile = 128;           // keys per staged tile
+static_assert(kGemmTile % 64 == 0, "a tile is groups of four 16-key steps, one per lane group in the block maxima");
+constexpr int kGemmSplitKeys = 16384;    // keys per workgroup, about (whole tiles, ranges of equal size)
+constexpr int32_t kGemmMinRows = 1024;   // Full calls with this many rows take this path
+constexpr int32_t kGemmBatchRows = 2048; // rows per pass (bounds the block-maxima workspace)
+
+template <int HT, int KS, bool PAGED>
+__global__ __launch_bounds__(kGemmRows * CSA2_WAVE) void k_index_bmax(
+    const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ ikeys,
+    const int64_t* __restrict__ seq_start, PageMap pm, const int32_t* __restrict__ row_seq,
+    const int32_t* __restrict__ row_len, int32_t n_cap, int32_t R, int32_t Hi, int32_t Di,
+    float* __restrict__ bmax, int64_t ld_bmax, int32_t split_keys)
+{
+    constexpr int RS = KS * 128 + 16;   // LDS bytes per staged key: 32-byte lane reads of 16 keys hit distinct banks
+    constexpr int CH = KS * 8;          // 16-byte chunks per key
+    constexpr int NST = (kGemmTile * CH + kGemmRows * CSA2_WAVE - 1) / (kGemmRows * CSA2_WAVE);
+    __shared__ __attribute__((aligned(16))) uint8_t kt[2][kGemmTile * RS];
+    __shared__ int s_seq[kGemmRows], s_n[kGemmRows];
+
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int col = lane & 15, grp = lane >> 4;
+    const int r = (int)blockIdx.y * kGemmRows + wave;   // grid: x = key range, y = row tile
+    const bool row_ok = r < R;
+    const int n_raw = row_ok ? row_len[r] : 0;
+    CSA2_DCHECK(blockIdx.x == 0 && lane == 0 && row_ok && (n_raw < 0 || n_raw > n_cap));
+    const int n = n_raw < 0 ? 0 : (n_raw > n_cap ? n_cap : n_raw);   // clamped as k_index_score does
+    const int seq = row_ok ? row_seq[r] : -1;
+    if (lane == 0) {
+        s_seq[wave] = seq;
+        s_n[wave] = n;
+    }
+    // the row's query (A operand: row = head, 32 bytes of the k-step per lane) and weights
+    i32x8 qa[HT][KS];
+    float wv[HT][4];
+#pragma unroll
+    for (int t = 0; t < HT; ++t) {
+        const int h = t * 16 + col;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int d0 = ks * 128 + grp * 32;
+            i32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (row_ok && h < Hi && d0 < Di) {
+                const uint4* p = reinterpret_cast<const uint4*>(qI + ((int64_t)r * Hi + h) * Di + d0);
+                const uint4 a = p[0], b = p[1];
+                v = (i32x8){(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+            }
+            qa[t][ks] = v;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hh = t * 16 + grp * 4 + i;
+            wv[t][i] = row_ok && hh < Hi ? w[(int64_t)r * Hi + hh] : 0.0f;
+        }
+    }
+    __syncthreads();
+    // The staged keys are those of the first row's sequence, up to the
+    // longest of its rows here; the workgroup's range ends at its longest row.
+    const int seq0 = s_seq[0];
+    int n0 = 0, nmax = 0;
+#pragma unroll
+    for (int i = 0; i < kGemmRows; ++i) {
+        nmax = max(nmax, s_n[i]);
+        if (s_seq[i] == seq0) n0 = max(n0, s_n[i]);
+    }
+    const int64_t k_begin64 = (int64_t)blockIdx.x * split_keys;
+    if (k_begin64 >= nmax) return;   // whole workgroup
+    const int k_begin = (int)k_begin64;
+    const int k_end = (int)min((int64_t)nmax, (int64_t)k_begin + split_keys);
+    const int ntiles = (k_end - k_begin + kGemmTile - 1) / kGemmTile;
+    const bool staged = seq == seq0;   // uniform in the wave
+    const uint8_t* const keys0 = PAGED ? ikeys : ikeys + (seq0 >= 0 ? seq_start[seq0] : 0) * (int64_t)Di;
+    const uint8_t* const keys_r = PAGED ? ikeys : ikeys + (seq >= 0 ? seq_start[seq] : 0) * (int64_t)Di;
+    // cache row of entry j of sequence s (-1: not visible)
+    auto key_row = [&](int s, int64_t j) -> int64_t {
+        if constexpr (PAGED) return pm.row_on(pm.page_id(s, j >> pm.shift), j);
+        else return j;
+    };
+
+    // Staging: thread t holds 16-byte chunks t, t + 512, ... of a tile (chunk
+    // e: key e / CH, bytes 16 (e % CH)); zeros past the keys or past Di.
+    uint4 stage[NST];
+    auto fetch = [&](int tile) {
+#pragma unroll
+        for (int u = 0; u < NST; ++u) {
+            const int e = (int)threadIdx.x + u * kGemmRows * CSA2_WAVE;
+            const int key = e / CH, c = e % CH;
+            const int j = k_begin + tile * kGemmTile + key;   // < max_len < 2^31
+            stage[u] = make_uint4(0u, 0u, 0u, 0u);
+            if (e < kGemmTile * CH && j < n0 && c * 16 < Di) {
+                const int64_t row = key_row(seq0, j);
+                if (row >= 0) stage[u] = *reinterpret_cast<const uint4*>(keys0 + row * Di + c * 16);
+            }
+        }
+    };
+    auto put = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < NST; ++u) {
+            const int e = (int)threadIdx.x + u * kGemmRows * CSA2_WAVE;
+            if (e < kGemmTile * CH)
+                *reinterpret_cast<uint4*>(&kt[buf][(e / CH) * RS + (e % CH) * 16]) = stage[u];
+        }
+    };
+    // One 16-key step of the wave's row: scores of keys j0 + col from the B
+    // operands kb, the sum over heads in the order k_index_score uses, and the
+    // maxima of its two 8-entry blocks (by lanes grp 0, col 0 and 8).
+    auto epilogue = [&](const f32x4 (&acc)[HT], int j0) {
+        float part = 0.0f;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part += wv[ht][i] * relu(acc[ht][i]);
+        part = sum_xor32(sum_xor16(part));
+        const int j = j0 + col;
+        bool ok = j < n;
+        if constexpr (PAGED) ok = ok && key_row(seq, j) >= 0;
+        const float m = block_max8(ok ? part : -INFINITY);
+        if (grp == 0 && (col & 7) == 0 && j < n) bmax[(int64_t)r * ld_bmax + (j >> 3)] = m;
+    };
+    auto products = [&](const i32x8 (&kb)[KS], f32x4 (&acc)[HT]) {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            acc[ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                acc[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[ht][ks], kb[ks], acc[ht], 0, 0, 0, 127, 0,
+                                                                          127);
+        }
+    };
+
+    fetch(0);
+    put(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < ntiles) fetch(t + 1);   // in flight during the products
+        const int tile0 = k_begin + t * kGemmTile;
+        if (staged) {
+            // The tile's four 16-key steps; lane (col, grp) sums its 16 heads
+            // of key col of each.  One reduce-scatter over the lane groups
+            // then leaves lane (col, g) with the whole score of key col of
+            // step g, added in the pairs sum_xor16 then sum_xor32 use (the
+            // same value), and the block maxima of all four steps come from
+            // one 8-lane maximum.
+#pragma unroll
+          for (int g4 = 0; g4 < kGemmTile / 64; ++g4) {
+            float ps[4];
+#pragma unroll
+            for (int sub = 0; sub < 4; ++sub) {
+                i32x8 kb[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const uint4* p =
+                        reinterpret_cast<const uint4*>(&kt[buf][((g4 * 4 + sub) * 16 + col) * RS + ks * 128 + grp * 32]);
+                    const uint4 a = p[0], b = p[1];
+                    kb[ks] = (i32x8){(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+                }
+                f32x4 acc[HT];
+                products(kb, acc);
+                float part = 0.0f;
+#pragma unroll
+                for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) part += wv[ht][i] * relu(acc[ht][i]);
+                ps[sub] = part;
+            }
+            // rows 2k, 2k+1: even rows get step 0 (2) summed over the pair,
+            // odd rows step 1 (3); then the halves: row g gets step g
+            const auto a01 = __builtin_amdgcn_permlane16_swap(__float_as_uint(ps[0]), __float_as_uint(ps[1]), false, false);
+            const auto a23 = __builtin_amdgcn_permlane16_swap(__float_as_uint(ps[2]), __float_as_uint(ps[3]), false, false);
+            const float q01 = __uint_as_float(a01[0]) + __uint_as_float(a01[1]);
+            const float q23 = __uint_as_float(a23[0]) + __uint_as_float(a23[1]);
+            const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(q01), __float_as_uint(q23), false, false);
+            const float total = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+            const int j = tile0 + g4 * 64 + grp * 16 + col;
+            bool ok = j < n;
+            if constexpr (PAGED) ok = ok && key_row(seq, j) >= 0;
+            const float m = block_max8(ok ? total : -INFINITY);
+            if ((col & 7) == 0 && j < n) bmax[(int64_t)r * ld_bmax + (j >> 3)] = m;
+          }
+        } else {
+#pragma unroll
+            for (int sub = 0; sub < kGemmTile / 16; ++sub) {
+                const int j = tile0 + sub * 16 + col;
+                const int64_t row = j < n ? key_row(seq, j) : -1;
+                i32x8 kb[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int d0 = ks * 128 + grp * 32;
+                    i32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+                    if (row >= 0 && d0 < Di) {
+                        const uint4* p = reinterpret_cast<const uint4*>(keys_r + row * Di + d0);
+                        const uint4 a = p[0], b = p[1];
+                        v = (i32x8){(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+                    }
+                    kb[ks] = v;
+                }
+                f32x4 acc[HT];
+                products(kb, acc);
+                epilogue(acc, tile0 + sub * 16);
+            }
+        }
+        if (t + 1 < ntiles) {
+            put(buf ^ 1);   // the other buffer's last readers passed the previous barrier
+            __syncthreads();
         }
     }
 }
@@ -821,7 +1059,8 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     int64_t ld_bmax, const int32_t* __restrict__ row_len, int32_t n_cap, const int32_t* __restrict__ pool_in,
     int32_t K, int32_t P, int32_t* __restrict__ topk, int32_t* __restrict__ pool_out,
     const uint32_t* __restrict__ gkey_g, const int32_t* __restrict__ gid_g, const int32_t* __restrict__ gcount,
-    int32_t nslices, const int32_t* __restrict__ row_seq, PageMap pm, int32_t* __restrict__ rows_out)
+    int32_t nslices, const int32_t* __restrict__ row_seq, PageMap pm, int32_t* __restrict__ rows_out,
+    int32_t* __restrict__ cand_out)
 {
     __shared__ typename std::conditional<FULL, SelectLdsFull, SelectLds>::type L;
     const int r = blockIdx.x;
@@ -957,6 +1196,13 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
                     for (int i = threadIdx.x; i < na; i += kSelThreads) po[i] = L.blocks[i];
                 for (int i = nsm + threadIdx.x; i < P; i += kSelThreads) po[i] = -1;
             }
+        }
+        // Blocks only (the entries' scores are not at hand): the candidate
+        // blocks, ascending, -1 padded to K, for rescoring.
+        if (cand_out) {
+            int32_t* co = cand_out + (int64_t)r * K;
+            for (int i = threadIdx.x; i < K; i += kSelThreads) co[i] = i < ncb ? cand[i] : -1;
+            return;   // uniform in the workgroup
         }
     } else {
         // Items are the pool slots in block-id order: the pool as given when
@@ -1134,9 +1380,15 @@ csa2_status_t check_indexer_dims(const char* who, int32_t R, int32_t Hi, int32_t
 extern "C" size_t csa2_index_full_workspace_bytes(int32_t R, int32_t max_len, int32_t Hi, int32_t K, int32_t P,
                                                   int32_t block)
 {
-    (void)Hi; (void)K; (void)P; (void)block;
+    (void)Hi; (void)P; (void)block;
     if (R < 0 || max_len < 0) return 0;
     const int64_t ld = full_ld(max_len);
+    if (R >= kGemmMinRows && K >= 1 && K <= kMaxK) {
+        // per batch of rows: the block maxima, the candidate blocks and their entries' scores
+        const size_t rb = R < kGemmBatchRows ? (size_t)R : (size_t)kGemmBatchRows;
+        return csa2::align_up(rb * (ld / 8) * 4, 256) + csa2::align_up(rb * K * 4, 256) +
+               csa2::align_up(rb * reindex_ld(K) * 4, 256);
+    }
     size_t b = csa2::align_up((size_t)R * ld * 4, 256) + csa2::align_up((size_t)R * (ld / 8) * 4, 256);
     if (full_prefilter(ld) && R < kPrefilterRows)
         b += 2 * csa2::align_up((size_t)R * (ld / 8) * 4, 256) + csa2::align_up((size_t)R * full_slices(ld) * 4, 256);
@@ -1144,6 +1396,81 @@ extern "C" size_t csa2_index_full_workspace_bytes(int32_t R, int32_t max_len, in
 }
 
 namespace {
+template <bool PAGED>
+void launch_bmax(int HT, int KS, dim3 grid, hipStream_t st, const uint8_t* qI, const float* w, const uint8_t* ikeys,
+                 const int64_t* seq_start, const PageMap& pm, const int32_t* row_seq, const int32_t* row_len,
+                 int32_t n_cap, int32_t R, int32_t Hi, int32_t Di, float* bm, int64_t ldb, int32_t split_keys)
+{
+#define CSA2_BMAX(ht, ks)                                                                                   \
+    if (HT == ht && KS == ks) {                                                                             \
+        hipLaunchKernelGGL((k_index_bmax<ht, ks, PAGED>), grid, dim3(kGemmRows * CSA2_WAVE), 0, st, qI, w, ikeys, \
+                           seq_start, pm, row_seq, row_len, n_cap, R, Hi, Di, bm, ldb, split_keys);       \
+        return;                                                                                             \
+    }
+    CSA2_BMAX(1, 1) CSA2_BMAX(2, 1) CSA2_BMAX(3, 1) CSA2_BMAX(4, 1)
+    CSA2_BMAX(1, 2) CSA2_BMAX(2, 2) CSA2_BMAX(3, 2) CSA2_BMAX(4, 2)
+#undef CSA2_BMAX
+}
+
+// Full mode for many rows (a prefill chunk), in batches of kGemmBatchRows:
+// block maxima by the GEMM kernel (key tiles shared by a workgroup's rows),
+// the pool and the top-K candidate blocks from them (every Top-K entry lies
+// in one of those blocks, see k_select), then the candidate blocks' entries
+// rescored and the Top-K taken among them, as Reindex does for its pool.  No
+// score of every entry is ever stored.  Arguments are validated by the caller.
+csa2_status_t index_full_gemm(const uint8_t* qI, const float* w, const uint8_t* ikeys, const int64_t* seq_start,
+                              const PageMap* pmp, const int32_t* row_seq, const int32_t* row_len, int32_t R,
+                              int32_t Hi, int32_t Di, int32_t max_len, int32_t K, int32_t P, int32_t* topk_idx,
+                              int32_t* topk_rows, int32_t* pool_blocks, void* workspace, void* stream)
+{
+    const int64_t ld = full_ld(max_len);
+    const int32_t rb = R < kGemmBatchRows ? R : kGemmBatchRows;
+    char* w8 = static_cast<char*>(workspace);
+    float* bm = reinterpret_cast<float*>(w8);
+    w8 += csa2::align_up((size_t)rb * (ld / 8) * 4, 256);
+    int32_t* cand = reinterpret_cast<int32_t*>(w8);
+    w8 += csa2::align_up((size_t)rb * K * 4, 256);
+    float* resc = reinterpret_cast<float*>(w8);
+    const int64_t rld = reindex_ld(K);
+    const int chunk = reindex_chunk(rb, rld);
+    hipStream_t st = csa2::as_stream(stream);
+    const int HT = (Hi + 15) / 16, KS = (Di + 127) / 128;
+    const PageMap pm = pmp ? *pmp : PageMap{nullptr, 0, 0, 0};
+    // key ranges of about kGemmSplitKeys, all of one size in whole tiles (the
+    // grid then comes to whole multiples of the row tiles, without a short last range)
+    int64_t nsplit = max_len / kGemmSplitKeys;
+    nsplit = nsplit < 1 ? (max_len > 0 ? 1 : 0) : nsplit;
+    const int64_t tiles = ((int64_t)max_len + kGemmTile - 1) / kGemmTile;
+    const int32_t split_keys = nsplit > 0 ? (int32_t)((tiles + nsplit - 1) / nsplit * kGemmTile) : 0;
+    if (nsplit > 0) nsplit = (max_len + split_keys - 1) / split_keys;
+    for (int32_t b0 = 0; b0 < R; b0 += rb) {
+        const int32_t nr = R - b0 < rb ? R - b0 : rb;
+        const uint8_t* q_b = qI + (int64_t)b0 * Hi * Di;
+        const float* w_b = w + (int64_t)b0 * Hi;
+        if (nsplit > 0) {
+            const dim3 grid((unsigned)nsplit, (unsigned)((nr + kGemmRows - 1) / kGemmRows));
+            if (pmp)
+                launch_bmax<true>(HT, KS, grid, st, q_b, w_b, ikeys, seq_start, pm, row_seq + b0, row_len + b0, max_len,
+                                  nr, Hi, Di, bm, ld / 8, split_keys);
+            else
+                launch_bmax<false>(HT, KS, grid, st, q_b, w_b, ikeys, seq_start, pm, row_seq + b0, row_len + b0,
+                                   max_len, nr, Hi, Di, bm, ld / 8, split_keys);
+        }
+        hipLaunchKernelGGL(k_select<true>, dim3((unsigned)nr), dim3(kSelThreads), 0, st, nullptr, 0, bm, ld / 8,
+                           row_len + b0, max_len, nullptr, K, P, topk_idx + (int64_t)b0 * K,
+                           pool_blocks ? pool_blocks + (int64_t)b0 * P : nullptr, nullptr, nullptr, nullptr, 0,
+                           row_seq + b0, pm, nullptr, cand);
+        launch_score<true>(pmp != nullptr, HT, KS, dim3((unsigned)(rld / chunk), (unsigned)nr), st, q_b, w_b, ikeys,
+                           seq_start, pm, row_seq + b0, row_len + b0, max_len, cand, Hi, Di, K, resc, rld, nullptr, 0,
+                           chunk);
+        hipLaunchKernelGGL(k_select<false>, dim3((unsigned)nr), dim3(kSelThreads), 0, st, resc, rld, nullptr, 0,
+                           row_len + b0, max_len, cand, K, K, topk_idx + (int64_t)b0 * K, nullptr, nullptr, nullptr,
+                           nullptr, 0, row_seq + b0, pm, pmp && topk_rows ? topk_rows + (int64_t)b0 * K : nullptr,
+                           nullptr);
+    }
+    return CSA2_FINISH(st, "index_full");
+}
+
 csa2_status_t index_full_impl(const uint8_t* qI, const float* w, const uint8_t* ikeys, const int64_t* seq_start,
                               const PageMap* pmp, const int32_t* row_seq, const int32_t* row_len, int32_t R,
                               int32_t Hi, int32_t Di, int32_t max_len, int32_t K, int32_t P, int32_t block,
@@ -1166,6 +1493,9 @@ csa2_status_t index_full_impl(const uint8_t* qI, const float* w, const uint8_t* 
     CSA2_REQUIRE(workspace && workspace_bytes >= need && ((uintptr_t)workspace & 255) == 0,
                  CSA2_ERR_WORKSPACE, "index_full: workspace needs %zu bytes, 256-byte aligned (got %zu)",
                  need, workspace_bytes);
+    if (R >= kGemmMinRows)
+        return index_full_gemm(qI, w, ikeys, seq_start, pmp, row_seq, row_len, R, Hi, Di, max_len, K, P, topk_idx,
+                               topk_rows, pool_blocks, workspace, stream);
     const int64_t ld = full_ld(max_len);
     char* w8 = static_cast<char*>(workspace);
     float* scores = reinterpret_cast<float*>(w8);
@@ -1201,7 +1531,7 @@ csa2_status_t index_full_impl(const uint8_t* qI, const float* w, const uint8_t* 
     }
     hipLaunchKernelGGL(k_select<true>, dim3((unsigned)R), dim3(kSelThreads), 0, st, scores, ld, bm, ld / 8,
                        row_len, max_len, nullptr, K, P, topk_idx, pool_blocks, gkey, gid, gcount, (int32_t)nslices, row_seq, pm,
-                       pmp ? topk_rows : nullptr);
+                       pmp ? topk_rows : nullptr, nullptr);
     return CSA2_FINISH(st, "index_full");
 }
 }  // namespace
@@ -1272,7 +1602,7 @@ csa2_status_t index_reindex_impl(const uint8_t* qI, const float* w, const uint8_
                        pool_blocks, Hi, Di, P, scores, ld, nullptr, 0, chunk);
     hipLaunchKernelGGL(k_select<false>, dim3((unsigned)R), dim3(kSelThreads), 0, st, scores, ld, nullptr, 0,
                        row_len, 0x7FFFFFFF, pool_blocks, K, P, topk_idx, nullptr, nullptr, nullptr, nullptr, 0, row_seq, pm,
-                       pmp ? topk_rows : nullptr);
+                       pmp ? topk_rows : nullptr, nullptr);
     return CSA2_FINISH(st, "index_reindex");
 }
 }  // namespace

@@ -213,11 +213,11 @@ def test_index_scores_sharing_low_bits_below_their_varying_bits():
     assert len(s0) >= K and rt[0].tolist() == s0[:K].tolist()
 
 
-def many_rows(seq_lengths, rows, Hi, Di, seed=21):
+def many_rows(seq_lengths, rows, Hi, Di, seed=21, idx_dist="int3"):
     """A workload of several sequences with `rows` = [(sequence, visible
     entries)] query rows (as in a prefill chunk), each with its own indexer
     query and weights."""
-    wl = small_workload(seq_lengths, Hi=Hi, Di=Di)
+    wl = small_workload(seq_lengths, Hi=Hi, Di=Di, idx_dist=idx_dist)
     g = gen(seed)
     R = len(rows)
     wl.row_seq = torch.tensor([s for s, _ in rows], dtype=torch.int32, device=DEV)
@@ -248,6 +248,47 @@ def test_index_full_many_rows_matches_oracle(case):
     check = [0, 1, 2, 3, 4, 5, 6, 7, 250, 301, len(rows) - 2, len(rows) - 1]
     rt, rp, _ = oracle_index_rows(wl, 0, check, K, P)
     assert np.array_equal(topk[check], rt) and np.array_equal(pool[check], rp)
+
+
+@pytest.mark.parametrize("case", ["one_sequence_two_batches", "mixed_sequences_ties", "hi64_di128", "hi40_di256"])
+def test_index_full_gemm_path_matches_oracle(case):
+    """From 1,024 rows Full mode takes the prefill path: block maxima from the
+    GEMM kernel (each key tile staged once for 8 rows), the pool and the
+    candidate blocks from them, the candidates' entries rescored.  Checked
+    against the oracle on sampled rows (both batches of 2,048 rows, tile and
+    batch edges): one sequence's causal chunk over two key ranges; rows of
+    four sequences interleaved (tiles holding rows of other sequences) with
+    tied scores; the 64 x 128 indexer shape; 40 heads x 256 dims."""
+    log(f"index_full gemm path: {case}")
+    rng = np.random.default_rng(31)
+    K, P, Hi, Di, idx = 64, 100, 16, 64, "int3"
+    if case == "one_sequence_two_batches":
+        seq_lengths = [20000]
+        rows = [(0, 17000 + i + 1) for i in range(2100)]
+    elif case == "mixed_sequences_ties":
+        seq_lengths = [5000, 7777, 300, 18000]
+        rows = [(3, 17000 + i) for i in range(40)]
+        for i in range(1060):
+            s = int(rng.integers(0, 4))
+            rows.append((s, int(rng.integers(0, seq_lengths[s] + 1))))
+        idx = "ties"
+    elif case == "hi64_di128":
+        seq_lengths = [12000]
+        rows = [(0, 10000 + i + 1) for i in range(1030)]
+        K, P, Hi, Di = 512, 2048, 64, 128
+    else:
+        seq_lengths = [9000, 4000]
+        rows = [(i % 5 == 0 and 1 or 0, (4000 if i % 5 == 0 else 8000) - i % 700) for i in range(1100)]
+        K, P, Hi, Di = 300, 500, 40, 256
+    wl = many_rows(seq_lengths, rows, Hi=Hi, Di=Di, idx_dist=idx)
+    topk, pool = gpu_index_full(wl, 0, K, P)
+    R = len(rows)
+    check = sorted({0, 1, 2, 7, 8, 9, 15, 16, R // 2, R - 9, R - 8, R - 1}
+                   | ({2047, 2048, 2049} if R > 2049 else set())
+                   | set(int(x) for x in rng.choice(R, 8, replace=False)))
+    rt, rp, _ = oracle_index_rows(wl, 0, check, K, P)
+    assert np.array_equal(topk[check], rt), f"{case}: top-k differs"
+    assert np.array_equal(pool[check], rp), f"{case}: pool differs"
 
 
 @pytest.mark.parametrize("name,lengths,Hi,Di,K,P,idx", [

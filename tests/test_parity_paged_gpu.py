@@ -218,6 +218,32 @@ def test_index_paged_many_rows_one_sequence():
         assert np.array_equal(topk[r], et) and np.array_equal(pool[r], ep), f"row {r} differs"
 
 
+def test_index_paged_gemm_path_one_sequence():
+    """From 1,024 rows the paged Full call takes the prefill path too (block
+    maxima by the GEMM kernel, staged keys read through the block table),
+    over a cache with an unmapped page."""
+    n_seq = 12000
+    R = 1100
+    wl = small_workload([n_seq])
+    g = torch.Generator(device=DEV)
+    g.manual_seed(19)
+    wl.row_seq = torch.zeros(R, dtype=torch.int32, device=DEV)
+    wl.row_len = torch.arange(n_seq - R + 1, n_seq + 1, dtype=torch.int32, device=DEV)
+    wl.qI[0] = workloads.to_e4m3_bytes(torch.randint(-3, 4, (R, 16, 64), generator=g, device=DEV).float())
+    wl.w[0] = torch.round(torch.rand(R, 16, generator=g, device=DEV) * 16.0) / 16.0
+    pages = Pages([n_seq], 64, seed=5, holes={(0, 11): -1, (0, 150): 10 ** 6})
+    ikeys = paged_ikeys(wl, pages)
+    K, P = 64, 100
+    topk, pool = run_full_paged(wl, pages, ikeys, 0, K, P)
+    scores = oracle.index_scores(np_(wl.qI[0]), np_(wl.w[0]), np_(wl.ikeys), np_(wl.seq_start), np_(wl.row_seq),
+                                 np_(wl.row_len), n_seq)
+    vis = pages.visible(0)
+    for r in [0, 1, 7, 8, 9, 513, R - 9, R - 8, R - 1]:
+        n = int(np_(wl.row_len)[r])
+        et, ep = expected_selection(scores[r, :n], vis[:n], K, P)
+        assert np.array_equal(topk[r], et) and np.array_equal(pool[r], ep), f"row {r} differs"
+
+
 def test_index_paged_unmapped_pages():
     lengths = [20000, 3001, 640]
     pr = 64
