@@ -55,12 +55,15 @@ MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp16": 2500.0}   # dense, MI355X
 # copy), keyed by (workload id, call, hash of the kernel source the counters
 # were taken on).  Reported as null whenever that source has changed since.
 TRAFFIC = {
-    # profiles/sparse_attn_decode_64k.md: k_sparse_attn + k_attn_combine per call
-    (2, "sparse_attn", "dbb3533f8d62e83a"): 32085009,
+    # profiles/sparse_attn_decode_64k.md: k_sparse_attn per call (two key splits merged in the kernel)
+    (2, "sparse_attn", "384e3432d0400376"): 23514000,
     # profiles/index_full_decode_64k.md: k_index_score (Full) + k_select (Full) per call
-    (2, "index_full", "3b324613329f3265"): 284831767,
+    (2, "index_full", "375c39e8797bac98"): 284870000,
     # profiles/index_reindex_decode_64k.md: k_index_score (Reindex) + k_select (Reindex) per call
-    (2, "index_reindex", "3b324613329f3265"): 74539671,
+    (2, "index_reindex", "375c39e8797bac98"): 74488000,
+    # profiles/index_full_prefill_4096x135k.md: k_index_bmax + k_select (blocks) + k_index_score (rescoring)
+    # + k_select (Top-K), twice (two batches of 2,048 rows) per call
+    (4, "index_full", "375c39e8797bac98"): 1918618000,
 }
 CALL_SOURCE = {"sparse_attn": "attn.hip", "index_full": "index.hip", "index_reindex": "index.hip",
                "quantize_append": "quantize.hip"}
@@ -68,6 +71,9 @@ CALL_KERNELS = {"sparse_attn": "k_sparse_attn (+ k_attn_combine when a row's key
                 "index_full": "k_index_score + k_select (Full)",
                 "index_reindex": "k_index_score + k_select (Reindex)",
                 "quantize_append": "k_quantize_append"}
+# csa2_index_full from 1,024 query rows (a prefill chunk), in batches of 2,048 rows
+GEMM_FULL_KERNELS = ("k_index_bmax (block maxima, FP8 GEMM) + k_select (pool and candidate blocks) + "
+                     "k_index_score (candidates rescored) + k_select (Top-K)")
 
 
 def log(msg):
@@ -463,7 +469,8 @@ def measure(cfg, args, flusher, copy_gbps, with_paged=True):
         def roof(call):
             us = breakdown[call]
             tr = TRAFFIC.get((cfg.cid, call, source_hash(CALL_SOURCE[call])))
-            extra = dict(kernel=f"csa2_{call}: {CALL_KERNELS[call]}", us_per_launch=round(us, 2),
+            label = GEMM_FULL_KERNELS if call == "index_full" and R >= 1024 else CALL_KERNELS[call]
+            extra = dict(kernel=f"csa2_{call}: {label}", us_per_launch=round(us, 2),
                          launches_per_step=calls_per_step[call], share_of_warm_step=round(shares[call], 3))
             if prefill and call != "quantize_append":
                 # the chunk's rows share one key set: bound by the matrix cores
