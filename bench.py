@@ -256,6 +256,49 @@ def per_call_times(step, reps=10):
     return out
 
 
+def fp4mma_times(step, reps=10):
+    """csa2_sparse_attn_fp4mma (query-key products on the native FP4 matrix-core
+    product where exact) beside csa2_sparse_attn, both on the last layer's
+    inputs made exact for the native product: every E4M3 scale byte rounded
+    down to its power of two and the two of each 32-channel block made equal,
+    the query rounded to E4M3 under one power-of-two scale per head.  (On such
+    inputs the two calls agree bit for bit: tests/test_fp4mma_gpu.py.)"""
+    import sparse_attention_fp4_amd as csa2
+    lu = len(step.modes) - 1
+    rows = step.scales.shape[0]
+    sc = (step.scales & 0xF8).view(rows, -1, 2)[:, :, :1].expand(-1, -1, 2).reshape(rows, -1).contiguous()
+    q = step.q[lu].float()
+    m = q.abs().amax(dim=-1, keepdim=True).clamp_min(2.0 ** -100)
+    e = ((m.view(torch.int32) >> 23) & 0xFF) - 127 - 7          # 2^e puts the head's largest |q| in [128, 256)
+    up = ((e + 127) << 23).view(torch.float32)                    # exact powers of two
+    down = ((127 - e) << 23).view(torch.float32)
+    qn = ((q * down).to(torch.float8_e4m3fn).float() * up).to(torch.bfloat16)
+    cnt = torch.zeros(1, dtype=torch.int32, device=q.device)
+    common = (step.seq_start, step.row_seq, step.row_len, step.topk[step.parents[lu]], step.swa[lu],
+              step.swa_row_start, step.swa_len, step.W, step.scale)
+    out = torch.empty_like(step.out[lu])
+    lse = torch.empty_like(step.lse[lu])
+    csa2.csa2_sparse_attn_fp4mma(qn, step.codes, sc, *common, out=out, lse=lse, workspace=step.attn_workspace,
+                                 native_fragments=cnt)
+    torch.cuda.synchronize()
+    native = int(cnt.item())
+    res = {"inputs": "last layer's, scales rounded down to powers of two shared per 32 channels, "
+                     "query rounded to E4M3 under one power-of-two scale per head",
+           "native_fragments": native}
+    calls = {
+        "fp4mma_us": lambda: csa2.csa2_sparse_attn_fp4mma(qn, step.codes, sc, *common, out=out, lse=lse,
+                                                          workspace=step.attn_workspace),
+        "dequant_us": lambda: csa2.csa2_sparse_attn(qn, step.codes, sc, *common, out=out, lse=lse,
+                                                    workspace=step.attn_workspace),
+    }
+    for name, fn in calls.items():
+        g = graph_of(fn, reps=reps)
+        time_graph(g, 2, reps)
+        res[name] = round(time_graph(g, 5, reps) * 1000.0, 2)
+    del sc, qn
+    return res
+
+
 def paged_call_times(step, reps=10):
     """per_call_times for a step in paged mode."""
     import sparse_attention_fp4_amd as csa2
@@ -497,6 +540,8 @@ def measure(cfg, args, flusher, copy_gbps, with_paged=True):
             res["roofline_index_reindex"] = roof("index_reindex")
         if not prefill:
             res["roofline_sparse_attn"] = roof("sparse_attn")
+            log("bench: native-FP4 attention form")
+            res["fp4mma"] = fp4mma_times(step)
 
     if with_paged and args.page_rows > 0:
         log(f"bench: paged step ({args.page_rows} entries per page)")

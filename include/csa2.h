@@ -233,6 +233,38 @@ csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* codes, const ui
                                int32_t W, float softmax_scale, float* out, float* lse,
                                void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * csa2_sparse_attn_fp4mma: csa2_sparse_attn whose query-key products for the
+ * selected main entries run on the scaled FP4 matrix-core product (the E2M1
+ * codes straight from the cache, no dequantisation) wherever that product is
+ * exact, and on the dequantising path elsewhere.  The E2M1 codes and E4M3
+ * scales are those of the FP4 KV cache paragraph of section 一 of the
+ * teardown; the hardware product takes one power-of-two scale per 32
+ * channels on each operand, so a 16-key fragment takes the native product
+ * only if, for every one of its entries, both E4M3 scales of each 32-channel
+ * block are the same power of two, and only if the row's query (per head
+ * group) is exact as E4M3 under one power-of-two scale per 32 channels.
+ * Where it is taken, each product is exact and the logits are those of the
+ * dequantising path whenever the fp32 sums are exact (e.g. values on a common
+ * grid of bounded range); otherwise they may differ in the last bits of the
+ * fp32 accumulation.  The value operand of the PV product is dequantised as in
+ * csa2_sparse_attn, SWA rows always take the dequantising path.
+ *   native_fragments: int32 device counter (may be NULL); the call adds the
+ *            number of 16-key fragments whose logits came from the native
+ *            product.
+ * Every other argument, the workspace (size and zero-between-calls rule),
+ * limits and errors are those of csa2_sparse_attn.  A research form: it
+ * moves the same bytes and is not faster.
+ */
+csa2_status_t csa2_sparse_attn_fp4mma(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                                      const int64_t* seq_start, const int32_t* row_seq,
+                                      const int32_t* row_len, const int32_t* topk_idx, int32_t K,
+                                      const uint8_t* swa, const int64_t* swa_row_start,
+                                      const int32_t* swa_len, int32_t R, int32_t H, int32_t D,
+                                      int32_t W, float softmax_scale, float* out, float* lse,
+                                      int32_t* native_fragments, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
 /* ---------------------------------------------------------------------- */
 /* Paged main cache and SWA ring.  The pages fix only what is cached (FP4    */
 /* main KV, FP8 SWA window, FP8 indexer keys; section 一 of the teardown);   */

@@ -33,7 +33,7 @@ EXPORTS = ("csa2_status_string", "csa2_last_error", "csa2_abi_version", "csa2_qu
            "csa2_index_reindex_workspace_bytes", "csa2_index_reindex",
            "csa2_sparse_attn_workspace_bytes", "csa2_sparse_attn",
            "csa2_index_full_paged", "csa2_index_reindex_paged", "csa2_paged_rows", "csa2_sparse_attn_phys",
-           "csa2_index_reindex_noalloc")
+           "csa2_index_reindex_noalloc", "csa2_sparse_attn_fp4mma")
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
 _lib = None
@@ -69,6 +69,8 @@ def load(path: str) -> ctypes.CDLL:
     L.csa2_sparse_attn_workspace_bytes.restype = sz
     L.csa2_sparse_attn.argtypes = [P, P, P, P, P, P, P, i32, P, P, P, i32, i32, i32, i32, f32, P, P, P,
                                    sz, P]
+    L.csa2_sparse_attn_fp4mma.argtypes = [P, P, P, P, P, P, P, i32, P, P, P, i32, i32, i32, i32, f32, P, P, P, P,
+                                          sz, P]
     L.csa2_index_full_paged.argtypes = [P, P, P, i64, P, i32, i32, P, P, i32, i32, i32, i32, i32, i32, i32,
                                         P, P, P, P, sz, P]
     L.csa2_index_reindex_paged.argtypes = [P, P, P, i64, P, i32, i32, P, P, P, i32, i32, i32, i32, i32, i32, P,
@@ -78,7 +80,7 @@ def load(path: str) -> ctypes.CDLL:
                                         sz, P]
     for f in ("csa2_quantize_append", "csa2_index_full", "csa2_index_reindex", "csa2_index_reindex_noalloc",
               "csa2_sparse_attn", "csa2_index_full_paged", "csa2_index_reindex_paged", "csa2_paged_rows",
-              "csa2_sparse_attn_phys"):
+              "csa2_sparse_attn_phys", "csa2_sparse_attn_fp4mma"):
         getattr(L, f).restype = ctypes.c_int
     if L.csa2_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{path} has ABI version {L.csa2_abi_version()}, expected {ABI_VERSION}: rebuild it")
@@ -294,6 +296,31 @@ def csa2_sparse_attn(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
                      stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Sparse MQA over the selected FP4 entries plus the FP8 SWA window.
     q: [R, H, D] bfloat16.  Returns (out [R, H, D] float32, lse [R, H] or None)."""
+    return _sparse_attn("csa2_sparse_attn", q, codes, scales, seq_start, row_seq, row_len, topk_idx, swa,
+                        swa_row_start, swa_len, W, softmax_scale, out, lse, want_lse, workspace, stream)
+
+
+def csa2_sparse_attn_fp4mma(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, seq_start: torch.Tensor,
+                            row_seq: torch.Tensor, row_len: torch.Tensor, topk_idx: torch.Tensor,
+                            swa: Optional[torch.Tensor], swa_row_start: Optional[torch.Tensor],
+                            swa_len: Optional[torch.Tensor], W: int, softmax_scale: float,
+                            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                            want_lse: bool = True, workspace: Optional[torch.Tensor] = None,
+                            native_fragments: Optional[torch.Tensor] = None,
+                            stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """csa2_sparse_attn with the query-key products of the selected entries on
+    the native FP4 matrix-core product where that is exact (include/csa2.h).
+    native_fragments: optional int32 [1] device counter the call adds the
+    number of natively scored 16-key fragments to."""
+    if native_fragments is not None:
+        _dev(native_fragments, "native_fragments", torch.int32, shape=(1,))
+    return _sparse_attn("csa2_sparse_attn_fp4mma", q, codes, scales, seq_start, row_seq, row_len, topk_idx, swa,
+                        swa_row_start, swa_len, W, softmax_scale, out, lse, want_lse, workspace, stream,
+                        native_fragments=native_fragments, fp4mma=True)
+
+
+def _sparse_attn(fn, q, codes, scales, seq_start, row_seq, row_len, topk_idx, swa, swa_row_start, swa_len, W,
+                 softmax_scale, out, lse, want_lse, workspace, stream, native_fragments=None, fp4mma=False):
     if q.dtype == torch.bfloat16:
         q = q.view(torch.int16)
     _dev(q, "q", torch.int16, 3)
@@ -315,18 +342,20 @@ def csa2_sparse_attn(q: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
         _dev(lse, "lse", torch.float32, shape=(R, H))
     dev = _same_gpu(q=q, codes=codes, scales=scales, seq_start=seq_start, row_seq=row_seq, row_len=row_len,
                     topk_idx=topk_idx, swa=swa if W > 0 else None, swa_row_start=swa_row_start if W > 0 else None,
-                    swa_len=swa_len if W > 0 else None, out=out, lse=lse)
+                    swa_len=swa_len if W > 0 else None, out=out, lse=lse, native_fragments=native_fragments)
     if out is None:
         out = torch.empty(R, H, D, dtype=torch.float32, device=dev)
     if want_lse and lse is None:
         lse = torch.empty(R, H, dtype=torch.float32, device=dev)
     ws = _workspace(csa2_sparse_attn_workspace_bytes(R, H, D, K, W), dev, workspace, zeroed=True)
-    st = lib().csa2_sparse_attn(_ptr(q), _ptr(codes), _ptr(scales), _ptr(seq_start), _ptr(row_seq),
-                                _ptr(row_len), _ptr(topk_idx), K, _ptr(swa if W > 0 else None),
-                                _ptr(swa_row_start if W > 0 else None), _ptr(swa_len if W > 0 else None),
-                                R, H, D, W, float(softmax_scale), _ptr(out), _ptr(lse), _ptr(ws),
-                                0 if ws is None else ws.numel() * ws.element_size(), _stream(stream))
-    _check("csa2_sparse_attn", st)
+    args = [_ptr(q), _ptr(codes), _ptr(scales), _ptr(seq_start), _ptr(row_seq), _ptr(row_len), _ptr(topk_idx), K,
+            _ptr(swa if W > 0 else None), _ptr(swa_row_start if W > 0 else None), _ptr(swa_len if W > 0 else None),
+            R, H, D, W, float(softmax_scale), _ptr(out), _ptr(lse)]
+    if fp4mma:
+        args.append(_ptr(native_fragments))
+    args += [_ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)]
+    st = getattr(lib(), fn)(*args)
+    _check(fn, st)
     return out, lse
 
 

@@ -288,29 +288,60 @@ __device__ __forceinline__ void v_store(_Float16* vrow, int grp, int t, f16x8 kf
     *reinterpret_cast<f16x8*>(vrow + step_ch<D>(grp, t)) = kf;
 }
 
+// Query pieces (B operand of the score MFMAs; piece (ht, t) = k-step t of head
+// tile ht, this lane's column) and their a-parts for exact scores (split of q
+// described at the top of the file).
+template <int HT, int D>
+struct QueryRegs {   // the query in registers, the a-parts in LDS ([HT * KS][64])
+    const f16x8 (&qf)[HT][D / 32];
+    const f16x8* qa;
+    __device__ __forceinline__ f16x8 q(int ht, int t) const { return qf[ht][t]; }
+    __device__ __forceinline__ f16x8 a(int ht, int t) const { return qa[(ht * (D / 32) + t) * CSA2_WAVE]; }
+};
+template <int HT, int D>
+struct QueryLds {    // the query in LDS ([HT * KS][64]); a-parts formed from it
+    const f16x8* qs;
+    const float (&C)[HT];   // per head tile: the rounding constant 1.5 * 2^(E + 12) of the a-part
+    __device__ __forceinline__ f16x8 q(int ht, int t) const { return qs[(ht * (D / 32) + t) * CSA2_WAVE]; }
+    __device__ __forceinline__ f16x8 a(int ht, int t) const
+    {
+        const f16x8 v = q(ht, t);
+        f16x8 r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = (_Float16)(((float)v[e] + C[ht]) - C[ht]);
+        return r;
+    }
+};
+
 // S^T of one fragment, fp32 MFMA chain; the dequantised keys also go to the
 // wave's V tile.
-template <int MODE, int HT, int D>
-__device__ __forceinline__ void s_frag(const FragRaw<D>& fr, const f16x8 (&qf)[HT][D / 32], _Float16* vrow, int grp,
-                                       f32x4 (&acc)[HT])
+template <int MODE, int HT, int D, class QS>
+__device__ __forceinline__ void s_frag(const FragRaw<D>& fr, const QS& qs, _Float16* vrow, int grp, f32x4 (&acc)[HT])
 {
 #pragma unroll
     for (int t = 0; t < D / 32; ++t) {
         const f16x8 kf = dequant_step<MODE, D>(fr, t);
         v_store<D>(vrow, grp, t, kf);
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[ht][t], acc[ht], 0, 0, 0);
+        for (int ht = 0; ht < HT; ++ht) acc[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qs.q(ht, t), acc[ht], 0, 0, 0);
     }
 }
 
+// Only the V tile of a fragment (its scores came from the native FP4 products).
+template <int MODE, int D>
+__device__ __forceinline__ void v_frag(const FragRaw<D>& fr, _Float16* vrow, int grp)
+{
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t) v_store<D>(vrow, grp, t, dequant_step<MODE, D>(fr, t));
+}
+
 // The same fragment with S computed exactly as (hi, lo) = K a^T + K b^T
-// (split of q described at the top of the file).  qa: this lane's a-part
-// pieces in LDS, [HT * KS][64 lanes]; b = q - a is formed from the query
-// registers (an exact fp16 subtraction: the difference is q's bits below the
-// quantum of a).  upper: lane >= 32.
-template <int HT, int D>
-__device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const f16x8* qa, const f16x8 (&qf)[HT][D / 32],
-                                             bool upper, _Float16* vrow, int grp, f32x4 (&acc)[HT], f32x4 (&lo)[HT])
+// (split of q described at the top of the file); b = q - a is an exact fp16
+// subtraction (the difference is q's bits below the quantum of a).  upper:
+// lane >= 32.
+template <int HT, int D, class QS>
+__device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const QS& qs, bool upper, _Float16* vrow, int grp,
+                                             f32x4 (&acc)[HT], f32x4 (&lo)[HT])
 {
     constexpr int KS = D / 32;
     double ex[HT][4];
@@ -330,8 +361,8 @@ __device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const f16x8* 
         const f16x8 k_hi = upper ? kf : zero;     // and scale group KS + t (p = 1)
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
-            const f16x8 a = qa[(ht * KS + t) * CSA2_WAVE];
-            const f16x8 b = qf[ht][t] - a;
+            const f16x8 a = qs.a(ht, t);
+            const f16x8 b = qs.q(ht, t) - a;
             sb[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, b, sb[ht], 0, 0, 0);
             const f32x4 g0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_lo, a, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
             const f32x4 g1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_hi, a, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
@@ -348,6 +379,56 @@ __device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const f16x8* 
             acc[ht][i] = h;
             lo[ht][i] = (float)(v - (double)h);
         }
+}
+
+// Native FP4 scores (the scaled FP4 matrix-core product, no dequantisation).
+// v_mfma_scale_f32_16x16x128_f8f6f4 takes the keys' E2M1 codes as the A
+// operand and the query as E4M3 (B operand), each lane block of 32 values with
+// one power-of-two (E8M0) scale.  Lane (key, g) holds, for k-step T < D/128,
+// the 32 channels g*D/4 + 32T .. +31: exactly the 16 code bytes it loaded as
+// words 4T .. 4T+3 (before unpair()), whose two E4M3 scale bytes are those of
+// groups g*D/64 + 2T and + 1 (bytes (D/64)*hf + 2T and + 1 of the lane's KS
+// scale bytes).  The products equal the dequantised ones only where both bytes
+// are the same power of two, which nat_key_scales() checks; the query side is
+// checked once per workgroup, where the query's operand layout (which pairs
+// each lane's values with the keys' in a fixed interleave) is built.  An
+// absent key has zero codes, so any scale gives it zero products.
+template <int D>
+__device__ __forceinline__ bool nat_key_scales(const FragRaw<D>& f, int hf, uint32_t& e8)
+{
+    bool ok = true;
+    e8 = 0u;
+#pragma unroll
+    for (int T = 0; T < D / 128; ++T) {
+        const int b0 = 2 * T, b1 = D / 64 + 2 * T;   // the pair's first byte for hf = 0, 1 (even: one word holds both)
+        const uint32_t w0 = f.sc[b0 >> 2] >> (8 * (b0 & 3)), w1 = f.sc[b1 >> 2] >> (8 * (b1 & 3));
+        const uint32_t w = hf ? w1 : w0;
+        const uint32_t s0 = w & 0xFFu, s1 = (w >> 8) & 0xFFu;
+        // E4M3 2^(e - 7) with e = bits 6..3, positive, mantissa zero -> E8M0 e + 120
+        ok = ok && s0 == s1 && (s0 & 0x87u) == 0u && s0 != 0u;
+        e8 |= ((s0 >> 3) + 120u) << (8 * T);
+    }
+    return ok || !f.valid;
+}
+
+// S^T of a fragment from the native products: one MFMA per k-step and head
+// tile, each lane's scales taken from byte T of the packed words.
+template <int HT, int D>
+__device__ __forceinline__ void s_frag_nat(const FragRaw<D>& fr, uint32_t ke8, const i32x8 (&qn)[HT][D / 128],
+                                           const uint32_t (&qe8)[HT], f32x4 (&acc)[HT])
+{
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+        acc[ht] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int T = 0; T < D / 128; ++T) {
+            const i32x8 a = {(int)fr.raw[4 * T], (int)fr.raw[4 * T + 1], (int)fr.raw[4 * T + 2], (int)fr.raw[4 * T + 3],
+                             0, 0, 0, 0};
+            acc[ht] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, qn[ht][T], acc[ht], 4, 0, 0,
+                                                                      (int)(ke8 >> (8 * T)), 0,
+                                                                      (int)(qe8[ht] >> (8 * T)));
+        }
+    }
 }
 
 // O[heads x the wave's channels] += P V for G fragment slots of the round,
@@ -441,8 +522,11 @@ struct AttnSmem {
 
 // PG: the index lists hold cache rows (paged caches) and the SWA window may be
 // a ring; the packed form is a separate instantiation so that it carries none
-// of that addressing.
-template <int HT, int D, bool PG>
+// of that addressing.  NAT: scores of Top-K fragments from the native FP4
+// products wherever they are exact (s_frag_nat); the query then lives in LDS
+// as fp16 for the other fragments and as E4M3 in registers, and nat_count (if
+// not null) counts the fragments scored natively.
+template <int HT, int D, bool PG, bool NAT>
 __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const int64_t* __restrict__ seq_start, const int32_t* __restrict__ row_seq,
@@ -450,7 +534,8 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
     const uint8_t* __restrict__ swa, const int64_t* __restrict__ swa_row_start,
     const int32_t* __restrict__ swa_len, const int32_t* __restrict__ swa_head, int64_t phys_rows, int32_t R,
     int32_t H, int32_t W, float scale_log2e, int32_t HG, int32_t S, int32_t nfrag, float* __restrict__ out,
-    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml, int32_t* __restrict__ pair_sync)
+    float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml, int32_t* __restrict__ pair_sync,
+    int32_t* __restrict__ nat_count)
 {
     using SM = AttnSmem<HT, D>;
     constexpr int KS = SM::KS;
@@ -589,8 +674,12 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
             qv[e] = (_Float16)q32;
             av[e] = (_Float16)((q32 + C) - C);
         }
-        qf_s[P * CSA2_WAVE + lane] = qv;
-        qa_s[P * CSA2_WAVE + lane] = av;
+        if constexpr (NAT) {
+            qa_s[P * CSA2_WAVE + lane] = qv;   // the query itself stays in LDS (its a-parts are formed when needed)
+        } else {
+            qf_s[P * CSA2_WAVE + lane] = qv;
+            qa_s[P * CSA2_WAVE + lane] = av;
+        }
     }
     const int p = grp >> 1;
     // The row's SWA rows through a buffer (reads outside it return zeros);
@@ -613,14 +702,80 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
     FragRaw<D> cur, nxt;   // cur is unpaired in place at the start of its round
     if (fw < f_end) load_frag(cur, fw, idx_c);
 
-    __syncthreads();   // the query is staged
-    f16x8 qf[HT][KS];
+    // Native form: the query as E4M3 with one power-of-two scale per lane
+    // block (B operand of s_frag_nat), and whether every value is exact in
+    // it.  In the product an E2M1 value of A lane group g, nibble e meets the
+    // E4M3 byte 16 (g >> 1) + (e & 15) of B lane group 2 (g & 1) + (e >> 4)
+    // (measured on gfx950), so B lane (head, g), k-step T, holds the 16
+    // channels from c0 = (g >> 1) D/4 + 32T + 16 (g & 1) in bytes 0 .. 15 and
+    // the 16 from c0 + D/2 in bytes 16 .. 31.  Every wave converts the whole
+    // query of its head group, so all waves agree.
+    constexpr int NT = D / 128;
+    i32x8 qn[NAT ? HT : 1][NAT ? NT : 1];
+    uint32_t qe8[NAT ? HT : 1];
+    bool nat_q = false;
+    if constexpr (NAT) {
+        typedef short s16x2 __attribute__((ext_vector_type(2)));
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + (int64_t)r * H * D, H * D * 2);
+        bool exact = true;
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
+        for (int ht = 0; ht < HT; ++ht) {
+            qe8[ht] = 0u;
 #pragma unroll
-        for (int t = 0; t < KS; ++t) {
-            qf[ht][t] = qf_s[(ht * KS + t) * CSA2_WAVE + lane];
+            for (int T = 0; T < NT; ++T) {
+                const int c0 = (grp >> 1) * (D / 4) + 32 * T + 16 * (grp & 1);
+                const uint32_t off = (uint32_t)(h0 + ht * 16 + col) * (D * 2) + 2 * c0;
+                uint32_t wq[16];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {   // 32 bytes at c0, then 32 at c0 + D/2
+                    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rq, off + (u >> 1) * D + 16 * (u & 1), 0, 0);
+                    wq[4 * u] = v[0]; wq[4 * u + 1] = v[1]; wq[4 * u + 2] = v[2]; wq[4 * u + 3] = v[3];
+                }
+                float x[32];
+                float m = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 32; ++e) {
+                    x[e] = __uint_as_float(e & 1 ? wq[e >> 1] & 0xFFFF0000u : wq[e >> 1] << 16);
+                    m = fmaxf(m, fabsf(x[e]));
+                }
+                // scale 2^sx puts the block's largest magnitude in [128, 256)
+                int sx = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 0xFF) - 134 : 0;
+                sx = sx < -127 ? -127 : sx;
+                const float down = __uint_as_float((uint32_t)(127 - sx) << 23);   // 2^-sx, exact
+                const float up = sx > -127 ? __uint_as_float((uint32_t)(127 + sx) << 23) : 0x1p-127f;
+                i32x8 pk;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const s16x2 z = {0, 0};
+                    const s16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, x[4 * k] * down, x[4 * k + 1] * down,
+                                                                              1.0f, false);
+                    const s16x2 both = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, x[4 * k + 2] * down,
+                                                                                x[4 * k + 3] * down, 1.0f, true);
+                    const uint32_t wv = __builtin_bit_cast(uint32_t, both);
+                    pk[k] = (int)wv;
+                    // exact iff each E4M3 value times 2^sx gives the bf16 value back
+                    const f32x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wv, 1.0f, false);
+                    const f32x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(wv, 1.0f, true);
+                    exact = exact && b0[0] * up == x[4 * k] && b0[1] * up == x[4 * k + 1] &&
+                            b1[0] * up == x[4 * k + 2] && b1[1] * up == x[4 * k + 3];
+                }
+                qn[ht][T] = pk;
+                qe8[ht] |= (uint32_t)(sx + 127) << (8 * T);
+            }
         }
+        nat_q = __ballot(!exact) == 0ull;
+    }
+
+    __syncthreads();   // the query is staged
+    f16x8 qf[NAT ? 1 : HT][NAT ? 1 : KS];
+    if constexpr (!NAT) {
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int t = 0; t < KS; ++t) {
+                qf[ht][t] = qf_s[(ht * KS + t) * CSA2_WAVE + lane];
+            }
+    }
     __syncthreads();   // every wave holds the query: its staging space becomes the V tiles
 
     // Softmax state (log2 domain), per head in the S^T layout (lane col =
@@ -640,6 +795,10 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
     }
     _Float16* const vrow = vtiles + wave * SM::kTile + col * VS;   // the lane's key row of the wave's tile
     const f16x8* const qa_lane = qa_s + lane;
+    const auto qsrc = [&]() {
+        if constexpr (NAT) return QueryLds<HT, D>{qa_lane, Cq};
+        else return QueryRegs<HT, D>{qf, qa_lane};
+    }();
     // the lane's PV operand address in slot 0's tile, at the wave's first channel
     const _Float16* const vr0 = vtiles + (4 * grp + (col >> 2)) * VS + 4 * (col & 3) + wave * SM::CW;
 
@@ -668,6 +827,19 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
         if (has) {
             const int kind = frag_kind(fr, Kp);
             precise = __ballot(kind == 0 ? cur.template big<0>() : cur.template big<1>()) != 0ull;
+            // native products first: they read the code words as loaded
+            bool nat = false;
+            if constexpr (NAT) {
+                if (kind == 0 && nat_q) {
+                    uint32_t ke8;
+                    const bool ok = nat_key_scales<D>(cur, hf, ke8);
+                    nat = __ballot(!ok) == 0ull;
+                    if (nat) {
+                        s_frag_nat<HT, D>(cur, ke8, qn, qe8, sh);
+                        if (nat_count && lane == 0) atomicAdd(nat_count, 1);
+                    }
+                }
+            }
             if (kind == 0) cur.template unpair<0>();
             else cur.template unpair<1>();
             const uint64_t vb = __ballot(cur.valid);   // bit k: key k of the fragment (lanes 0..15)
@@ -679,9 +851,10 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
                     if (f1 + kWaves < f_end) load_idx(f1 + kWaves, idx_n);
                 }
             }
-            if (precise) s_frag_exact<HT, D>(cur, qa_lane, qf, upper, vrow, grp, sh, sl);
-            else if (kind == 0) s_frag<0, HT, D>(cur, qf, vrow, grp, sh);
-            else s_frag<1, HT, D>(cur, qf, vrow, grp, sh);
+            if (nat) v_frag<0, D>(cur, vrow, grp);
+            else if (precise) s_frag_exact<HT, D>(cur, qsrc, upper, vrow, grp, sh, sl);
+            else if (kind == 0) s_frag<0, HT, D>(cur, qsrc, vrow, grp, sh);
+            else s_frag<1, HT, D>(cur, qsrc, vrow, grp, sh);
             // S^T lane layout: head h0 + 16 ht + col, keys 4 grp + i.
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht)
@@ -997,16 +1170,16 @@ AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
     return p;
 }
 
-template <int HT, int D, bool PG>
+template <int HT, int D, bool PG, bool NAT>
 void launch_attn(dim3 grid, hipStream_t st, const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
                  const int64_t* seq_start, const int32_t* row_seq, const int32_t* row_len, const int32_t* topk,
                  int32_t K, const uint8_t* swa, const int64_t* swa_row_start, const int32_t* swa_len,
                  const int32_t* swa_head, int64_t phys_rows, int32_t H, int32_t R, int32_t W, float sl2e, int HG,
-                 int S, int nfrag, float* out, float* lse, float* po, float* pml, int32_t* sync)
+                 int S, int nfrag, float* out, float* lse, float* po, float* pml, int32_t* sync, int32_t* nat_count)
 {
-    hipLaunchKernelGGL((k_sparse_attn<HT, D, PG>), grid, dim3(CSA2_WAVE * kWaves), 0, st, q, codes, scales, seq_start,
-                       row_seq, row_len, topk, K, swa, swa_row_start, swa_len, swa_head, phys_rows, R, H, W, sl2e,
-                       HG, S, nfrag, out, lse, po, pml, sync);
+    hipLaunchKernelGGL((k_sparse_attn<HT, D, PG, NAT>), grid, dim3(CSA2_WAVE * kWaves), 0, st, q, codes, scales,
+                       seq_start, row_seq, row_len, topk, K, swa, swa_row_start, swa_len, swa_head, phys_rows, R, H, W,
+                       sl2e, HG, S, nfrag, out, lse, po, pml, sync, nat_count);
 }
 
 // Cache rows of the entries of index lists over a paged cache: entry j of the
@@ -1041,7 +1214,8 @@ csa2_status_t sparse_attn_impl(const uint16_t* q, const uint8_t* codes, const ui
                                int64_t phys_rows, const int32_t* topk_idx, int32_t K, const uint8_t* swa,
                                const int64_t* swa_row_start, const int32_t* swa_len, const int32_t* swa_head,
                                int32_t R, int32_t H, int32_t D, int32_t W, float softmax_scale, float* out,
-                               float* lse, void* workspace, size_t workspace_bytes, void* stream);
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream, bool nat = false,
+                               int32_t* nat_count = nullptr);
 
 }  // namespace
 
@@ -1068,7 +1242,8 @@ csa2_status_t sparse_attn_impl(const uint16_t* q, const uint8_t* codes, const ui
                                int64_t phys_rows, const int32_t* topk_idx, int32_t K, const uint8_t* swa,
                                const int64_t* swa_row_start, const int32_t* swa_len, const int32_t* swa_head,
                                int32_t R, int32_t H, int32_t D, int32_t W, float softmax_scale, float* out,
-                               float* lse, void* workspace, size_t workspace_bytes, void* stream)
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream, bool nat,
+                               int32_t* nat_count)
 {
     CSA2_REQUIRE(R >= 0, CSA2_ERR_SHAPE, "sparse_attn: R=%d < 0", R);
     CSA2_REQUIRE(H >= 1, CSA2_ERR_SHAPE, "sparse_attn: H=%d < 1", H);
@@ -1111,9 +1286,10 @@ csa2_status_t sparse_attn_impl(const uint16_t* q, const uint8_t* codes, const ui
     const dim3 grid((unsigned)xcd_grid(R, p.HG * p.S));
 #define CSA2_ATTN(ht, d)                                                                                    \
     if (p.HT == ht && D == d)                                                                               \
-        (phys_rows > 0 ? launch_attn<ht, d, true> : launch_attn<ht, d, false>)(                             \
+        (nat ? launch_attn<ht, d, false, true>                                                              \
+             : phys_rows > 0 ? launch_attn<ht, d, true, false> : launch_attn<ht, d, false, false>)(         \
             grid, st, q, codes, scales, seq_start, row_seq, row_len, topk_idx, K, swa, swa_row_start, swa_len, \
-            swa_head, phys_rows, H, R, W, sl2e, p.HG, p.S, p.nfrag, out, lse, po, pml, sync);
+            swa_head, phys_rows, H, R, W, sl2e, p.HG, p.S, p.nfrag, out, lse, po, pml, sync, nat_count);
     CSA2_ATTN(1, 128) CSA2_ATTN(2, 128) CSA2_ATTN(4, 128)
     CSA2_ATTN(1, 256) CSA2_ATTN(2, 256)
     CSA2_ATTN(1, 512)
@@ -1135,6 +1311,19 @@ extern "C" csa2_status_t csa2_sparse_attn(const uint16_t* q, const uint8_t* code
 {
     return sparse_attn_impl(q, codes, scales, seq_start, row_seq, row_len, 0, topk_idx, K, swa, swa_row_start, swa_len,
                             nullptr, R, H, D, W, softmax_scale, out, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" csa2_status_t csa2_sparse_attn_fp4mma(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
+                                                const int64_t* seq_start, const int32_t* row_seq,
+                                                const int32_t* row_len, const int32_t* topk_idx, int32_t K,
+                                                const uint8_t* swa, const int64_t* swa_row_start,
+                                                const int32_t* swa_len, int32_t R, int32_t H, int32_t D, int32_t W,
+                                                float softmax_scale, float* out, float* lse, int32_t* native_fragments,
+                                                void* workspace, size_t workspace_bytes, void* stream)
+{
+    return sparse_attn_impl(q, codes, scales, seq_start, row_seq, row_len, 0, topk_idx, K, swa, swa_row_start, swa_len,
+                            nullptr, R, H, D, W, softmax_scale, out, lse, workspace, workspace_bytes, stream, true,
+                            native_fragments);
 }
 
 extern "C" csa2_status_t csa2_sparse_attn_phys(const uint16_t* q, const uint8_t* codes, const uint8_t* scales,

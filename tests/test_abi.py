@@ -163,6 +163,24 @@ def test_sparse_attn_validation():
     assert f(*attn_args(R=0)) == 0
 
 
+def test_sparse_attn_fp4mma_validation():
+    """The native-FP4 form validates its arguments as csa2_sparse_attn does
+    (its extra counter pointer may be NULL)."""
+    f = csa2.lib().csa2_sparse_attn_fp4mma
+
+    def args(**kw):
+        a = attn_args(**kw)
+        return a[:18] + [None] + a[18:]   # native_fragments after lse
+    assert f(*args(D=96)) == 3
+    assert f(*args(D=40)) == 2
+    assert f(*args(H=0)) == 2
+    assert f(*args(K=-1)) == 2
+    assert f(*args(topk=None)) == 1
+    assert f(*args(out=None)) == 1
+    assert f(*args(R=2, wsb=0)) == 4
+    assert f(*args(R=0)) == 0
+
+
 def test_attn_workspace_only_when_split():
     L = csa2.lib()
     # many rows: one workgroup per (row, head group) fills the GPU -> no split, no workspace

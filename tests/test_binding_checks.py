@@ -47,6 +47,13 @@ def attn(**kw):
                                  a["topk_idx"], a["swa"], a["swa_row_start"], a["swa_len"], W, 0.1, **kw)
 
 
+def attn_fp4mma(**kw):
+    a = attn_inputs()
+    return csa2.csa2_sparse_attn_fp4mma(a["q"], a["codes"], a["scales"], a["seq_start"], a["row_seq"],
+                                        a["row_len"], a["topk_idx"], a["swa"], a["swa_row_start"], a["swa_len"], W,
+                                        0.1, **kw)
+
+
 def attn_phys(**kw):
     a = attn_inputs()
     return csa2.csa2_sparse_attn_phys(a["q"], a["codes"], a["scales"], a["topk_idx"], a["swa"], a["swa_row_start"],
@@ -54,7 +61,7 @@ def attn_phys(**kw):
 
 
 def test_correct_shapes_on_the_host_fail_only_the_device_check():
-    for call in (full, reindex, attn, attn_phys):
+    for call in (full, reindex, attn, attn_phys, attn_fp4mma):
         with pytest.raises(ValueError, match="must live on the GPU"):
             call()
 
@@ -84,7 +91,7 @@ def test_index_reindex_shapes():
         reindex(pool=torch.zeros(R, P, dtype=torch.int64))
 
 
-@pytest.mark.parametrize("call", [attn, attn_phys])
+@pytest.mark.parametrize("call", [attn, attn_phys, attn_fp4mma])
 def test_attention_output_shapes(call):
     with pytest.raises(ValueError, match="out must have shape"):
         call(out=torch.zeros(R, H, D - 16))
@@ -136,3 +143,10 @@ def test_quantize_shapes():
     with pytest.raises(ValueError, match="scales must have shape"):
         csa2.csa2_quantize_append(x, torch.zeros(4, dtype=torch.int64), torch.zeros(8, D // 2, dtype=torch.uint8),
                                   torch.zeros(7, D // 16, dtype=torch.uint8))
+
+
+def test_fp4mma_counter_shape_and_dtype():
+    with pytest.raises(ValueError, match="native_fragments must have shape"):
+        attn_fp4mma(native_fragments=i32(2))
+    with pytest.raises(TypeError, match="int32"):
+        attn_fp4mma(native_fragments=torch.zeros(1, dtype=torch.int64))
