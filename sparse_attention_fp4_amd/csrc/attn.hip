@@ -28,7 +28,10 @@
 //     (ds_read_b64_tr_b16).
 // So each key is dequantised once per workgroup, a wave's accumulators hold
 // only its channels (two waves fit one SIMD and hide each other's latency),
-// and the end needs no merge of outputs between waves.  Rows whose fragments
+// and the end needs no merge of outputs between waves.  With rows enough for
+// two workgroups per compute unit (prefill chunks, large batches) the same
+// scheme runs with four waves and rounds of four fragments: half the LDS, so
+// two workgroups share each compute unit and their phases interleave.  Rows whose fragments
 // are split across workgroups write unnormalised partial outputs plus (max,
 // sums): with two splits the second workgroup of the pair to finish merges
 // the first's partial into its own output; with more, k_attn_combine merges
@@ -55,6 +58,7 @@ namespace {
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kFrag = 16;           // keys per fragment (one MFMA row block)
 constexpr int kWaves = 8;           // waves per workgroup (two per SIMD), fragments per round
+constexpr int kWavesMany = 4;       // the same with many rows: half the LDS, two workgroups per compute unit
 constexpr float kLazy = 8.0f;       // log2-domain slack before a running max is raised
 constexpr int kMaxPlanSplits = 8;   // key splits per row, at most
 
@@ -299,6 +303,24 @@ struct QueryRegs {   // the query in registers, the a-parts in LDS ([HT * KS][64
     __device__ __forceinline__ f16x8 a(int ht, int t) const { return qa[(ht * (D / 32) + t) * CSA2_WAVE]; }
 };
 template <int HT, int D>
+struct QueryRegsC {   // the query in registers, the a-parts formed from it
+    const f16x8 (&qf)[HT][D / 32];
+    const float (&C)[HT];   // per head tile: the rounding constant 1.5 * 2^(E + 12) of the a-part
+    __device__ __forceinline__ f16x8 q(int ht, int t) const { return qf[ht][t]; }
+    __device__ __forceinline__ f16x8 a(int ht, int t) const
+    {
+        // formed where it is used: kept from being hoisted out of the
+        // fragment loop, where all of them would hold registers throughout
+        u32x4 w = __builtin_bit_cast(u32x4, qf[ht][t]);
+        asm volatile("" : "+v"(w[0]), "+v"(w[1]), "+v"(w[2]), "+v"(w[3]));
+        const f16x8 v = __builtin_bit_cast(f16x8, w);
+        f16x8 r;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = (_Float16)(((float)v[e] + C[ht]) - C[ht]);
+        return r;
+    }
+};
+template <int HT, int D>
 struct QueryLds {    // the query in LDS ([HT * KS][64]); a-parts formed from it
     const f16x8* qs;
     const float (&C)[HT];   // per head tile: the rounding constant 1.5 * 2^(E + 12) of the a-part
@@ -504,20 +526,23 @@ __device__ __forceinline__ int frag_kind(int fr, int Kp) { return fr * kFrag >= 
 // LDS of one workgroup: one V tile per fragment slot of a round (slot w
 // filled by wave w), the a-part of the query (exact scores) and the round's
 // probabilities; before the loop the query is staged where the tiles go.
-template <int HT, int D>
+template <int HT, int D, int NW>
 struct AttnSmem {
     static constexpr int KS = D / 32;
     static constexpr int NH = HT * 16;
-    static constexpr int CW = D / kWaves;          // output channels of a wave
+    static constexpr int CW = D / NW;              // output channels of a wave
     static constexpr int NDT = CW / 16;            // its output tiles per head tile
     static constexpr int VS = D + 8;               // V row stride in halves (conflict-free rows and transposes)
     static constexpr int kTile = kFrag * VS;       // halves per V tile
-    static constexpr int kVBytes = kWaves * kTile * 2;
-    static constexpr int kQaBytes = HT * KS * CSA2_WAVE * 16;         // [HT * KS][64] f16x8
-    static constexpr int kPBytes = kWaves * 2 * HT * CSA2_WAVE * 8;   // [slot][hi, lo][HT][64] f16x4
+    static constexpr int kVBytes = NW * kTile * 2;
+    // [HT * KS][64] f16x8: the a-parts of the query (eight waves) or, in the
+    // native-FP4 form, the query itself; four waves form the a-parts from
+    // the query registers instead, which halves the LDS per workgroup
+    static constexpr int kQaBytes = NW == kWaves ? HT * KS * CSA2_WAVE * 16 : 0;
+    static constexpr int kPBytes = NW * 2 * HT * CSA2_WAVE * 8;       // [slot][hi, lo][HT][64] f16x4
     static constexpr int kBytes = kVBytes + kQaBytes + kPBytes;
     static_assert(HT * KS * CSA2_WAVE * 16 <= kVBytes, "the query staging fits the V tiles");
-    static_assert(D % (16 * kWaves) == 0 && NDT >= 1, "whole output tiles per wave");
+    static_assert(D % (16 * NW) == 0 && NDT >= 1, "whole output tiles per wave");
 };
 
 // PG: the index lists hold cache rows (paged caches) and the SWA window may be
@@ -526,8 +551,11 @@ struct AttnSmem {
 // products wherever they are exact (s_frag_nat); the query then lives in LDS
 // as fp16 for the other fragments and as E4M3 in registers, and nat_count (if
 // not null) counts the fragments scored natively.
-template <int HT, int D, bool PG, bool NAT>
-__global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
+// NW: waves per workgroup, kWaves (one workgroup per compute unit) or
+// kWavesMany (rows enough for two per compute unit: half the fragments per
+// round, no LDS copy of the a-parts).
+template <int HT, int D, bool PG, bool NAT, int NW>
+__global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse_attn(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const int64_t* __restrict__ seq_start, const int32_t* __restrict__ row_seq,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ topk, int32_t K,
@@ -537,17 +565,18 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
     float* __restrict__ lse, float* __restrict__ part_o, float* __restrict__ part_ml, int32_t* __restrict__ pair_sync,
     int32_t* __restrict__ nat_count)
 {
-    using SM = AttnSmem<HT, D>;
+    static_assert(NW == kWaves || (NW == kWavesMany && !NAT), "the native form runs with eight waves");
+    using SM = AttnSmem<HT, D, NW>;
     constexpr int KS = SM::KS;
     constexpr int NH = SM::NH;
     constexpr int NDT = SM::NDT;
     constexpr int VS = SM::VS;
 
     __shared__ __attribute__((aligned(16))) char smem[SM::kBytes];
-    __shared__ float4 fmx[NH][kWaves / 4];   // per head: each slot's largest logit of the head
-    __shared__ float wsum[2][kWaves][NH];    // at the end: each wave's sums (PV weights, unrounded)
-    __shared__ uint32_t wqm[kWaves][NH];     // per wave: bf16 bits of the max |q| of each head over its pieces
-    __shared__ int fprec[kWaves];            // per slot: exact scores, two-part probabilities
+    __shared__ float4 fmx[NH][NW / 4];   // per head: each slot's largest logit of the head
+    __shared__ float wsum[2][NW][NH];    // at the end: each wave's sums (PV weights, unrounded)
+    __shared__ uint32_t wqm[NW][NH];     // per wave: bf16 bits of the max |q| of each head over its pieces
+    __shared__ int fprec[NW];            // per slot: exact scores, two-part probabilities
     _Float16* const vtiles = reinterpret_cast<_Float16*>(smem);
     f16x8* const qa_s = reinterpret_cast<f16x8*>(smem + SM::kVBytes);                  // [HT * KS][64]
     f16x4* const p_s = reinterpret_cast<f16x4*>(smem + SM::kVBytes + SM::kQaBytes);   // [slot][2][HT][64]
@@ -598,20 +627,20 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
     const int fw = f_begin + wave;   // the wave's fragment in the first round
     int idx_c = 0, idx_n = 0;
     if (fw < f_end) load_idx(fw, idx_c);
-    if (fw + kWaves < f_end) load_idx(fw + kWaves, idx_n);
+    if (fw + NW < f_end) load_idx(fw + NW, idx_n);
     // The query, as NQP pieces (piece P = ht * KS + t: k-step t of head tile
     // ht, the B operand layout); wave w loads and converts pieces w, w + 8, ...,
     // which go to LDS; every wave reads the whole query back after the
     // barrier.  The query is read through a buffer over its H heads: heads past
     // H read as zeros.
     constexpr int NQP = HT * KS;
-    constexpr int NPW = (NQP + kWaves - 1) / kWaves;
+    constexpr int NPW = (NQP + NW - 1) / NW;
     uint4 qraw[NPW];
     {
         const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(q + (int64_t)r * H * D, H * D * 2);
 #pragma unroll
         for (int k = 0; k < NPW; ++k) {
-            const int P = k * kWaves + wave;
+            const int P = k * NW + wave;
             qraw[k] = make_uint4(0u, 0u, 0u, 0u);
             if (P < NQP) {
                 const uint32_t hoff = (uint32_t)(h0 + (P / KS) * 16 + col) * (D * 2);
@@ -630,7 +659,7 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
         u16x2 mx = {0, 0};
 #pragma unroll
         for (int k = 0; k < NPW; ++k) {
-            const int P = k * kWaves + wave;
+            const int P = k * NW + wave;
             if (P < NQP && P / KS == ht) {
                 const uint32_t ws[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
 #pragma unroll
@@ -653,7 +682,7 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
     for (int ht = 0; ht < HT; ++ht) {
         uint32_t mb = 0u;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) mb = max(mb, wqm[w][ht * 16 + col]);
+        for (int w = 0; w < NW; ++w) mb = max(mb, wqm[w][ht * 16 + col]);
         const float m = __uint_as_float(mb << 16);
         int E = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 0xFF) - 126 : -13;
         E = E < -13 ? -13 : E;
@@ -661,7 +690,7 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
     }
 #pragma unroll
     for (int k = 0; k < NPW; ++k) {
-        const int P = k * kWaves + wave;
+        const int P = k * NW + wave;
         if (P >= NQP) continue;
         float C = Cq[0];
 #pragma unroll
@@ -676,9 +705,11 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
         }
         if constexpr (NAT) {
             qa_s[P * CSA2_WAVE + lane] = qv;   // the query itself stays in LDS (its a-parts are formed when needed)
-        } else {
+        } else if constexpr (NW == kWaves) {
             qf_s[P * CSA2_WAVE + lane] = qv;
             qa_s[P * CSA2_WAVE + lane] = av;
+        } else {
+            qf_s[P * CSA2_WAVE + lane] = qv;   // (the a-parts are formed from the query registers)
         }
     }
     const int p = grp >> 1;
@@ -797,7 +828,8 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
     const f16x8* const qa_lane = qa_s + lane;
     const auto qsrc = [&]() {
         if constexpr (NAT) return QueryLds<HT, D>{qa_lane, Cq};
-        else return QueryRegs<HT, D>{qf, qa_lane};
+        else if constexpr (NW == kWaves) return QueryRegs<HT, D>{qf, qa_lane};
+        else return QueryRegsC<HT, D>{qf, Cq};
     }();
     // the lane's PV operand address in slot 0's tile, at the wave's first channel
     const _Float16* const vr0 = vtiles + (4 * grp + (col >> 2)) * VS + 4 * (col & 3) + wave * SM::CW;
@@ -806,10 +838,10 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
     // accumulators in ordinary VGPRs (-amdgpu-mfma-vgpr-form), so that the
     // query (64 registers at HT * D = 512), the output and the fragment bytes
     // share one budget of 256 per wave, two waves per SIMD.
-    for (int f0 = f_begin; f0 < f_end; f0 += kWaves) {
+    for (int f0 = f_begin; f0 < f_end; f0 += NW) {
         const int fr = f0 + wave;
         const bool has = fr < f_end;                               // uniform in the wave
-        const int nslot = f_end - f0 < kWaves ? f_end - f0 : kWaves;   // uniform in the workgroup
+        const int nslot = f_end - f0 < NW ? f_end - f0 : NW;   // uniform in the workgroup
         // ---- the wave's fragment: scores, V tile, per-head maximum.
         // Large values (|v| > 8) make the output sensitive to logit rounding:
         // a logit error e moves the output by about e * |v - out|.  Such a
@@ -845,10 +877,10 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
             const uint64_t vb = __ballot(cur.valid);   // bit k: key k of the fragment (lanes 0..15)
             // prefetch: raw bytes of the wave's next fragment, Top-K entry of the one after
             {
-                const int f1 = fr + kWaves;
+                const int f1 = fr + NW;
                 if (f1 < f_end) {
                     load_frag(nxt, f1, idx_n);
-                    if (f1 + kWaves < f_end) load_idx(f1 + kWaves, idx_n);
+                    if (f1 + NW < f_end) load_idx(f1 + NW, idx_n);
                 }
             }
             if (nat) v_frag<0, D>(cur, vrow, grp);
@@ -883,7 +915,7 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
         for (int ht = 0; ht < HT; ++ht) {
             float rm = -INFINITY;
 #pragma unroll
-            for (int w4 = 0; w4 < kWaves / 4; ++w4) {
+            for (int w4 = 0; w4 < NW / 4; ++w4) {
                 const float4 v = fmx[ht * 16 + col][w4];
                 rm = fmaxf(rm, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
             }
@@ -935,9 +967,11 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
 
         // ---- PV: the probabilities of every slot into the wave's channels
         // (then the low parts of precise slots).
-        for (int j0 = 0; j0 < nslot; j0 += kPvGroup) {
-            if (j0 + kPvGroup <= nslot)
-                pv_slots<kPvGroup, HT, NDT>(p_s + (j0 * 2 * HT) * CSA2_WAVE + lane, 2 * HT * CSA2_WAVE,
+        // (four waves hold twice the output channels each: two slots' operands at a time)
+        constexpr int PVG = NW == kWaves ? kPvGroup : (HT * D >= 512 ? 1 : 2);
+        for (int j0 = 0; j0 < nslot; j0 += PVG) {
+            if (j0 + PVG <= nslot)
+                pv_slots<PVG, HT, NDT>(p_s + (j0 * 2 * HT) * CSA2_WAVE + lane, 2 * HT * CSA2_WAVE,
                                             vr0 + j0 * SM::kTile, SM::kTile, o);
             else
                 for (int j = j0; j < nslot; ++j)
@@ -970,7 +1004,7 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
         Lh[ht] = 0.0f;
         Leh[ht] = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < NW; ++w) {
             Lh[ht] += wsum[0][w][ht * 16 + col];
             Leh[ht] += wsum[1][w][ht * 16 + col];
         }
@@ -988,7 +1022,7 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
         int32_t* const sync = pair_sync + (r * HG + hg);
         CSA2_DCHECK(threadIdx.x == 0 && r * HG + hg >= kPairWords);
         constexpr int NE = HT * NDT * 4;   // output values per lane
-        float* const po = part_o + ((int64_t)r * HG + hg) * (kWaves * CSA2_WAVE * NE) + wave * CSA2_WAVE + lane;
+        float* const po = part_o + ((int64_t)r * HG + hg) * (NW * CSA2_WAVE * NE) + wave * CSA2_WAVE + lane;
         float* const pml = part_ml + ((int64_t)r * HG + hg) * (NH * 4);
         if (threadIdx.x == 0)
             second = __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 ? 0 : 1;
@@ -1000,7 +1034,7 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
                 for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        store_coherent(po + ((ht * NDT + dt) * 4 + i) * (kWaves * CSA2_WAVE), o[ht][dt][i]);
+                        store_coherent(po + ((ht * NDT + dt) * 4 + i) * (NW * CSA2_WAVE), o[ht][dt][i]);
                 if (wave == 0 && grp == 0) {
                     float* const ml = pml + (ht * 16 + col) * 4;
                     store_coherent(ml + 0, Mh[ht]);
@@ -1052,7 +1086,7 @@ __global__ __launch_bounds__(CSA2_WAVE * kWaves, 1) void k_sparse_attn(
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float ob = __hip_atomic_load(po + ((ht * NDT + dt) * 4 + i) * (kWaves * CSA2_WAVE),
+                    const float ob = __hip_atomic_load(po + ((ht * NDT + dt) * 4 + i) * (NW * CSA2_WAVE),
                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     o[ht][dt][i] = o[ht][dt][i] * wai[i] + ob * wbi[i];
                 }
@@ -1133,7 +1167,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(const float* __restrict__ 
 }
 
 struct AttnPlan {
-    int HT, HG, S, nfrag;
+    int HT, HG, S, nfrag, NW;
 };
 
 // Workgroup shape: heads per workgroup (16 HT) and key splits S per row.  A
@@ -1144,7 +1178,9 @@ struct AttnPlan {
 //     alone give about one workgroup per compute unit;
 //   * otherwise HT = 1 and a row's keys are split over up to kMaxPlanSplits
 //     workgroups, keeping at least one fragment per wave (each split adds a
-//     partial output to the merge).
+//     partial output to the merge);
+//   * with at least two workgroups per compute unit, they take four waves
+//     each (half the LDS), so two run on each compute unit at once.
 AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
 {
     constexpr int64_t kTargetGroups = 256;
@@ -1167,17 +1203,18 @@ AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
     if (S > kMaxPlanSplits) S = kMaxPlanSplits;
     if (S > smax) S = smax;
     p.S = (int)S;
+    p.NW = base >= 2 * kTargetGroups ? kWavesMany : kWaves;
     return p;
 }
 
-template <int HT, int D, bool PG, bool NAT>
+template <int HT, int D, bool PG, bool NAT, int NW>
 void launch_attn(dim3 grid, hipStream_t st, const uint16_t* q, const uint8_t* codes, const uint8_t* scales,
                  const int64_t* seq_start, const int32_t* row_seq, const int32_t* row_len, const int32_t* topk,
                  int32_t K, const uint8_t* swa, const int64_t* swa_row_start, const int32_t* swa_len,
                  const int32_t* swa_head, int64_t phys_rows, int32_t H, int32_t R, int32_t W, float sl2e, int HG,
                  int S, int nfrag, float* out, float* lse, float* po, float* pml, int32_t* sync, int32_t* nat_count)
 {
-    hipLaunchKernelGGL((k_sparse_attn<HT, D, PG, NAT>), grid, dim3(CSA2_WAVE * kWaves), 0, st, q, codes, scales,
+    hipLaunchKernelGGL((k_sparse_attn<HT, D, PG, NAT, NW>), grid, dim3(CSA2_WAVE * NW), 0, st, q, codes, scales,
                        seq_start, row_seq, row_len, topk, K, swa, swa_row_start, swa_len, swa_head, phys_rows, R, H, W,
                        sl2e, HG, S, nfrag, out, lse, po, pml, sync, nat_count);
 }
@@ -1286,8 +1323,10 @@ csa2_status_t sparse_attn_impl(const uint16_t* q, const uint8_t* codes, const ui
     const dim3 grid((unsigned)xcd_grid(R, p.HG * p.S));
 #define CSA2_ATTN(ht, d)                                                                                    \
     if (p.HT == ht && D == d)                                                                               \
-        (nat ? launch_attn<ht, d, false, true>                                                              \
-             : phys_rows > 0 ? launch_attn<ht, d, true, false> : launch_attn<ht, d, false, false>)(         \
+        (nat                      ? launch_attn<ht, d, false, true, kWaves>                                 \
+         : p.NW == kWavesMany     ? (phys_rows > 0 ? launch_attn<ht, d, true, false, kWavesMany>            \
+                                                   : launch_attn<ht, d, false, false, kWavesMany>)          \
+         : phys_rows > 0 ? launch_attn<ht, d, true, false, kWaves> : launch_attn<ht, d, false, false, kWaves>)( \
             grid, st, q, codes, scales, seq_start, row_seq, row_len, topk_idx, K, swa, swa_row_start, swa_len, \
             swa_head, phys_rows, H, R, W, sl2e, p.HG, p.S, p.nfrag, out, lse, po, pml, sync, nat_count);
     CSA2_ATTN(1, 128) CSA2_ATTN(2, 128) CSA2_ATTN(4, 128)
