@@ -28,10 +28,10 @@
 //     (ds_read_b64_tr_b16).
 // So each key is dequantised once per workgroup, a wave's accumulators hold
 // only its channels (two waves fit one SIMD and hide each other's latency),
-// and the end needs no merge of outputs between waves.  With rows enough for
-// two workgroups per compute unit (prefill chunks, large batches) the same
-// scheme runs with four waves and rounds of four fragments: half the LDS, so
-// two workgroups share each compute unit and their phases interleave.  Rows whose fragments
+// and the end needs no merge of outputs between waves.  With many rows
+// (prefill chunks) the same scheme runs with four waves and rounds of four
+// fragments: half the LDS, so two workgroups share each compute unit and
+// their phases interleave.  Rows whose fragments
 // are split across workgroups write unnormalised partial outputs plus (max,
 // sums): with two splits the second workgroup of the pair to finish merges
 // the first's partial into its own output; with more, k_attn_combine merges
@@ -1179,8 +1179,12 @@ struct AttnPlan {
 //   * otherwise HT = 1 and a row's keys are split over up to kMaxPlanSplits
 //     workgroups, keeping at least one fragment per wave (each split adds a
 //     partial output to the merge);
-//   * with at least two workgroups per compute unit, they take four waves
-//     each (half the LDS), so two run on each compute unit at once.
+//   * with at least eight workgroups per compute unit (prefill chunks), they
+//     take four waves each (half the LDS), so two run on each compute unit at
+//     once.  (Four waves form the exact-score a-parts from the query
+//     registers, which costs VALU work on large-valued keys: with fewer rows,
+//     e.g. a 256-row ragged batch of heavy-tailed values, eight waves are
+//     faster.)
 AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
 {
     constexpr int64_t kTargetGroups = 256;
@@ -1203,7 +1207,7 @@ AttnPlan plan_attn(int32_t R, int32_t H, int32_t D, int32_t K, int32_t W)
     if (S > kMaxPlanSplits) S = kMaxPlanSplits;
     if (S > smax) S = smax;
     p.S = (int)S;
-    p.NW = base >= 2 * kTargetGroups ? kWavesMany : kWaves;
+    p.NW = base >= 8 * kTargetGroups ? kWavesMany : kWaves;
     return p;
 }
 

@@ -420,6 +420,43 @@ def test_sparse_attn_matches_oracle(name, lengths, D, H, K, W):
                what=name)
 
 
+@pytest.mark.parametrize("name,D,H,rows,K,W,kv", [
+    ("d512_h64_2080_groups", 512, 64, 520, 512, 128, "normal"),
+    ("d512_h64_2080_groups_student_outliers", 512, 64, 520, 512, 128, "student_t_outliers"),
+    ("d256_h64_32heads_2060_groups_outliers", 256, 64, 1030, 200, 32, "student_t_outliers"),
+    ("d128_h64_64heads_2050_groups", 128, 64, 2050, 64, 16, "normal"),
+])
+def test_sparse_attn_four_wave_workgroups(name, D, H, rows, K, W, kv):
+    """Enough (row, head group) pairs for two four-wave workgroups per compute
+    unit (at least 2,048): rounds of four fragments, a-parts of exact scores
+    formed from the query registers.  All rows are computed; the oracle checks
+    a seeded sample of them."""
+    log(f"sparse_attn four-wave parity: {name}")
+    lengths = [300 + (37 * i) % 900 for i in range(rows)]
+    wl = with_cache(small_workload(lengths, Hi=8, Di=64, D=D, H=H, W=W, layers="F", kv_dist=kv))
+    rng = np.random.default_rng(rows)
+    topk = np.full((rows, K), -1, np.int32)
+    for r, n in enumerate(lengths):
+        k = min(K, n)
+        topk[r, :k] = np.sort(rng.choice(n, k, replace=False))
+    scale = 1.0 / math.sqrt(D)
+    out, lse = run_attn(wl, 0, torch.tensor(topk, device=DEV), W, scale)
+    assert np.isfinite(out).all()
+    if kv == "normal":
+        # the cache-row form (paged caches) of the same call: same keys in the
+        # same order, so the same bits
+        base = np_(wl.seq_start)[np_(wl.row_seq)][:, None]
+        phys = torch.tensor(np.where(topk >= 0, topk + base, -1).astype(np.int32), device=DEV)
+        o2, l2 = csa2.csa2_sparse_attn_phys(wl.q[0], wl.codes_dev, wl.scales_dev, phys, wl.swa[0], wl.swa_row_start,
+                                            wl.swa_len, W, scale)
+        torch.cuda.synchronize()
+        assert np.array_equal(np_(o2), out) and np.array_equal(np_(l2), lse)
+    sample = sorted(set([0, rows - 1] + rng.choice(rows, 10, replace=False).tolist()))
+    ref = oracle_attn_rows(wl, {r: topk[r] for r in sample}, 0, sample, W, scale)
+    check_attn(out[sample], np.stack([ref[r][0] for r in sample]), lse[sample], np.stack([ref[r][1] for r in sample]),
+               what=name)
+
+
 def test_sparse_attn_pair_merge_is_deterministic_and_leaves_its_workspace_zero():
     """Two key splits per row (24 rows x 4 head groups): the second split of a
     pair merges the first's partial.  Two calls on one workspace give
