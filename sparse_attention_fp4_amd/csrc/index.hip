@@ -914,18 +914,21 @@ __device__ __forceinline__ void radix_select2(SelShared& sh, int& phase, const S
     }
 }
 
-// Ordered compaction: emit(pos, item, key) for the selected items in item
-// order.  A thread counts the keys above the threshold and those equal to it
-// among its items; one block scan of the packed counts per round gives every
+// Ordered compaction: emit(pos, item, key, pre(round)) for the selected
+// items in item order; pre(rd) is read once per thread and round, before the
+// (divergent) emits, so that no emit waits on a load of its own.  A thread
+// counts the keys above the threshold and those equal to it among its items;
+// one block scan of the packed counts per round gives every
 // thread the number of selected items before its own (all keys above, plus the
 // first `need` equal keys: ties go to the lowest item), and the thread then
 // writes its items in order.  Returns the number selected.
-template <class Src, class Emit>
+template <class Src, class Emit, class Pre>
 __device__ __forceinline__ int select_compact(SelShared& sh, int& phase, const Src& src, const RegKeys& reg,
-                                              SelState st, Emit emit)
+                                              SelState st, Emit emit, Pre pre)
 {
     int gt_run = 0, eq_run = 0;
     for_rounds(src, reg, [&](int rd, const uint32_t (&key)[kE]) {
+        const int pv = pre(rd);
         int gt = 0, eq = 0;
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
@@ -944,7 +947,7 @@ __device__ __forceinline__ int select_compact(SelShared& sh, int& phase, const S
             const uint32_t mk = key[e] & st.mask;
             const bool is_gt = key[e] && mk > st.prefix, is_eq = key[e] && mk == st.prefix;
             const bool sel = is_gt || (is_eq && eq_seen < st.need);
-            if (sel) emit(out++, i0 + e, key[e]);
+            if (sel) emit(out++, i0 + e, key[e], pv);
             eq_seen += is_eq ? 1 : 0;
         }
         gt_run += total >> 16;
@@ -1075,6 +1078,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     const int* cand_slot;   // their pool slots (Reindex)
     int ncb;                // number of candidate blocks
     bool preloaded = false; // reg already holds the candidates' keys
+    int pool_late = -1;     // Full, pool = A: its size, the pool being written at the end
 
     if constexpr (FULL) {
         // A = the top max(P, K) blocks (all of them when nb is smaller) and B
@@ -1093,18 +1097,18 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
             SelState sa, sb;
             if (P > 0) radix_select2(L.sh, phase, src, rg, big, small, sa, sb);
             else sa = radix_select(L.sh, phase, src, rg, big);
-            na = select_compact(L.sh, phase, src, rg, sa, [&](int pos, int i, uint32_t) {
+            na = select_compact(L.sh, phase, src, rg, sa, [&](int pos, int i, uint32_t, int) {
                 if (pos < big) L.blocks[pos] = id(i);
-            });
+            }, [](int) { return 0; });
             na = na < big ? na : big;
             if (P > 0 && na > small) {
                 int32_t* po = pool_out + (int64_t)r * P;
-                nsm = select_compact(L.sh, phase, src, rg, sb, [&](int pos, int i, uint32_t) {
+                nsm = select_compact(L.sh, phase, src, rg, sb, [&](int pos, int i, uint32_t, int) {
                     if (pos < small) {
                         if (P >= K) L.cblk[pos] = id(i);
                         else po[pos] = id(i);
                     }
-                });
+                }, [](int) { return 0; });
                 nsm = nsm < small ? nsm : small;
             } else {
                 nsm = na;   // B = A
@@ -1186,7 +1190,12 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
         if (P > 0) {
             int32_t* po = pool_out + (int64_t)r * P;
             if (P >= K) {   // pool = A, candidates = B
-                for (int i = threadIdx.x; i < P; i += kSelThreads) po[i] = i < na ? L.blocks[i] : -1;
+                // (written at the end, where no barrier follows the stores;
+                // L.blocks is only read from here on)
+                if (cand_out)
+                    for (int i = threadIdx.x; i < P; i += kSelThreads) po[i] = i < na ? L.blocks[i] : -1;
+                else
+                    pool_late = na;
                 if (na > K) {
                     cand = L.cblk;
                     ncb = nsm;
@@ -1212,19 +1221,33 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
         // visible entry, so for a pool in order (the usual case: a Full
         // layer's pool) the keys are the scores in slot order; they are
         // requested before the order is checked.
+        // (the pool ids are requested first, so that their latency and the
+        // scores' overlap)
         const int32_t* pl = pool_in + (int64_t)r * P;
+        constexpr int PPT = kMaxP / kSelThreads;
+        int pb[PPT], pb2[PPT];
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int i = (int)threadIdx.x + k * kSelThreads;
+            pb[k] = i < P ? pl[i] : -1;
+            pb2[k] = i + 1 < P ? pl[i + 1] : -1;
+        }
         load_regs(SlotSrc{{}, sc, P}, reg);
         preloaded = true;
         if (threadIdx.x == 0) L.flag = 0;
         __syncthreads();
-        for (int i = threadIdx.x; i < P; i += kSelThreads) {
-            const int b = pl[i];
-            const bool ok = b >= 0 && b < nb;
-            L.blocks[i] = ok ? b : -1;
-            L.slots[i] = i;
-            if (i + 1 < P) {
-                const int b2 = pl[i + 1];
-                if (b2 >= 0 && b2 < nb && !(ok && b < b2)) L.flag = 1;
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int i = (int)threadIdx.x + k * kSelThreads;
+            if (i < P) {
+                const int b = pb[k];
+                const bool ok = b >= 0 && b < nb;
+                L.blocks[i] = ok ? b : -1;
+                L.slots[i] = i;
+                if (i + 1 < P) {
+                    const int b2 = pb2[k];
+                    if (b2 >= 0 && b2 < nb && !(ok && b < b2)) L.flag = 1;
+                }
             }
         }
         __syncthreads();
@@ -1258,10 +1281,11 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     }
     __syncthreads();
 
-    // Paged caches: the cache row of each selected entry is written too (-1
-    // when beyond 32-bit row numbers), so attention needs no separate
-    // translation.  The selected ids are kept in LDS (the sort buffer is free
-    // by now) and translated after the compaction.
+    // The selected ids are kept in LDS (the sort buffer is free by now) and
+    // written out after the compaction, so no barrier of the compaction waits
+    // for global stores.  Paged caches: the cache row of each selected entry
+    // is written too (-1 when beyond 32-bit row numbers), so attention needs
+    // no separate translation.
     int32_t* tr = rows_out ? rows_out + (int64_t)r * K : nullptr;
     int* const sel_ids = reinterpret_cast<int*>(L.sortbuf);   // kMaxP 64-bit words hold kMaxK ids
     static_assert(sizeof(L.sortbuf) >= kMaxK * sizeof(int), "selected ids fit the sort buffer");
@@ -1272,17 +1296,19 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     if (!preloaded) load_regs(csrc, reg);
     const SelState st = radix_select(L.sh, phase, csrc, reg, K);
     int32_t* to = topk + (int64_t)r * K;
-    int nk = select_compact(L.sh, phase, csrc, reg, st, [&](int pos, int c, uint32_t) {
-        if (pos < K) {
-            const int j = cand[c >> 3] * 8 + (c & 7);
-            to[pos] = j;
-            if (tr) sel_ids[pos] = j;
-        }
+    // (a thread's kE items of a round are the 8 positions of one candidate
+    // block: its id is read once per round)
+    static_assert(kE == 8, "one candidate block per thread and round");
+    int nk = select_compact(L.sh, phase, csrc, reg, st, [&](int pos, int c, uint32_t, int blk) {
+        if (pos < K) sel_ids[pos] = blk * 8 + (c & 7);
+    }, [&](int rd) {
+        const int cb = rd * kSelThreads + (int)threadIdx.x;
+        return cb < ncb ? cand[cb] : 0;
     });
     nk = nk < K ? nk : K;
-    for (int i = nk + threadIdx.x; i < K; i += kSelThreads) {
-        to[i] = -1;
-        if (tr) tr[i] = -1;
+    for (int i = threadIdx.x; i < K; i += kSelThreads) {   // (select_compact ends with a barrier)
+        to[i] = i < nk ? sel_ids[i] : -1;
+        if (tr && i >= nk) tr[i] = -1;
     }
     if (tr) {   // (select_compact ends with a barrier: sel_ids is complete)
         const int seq = row_seq[r];
@@ -1291,6 +1317,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
             const int64_t ph = pm.row_on(pm.page_id(seq, j >> pm.shift), j);
             tr[i] = ph <= 0x7FFFFFFF ? (int32_t)ph : -1;
         }
+    }
+    if (FULL && pool_late >= 0) {
+        int32_t* po = pool_out + (int64_t)r * P;
+        for (int i = threadIdx.x; i < P; i += kSelThreads) po[i] = i < pool_late ? L.blocks[i] : -1;
     }
 }
 
