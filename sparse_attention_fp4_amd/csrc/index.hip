@@ -522,6 +522,33 @@ __device__ __forceinline__ int block_excl_sum(SelShared& sh, int& phase, int v, 
     return total;
 }
 
+// The same for two ints at once (one barrier).
+__device__ __forceinline__ void block_excl_sum2(SelShared& sh, int& phase, int v0, int v1, int& excl0, int& excl1,
+                                                int& total0, int& total1)
+{
+    const int lane = lane_id(), wave = threadIdx.x / CSA2_WAVE;
+    const int incl0 = wave_incl_sum(v0), incl1 = wave_incl_sum(v1);
+    int (*slot)[kSelWaves] = sh.wave_x[phase];
+    phase ^= 1;
+    if (lane == CSA2_WAVE - 1) {
+        slot[0][wave] = incl0;
+        slot[1][wave] = incl1;
+    }
+    __syncthreads();
+    int b0 = 0, b1 = 0, t0 = 0, t1 = 0;
+#pragma unroll
+    for (int i = 0; i < kSelWaves; ++i) {
+        const int x0 = slot[0][i], x1 = slot[1][i];
+        if (i < wave) { b0 += x0; b1 += x1; }
+        t0 += x0;
+        t1 += x1;
+    }
+    excl0 = b0 + incl0 - v0;
+    excl1 = b1 + incl1 - v1;
+    total0 = t0;
+    total1 = t1;
+}
+
 // Items are processed in rounds of kRound; within a round thread t holds the
 // kE consecutive items t*kE .. t*kE+kE-1 in registers (one 8-entry block of
 // candidates, or eight block maxima: two 16-byte loads).  Key 0 marks an
@@ -957,6 +984,50 @@ __device__ __forceinline__ int select_compact(SelShared& sh, int& phase, const S
     return gt_run + (eq_run < st.need ? eq_run : st.need);
 }
 
+// Ordered compaction for two thresholds in the same rounds and scans:
+// emit_a(pos, item) for the items of sa, emit_b(pos, item) for those of sb.
+// Returns both counts (before any cap).
+template <class Src, class EmitA, class EmitB>
+__device__ __forceinline__ int2 select_compact2(SelShared& sh, int& phase, const Src& src, const RegKeys& reg,
+                                                SelState sa, SelState sb, EmitA emit_a, EmitB emit_b)
+{
+    int gta_run = 0, eqa_run = 0, gtb_run = 0, eqb_run = 0;
+    for_rounds(src, reg, [&](int rd, const uint32_t (&key)[kE]) {
+        int gta = 0, eqa = 0, gtb = 0, eqb = 0;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            const uint32_t ma = key[e] & sa.mask, mb = key[e] & sb.mask;
+            gta += (key[e] && ma > sa.prefix) ? 1 : 0;
+            eqa += (key[e] && ma == sa.prefix) ? 1 : 0;
+            gtb += (key[e] && mb > sb.prefix) ? 1 : 0;
+            eqb += (key[e] && mb == sb.prefix) ? 1 : 0;
+        }
+        int bfa, bfb, tta, ttb;
+        block_excl_sum2(sh, phase, (gta << 16) | eqa, (gtb << 16) | eqb, bfa, bfb, tta, ttb);   // counts < 2^15
+        const int gta_b = gta_run + (bfa >> 16), eqa_b = eqa_run + (bfa & 0xFFFF);
+        const int gtb_b = gtb_run + (bfb >> 16), eqb_b = eqb_run + (bfb & 0xFFFF);
+        int outa = gta_b + (eqa_b < sa.need ? eqa_b : sa.need), outb = gtb_b + (eqb_b < sb.need ? eqb_b : sb.need);
+        int eqa_seen = eqa_b, eqb_seen = eqb_b;
+        const int i0 = rd * kRound + (int)threadIdx.x * kE;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+            const uint32_t ma = key[e] & sa.mask, mb = key[e] & sb.mask;
+            const bool a_gt = key[e] && ma > sa.prefix, a_eq = key[e] && ma == sa.prefix;
+            const bool b_gt = key[e] && mb > sb.prefix, b_eq = key[e] && mb == sb.prefix;
+            if (a_gt || (a_eq && eqa_seen < sa.need)) emit_a(outa++, i0 + e);
+            if (b_gt || (b_eq && eqb_seen < sb.need)) emit_b(outb++, i0 + e);
+            eqa_seen += a_eq ? 1 : 0;
+            eqb_seen += b_eq ? 1 : 0;
+        }
+        gta_run += tta >> 16;
+        eqa_run += tta & 0xFFFF;
+        gtb_run += ttb >> 16;
+        eqb_run += ttb & 0xFFFF;
+    });
+    __syncthreads();
+    return make_int2(gta_run + (eqa_run < sa.need ? eqa_run : sa.need), gtb_run + (eqb_run < sb.need ? eqb_run : sb.need));
+}
+
 // Bitonic sort (ascending) of n_pow2 64-bit keys in LDS.
 __device__ void bitonic_sort(unsigned long long* a, int n_pow2)
 {
@@ -1095,22 +1166,27 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
         // id(i)), whose keys `rg` holds.
         auto select_ab = [&](const auto& src, const RegKeys& rg, auto id) {
             SelState sa, sb;
-            if (P > 0) radix_select2(L.sh, phase, src, rg, big, small, sa, sb);
-            else sa = radix_select(L.sh, phase, src, rg, big);
-            na = select_compact(L.sh, phase, src, rg, sa, [&](int pos, int i, uint32_t, int) {
-                if (pos < big) L.blocks[pos] = id(i);
-            }, [](int) { return 0; });
-            na = na < big ? na : big;
-            if (P > 0 && na > small) {
+            if (P > 0) {
+                // A and B in the same rounds and scans (when A holds at most
+                // `small` items, B selects all of them: B = A)
+                radix_select2(L.sh, phase, src, rg, big, small, sa, sb);
                 int32_t* po = pool_out + (int64_t)r * P;
-                nsm = select_compact(L.sh, phase, src, rg, sb, [&](int pos, int i, uint32_t, int) {
-                    if (pos < small) {
-                        if (P >= K) L.cblk[pos] = id(i);
-                        else po[pos] = id(i);
-                    }
-                }, [](int) { return 0; });
-                nsm = nsm < small ? nsm : small;
+                const int2 nn = select_compact2(L.sh, phase, src, rg, sa, sb,
+                    [&](int pos, int i) { if (pos < big) L.blocks[pos] = id(i); },
+                    [&](int pos, int i) {
+                        if (pos < small) {
+                            if (P >= K) L.cblk[pos] = id(i);
+                            else po[pos] = id(i);
+                        }
+                    });
+                na = nn.x < big ? nn.x : big;
+                nsm = nn.y < small ? nn.y : small;
             } else {
+                sa = radix_select(L.sh, phase, src, rg, big);
+                na = select_compact(L.sh, phase, src, rg, sa, [&](int pos, int i, uint32_t, int) {
+                    if (pos < big) L.blocks[pos] = id(i);
+                }, [](int) { return 0; });
+                na = na < big ? na : big;
                 nsm = na;   // B = A
             }
         };
