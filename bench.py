@@ -58,14 +58,14 @@ TRAFFIC = {
     # profiles/sparse_attn_decode_64k.md: k_sparse_attn per call (two key splits merged in the kernel)
     (2, "sparse_attn", "83eb570d4d2e6a81"): 23483000,
     # profiles/sparse_attn_prefill_4096x135k.md: k_sparse_attn per call (four-wave workgroups)
-    (4, "sparse_attn", "83eb570d4d2e6a81"): 1645534000,
+    (4, "sparse_attn", "83eb570d4d2e6a81"): 1645300000,
     # profiles/index_full_decode_64k.md: k_index_score (Full) + k_select (Full) per call
-    (2, "index_full", "375c39e8797bac98"): 284870000,
+    (2, "index_full", "873020afc9d93890"): 284830000,
     # profiles/index_reindex_decode_64k.md: k_index_score (Reindex) + k_select (Reindex) per call
-    (2, "index_reindex", "375c39e8797bac98"): 74488000,
+    (2, "index_reindex", "873020afc9d93890"): 74530000,
     # profiles/index_full_prefill_4096x135k.md: k_index_bmax + k_select (blocks) + k_index_score (rescoring)
     # + k_select (Top-K), twice (two batches of 2,048 rows) per call
-    (4, "index_full", "375c39e8797bac98"): 1918618000,
+    (4, "index_full", "873020afc9d93890"): 1918400000,
 }
 CALL_SOURCE = {"sparse_attn": "attn.hip", "index_full": "index.hip", "index_reindex": "index.hip",
                "quantize_append": "quantize.hip"}
