@@ -111,7 +111,7 @@ def test_index_reindex_bad_and_duplicate_pool_ids(dbg):
     assert torch.equal(t_dup_r, call_reindex(csa2.lib(), qI, w, keys, row_len, drop, 64)[1])
 
 
-def call_attn(L, q, codes, scales, row_len, topk, swa, swa_len, W):
+def call_attn(L, q, codes, scales, row_len, topk, swa, swa_len, W, fp4mma=False):
     R, H, D = q.shape
     K = topk.shape[1]
     ss = torch.zeros(1, dtype=torch.int64, device=DEV)
@@ -121,15 +121,21 @@ def call_attn(L, q, codes, scales, row_len, topk, swa, swa_len, W):
     lse = torch.empty(R, H, device=DEV)
     nb = L.csa2_sparse_attn_workspace_bytes(R, H, D, K, W)
     ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=DEV)
-    st = L.csa2_sparse_attn(p(q), p(codes), p(scales), p(ss), p(rs), p(row_len), p(topk), K, p(swa), p(srs),
-                            p(swa_len), R, H, D, W, ctypes.c_float(D ** -0.5), p(out), p(lse), p(ws), ws.numel(),
-                            stream())
+    args = [p(q), p(codes), p(scales), p(ss), p(rs), p(row_len), p(topk), K, p(swa), p(srs), p(swa_len), R, H, D, W,
+            ctypes.c_float(D ** -0.5), p(out), p(lse)]
+    if fp4mma:
+        st = L.csa2_sparse_attn_fp4mma(*args, None, p(ws), ws.numel(), stream())
+    else:
+        st = L.csa2_sparse_attn(*args, p(ws), ws.numel(), stream())
     torch.cuda.synchronize()
     return st, out, lse
 
 
-def test_sparse_attn_bad_ids_and_window(dbg):
-    R, H, D, K, W, n = 2, 16, 128, 64, 16, 1000
+# two rows (eight-wave workgroups, split keys); 2,048 rows (four-wave
+# workgroups); the native-FP4 form
+@pytest.mark.parametrize("R,fp4mma", [(2, False), (2048, False), (2, True)])
+def test_sparse_attn_bad_ids_and_window(dbg, R, fp4mma):
+    H, D, K, W, n = 16, 128, 64, 16, 1000
     g = torch.Generator(device=DEV)
     g.manual_seed(3)
     kv = torch.randn(n, D, generator=g, device=DEV)
@@ -142,16 +148,16 @@ def test_sparse_attn_bad_ids_and_window(dbg):
     topk = torch.stack([torch.randperm(n, generator=g, device=DEV)[:K].sort().values for _ in range(R)]).int()
     topk[:, -4:] = -1
     swa_len = torch.full((R,), W, dtype=torch.int32, device=DEV)
-    st_d, o_d, l_d = call_attn(dbg, q, codes, scales, row_len, topk, swa, swa_len, W)
-    st_r, o_r, l_r = call_attn(csa2.lib(), q, codes, scales, row_len, topk, swa, swa_len, W)
+    st_d, o_d, l_d = call_attn(dbg, q, codes, scales, row_len, topk, swa, swa_len, W, fp4mma)
+    st_r, o_r, l_r = call_attn(csa2.lib(), q, codes, scales, row_len, topk, swa, swa_len, W, fp4mma)
     assert st_d == OK and st_r == OK
     assert torch.equal(o_d, o_r) and torch.equal(l_d, l_r)
     bad = topk.clone()
     bad[1, 3] = n + 5                        # past the row
-    assert call_attn(dbg, q, codes, scales, row_len, bad, swa, swa_len, W)[0] == DEVICE_CHECK
+    assert call_attn(dbg, q, codes, scales, row_len, bad, swa, swa_len, W, fp4mma)[0] == DEVICE_CHECK
     long_w = swa_len.clone()
     long_w[0] = W + 1                        # window longer than W
-    assert call_attn(dbg, q, codes, scales, row_len, topk, swa, long_w, W)[0] == DEVICE_CHECK
+    assert call_attn(dbg, q, codes, scales, row_len, topk, swa, long_w, W, fp4mma)[0] == DEVICE_CHECK
 
 
 def test_quantize_destination_past_cache(dbg):
