@@ -1024,8 +1024,11 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
         constexpr int NE = HT * NDT * 4;   // output values per lane
         float* const po = part_o + ((int64_t)r * HG + hg) * (NW * CSA2_WAVE * NE) + wave * CSA2_WAVE + lane;
         float* const pml = part_ml + ((int64_t)r * HG + hg) * (NH * 4);
-        if (threadIdx.x == 0)
-            second = __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0 ? 0 : 1;
+        int prev = 0;   // thread 0: the word before this workgroup's arrival
+        if (threadIdx.x == 0) {
+            prev = __hip_atomic_fetch_add(sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            second = prev == 0 ? 0 : 1;
+        }
         __syncthreads();
         if (!second) {
 #pragma unroll
@@ -1048,12 +1051,22 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
             return;
         }
         if (threadIdx.x == 0) {
-            int n = 0;
-            while ((__hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 4) == 0 && n < kSpinLimit) {
-                __builtin_amdgcn_s_sleep(2);
-                ++n;
+            // The first publishes about a microsecond after it arrives (its
+            // device-coherent stores complete first).  Device-coherent loads
+            // of the word slow each other down, so the second waits about
+            // that long (2,560 cycles) before its first look and then looks
+            // at short intervals; nothing to wait for if the first had
+            // already published when this one arrived.
+            if ((prev & 4) == 0) {
+                __builtin_amdgcn_s_sleep(40);
+                int n = 0;
+                while ((__hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 4) == 0 &&
+                       n < kSpinLimit) {
+                    __builtin_amdgcn_s_sleep(4);
+                    ++n;
+                }
+                CSA2_DCHECK(n >= kSpinLimit);
             }
-            CSA2_DCHECK(n >= kSpinLimit);
             __hip_atomic_store(sync, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
