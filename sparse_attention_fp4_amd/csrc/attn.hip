@@ -597,7 +597,18 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
     if (r >= R) return;   // padding of the XCD mapping (whole workgroup, before any barrier)
     const int h0 = hg * NH;
     const bool upper = lane >= 32;
-    const int f_begin = (int)((int64_t)nfrag * s / S), f_end = (int)((int64_t)nfrag * (s + 1) / S);
+    // Key splits take contiguous fragment ranges.  Two splits divide whole
+    // rounds, the first taking half of them rounded up: with an odd number of
+    // rounds the second finishes a round earlier and has published its partial
+    // when the first needs it, instead of both finishing a half-filled last
+    // round together with the merger then waiting for the publication.
+    int f_begin = (int)((int64_t)nfrag * s / S), f_end = (int)((int64_t)nfrag * (s + 1) / S);
+    if (S == 2) {
+        const int rounds = (nfrag + NW - 1) / NW;
+        const int mid = (rounds + 1) / 2 * NW < nfrag ? (rounds + 1) / 2 * NW : nfrag;
+        f_begin = s == 0 ? 0 : mid;
+        f_end = s == 0 ? mid : nfrag;
+    }
     const int32_t* topk_row = topk + (int64_t)r * K;
 
     // Loads are issued in dependency order so that waiting for one never waits
