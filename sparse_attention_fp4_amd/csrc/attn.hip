@@ -295,13 +295,14 @@ __device__ __forceinline__ void v_store(_Float16* vrow, int grp, int t, f16x8 kf
 // Query pieces (B operand of the score MFMAs; piece (ht, t) = k-step t of head
 // tile ht, this lane's column) and their a-parts for exact scores (split of q
 // described at the top of the file).
-template <int HT, int D>
-struct QueryRegs {   // the query in registers, the a-parts in LDS ([HT * KS][64])
-    const f16x8 (&qf)[HT][D / 32];
-    const f16x8* qa;
-    __device__ __forceinline__ f16x8 q(int ht, int t) const { return qf[ht][t]; }
-    __device__ __forceinline__ f16x8 a(int ht, int t) const { return qa[(ht * (D / 32) + t) * CSA2_WAVE]; }
-};
+// Rounding constant of a head's a-parts from its largest magnitude m:
+// 1.5 * 2^(E+12) with 2^E > m, E >= -13.
+__device__ __forceinline__ float a_part_const(float m)
+{
+    int E = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 0xFF) - 126 : -13;
+    E = E < -13 ? -13 : E;
+    return __uint_as_float((uint32_t)(E + 12 + 127) << 23 | 0x400000u);
+}
 template <int HT, int D>
 struct QueryRegsC {   // the query in registers, the a-parts formed from it
     const f16x8 (&qf)[HT][D / 32];
@@ -524,8 +525,8 @@ __host__ __device__ inline int pad_topk(int K) { return (K + kFrag - 1) / kFrag 
 __device__ __forceinline__ int frag_kind(int fr, int Kp) { return fr * kFrag >= Kp ? 1 : 0; }
 
 // LDS of one workgroup: one V tile per fragment slot of a round (slot w
-// filled by wave w), the a-part of the query (exact scores) and the round's
-// probabilities; before the loop the query is staged where the tiles go.
+// filled by wave w), the query's staging area (eight waves) and the round's
+// probabilities.
 template <int HT, int D, int NW>
 struct AttnSmem {
     static constexpr int KS = D / 32;
@@ -535,9 +536,10 @@ struct AttnSmem {
     static constexpr int VS = D + 8;               // V row stride in halves (conflict-free rows and transposes)
     static constexpr int kTile = kFrag * VS;       // halves per V tile
     static constexpr int kVBytes = NW * kTile * 2;
-    // [HT * KS][64] f16x8: the a-parts of the query (eight waves) or, in the
-    // native-FP4 form, the query itself; four waves form the a-parts from
-    // the query registers instead, which halves the LDS per workgroup
+    // [HT * KS][64] f16x8: with eight waves the fp16 query as staged before
+    // the loop (apart from the V tiles, so the first round needs no barrier
+    // for it), which the native-FP4 form keeps there; four waves stage it in
+    // the V tiles' space instead, which halves the LDS per workgroup
     static constexpr int kQaBytes = NW == kWaves ? HT * KS * CSA2_WAVE * 16 : 0;
     static constexpr int kPBytes = NW * 2 * HT * CSA2_WAVE * 8;       // [slot][hi, lo][HT][64] f16x4
     static constexpr int kBytes = kVBytes + kQaBytes + kPBytes;
@@ -663,65 +665,58 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
     CSA2_DCHECK(g_first && threadIdx.x == 0 && (nsw < 0 || nsw > W));
     nsw = nsw < 0 ? 0 : (nsw > W ? W : nsw);
     const int64_t base = PG ? 0 : seq_start[seq];
-    // Max |q| of each head over the wave's pieces: an integer max of the bf16
-    // magnitude bits (two per instruction), then over the lane groups.
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        u16x2 mx = {0, 0};
-#pragma unroll
-        for (int k = 0; k < NPW; ++k) {
-            const int P = k * NW + wave;
-            if (P < NQP && P / KS == ht) {
-                const uint32_t ws[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, ws[e] & 0x7FFF7FFFu));
-            }
-        }
-        uint32_t mb = mx[0] > mx[1] ? mx[0] : mx[1];
-        mb = umax_xor32(umax_xor16(mb));
-        if (grp == 0) wqm[wave][ht * 16 + col] = mb;
-    }
-    __syncthreads();
     // Query heads (B operand): lane (head col, grp) holds channels
     // step_ch(grp, t) .. +8 for k-step t.  bf16 -> fp16 is exact for |q| in
     // [2^-14, 65504].  a-part of a head: q rounded to a multiple of 2^(E-11),
     // 2^E > max|q| (E >= -13 keeps the quantum within fp16's subnormal grid).
-    // Adding and subtracting 1.5 * 2^(E+12) rounds to that multiple in fp32.
+    // Adding and subtracting Cq = 1.5 * 2^(E+12) rounds to that multiple in
+    // fp32.  The a-parts are formed from the fp16 query where they are used,
+    // and E from the largest fp16 magnitude of the head: below 2^-13, where
+    // fp16 may round a bf16 value, E is -13 either way.
     float Cq[HT];
+    if constexpr (NAT) {
+        // the native form needs Cq before the query goes to LDS: the maximum
+        // of each head over the waves' pieces (integer max of bf16 magnitudes)
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-        uint32_t mb = 0u;
+        for (int ht = 0; ht < HT; ++ht) {
+            u16x2 mx = {0, 0};
 #pragma unroll
-        for (int w = 0; w < NW; ++w) mb = max(mb, wqm[w][ht * 16 + col]);
-        const float m = __uint_as_float(mb << 16);
-        int E = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 0xFF) - 126 : -13;
-        E = E < -13 ? -13 : E;
-        Cq[ht] = __uint_as_float((uint32_t)(E + 12 + 127) << 23 | 0x400000u);
+            for (int k = 0; k < NPW; ++k) {
+                const int P = k * NW + wave;
+                if (P < NQP && P / KS == ht) {
+                    const uint32_t ws[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, ws[e] & 0x7FFF7FFFu));
+                }
+            }
+            uint32_t mb = mx[0] > mx[1] ? mx[0] : mx[1];
+            mb = umax_xor32(umax_xor16(mb));
+            if (grp == 0) wqm[wave][ht * 16 + col] = mb;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            uint32_t mb = 0u;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) mb = max(mb, wqm[w][ht * 16 + col]);
+            Cq[ht] = a_part_const(__uint_as_float(mb << 16));
+        }
     }
+    // Staging: wave w converts pieces w, w + NW, ... to fp16 and stores them
+    // in LDS, in the a-part region with eight waves (not needed there: the
+    // a-parts are formed from registers) and in the V tiles' space with four.
+    f16x8* const stage = NW == kWaves ? qa_s : qf_s;
 #pragma unroll
     for (int k = 0; k < NPW; ++k) {
         const int P = k * NW + wave;
         if (P >= NQP) continue;
-        float C = Cq[0];
-#pragma unroll
-        for (int ht = 1; ht < HT; ++ht) C = P / KS == ht ? Cq[ht] : C;
         const uint32_t ws[4] = {qraw[k].x, qraw[k].y, qraw[k].z, qraw[k].w};
-        f16x8 qv, av;
+        f16x8 qv;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float q32 = __uint_as_float(e & 1 ? ws[e >> 1] & 0xFFFF0000u : ws[e >> 1] << 16);
-            qv[e] = (_Float16)q32;
-            av[e] = (_Float16)((q32 + C) - C);
-        }
-        if constexpr (NAT) {
-            qa_s[P * CSA2_WAVE + lane] = qv;   // the query itself stays in LDS (its a-parts are formed when needed)
-        } else if constexpr (NW == kWaves) {
-            qf_s[P * CSA2_WAVE + lane] = qv;
-            qa_s[P * CSA2_WAVE + lane] = av;
-        } else {
-            qf_s[P * CSA2_WAVE + lane] = qv;   // (the a-parts are formed from the query registers)
-        }
+        for (int e = 0; e < 8; ++e)
+            qv[e] = (_Float16)__uint_as_float(e & 1 ? ws[e >> 1] & 0xFFFF0000u : ws[e >> 1] << 16);
+        stage[P * CSA2_WAVE + lane] = qv;   // (the native form keeps the query there)
     }
     const int p = grp >> 1;
     // The row's SWA rows through a buffer (reads outside it return zeros);
@@ -812,13 +807,22 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
     f16x8 qf[NAT ? 1 : HT][NAT ? 1 : KS];
     if constexpr (!NAT) {
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
+        for (int ht = 0; ht < HT; ++ht) {
+            u16x2 mx = {0, 0};
 #pragma unroll
             for (int t = 0; t < KS; ++t) {
-                qf[ht][t] = qf_s[(ht * KS + t) * CSA2_WAVE + lane];
+                qf[ht][t] = stage[(ht * KS + t) * CSA2_WAVE + lane];
+                const u32x4 w4 = __builtin_bit_cast(u32x4, qf[ht][t]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, w4[e] & 0x7FFF7FFFu));
             }
+            uint32_t mb = mx[0] > mx[1] ? mx[0] : mx[1];
+            mb = umax_xor32(umax_xor16(mb));   // over the head's lanes
+            Cq[ht] = a_part_const((float)__builtin_bit_cast(_Float16, (uint16_t)mb));
+        }
     }
-    __syncthreads();   // every wave holds the query: its staging space becomes the V tiles
+    if constexpr (NW != kWaves) __syncthreads();   // every wave holds the query: the V tiles' space is free
 
     // Softmax state (log2 domain), per head in the S^T layout (lane col =
     // head).  m_run, the reference maximum, is the same in every wave.  l_p:
@@ -839,7 +843,6 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
     const f16x8* const qa_lane = qa_s + lane;
     const auto qsrc = [&]() {
         if constexpr (NAT) return QueryLds<HT, D>{qa_lane, Cq};
-        else if constexpr (NW == kWaves) return QueryRegs<HT, D>{qf, qa_lane};
         else return QueryRegsC<HT, D>{qf, Cq};
     }();
     // the lane's PV operand address in slot 0's tile, at the wave's first channel
