@@ -295,6 +295,13 @@ __device__ __forceinline__ void v_store(_Float16* vrow, int grp, int t, f16x8 kf
 // Query pieces (B operand of the score MFMAs; piece (ht, t) = k-step t of head
 // tile ht, this lane's column) and their a-parts for exact scores (split of q
 // described at the top of the file).
+template <int HT, int D>
+struct QueryRegs {   // the query in registers, the a-parts in LDS ([HT * KS][64])
+    const f16x8 (&qf)[HT][D / 32];
+    const f16x8* qa;
+    __device__ __forceinline__ f16x8 q(int ht, int t) const { return qf[ht][t]; }
+    __device__ __forceinline__ f16x8 a(int ht, int t) const { return qa[(ht * (D / 32) + t) * CSA2_WAVE]; }
+};
 // Rounding constant of a head's a-parts from its largest magnitude m:
 // 1.5 * 2^(E+12) with 2^E > m, E >= -13.
 __device__ __forceinline__ float a_part_const(float m)
@@ -525,8 +532,9 @@ __host__ __device__ inline int pad_topk(int K) { return (K + kFrag - 1) / kFrag 
 __device__ __forceinline__ int frag_kind(int fr, int Kp) { return fr * kFrag >= Kp ? 1 : 0; }
 
 // LDS of one workgroup: one V tile per fragment slot of a round (slot w
-// filled by wave w), the query's staging area (eight waves) and the round's
-// probabilities.
+// filled by wave w), the a-parts of the query (exact scores, eight waves) and
+// the round's probabilities; before the loop the query is staged where the
+// tiles go.
 template <int HT, int D, int NW>
 struct AttnSmem {
     static constexpr int KS = D / 32;
@@ -536,10 +544,9 @@ struct AttnSmem {
     static constexpr int VS = D + 8;               // V row stride in halves (conflict-free rows and transposes)
     static constexpr int kTile = kFrag * VS;       // halves per V tile
     static constexpr int kVBytes = NW * kTile * 2;
-    // [HT * KS][64] f16x8: with eight waves the fp16 query as staged before
-    // the loop (apart from the V tiles, so the first round needs no barrier
-    // for it), which the native-FP4 form keeps there; four waves stage it in
-    // the V tiles' space instead, which halves the LDS per workgroup
+    // [HT * KS][64] f16x8: the a-parts of the query (eight waves) or, in the
+    // native-FP4 form, the query itself; four waves form the a-parts from
+    // the query registers instead, which halves the LDS per workgroup
     static constexpr int kQaBytes = NW == kWaves ? HT * KS * CSA2_WAVE * 16 : 0;
     static constexpr int kPBytes = NW * 2 * HT * CSA2_WAVE * 8;       // [slot][hi, lo][HT][64] f16x4
     static constexpr int kBytes = kVBytes + kQaBytes + kPBytes;
@@ -704,9 +711,9 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
         }
     }
     // Staging: wave w converts pieces w, w + NW, ... to fp16 and stores them
-    // in LDS, in the a-part region with eight waves (not needed there: the
-    // a-parts are formed from registers) and in the V tiles' space with four.
-    f16x8* const stage = NW == kWaves ? qa_s : qf_s;
+    // in LDS, in the V tiles' space (the native form: in its query region,
+    // where the query stays).
+    f16x8* const stage = NAT ? qa_s : qf_s;
 #pragma unroll
     for (int k = 0; k < NPW; ++k) {
         const int P = k * NW + wave;
@@ -822,7 +829,25 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
             Cq[ht] = a_part_const((float)__builtin_bit_cast(_Float16, (uint16_t)mb));
         }
     }
-    if constexpr (NW != kWaves) __syncthreads();   // every wave holds the query: the V tiles' space is free
+    if constexpr (!NAT && NW == kWaves) {
+        // eight waves: the a-parts of the wave's pieces go to LDS once (the
+        // exact-score path reads them there)
+#pragma unroll
+        for (int k = 0; k < NPW; ++k) {
+            const int P = k * NW + wave;
+            if (P >= NQP) continue;
+            float C = Cq[0];
+#pragma unroll
+            for (int ht = 1; ht < HT; ++ht) C = P / KS == ht ? Cq[ht] : C;
+            const f16x8 v = stage[P * CSA2_WAVE + lane];
+            f16x8 av;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) av[e] = (_Float16)(((float)v[e] + C) - C);
+            qa_s[P * CSA2_WAVE + lane] = av;
+        }
+    }
+    // every wave holds the query and the a-parts are in LDS: the V tiles' space is free
+    if constexpr (!NAT) __syncthreads();
 
     // Softmax state (log2 domain), per head in the S^T layout (lane col =
     // head).  m_run, the reference maximum, is the same in every wave.  l_p:
@@ -843,6 +868,7 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
     const f16x8* const qa_lane = qa_s + lane;
     const auto qsrc = [&]() {
         if constexpr (NAT) return QueryLds<HT, D>{qa_lane, Cq};
+        else if constexpr (NW == kWaves) return QueryRegs<HT, D>{qf, qa_lane};
         else return QueryRegsC<HT, D>{qf, Cq};
     }();
     // the lane's PV operand address in slot 0's tile, at the wave's first channel
