@@ -380,6 +380,12 @@ def with_cache(wl):
     ("d128_h8_k512_w64_single_row_4_splits", [4096], 128, 8, 512, 64),
     ("d512_h64_rows24_2_splits", [60 + (977 * i) % 20000 for i in range(24)], 512, 64, 512, 128),
     ("d512_h64_rows24_2_splits_one_empty", [5] + [3000 + 11 * i for i in range(23)], 512, 64, 512, 128),
+    # two splits at whole rounds of 8 fragments: 33 fragments (24 + 9), 16 (8 + 8), 17 (16 + 1: the second split
+    # holds only the SWA fragment), and one head group per row (100 rows x 16 heads)
+    ("d512_h64_rows24_2_splits_k512_w8", [700 + (613 * i) % 9000 for i in range(24)], 512, 64, 512, 8),
+    ("d512_h64_rows24_2_splits_k256_w0", [700 + (613 * i) % 9000 for i in range(24)], 512, 64, 256, 0),
+    ("d512_h64_rows24_2_splits_k256_w16", [700 + (613 * i) % 9000 for i in range(24)], 512, 64, 256, 16),
+    ("d512_h16_rows100_2_splits", [400 + (211 * i) % 5000 for i in range(100)], 512, 16, 512, 128),
     ("d512_h64_student_outliers", [9000, 3000, 20000], 512, 64, 512, 128),
     ("d128_h8_student_outliers_nosplit_rows", [500 + 11 * i for i in range(140)], 128, 8, 64, 32),
     ("d512_h64_k512_w128_split", [9000, 700, 30000], 512, 64, 512, 128),
