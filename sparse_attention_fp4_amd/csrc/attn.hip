@@ -45,11 +45,11 @@
 // head is split as q = a + b, a being q rounded to a multiple of 2^(E-11) with
 // 2^E > max|q| of the head (11 bits, exact in fp16), b the small remainder.
 // Within one scale group every a*k product is then an integer multiple of one
-// quantum and the 16 products sum to less than 2^24 quanta, so an MFMA
-// restricted to one group (the other lane half masked to zero) returns the
-// group sum exactly; the group sums are accumulated in fp64, and K b^T (small,
-// nonzero only for channels with |q| < max|q|/16) is added from an ordinary
-// MFMA chain.
+// quantum and the 16 products sum to less than 2^24 quanta, so MFMAs
+// restricted to one group (a lane group's two k-steps over it, the other lane
+// groups masked to zero) return the group sum exactly; the group sums are
+// accumulated in fp64, and K b^T (small, nonzero only for channels with
+// |q| < max|q|/16) is added from an ordinary MFMA chain.
 #include "csa2_device.h"
 #include "csa2_host.h"
 
@@ -62,24 +62,17 @@ constexpr int kWavesMany = 4;       // the same with many rows: half the LDS, tw
 constexpr float kLazy = 8.0f;       // log2-domain slack before a running max is raised
 constexpr int kMaxPlanSplits = 8;   // key splits per row, at most
 
-// Channel layout of a lane (col, grp), p = grp / 2, hf = grp % 2: k-step t
-// (t < KS = D/32) covers the 8 channels
-//   D/2*p + 16*t + 8*hf .. +8,
-// i.e. half hf of scale group KS*p + t.  In each MFMA the lanes with p = 0
-// thus hold one whole scale group and those with p = 1 another.
+// Channel layout of a lane (col, grp): k-step t (t < KS = D/32) covers the
+// 8 channels
+//   D/4*grp + 8*t .. +8,
+// so each lane's k-steps run through one contiguous quarter of the channels,
+// which is the block of a key's bytes it loads (no exchange between lanes),
+// and k-steps 2u, 2u+1 of a lane share scale group D/64*grp + u.  In each
+// MFMA the four lane groups hold 8 channels of four different scale groups.
 template <int D>
 __device__ __forceinline__ int step_ch(int grp, int t)
 {
-    return (D / 2) * (grp >> 1) + 16 * t + 8 * (grp & 1);
-}
-
-// Local unit holding piece t after FragRaw::unpair(): pieces 0 .. KS/2-1 sit
-// at even units, the rest at odd ones.
-template <int D>
-__device__ __forceinline__ constexpr int kperm(int t)
-{
-    constexpr int KS = D / 32;
-    return t < KS / 2 ? 2 * t : 2 * t - KS + 1;
+    return (D / 4) * grp + 8 * t;
 }
 
 // Main entries are read through 64-bit addresses once the slot's entry is
@@ -109,39 +102,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 template <int D>
 struct FragRaw {
     static constexpr int KS = D / 32;
-    static constexpr int NSC = KS / 4;
+    static constexpr int NSC = KS / 8 > 1 ? KS / 8 : 1;   // words of the lane's KS/2 scale bytes (D = 128: one
+                                                        // word, its two bytes in the low half)
     uint32_t raw[2 * KS];
     uint32_t sc[NSC];
-    f16x2 sp[KS / 2];   // scales of pieces 2u, 2u+1 as fp16 (set by unpair())
+    _Float16 sp[KS / 2];   // the lane's scale groups as fp16 (set by scales_f16())
     bool valid, is_main;
 
     // SWA row i of the lane's slot (vs: the slot holds one) through rw, the
-    // buffer over the row's window.  The lane pair (p, 0), (p, 1) of a row
-    // needs one contiguous block of D/2 bytes; each lane loads its half into
-    // consecutive words and unpair() exchanges the halves.  An absent row
-    // gets the offset kNoKey and reads as zeros; the loads are unconditional.
-    __device__ __forceinline__ void load_swa(bool vs, int i, int p, int hf, __amdgpu_buffer_rsrc_t rw)
+    // buffer over the row's window: the lane's quarter of the row (D/4
+    // contiguous bytes) into consecutive words.  An absent row gets the offset
+    // kNoKey and reads as zeros; the loads are unconditional.
+    __device__ __forceinline__ void load_swa(bool vs, int i, int grp, __amdgpu_buffer_rsrc_t rw)
     {
         valid = vs;
         is_main = false;
-        const uint32_t off1 = vs ? (uint32_t)i * D + (D / 2) * p + (D / 4) * hf : kNoKey;
+        const uint32_t off1 = vs ? (uint32_t)i * D + (D / 4) * grp : kNoKey;
 #pragma unroll
-        for (int u = 0; u < KS / 4; ++u) {
+        for (int u = 0; u < KS / 2; ++u) {
             const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, off1 + 16 * u, 0, 0);
             raw[4 * u] = v[0]; raw[4 * u + 1] = v[1]; raw[4 * u + 2] = v[2]; raw[4 * u + 3] = v[3];
-        }
-#pragma unroll
-        for (int u = 0; u < KS / 4; ++u) {   // second half of the lane's bytes
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, off1 + D / 8 + 16 * u, 0, 0);
-            raw[KS + 4 * u] = v[0]; raw[KS + 4 * u + 1] = v[1]; raw[KS + 4 * u + 2] = v[2]; raw[KS + 4 * u + 3] = v[3];
         }
         // (the scale words are loaded too, as zeros from past the buffer's
         // end, so that on either kind of fragment every raw register is
         // written by a load: the loop then waits on loads in issue order)
-        if constexpr (NSC == 4) {
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rw, kNoKey, 0, 0);
-            sc[0] = v[0]; sc[1] = v[1]; sc[2] = v[2]; sc[3] = v[3];
-        } else if constexpr (NSC == 2) {
+        if constexpr (NSC == 2) {
             const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rw, kNoKey, 0, 0);
             sc[0] = v[0]; sc[1] = v[1];
         } else {
@@ -151,12 +136,11 @@ struct FragRaw {
 
     // The lane's bytes of main entry j (vm: the slot holds a visible entry)
     // from codes / scales, which start at the row's first entry (or at the
-    // cache's first row in the cache-row form): its D/4-byte half-block of
-    // codes (the lane pair exchanges halves in unpair()) and its KS scale
-    // bytes, through 64-bit addresses, so entries anywhere in a cache of any
-    // size are reachable; an absent slot loads nothing and keeps zeros.
-    __device__ __forceinline__ void load_row(bool vm, int j, int p, int hf, const uint8_t* codes,
-                                             const uint8_t* scales)
+    // cache's first row in the cache-row form): the codes of its quarter of
+    // the channels (D/8 bytes) and the KS/2 scale bytes of their groups,
+    // through 64-bit addresses, so entries anywhere in a cache of any size are
+    // reachable; an absent slot loads nothing and keeps zeros.
+    __device__ __forceinline__ void load_row(bool vm, int j, int grp, const uint8_t* codes, const uint8_t* scales)
     {
         valid = vm;
         is_main = true;
@@ -165,70 +149,38 @@ struct FragRaw {
 #pragma unroll
         for (int w = 0; w < NSC; ++w) sc[w] = 0u;
         if (vm) {
-            const uint8_t* pc = codes + (uint64_t)(uint32_t)j * (D / 2) + (D / 4) * p + (D / 8) * hf;
+            const uint8_t* pc = codes + (uint64_t)(uint32_t)j * (D / 2) + (D / 8) * grp;
 #pragma unroll
             for (int u = 0; u < KS / 4; ++u) {
                 const u32x4 v = *reinterpret_cast<const u32x4*>(pc + 16 * u);
                 raw[4 * u] = v[0]; raw[4 * u + 1] = v[1]; raw[4 * u + 2] = v[2]; raw[4 * u + 3] = v[3];
             }
-            const uint8_t* ps = scales + (uint64_t)(uint32_t)j * (D / 16) + KS * p;
-            if constexpr (NSC == 4) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(ps);
-                sc[0] = v[0]; sc[1] = v[1]; sc[2] = v[2]; sc[3] = v[3];
-            } else if constexpr (NSC == 2) {
-                const u32x2 v = *reinterpret_cast<const u32x2*>(ps);
+            const uint8_t* ps = scales + (uint64_t)(uint32_t)j * (D / 16);
+            if constexpr (KS / 2 == 8) {
+                const u32x2 v = *reinterpret_cast<const u32x2*>(ps + 8 * grp);
                 sc[0] = v[0]; sc[1] = v[1];
-            } else {
-                sc[0] = *reinterpret_cast<const uint32_t*>(ps);
+            } else if constexpr (KS / 2 == 4) {
+                sc[0] = *reinterpret_cast<const uint32_t*>(ps + 4 * grp);
+            } else {   // two bytes: the word of the lane pair, the lane's half shifted down
+                sc[0] = *reinterpret_cast<const uint32_t*>(ps + 4 * (grp >> 1)) >> (16 * (grp & 1));
             }
         }
     }
 
-    // Unit u of a pair's block (a code word, or 8 FP8 bytes) is piece u/2 of
-    // half u%2; after load() lane hf holds units KS*hf .. KS*hf + KS-1 in
-    // consecutive words.  v_permlane16_swap(x, y) exchanges row 1 of x with
-    // row 0 of y (rows are the 16-lane groups: rows 0/1 are the halves hf =
-    // 0/1 of p = 0, rows 2/3 those of p = 1).  Swapping local units 2v and
-    // 2v+1 leaves the lane's own half of piece t in local unit kperm(t): code
-    // word kperm(t), or FP8 words 2 kperm(t) and 2 kperm(t) + 1.  KIND: 0
-    // Top-K slots only, 1 SWA rows only, 2 either (chosen per lane).
+    // The scale bytes as fp16, converted before the next fragment's loads are
+    // issued, so that nothing after those loads reads the raw scale words.
+    // KIND: 0 Top-K slots only, 1 SWA rows only (no scales).
     template <int KIND>
-    __device__ __forceinline__ void unpair()
+    __device__ __forceinline__ void scales_f16()
     {
-        // The scales are converted here, before the next fragment's loads are
-        // issued, so that nothing after those loads reads the raw scale words.
         if (KIND != 1) {
 #pragma unroll
-            for (int u = 0; u < KS / 2; ++u)
-                sp[u] = (u & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[u >> 1], 1.0f, true)
-                                : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[u >> 1], 1.0f, false);
-        }
-        uint32_t c[KS], w[2 * KS];
-#pragma unroll
-        for (int v = 0; v < KS / 2; ++v) {
-            if (KIND != 1) {
-                const auto r = __builtin_amdgcn_permlane16_swap(raw[2 * v], raw[2 * v + 1], false, false);
-                c[2 * v] = r[0];
-                c[2 * v + 1] = r[1];
+            for (int u = 0; u < KS / 4; ++u) {
+                const f16x2 v = (u & 1) ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[u >> 1], 1.0f, true)
+                                        : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[u >> 1], 1.0f, false);
+                sp[2 * u] = v[0];
+                sp[2 * u + 1] = v[1];
             }
-            if (KIND != 0) {
-                const auto ra = __builtin_amdgcn_permlane16_swap(raw[4 * v], raw[4 * v + 2], false, false);
-                const auto rb = __builtin_amdgcn_permlane16_swap(raw[4 * v + 1], raw[4 * v + 3], false, false);
-                w[4 * v] = ra[0];
-                w[4 * v + 2] = ra[1];
-                w[4 * v + 1] = rb[0];
-                w[4 * v + 3] = rb[1];
-            }
-        }
-        if (KIND == 0) {
-#pragma unroll
-            for (int k = 0; k < KS; ++k) raw[k] = c[k];
-        } else if (KIND == 1) {
-#pragma unroll
-            for (int k = 0; k < 2 * KS; ++k) raw[k] = w[k];
-        } else {
-#pragma unroll
-            for (int k = 0; k < 2 * KS; ++k) raw[k] = is_main ? (k < KS ? c[k] : 0u) : w[k];
         }
     }
 
@@ -255,25 +207,25 @@ struct FragRaw {
 };
 
 // Dequantise k-step t (8 channels) of the lane's key to fp16.
-//   MODE 0: FP4 codes (word kperm(t)) times the group's E4M3 scale (scale
-//           byte t of the lane's KS scale bytes);
-//   MODE 1: FP8 E4M3 bytes (words 2 kperm(t), +1), unscaled;
+//   MODE 0: FP4 codes (word t) times the group's E4M3 scale (scale byte t/2
+//           of the lane's KS/2 scale bytes);
+//   MODE 1: FP8 E4M3 bytes (words 2t, 2t+1), unscaled;
 //   MODE 2: either, chosen per lane.
 template <int MODE, int D>
 __device__ __forceinline__ f16x8 dequant_step(const FragRaw<D>& fr, int t)
 {
     f16x8 a, b;
     if (MODE != 1) {
-        const uint32_t c = fr.raw[kperm<D>(t)];
+        const uint32_t c = fr.raw[t];
         const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0);
         const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1);
         const f16x2 a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2);
         const f16x2 a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3);
-        const _Float16 s = fr.sp[t >> 1][t & 1];
+        const _Float16 s = fr.sp[t >> 1];
         a = (f16x8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]} * s;
     }
     if (MODE != 0) {
-        const uint32_t c0 = fr.raw[2 * kperm<D>(t)], c1 = fr.raw[2 * kperm<D>(t) + 1];
+        const uint32_t c0 = fr.raw[2 * t], c1 = fr.raw[2 * t + 1];
         const f16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, false);
         const f16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, true);
         const f16x2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1, 1.0f, false);
@@ -367,10 +319,9 @@ __device__ __forceinline__ void v_frag(const FragRaw<D>& fr, _Float16* vrow, int
 
 // The same fragment with S computed exactly as (hi, lo) = K a^T + K b^T
 // (split of q described at the top of the file); b = q - a is an exact fp16
-// subtraction (the difference is q's bits below the quantum of a).  upper:
-// lane >= 32.
+// subtraction (the difference is q's bits below the quantum of a).
 template <int HT, int D, class QS>
-__device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const QS& qs, bool upper, _Float16* vrow, int grp,
+__device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const QS& qs, _Float16* vrow, int grp,
                                              f32x4 (&acc)[HT], f32x4 (&lo)[HT])
 {
     constexpr int KS = D / 32;
@@ -383,21 +334,49 @@ __device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const QS& qs,
         for (int i = 0; i < 4; ++i) ex[ht][i] = 0.0;
     }
     const f16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
+    // k-steps 2u and 2u + 1 of a lane hold the two halves of one scale group
+    // (D/64 grp + u).  One head tile: two products chained per lane group sum
+    // its 16 channels; more (fewer registers to spare): one product per
+    // k-step and lane group, 8 channels.
+    if constexpr (HT == 1) {
 #pragma unroll
-    for (int t = 0; t < KS; ++t) {
-        const f16x8 kf = dequant_step<2, D>(fr, t);
-        v_store<D>(vrow, grp, t, kf);
-        const f16x8 k_lo = upper ? zero : kf;     // scale group t (p = 0)
-        const f16x8 k_hi = upper ? kf : zero;     // and scale group KS + t (p = 1)
+        for (int t = 0; t < KS; t += 2) {
+            const f16x8 kf0 = dequant_step<2, D>(fr, t), kf1 = dequant_step<2, D>(fr, t + 1);
+            v_store<D>(vrow, grp, t, kf0);
+            v_store<D>(vrow, grp, t + 1, kf1);
+            const f16x8 a0 = qs.a(0, t), a1 = qs.a(0, t + 1);
+            const f16x8 b0 = qs.q(0, t) - a0, b1 = qs.q(0, t + 1) - a1;
+            sb[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf0, b0, sb[0], 0, 0, 0);
+            sb[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf1, b1, sb[0], 0, 0, 0);
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-            const f16x8 a = qs.a(ht, t);
-            const f16x8 b = qs.q(ht, t) - a;
-            sb[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, b, sb[ht], 0, 0, 0);
-            const f32x4 g0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_lo, a, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-            const f32x4 g1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_hi, a, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            for (int g = 0; g < 4; ++g) {
+                // lane group g's channels of its scale group, the others zero
+                const f16x8 k0 = grp == g ? kf0 : zero, k1 = grp == g ? kf1 : zero;
+                f32x4 gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(k0, a0, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                gs = __builtin_amdgcn_mfma_f32_16x16x32_f16(k1, a1, gs, 0, 0, 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ex[ht][i] += (double)g0[i] + (double)g1[i];
+                for (int i = 0; i < 4; ++i) ex[0][i] += (double)gs[i];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < KS; ++t) {
+            const f16x8 kf = dequant_step<2, D>(fr, t);
+            v_store<D>(vrow, grp, t, kf);
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) {
+                const f16x8 a = qs.a(ht, t);
+                const f16x8 b = qs.q(ht, t) - a;
+                sb[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, b, sb[ht], 0, 0, 0);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f16x8 kg = grp == g ? kf : zero;
+                    const f32x4 gs =
+                        __builtin_amdgcn_mfma_f32_16x16x32_f16(kg, a, (f32x4){0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) ex[ht][i] += (double)gs[i];
+                }
+            }
         }
     }
 #pragma unroll
@@ -416,23 +395,22 @@ __device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const QS& qs,
 // operand and the query as E4M3 (B operand), each lane block of 32 values with
 // one power-of-two (E8M0) scale.  Lane (key, g) holds, for k-step T < D/128,
 // the 32 channels g*D/4 + 32T .. +31: exactly the 16 code bytes it loaded as
-// words 4T .. 4T+3 (before unpair()), whose two E4M3 scale bytes are those of
-// groups g*D/64 + 2T and + 1 (bytes (D/64)*hf + 2T and + 1 of the lane's KS
-// scale bytes).  The products equal the dequantised ones only where both bytes
+// words 4T .. 4T+3, whose two E4M3 scale bytes are those of groups
+// g*D/64 + 2T and + 1 (bytes 2T and 2T + 1 of the lane's scale bytes).  The
+// products equal the dequantised ones only where both bytes
 // are the same power of two, which nat_key_scales() checks; the query side is
 // checked once per workgroup, where the query's operand layout (which pairs
 // each lane's values with the keys' in a fixed interleave) is built.  An
 // absent key has zero codes, so any scale gives it zero products.
 template <int D>
-__device__ __forceinline__ bool nat_key_scales(const FragRaw<D>& f, int hf, uint32_t& e8)
+__device__ __forceinline__ bool nat_key_scales(const FragRaw<D>& f, uint32_t& e8)
 {
     bool ok = true;
     e8 = 0u;
 #pragma unroll
     for (int T = 0; T < D / 128; ++T) {
-        const int b0 = 2 * T, b1 = D / 64 + 2 * T;   // the pair's first byte for hf = 0, 1 (even: one word holds both)
-        const uint32_t w0 = f.sc[b0 >> 2] >> (8 * (b0 & 3)), w1 = f.sc[b1 >> 2] >> (8 * (b1 & 3));
-        const uint32_t w = hf ? w1 : w0;
+        const int b = 2 * T;   // the pair's first byte among the lane's (even: one word holds both)
+        const uint32_t w = f.sc[b >> 2] >> (8 * (b & 3));
         const uint32_t s0 = w & 0xFFu, s1 = (w >> 8) & 0xFFu;
         // E4M3 2^(e - 7) with e = bits 6..3, positive, mantissa zero -> E8M0 e + 120
         ok = ok && s0 == s1 && (s0 & 0x87u) == 0u && s0 != 0u;
@@ -593,7 +571,7 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
 
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform: branches on it are scalar
-    const int col = lane & 15, grp = lane >> 4, hf = grp & 1;
+    const int col = lane & 15, grp = lane >> 4;
     int r, hg, s;   // row, head group, key split
     bool g_first;   // the row's first workgroup
     {
@@ -605,7 +583,6 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
     (void)g_first;
     if (r >= R) return;   // padding of the XCD mapping (whole workgroup, before any barrier)
     const int h0 = hg * NH;
-    const bool upper = lane >= 32;
     // Key splits take contiguous fragment ranges.  Two splits divide whole
     // rounds, the first taking half of them rounded up: with an odd number of
     // rounds the second finishes a round earlier and has published its partial
@@ -725,7 +702,6 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
             qv[e] = (_Float16)__uint_as_float(e & 1 ? ws[e >> 1] & 0xFFFF0000u : ws[e >> 1] << 16);
         stage[P * CSA2_WAVE + lane] = qv;   // (the native form keeps the query there)
     }
-    const int p = grp >> 1;
     // The row's SWA rows through a buffer (reads outside it return zeros);
     // main entries are read through 64-bit addresses (FragRaw::load_row),
     // so entry ids are bounded only by the row's length.
@@ -739,11 +715,11 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
         const bool vs = i >= 0 && i < nsw;
         const int iw = PG ? (head + i >= W ? head + i - W : head + i) : i;
         if (frag_kind(fr_, Kp) == 0)
-            f.load_row(vm, j, p, hf, codes + base * (D / 2), scales + base * (D / 16));
+            f.load_row(vm, j, grp, codes + base * (D / 2), scales + base * (D / 16));
         else
-            f.load_swa(vs, iw, p, hf, rw);
+            f.load_swa(vs, iw, grp, rw);
     };
-    FragRaw<D> cur, nxt;   // cur is unpaired in place at the start of its round
+    FragRaw<D> cur, nxt;   // cur's scales are converted at the start of its round
     if (fw < f_end) load_frag(cur, fw, idx_c);
 
     // Native form: the query as E4M3 with one power-of-two scale per lane
@@ -904,7 +880,7 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
             if constexpr (NAT) {
                 if (kind == 0 && nat_q) {
                     uint32_t ke8;
-                    const bool ok = nat_key_scales<D>(cur, hf, ke8);
+                    const bool ok = nat_key_scales<D>(cur, ke8);
                     nat = __ballot(!ok) == 0ull;
                     if (nat) {
                         s_frag_nat<HT, D>(cur, ke8, qn, qe8, sh);
@@ -912,8 +888,7 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
                     }
                 }
             }
-            if (kind == 0) cur.template unpair<0>();
-            else cur.template unpair<1>();
+            if (kind == 0) cur.template scales_f16<0>();
             const uint64_t vb = __ballot(cur.valid);   // bit k: key k of the fragment (lanes 0..15)
             // prefetch: raw bytes of the wave's next fragment, Top-K entry of the one after
             {
@@ -924,7 +899,7 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
                 }
             }
             if (nat) v_frag<0, D>(cur, vrow, grp);
-            else if (precise) s_frag_exact<HT, D>(cur, qsrc, upper, vrow, grp, sh, sl);
+            else if (precise) s_frag_exact<HT, D>(cur, qsrc, vrow, grp, sh, sl);
             else if (kind == 0) s_frag<0, HT, D>(cur, qsrc, vrow, grp, sh);
             else s_frag<1, HT, D>(cur, qsrc, vrow, grp, sh);
             // S^T lane layout: head h0 + 16 ht + col, keys 4 grp + i.
