@@ -563,7 +563,7 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
     __shared__ float4 fmx[NH][NW / 4];   // per head: each slot's largest logit of the head
     __shared__ float wsum[2][NW][NH];    // at the end: each wave's sums (PV weights, unrounded)
     __shared__ uint32_t wqm[NW][NH];     // per wave: bf16 bits of the max |q| of each head over its pieces
-    __shared__ int fprec[NW];            // per slot: exact scores, two-part probabilities
+    __shared__ __attribute__((aligned(16))) int fprec[NW];   // per slot: exact scores, two-part probabilities
     _Float16* const vtiles = reinterpret_cast<_Float16*>(smem);
     f16x8* const qa_s = reinterpret_cast<f16x8*>(smem + SM::kVBytes);                  // [HT * KS][64]
     f16x4* const p_s = reinterpret_cast<f16x4*>(smem + SM::kVBytes + SM::kQaBytes);   // [slot][2][HT][64]
@@ -917,6 +917,15 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
         }
         if (lane == 0) fprec[wave] = precise ? 1 : 0;
         __syncthreads();   // the round's V tiles, maxima and flags
+        // The round's precise slots as one mask, their flags read together
+        // (a read per slot ahead of its branch would chain the LDS latencies).
+        uint32_t pmask = 0u;
+#pragma unroll
+        for (int w4 = 0; w4 < NW / 4; ++w4) {
+            const int4 f = reinterpret_cast<const int4*>(fprec)[w4];
+            pmask |= ((f.x ? 1u : 0u) | (f.y ? 2u : 0u) | (f.z ? 4u : 0u) | (f.w ? 8u : 0u)) << (4 * w4);
+        }
+        pmask = __builtin_amdgcn_readfirstlane(pmask) & ((1u << nslot) - 1u);
 
         // ---- reference maximum of each head (the same in every wave): raised
         // to the round's maximum when that exceeds it by more than kLazy (a
@@ -992,10 +1001,9 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
                 for (int j = j0; j < nslot; ++j)
                     pv_slots<1, HT, NDT>(p_s + (j * 2 * HT) * CSA2_WAVE + lane, 0, vr0 + j * SM::kTile, 0, o);
         }
-        for (int j = 0; j < nslot; ++j) {
-            if (fprec[j]) {
-                pv_slots<1, HT, NDT>(p_s + ((j * 2 + 1) * HT) * CSA2_WAVE + lane, 0, vr0 + j * SM::kTile, 0, o);
-            }
+        for (uint32_t m = pmask; m != 0u; m &= m - 1u) {
+            const int j = __builtin_ctz(m);
+            pv_slots<1, HT, NDT>(p_s + ((j * 2 + 1) * HT) * CSA2_WAVE + lane, 0, vr0 + j * SM::kTile, 0, o);
         }
         cur = nxt;
         __syncthreads();   // the round's tiles and probabilities are consumed
