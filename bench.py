@@ -56,9 +56,9 @@ MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp16": 2500.0}   # dense, MI355X
 # were taken on).  Reported as null whenever that source has changed since.
 TRAFFIC = {
     # profiles/sparse_attn_decode_64k.md: k_sparse_attn per call (two key splits merged in the kernel)
-    (2, "sparse_attn", "e30496094d496edd"): 23512100,
+    (2, "sparse_attn", "a62557f6c8883823"): 23495680,
     # profiles/sparse_attn_prefill_4096x135k.md: k_sparse_attn per call (four-wave workgroups)
-    (4, "sparse_attn", "e30496094d496edd"): 1600851600,
+    (4, "sparse_attn", "a62557f6c8883823"): 1562032435,
     # profiles/index_full_decode_64k.md: k_index_score (Full) + k_select (Full) per call
     (2, "index_full", "873020afc9d93890"): 284830000,
     # profiles/index_reindex_decode_64k.md: k_index_score (Reindex) + k_select (Reindex) per call

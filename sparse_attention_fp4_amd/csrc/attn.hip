@@ -1096,14 +1096,25 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
         // merge: o = (o_a 2^(m_a - M) + o_b 2^(m_b - M)) / L, per head; each
         // product is rounded on its own (no contraction into an fma) and the
         // sum commutes, so the result does not depend on which split arrived
-        // first.
+        // first.  The partial's statistics and values are requested together
+        // (one round trip).
+        float mlb[HT][3], obv[HT][NDT][4];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+            const float* const ml = pml + (ht * 16 + col) * 4;
+#pragma unroll
+            for (int k = 0; k < 3; ++k) mlb[ht][k] = __hip_atomic_load(ml + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    obv[ht][dt][i] = __hip_atomic_load(po + ((ht * NDT + dt) * 4 + i) * (NW * CSA2_WAVE),
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
 #pragma clang fp contract(off)
-            const float* const ml = pml + (ht * 16 + col) * 4;
-            const float Mb = __hip_atomic_load(ml + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float Lb = __hip_atomic_load(ml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const float Leb = __hip_atomic_load(ml + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float Mb = mlb[ht][0], Lb = mlb[ht][1], Leb = mlb[ht][2];
             float M = -INFINITY;
             if (Lh[ht] > 0.0f) M = Mh[ht];
             if (Lb > 0.0f) M = fmaxf(M, Mb);
@@ -1121,11 +1132,7 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float ob = __hip_atomic_load(po + ((ht * NDT + dt) * 4 + i) * (NW * CSA2_WAVE),
-                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    o[ht][dt][i] = o[ht][dt][i] * wai[i] + ob * wbi[i];
-                }
+                for (int i = 0; i < 4; ++i) o[ht][dt][i] = o[ht][dt][i] * wai[i] + obv[ht][dt][i] * wbi[i];
         }
     }
     const bool whole = S <= 2;   // this workgroup writes the normalised output
