@@ -407,7 +407,8 @@ def test_sparse_attn_phys_matches_packed_and_oracle(name, lengths, D, H, K, W, p
 
 def test_sparse_attn_phys_cache_beyond_2gib():
     """Cache rows past 2^31 bytes of codes (9.4M rows at D = 512): the row form
-    reads them through 64-bit addresses and matches the packed call."""
+    reads them through 64-bit addresses, matches the packed call and meets the
+    oracle's outputs."""
     lengths = [3000, 5000]
     D, H, K, W, pr = 512, 16, 128, 32, 64
     wl = small_workload(lengths, D=D, H=H, W=W, Hi=8, Di=64)
@@ -434,6 +435,9 @@ def test_sparse_attn_phys_cache_beyond_2gib():
                                               W, scale)
     torch.cuda.synchronize()
     assert torch.equal(out_f, out_p) and torch.equal(lse_f, lse_p)
+    ref = oracle_attn_rows(wl, {r: topk[r] for r in range(2)}, 0, [0, 1], W, scale)
+    check_attn(np_(out_f), np.stack([ref[r][0] for r in range(2)]), np_(lse_f),
+               np.stack([ref[r][1] for r in range(2)]), what="rows beyond 2 GiB")
 
 
 @pytest.mark.parametrize("cid", [1, 2])
