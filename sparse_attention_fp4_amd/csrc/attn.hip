@@ -144,8 +144,10 @@ struct FragRaw {
     {
         valid = vm;
         is_main = true;
+        // (words KS .. 2 KS - 1 hold FP8 bytes of window rows only: nothing
+        // reads them for a main entry)
 #pragma unroll
-        for (int k = 0; k < 2 * KS; ++k) raw[k] = 0u;
+        for (int k = 0; k < KS; ++k) raw[k] = 0u;
 #pragma unroll
         for (int w = 0; w < NSC; ++w) sc[w] = 0u;
         if (vm) {
@@ -563,7 +565,8 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
     __shared__ float4 fmx[NH][NW / 4];   // per head: each slot's largest logit of the head
     __shared__ float wsum[2][NW][NH];    // at the end: each wave's sums (PV weights, unrounded)
     __shared__ uint32_t wqm[NW][NH];     // per wave: bf16 bits of the max |q| of each head over its pieces
-    __shared__ __attribute__((aligned(16))) int fprec[NW];   // per slot: exact scores, two-part probabilities
+    __shared__ __attribute__((aligned(16))) uint32_t fprec[NW];   // per slot: its bit if the slot is precise (exact
+                                                                  // scores, two-part probabilities), else 0
     _Float16* const vtiles = reinterpret_cast<_Float16*>(smem);
     f16x8* const qa_s = reinterpret_cast<f16x8*>(smem + SM::kVBytes);                  // [HT * KS][64]
     f16x4* const p_s = reinterpret_cast<f16x4*>(smem + SM::kVBytes + SM::kQaBytes);   // [slot][2][HT][64]
@@ -915,15 +918,15 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
             mx = max_xor32(max_xor16(mx));
             if (grp == 0) reinterpret_cast<float*>(fmx[ht * 16 + col])[wave] = mx;
         }
-        if (lane == 0) fprec[wave] = precise ? 1 : 0;
+        if (lane == 0) fprec[wave] = precise ? 1u << wave : 0u;
         __syncthreads();   // the round's V tiles, maxima and flags
         // The round's precise slots as one mask, their flags read together
         // (a read per slot ahead of its branch would chain the LDS latencies).
         uint32_t pmask = 0u;
 #pragma unroll
         for (int w4 = 0; w4 < NW / 4; ++w4) {
-            const int4 f = reinterpret_cast<const int4*>(fprec)[w4];
-            pmask |= ((f.x ? 1u : 0u) | (f.y ? 2u : 0u) | (f.z ? 4u : 0u) | (f.w ? 8u : 0u)) << (4 * w4);
+            const uint4 f = reinterpret_cast<const uint4*>(fprec)[w4];
+            pmask |= f.x | f.y | f.z | f.w;
         }
         pmask = __builtin_amdgcn_readfirstlane(pmask) & ((1u << nslot) - 1u);
 
