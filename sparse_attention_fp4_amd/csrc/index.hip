@@ -941,14 +941,27 @@ __device__ __forceinline__ void radix_select2(SelShared& sh, int& phase, const S
     }
 }
 
-// Ordered compaction: emit(pos, item, key, pre(round)) for the selected
-// items in item order; pre(rd) is read once per thread and round, before the
-// (divergent) emits, so that no emit waits on a load of its own.  A thread
-// counts the keys above the threshold and those equal to it among its items;
-// one block scan of the packed counts per round gives every
-// thread the number of selected items before its own (all keys above, plus the
-// first `need` equal keys: ties go to the lowest item), and the thread then
-// writes its items in order.  Returns the number selected.
+// The lowest n set bits of m (n <= popcount(m)).
+__device__ __forceinline__ uint32_t lowest_bits(uint32_t m, int n)
+{
+    if (n >= __builtin_popcount(m)) return m;
+    uint32_t r = 0u;
+    for (int k = 0; k < n; ++k) {
+        r |= m & (0u - m);
+        m &= m - 1u;
+    }
+    return r;
+}
+
+// Ordered compaction: emit(pos, item, pre(round)) for the selected items in
+// item order; pre(rd) is read once per thread and round, before the emits,
+// so that no emit waits on a load of its own.  A thread marks the keys above
+// the threshold and those equal to it among its items (two bit masks); one
+// block scan of the packed counts per round gives every thread the number of
+// selected items before its own (all keys above, plus the first `need` equal
+// keys: ties go to the lowest item), and the thread then writes its selected
+// items in order, visiting only the set bits (most threads of a round hold
+// none).  Returns the number selected.
 template <class Src, class Emit, class Pre>
 __device__ __forceinline__ int select_compact(SelShared& sh, int& phase, const Src& src, const RegKeys& reg,
                                               SelState st, Emit emit, Pre pre)
@@ -956,26 +969,25 @@ __device__ __forceinline__ int select_compact(SelShared& sh, int& phase, const S
     int gt_run = 0, eq_run = 0;
     for_rounds(src, reg, [&](int rd, const uint32_t (&key)[kE]) {
         const int pv = pre(rd);
-        int gt = 0, eq = 0;
+        uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
             const uint32_t mk = key[e] & st.mask;
-            gt += (key[e] && mk > st.prefix) ? 1 : 0;
-            eq += (key[e] && mk == st.prefix) ? 1 : 0;
+            gtm |= (key[e] && mk > st.prefix) ? 1u << e : 0u;
+            eqm |= (key[e] && mk == st.prefix) ? 1u << e : 0u;
         }
+        const int gt = __builtin_popcount(gtm), eq = __builtin_popcount(eqm);
         int before;
         const int total = block_excl_sum(sh, phase, (gt << 16) | eq, before);   // counts <= kRound < 2^15
         const int gt_before = gt_run + (before >> 16), eq_before = eq_run + (before & 0xFFFF);
         int out = gt_before + (eq_before < st.need ? eq_before : st.need);
-        int eq_seen = eq_before;
+        const int take = st.need - eq_before;   // equal keys this thread may still take
+        uint32_t sel = gtm | (take <= 0 ? 0u : lowest_bits(eqm, take));
         const int i0 = rd * kRound + (int)threadIdx.x * kE;
-#pragma unroll
-        for (int e = 0; e < kE; ++e) {
-            const uint32_t mk = key[e] & st.mask;
-            const bool is_gt = key[e] && mk > st.prefix, is_eq = key[e] && mk == st.prefix;
-            const bool sel = is_gt || (is_eq && eq_seen < st.need);
-            if (sel) emit(out++, i0 + e, key[e], pv);
-            eq_seen += is_eq ? 1 : 0;
+        while (sel != 0u) {
+            const int e = __builtin_ctz(sel);
+            sel &= sel - 1u;
+            emit(out++, i0 + e, pv);
         }
         gt_run += total >> 16;
         eq_run += total & 0xFFFF;
@@ -993,31 +1005,35 @@ __device__ __forceinline__ int2 select_compact2(SelShared& sh, int& phase, const
 {
     int gta_run = 0, eqa_run = 0, gtb_run = 0, eqb_run = 0;
     for_rounds(src, reg, [&](int rd, const uint32_t (&key)[kE]) {
-        int gta = 0, eqa = 0, gtb = 0, eqb = 0;
+        uint32_t gam = 0u, eam = 0u, gbm = 0u, ebm = 0u;
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
             const uint32_t ma = key[e] & sa.mask, mb = key[e] & sb.mask;
-            gta += (key[e] && ma > sa.prefix) ? 1 : 0;
-            eqa += (key[e] && ma == sa.prefix) ? 1 : 0;
-            gtb += (key[e] && mb > sb.prefix) ? 1 : 0;
-            eqb += (key[e] && mb == sb.prefix) ? 1 : 0;
+            gam |= (key[e] && ma > sa.prefix) ? 1u << e : 0u;
+            eam |= (key[e] && ma == sa.prefix) ? 1u << e : 0u;
+            gbm |= (key[e] && mb > sb.prefix) ? 1u << e : 0u;
+            ebm |= (key[e] && mb == sb.prefix) ? 1u << e : 0u;
         }
+        const int gta = __builtin_popcount(gam), eqa = __builtin_popcount(eam);
+        const int gtb = __builtin_popcount(gbm), eqb = __builtin_popcount(ebm);
         int bfa, bfb, tta, ttb;
         block_excl_sum2(sh, phase, (gta << 16) | eqa, (gtb << 16) | eqb, bfa, bfb, tta, ttb);   // counts < 2^15
         const int gta_b = gta_run + (bfa >> 16), eqa_b = eqa_run + (bfa & 0xFFFF);
         const int gtb_b = gtb_run + (bfb >> 16), eqb_b = eqb_run + (bfb & 0xFFFF);
         int outa = gta_b + (eqa_b < sa.need ? eqa_b : sa.need), outb = gtb_b + (eqb_b < sb.need ? eqb_b : sb.need);
-        int eqa_seen = eqa_b, eqb_seen = eqb_b;
+        const int take_a = sa.need - eqa_b, take_b = sb.need - eqb_b;
+        uint32_t sel_a = gam | (take_a <= 0 ? 0u : lowest_bits(eam, take_a));
+        uint32_t sel_b = gbm | (take_b <= 0 ? 0u : lowest_bits(ebm, take_b));
         const int i0 = rd * kRound + (int)threadIdx.x * kE;
-#pragma unroll
-        for (int e = 0; e < kE; ++e) {
-            const uint32_t ma = key[e] & sa.mask, mb = key[e] & sb.mask;
-            const bool a_gt = key[e] && ma > sa.prefix, a_eq = key[e] && ma == sa.prefix;
-            const bool b_gt = key[e] && mb > sb.prefix, b_eq = key[e] && mb == sb.prefix;
-            if (a_gt || (a_eq && eqa_seen < sa.need)) emit_a(outa++, i0 + e);
-            if (b_gt || (b_eq && eqb_seen < sb.need)) emit_b(outb++, i0 + e);
-            eqa_seen += a_eq ? 1 : 0;
-            eqb_seen += b_eq ? 1 : 0;
+        while (sel_a != 0u) {
+            const int e = __builtin_ctz(sel_a);
+            sel_a &= sel_a - 1u;
+            emit_a(outa++, i0 + e);
+        }
+        while (sel_b != 0u) {
+            const int e = __builtin_ctz(sel_b);
+            sel_b &= sel_b - 1u;
+            emit_b(outb++, i0 + e);
         }
         gta_run += tta >> 16;
         eqa_run += tta & 0xFFFF;
@@ -1028,7 +1044,6 @@ __device__ __forceinline__ int2 select_compact2(SelShared& sh, int& phase, const
     return make_int2(gta_run + (eqa_run < sa.need ? eqa_run : sa.need), gtb_run + (eqb_run < sb.need ? eqb_run : sb.need));
 }
 
-// Bitonic sort (ascending) of n_pow2 64-bit keys in LDS.
 __device__ void bitonic_sort(unsigned long long* a, int n_pow2)
 {
     for (int k = 2; k <= n_pow2; k <<= 1) {
@@ -1183,7 +1198,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
                 nsm = nn.y < small ? nn.y : small;
             } else {
                 sa = radix_select(L.sh, phase, src, rg, big);
-                na = select_compact(L.sh, phase, src, rg, sa, [&](int pos, int i, uint32_t, int) {
+                na = select_compact(L.sh, phase, src, rg, sa, [&](int pos, int i, int) {
                     if (pos < big) L.blocks[pos] = id(i);
                 }, [](int) { return 0; });
                 na = na < big ? na : big;
@@ -1375,7 +1390,7 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
     // (a thread's kE items of a round are the 8 positions of one candidate
     // block: its id is read once per round)
     static_assert(kE == 8, "one candidate block per thread and round");
-    int nk = select_compact(L.sh, phase, csrc, reg, st, [&](int pos, int c, uint32_t, int blk) {
+    int nk = select_compact(L.sh, phase, csrc, reg, st, [&](int pos, int c, int blk) {
         if (pos < K) sel_ids[pos] = blk * 8 + (c & 7);
     }, [&](int rd) {
         const int cb = rd * kSelThreads + (int)threadIdx.x;
