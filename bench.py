@@ -56,16 +56,16 @@ MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp16": 2500.0}   # dense, MI355X
 # were taken on).  Reported as null whenever that source has changed since.
 TRAFFIC = {
     # profiles/sparse_attn_decode_64k.md: k_sparse_attn per call (two key splits merged in the kernel)
-    (2, "sparse_attn", "a62557f6c8883823"): 23495680,
+    (2, "sparse_attn", "b34ebecfa6f7958c"): 23492608,
     # profiles/sparse_attn_prefill_4096x135k.md: k_sparse_attn per call (four-wave workgroups)
-    (4, "sparse_attn", "a62557f6c8883823"): 1562032435,
+    (4, "sparse_attn", "b34ebecfa6f7958c"): 1562216550,
     # profiles/index_full_decode_64k.md: k_index_score (Full) + k_select (Full) per call
-    (2, "index_full", "873020afc9d93890"): 284830000,
+    (2, "index_full", "6efd787f3eacfebd"): 284797850,
     # profiles/index_reindex_decode_64k.md: k_index_score (Reindex) + k_select (Reindex) per call
-    (2, "index_reindex", "873020afc9d93890"): 74530000,
+    (2, "index_reindex", "6efd787f3eacfebd"): 74490163,
     # profiles/index_full_prefill_4096x135k.md: k_index_bmax + k_select (blocks) + k_index_score (rescoring)
     # + k_select (Top-K), twice (two batches of 2,048 rows) per call
-    (4, "index_full", "873020afc9d93890"): 1918400000,
+    (4, "index_full", "6efd787f3eacfebd"): 1918335795,
 }
 CALL_SOURCE = {"sparse_attn": "attn.hip", "index_full": "index.hip", "index_reindex": "index.hip",
                "quantize_append": "quantize.hip"}
