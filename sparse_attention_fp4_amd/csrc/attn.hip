@@ -251,6 +251,7 @@ __device__ __forceinline__ void v_store(_Float16* vrow, int grp, int t, f16x8 kf
 // described at the top of the file).
 template <int HT, int D>
 struct QueryRegs {   // the query in registers, the a-parts in LDS ([HT * KS][64])
+    static constexpr bool kPackedSub = true;   // b-parts by packed adds (eight waves: registers to spare)
     const f16x8 (&qf)[HT][D / 32];
     const f16x8* qa;
     __device__ __forceinline__ f16x8 q(int ht, int t) const { return qf[ht][t]; }
@@ -266,6 +267,7 @@ __device__ __forceinline__ float a_part_const(float m)
 }
 template <int HT, int D>
 struct QueryRegsC {   // the query in registers, the a-parts formed from it
+    static constexpr bool kPackedSub = false;   // (four waves: the compiler's form schedules better at their budget)
     const f16x8 (&qf)[HT][D / 32];
     const float (&C)[HT];   // per head tile: the rounding constant 1.5 * 2^(E + 12) of the a-part
     __device__ __forceinline__ f16x8 q(int ht, int t) const { return qf[ht][t]; }
@@ -284,6 +286,7 @@ struct QueryRegsC {   // the query in registers, the a-parts formed from it
 };
 template <int HT, int D>
 struct QueryLds {    // the query in LDS ([HT * KS][64]); a-parts formed from it
+    static constexpr bool kPackedSub = true;
     const f16x8* qs;
     const float (&C)[HT];   // per head tile: the rounding constant 1.5 * 2^(E + 12) of the a-part
     __device__ __forceinline__ f16x8 q(int ht, int t) const { return qs[(ht * (D / 32) + t) * CSA2_WAVE]; }
@@ -322,6 +325,18 @@ __device__ __forceinline__ void v_frag(const FragRaw<D>& fr, _Float16* vrow, int
 // The same fragment with S computed exactly as (hi, lo) = K a^T + K b^T
 // (split of q described at the top of the file); b = q - a is an exact fp16
 // subtraction (the difference is q's bits below the quantum of a).
+// x - y on eight fp16 values as four packed adds of x and -y (the compiler
+// splits a vector fp16 subtraction into single-half subtractions and packs).
+__device__ __forceinline__ f16x8 sub_f16x8(f16x8 x, f16x8 y)
+{
+    const u32x4 xw = __builtin_bit_cast(u32x4, x), yw = __builtin_bit_cast(u32x4, y);
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        asm("v_pk_add_f16 %0, %1, %2 neg_lo:[0,1] neg_hi:[0,1]" : "=v"(r[i]) : "v"(xw[i]), "v"(yw[i]));
+    return __builtin_bit_cast(f16x8, r);
+}
+
 template <int HT, int D, class QS>
 __device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const QS& qs, _Float16* vrow, int grp,
                                              f32x4 (&acc)[HT], f32x4 (&lo)[HT])
@@ -347,7 +362,8 @@ __device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const QS& qs,
             v_store<D>(vrow, grp, t, kf0);
             v_store<D>(vrow, grp, t + 1, kf1);
             const f16x8 a0 = qs.a(0, t), a1 = qs.a(0, t + 1);
-            const f16x8 b0 = qs.q(0, t) - a0, b1 = qs.q(0, t + 1) - a1;
+            const f16x8 b0 = QS::kPackedSub ? sub_f16x8(qs.q(0, t), a0) : qs.q(0, t) - a0;
+            const f16x8 b1 = QS::kPackedSub ? sub_f16x8(qs.q(0, t + 1), a1) : qs.q(0, t + 1) - a1;
             sb[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf0, b0, sb[0], 0, 0, 0);
             sb[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf1, b1, sb[0], 0, 0, 0);
 #pragma unroll
@@ -368,7 +384,7 @@ __device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const QS& qs,
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
                 const f16x8 a = qs.a(ht, t);
-                const f16x8 b = qs.q(ht, t) - a;
+                const f16x8 b = QS::kPackedSub ? sub_f16x8(qs.q(ht, t), a) : qs.q(ht, t) - a;
                 sb[ht] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, b, sb[ht], 0, 0, 0);
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
