@@ -107,7 +107,7 @@ struct FragRaw {
     uint32_t raw[2 * KS];
     uint32_t sc[NSC];
     _Float16 sp[KS / 2];   // the lane's scale groups as fp16 (set by scales_f16())
-    bool valid, is_main;
+    bool valid;
 
     // SWA row i of the lane's slot (vs: the slot holds one) through rw, the
     // buffer over the row's window: the lane's quarter of the row (D/4
@@ -116,7 +116,6 @@ struct FragRaw {
     __device__ __forceinline__ void load_swa(bool vs, int i, int grp, __amdgpu_buffer_rsrc_t rw)
     {
         valid = vs;
-        is_main = false;
         const uint32_t off1 = vs ? (uint32_t)i * D + (D / 4) * grp : kNoKey;
 #pragma unroll
         for (int u = 0; u < KS / 2; ++u) {
@@ -143,7 +142,6 @@ struct FragRaw {
     __device__ __forceinline__ void load_row(bool vm, int j, int grp, const uint8_t* codes, const uint8_t* scales)
     {
         valid = vm;
-        is_main = true;
         // (words KS .. 2 KS - 1 hold FP8 bytes of window rows only: nothing
         // reads them for a main entry)
 #pragma unroll
@@ -194,16 +192,17 @@ struct FragRaw {
     template <int KIND>
     __device__ __forceinline__ bool big() const
     {
-        uint32_t bm = 0u, bs = 0u;   // both reductions in full, then one select
-        if (KIND != 1) {
+        static_assert(KIND == 0 || KIND == 1, "a fragment holds one kind of slot");
+        uint32_t bm = 0u, bs = 0u;
+        if (KIND == 0) {
 #pragma unroll
             for (int w = 0; w < NSC; ++w) bm |= ((sc[w] & 0x7F7F7F7Fu) + 0x45454545u) & 0x80808080u;
         }
-        if (KIND != 0) {
+        if (KIND == 1) {
 #pragma unroll
             for (int w = 0; w < 2 * KS; ++w) bs |= ((raw[w] & 0x7F7F7F7Fu) + 0x30303030u) & 0x80808080u;
         }
-        const uint32_t bits = KIND == 0 ? bm : (KIND == 1 ? bs : (is_main ? bm : bs));
+        const uint32_t bits = KIND == 0 ? bm : bs;
         return valid && bits != 0u;
     }
 };
@@ -211,13 +210,13 @@ struct FragRaw {
 // Dequantise k-step t (8 channels) of the lane's key to fp16.
 //   MODE 0: FP4 codes (word t) times the group's E4M3 scale (scale byte t/2
 //           of the lane's KS/2 scale bytes);
-//   MODE 1: FP8 E4M3 bytes (words 2t, 2t+1), unscaled;
-//   MODE 2: either, chosen per lane.
+//   MODE 1: FP8 E4M3 bytes (words 2t, 2t+1), unscaled.
 template <int MODE, int D>
 __device__ __forceinline__ f16x8 dequant_step(const FragRaw<D>& fr, int t)
 {
+    static_assert(MODE == 0 || MODE == 1, "a fragment holds one kind of slot");
     f16x8 a, b;
-    if (MODE != 1) {
+    if (MODE == 0) {
         const uint32_t c = fr.raw[t];
         const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0);
         const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1);
@@ -226,7 +225,7 @@ __device__ __forceinline__ f16x8 dequant_step(const FragRaw<D>& fr, int t)
         const _Float16 s = fr.sp[t >> 1];
         a = (f16x8){a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]} * s;
     }
-    if (MODE != 0) {
+    if (MODE == 1) {
         const uint32_t c0 = fr.raw[2 * t], c1 = fr.raw[2 * t + 1];
         const f16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, false);
         const f16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c0, 1.0f, true);
@@ -234,9 +233,8 @@ __device__ __forceinline__ f16x8 dequant_step(const FragRaw<D>& fr, int t)
         const f16x2 b3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(c1, 1.0f, true);
         b = (f16x8){b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
     }
-    if (MODE == 0) return a;
-    if (MODE == 1) return b;
-    return fr.is_main ? a : b;
+    if constexpr (MODE == 0) return a;
+    else return b;
 }
 
 // Store k-step t of the lane's key to its row (vrow) of the wave's V tile.
@@ -322,9 +320,6 @@ __device__ __forceinline__ void v_frag(const FragRaw<D>& fr, _Float16* vrow, int
     for (int t = 0; t < D / 32; ++t) v_store<D>(vrow, grp, t, dequant_step<MODE, D>(fr, t));
 }
 
-// The same fragment with S computed exactly as (hi, lo) = K a^T + K b^T
-// (split of q described at the top of the file); b = q - a is an exact fp16
-// subtraction (the difference is q's bits below the quantum of a).
 // x - y on eight fp16 values as four packed adds of x and -y (the compiler
 // splits a vector fp16 subtraction into single-half subtractions and packs).
 __device__ __forceinline__ f16x8 sub_f16x8(f16x8 x, f16x8 y)
@@ -337,7 +332,12 @@ __device__ __forceinline__ f16x8 sub_f16x8(f16x8 x, f16x8 y)
     return __builtin_bit_cast(f16x8, r);
 }
 
-template <int HT, int D, class QS>
+// The same fragment with S computed exactly as (hi, lo) = K a^T + K b^T
+// (split of q described at the top of the file); b = q - a is an exact fp16
+// subtraction (the difference is q's bits below the quantum of a).  MODE: the
+// fragment's kind, as in dequant_step.
+
+template <int MODE, int HT, int D, class QS>
 __device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const QS& qs, _Float16* vrow, int grp,
                                              f32x4 (&acc)[HT], f32x4 (&lo)[HT])
 {
@@ -358,7 +358,7 @@ __device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const QS& qs,
     if constexpr (HT == 1) {
 #pragma unroll
         for (int t = 0; t < KS; t += 2) {
-            const f16x8 kf0 = dequant_step<2, D>(fr, t), kf1 = dequant_step<2, D>(fr, t + 1);
+            const f16x8 kf0 = dequant_step<MODE, D>(fr, t), kf1 = dequant_step<MODE, D>(fr, t + 1);
             v_store<D>(vrow, grp, t, kf0);
             v_store<D>(vrow, grp, t + 1, kf1);
             const f16x8 a0 = qs.a(0, t), a1 = qs.a(0, t + 1);
@@ -379,7 +379,7 @@ __device__ __forceinline__ void s_frag_exact(const FragRaw<D>& fr, const QS& qs,
     } else {
 #pragma unroll
         for (int t = 0; t < KS; ++t) {
-            const f16x8 kf = dequant_step<2, D>(fr, t);
+            const f16x8 kf = dequant_step<MODE, D>(fr, t);
             v_store<D>(vrow, grp, t, kf);
 #pragma unroll
             for (int ht = 0; ht < HT; ++ht) {
@@ -918,7 +918,8 @@ __global__ __launch_bounds__(CSA2_WAVE * NW, NW == kWaves ? 1 : 2) void k_sparse
                 }
             }
             if (nat) v_frag<0, D>(cur, vrow, grp);
-            else if (precise) s_frag_exact<HT, D>(cur, qsrc, vrow, grp, sh, sl);
+            else if (precise && kind == 0) s_frag_exact<0, HT, D>(cur, qsrc, vrow, grp, sh, sl);
+            else if (precise) s_frag_exact<1, HT, D>(cur, qsrc, vrow, grp, sh, sl);
             else if (kind == 0) s_frag<0, HT, D>(cur, qsrc, vrow, grp, sh);
             else s_frag<1, HT, D>(cur, qsrc, vrow, grp, sh);
             // S^T lane layout: head h0 + 16 ht + col, keys 4 grp + i.
