@@ -56,9 +56,9 @@ MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "fp16": 2500.0}   # dense, MI355X
 # were taken on).  Reported as null whenever that source has changed since.
 TRAFFIC = {
     # profiles/sparse_attn_decode_64k.md: k_sparse_attn per call (two key splits merged in the kernel)
-    (2, "sparse_attn", "b34ebecfa6f7958c"): 23492608,
+    (2, "sparse_attn", "9971ea8daa8c5e19"): 23518208,
     # profiles/sparse_attn_prefill_4096x135k.md: k_sparse_attn per call (four-wave workgroups)
-    (4, "sparse_attn", "b34ebecfa6f7958c"): 1562216550,
+    (4, "sparse_attn", "9971ea8daa8c5e19"): 1562454118,
     # profiles/index_full_decode_64k.md: k_index_score (Full) + k_select (Full) per call
     (2, "index_full", "6efd787f3eacfebd"): 284797850,
     # profiles/index_reindex_decode_64k.md: k_index_score (Reindex) + k_select (Reindex) per call
