@@ -426,6 +426,38 @@ def test_sparse_attn_matches_oracle(name, lengths, D, H, K, W):
                what=name)
 
 
+@pytest.mark.parametrize("name,lengths,D,H,K,W,kv", [
+    # eight waves, two key splits per row
+    ("d512_h64_split_rows", [9000, 3000, 20000], 512, 64, 512, 128, "normal"),
+    # eight waves, outliers in the main cache too
+    ("d512_h64_student_outliers", [700 + 31 * i for i in range(40)], 512, 64, 512, 128, "student_t_outliers"),
+    # four-wave workgroups (520 rows x 4 head groups = 2,080 groups)
+    ("d512_h64_four_waves", [300 + (37 * i) % 900 for i in range(520)], 512, 64, 512, 128, "normal"),
+])
+def test_sparse_attn_large_window_values(name, lengths, D, H, K, W, kv):
+    """Window rows with FP8 values of magnitude 8 and above (most bytes of
+    24 x N(0,1)), so window fragments take the exact-score path: checked
+    against the oracle on every row (or a seeded sample of many rows)."""
+    log(f"sparse_attn large window values: {name}")
+    wl = with_cache(small_workload(lengths, Hi=8, Di=64, D=D, H=H, W=W, layers="F", kv_dist=kv))
+    g = torch.Generator(device=DEV)
+    g.manual_seed(len(name))
+    wl.swa[0] = workloads.to_e4m3_bytes(24.0 * torch.randn(wl.swa[0].shape, generator=g, device=DEV))
+    assert int(((wl.swa[0] & 0x7F) >= 0x50).sum()) > wl.swa[0].numel() // 2   # |v| >= 8 in most bytes
+    R = len(lengths)
+    rng = np.random.default_rng(len(name))
+    topk = np.full((R, K), -1, np.int32)
+    for r, n in enumerate(lengths):
+        k = min(K, n)
+        topk[r, :k] = np.sort(rng.choice(n, k, replace=False))
+    scale = 1.0 / math.sqrt(D)
+    out, lse = run_attn(wl, 0, torch.tensor(topk, device=DEV), W, scale)
+    rows = list(range(R)) if R <= 40 else sorted(set([0, R - 1] + rng.choice(R, 14, replace=False).tolist()))
+    ref = oracle_attn_rows(wl, {r: topk[r] for r in rows}, 0, rows, W, scale)
+    check_attn(out[rows], np.stack([ref[r][0] for r in rows]), lse[rows], np.stack([ref[r][1] for r in rows]),
+               what=name)
+
+
 @pytest.mark.parametrize("name,D,H,rows,K,W,kv", [
     ("d512_h64_2080_groups", 512, 64, 520, 512, 128, "normal"),
     ("d512_h64_2080_groups_student_outliers", 512, 64, 520, 512, 128, "student_t_outliers"),
